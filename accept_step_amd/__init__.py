@@ -1,0 +1,306 @@
+"""Python binding of the verify-step library ``libspecverify.so``.
+
+Argument marshalling only: every step of the verify pass (logits, row
+statistics, acceptance, resampling, cache-length commit) runs in the HIP
+library behind the C ABI declared in ``include/specverify.h``.  torch supplies
+device memory and streams.  The binding fails loudly when the library is
+missing or a call returns an error; it has no fallback path.
+
+Functions mirror the C entry points: :func:`verify_forward`,
+:func:`spec_verify_greedy`, :func:`spec_verify_sample`.
+"""
+import ctypes
+import os
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import torch
+
+__all__ = ["SV_F32", "SV_BF16", "SV_IN_LOGITS", "SV_IN_HIDDEN", "SV_IN_TOKENS", "VerifyError",
+           "Model", "KVCache", "Workspace", "lm_head_model", "logits_model", "decoder_model",
+           "verify_forward", "spec_verify_greedy", "spec_verify_sample", "library", "library_path",
+           "timing_enable", "timing_read", "LAYER_KEYS"]
+
+SV_F32, SV_BF16 = 0, 1
+SV_IN_LOGITS, SV_IN_HIDDEN, SV_IN_TOKENS = 0, 1, 2
+LAYER_KEYS = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path():
+    return os.path.join(_HERE, "libspecverify.so")
+
+
+class VerifyError(RuntimeError):
+    """A non-zero status returned by the library."""
+
+    def __init__(self, status, name, message):
+        super().__init__(f"{name}: {message}")
+        self.status = status
+
+
+class _SvModel(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("wdtype", ctypes.c_int32), ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
+                ("embed", ctypes.c_void_p), ("layers", ctypes.POINTER(ctypes.c_void_p)),
+                ("final_norm", ctypes.c_void_p), ("lm_head", ctypes.c_void_p)]
+
+
+class _SvKV(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("max_len", ctypes.c_int32),
+                ("len", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def library():
+    """Load ``libspecverify.so`` (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m accept_step_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)
+    M, KV = ctypes.POINTER(_SvModel), ctypes.POINTER(_SvKV)
+    lib.verify_forward.argtypes = [M, i32, vp, i32, i32, KV, vp, vp, sz, vp]
+    lib.spec_verify_greedy.argtypes = [M, i32, vp, i32, i32, vp, KV, vp, vp, vp, vp, sz, vp]
+    lib.spec_verify_sample.argtypes = [M, i32, vp, i32, i32, vp, vp, i32, ctypes.c_float, ctypes.c_uint64, vp,
+                                       KV, vp, vp, vp, vp, sz, vp]
+    for f in (lib.verify_forward, lib.spec_verify_greedy, lib.spec_verify_sample, lib.sv_timing_enable,
+              lib.sv_timing_read):
+        f.restype = i32
+    lib.sv_version.restype = i32
+    lib.sv_status_string.restype = ctypes.c_char_p
+    lib.sv_status_string.argtypes = [i32]
+    lib.sv_last_error.restype = ctypes.c_char_p
+    lib.sv_timing_enable.argtypes = [i32]
+    lib.sv_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != 0:
+        lib = library()
+        raise VerifyError(status, lib.sv_status_string(status).decode(), lib.sv_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev_tensor(t, name, dtype=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    return t
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+@dataclass
+class Model:
+    """A target model for the library: the C struct plus the tensors it points to."""
+    struct: _SvModel
+    keep: list = field(default_factory=list)
+    layer_ptrs: Optional[ctypes.Array] = None
+
+    @property
+    def vocab(self):
+        return self.struct.vocab
+
+
+def logits_model(vocab):
+    """Model for SV_IN_LOGITS inputs (only the vocabulary size is read)."""
+    s = _SvModel()
+    s.vocab = int(vocab)
+    return Model(s)
+
+
+def lm_head_model(w):
+    """LM-head-only model from a [V, d] bfloat16 or float32 device tensor."""
+    _dev_tensor(w, "lm_head")
+    s = _SvModel()
+    s.n_layers = 0
+    s.vocab, s.d_model = int(w.shape[0]), int(w.shape[1])
+    if w.dtype == torch.bfloat16:
+        s.wdtype = SV_BF16
+    elif w.dtype == torch.float32:
+        s.wdtype = SV_F32
+    else:
+        raise ValueError("lm_head must be bfloat16 or float32")
+    s.lm_head = w.data_ptr()
+    return Model(s, [w])
+
+
+def decoder_model(embed, layers, final_norm, lm_head, n_heads, head_dim, rms_eps=1e-5, rope_theta=10000.0):
+    """Decoder model from bf16 device tensors; ``layers`` is a list of dicts keyed by LAYER_KEYS."""
+    keep = [embed, final_norm, lm_head]
+    for t, n in ((embed, "embed"), (final_norm, "final_norm"), (lm_head, "lm_head")):
+        _dev_tensor(t, n, torch.bfloat16)
+    ptrs = (ctypes.c_void_p * (9 * len(layers)))()
+    for i, L in enumerate(layers):
+        for j, key in enumerate(LAYER_KEYS):
+            t = _dev_tensor(L[key], key, torch.bfloat16)
+            keep.append(t)
+            ptrs[9 * i + j] = t.data_ptr()
+    s = _SvModel()
+    s.n_layers = len(layers)
+    s.d_model = int(embed.shape[1])
+    s.n_heads, s.head_dim = int(n_heads), int(head_dim)
+    s.d_ff = int(layers[0]["w_gate"].shape[0])
+    s.vocab = int(lm_head.shape[0])
+    s.wdtype = SV_BF16
+    s.rms_eps, s.rope_theta = float(rms_eps), float(rope_theta)
+    s.embed, s.final_norm, s.lm_head = embed.data_ptr(), final_norm.data_ptr(), lm_head.data_ptr()
+    s.layers = ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p))
+    return Model(s, keep, ptrs)
+
+
+@dataclass
+class KVCache:
+    """bf16 K/V [n_layers, B, n_heads, max_len, head_dim] and int32 lengths [B]."""
+    k: torch.Tensor
+    v: torch.Tensor
+    length: torch.Tensor
+
+    def struct(self):
+        for t, n in ((self.k, "k"), (self.v, "v")):
+            _dev_tensor(t, n, torch.bfloat16)
+        _dev_tensor(self.length, "length", torch.int32)
+        s = _SvKV()
+        s.k, s.v = self.k.data_ptr(), self.v.data_ptr()
+        s.max_len = int(self.k.shape[3])
+        s.len = self.length.data_ptr()
+        return s
+
+
+class Workspace:
+    """Caller-owned scratch for the library, grown on demand (one per device)."""
+
+    def __init__(self):
+        self.buf = None
+
+    def get(self, nbytes, device):
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
+            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        return self.buf
+
+
+_default_ws = {}
+
+
+def _workspace(ws, device):
+    if ws is not None:
+        return ws
+    key = device.index
+    if key not in _default_ws:
+        _default_ws[key] = Workspace()
+    return _default_ws[key]
+
+
+def _call_with_ws(fn, args_before_ws, device, ws, stream):
+    """Two-phase call: size query, then the real call."""
+    nbytes = ctypes.c_size_t(0)
+    _check(fn(*args_before_ws, None, ctypes.byref(nbytes), None))
+    buf = _workspace(ws, device).get(nbytes.value, device)
+    nbytes = ctypes.c_size_t(buf.numel())
+    _check(fn(*args_before_ws, ctypes.c_void_p(buf.data_ptr()), ctypes.byref(nbytes), _stream(stream)))
+
+
+def _kind_input(kind, inp):
+    dt = {SV_IN_LOGITS: torch.float32, SV_IN_TOKENS: torch.int32}.get(kind)
+    return _dev_tensor(inp, "input", dt)
+
+
+def verify_forward(model, kind, inp, B, gamma, kv=None, logits=None, ws=None, stream=None):
+    """Logits [B, gamma+1, V] float32 of all slots (C: verify_forward)."""
+    lib = library()
+    inp = _kind_input(kind, inp)
+    if logits is None:
+        logits = torch.empty((B, gamma + 1, model.vocab), dtype=torch.float32, device=inp.device)
+    _dev_tensor(logits, "logits", torch.float32)
+    kvs = kv.struct() if kv is not None else None
+    _call_with_ws(lib.verify_forward,
+                  (ctypes.byref(model.struct), kind, _ptr(inp), B, gamma,
+                   ctypes.byref(kvs) if kvs is not None else None, _ptr(logits)),
+                  inp.device, ws, stream)
+    return logits
+
+
+def _outs(B, gamma, device, out):
+    if out is not None:
+        n, tok = out
+        _dev_tensor(n, "n_accepted", torch.int32)
+        _dev_tensor(tok, "tokens_out", torch.int32)
+        return n, tok
+    return (torch.empty(B, dtype=torch.int32, device=device),
+            torch.empty((B, gamma + 1), dtype=torch.int32, device=device))
+
+
+def spec_verify_greedy(model, kind, inp, B, gamma, draft=None, kv=None, logits_out=None, out=None, ws=None,
+                       stream=None):
+    """Greedy verify (C: spec_verify_greedy).  Returns (n_accepted [B], tokens_out [B, gamma+1])."""
+    lib = library()
+    inp = _kind_input(kind, inp)
+    _dev_tensor(draft, "draft", torch.int32)
+    _dev_tensor(logits_out, "logits_out", torch.float32)
+    n, tok = _outs(B, gamma, inp.device, out)
+    kvs = kv.struct() if kv is not None else None
+    _call_with_ws(lib.spec_verify_greedy,
+                  (ctypes.byref(model.struct), kind, _ptr(inp), B, gamma, _ptr(draft),
+                   ctypes.byref(kvs) if kvs is not None else None, _ptr(n), _ptr(tok), _ptr(logits_out)),
+                  inp.device, ws, stream)
+    return n, tok
+
+
+def spec_verify_sample(model, kind, inp, B, gamma, draft, q, temperature, seed, pos0, kv=None, logits_out=None,
+                       out=None, ws=None, stream=None):
+    """Speculative-sampling verify (C: spec_verify_sample).  ``q`` is float32 or
+    bfloat16 [B, gamma, V]; ``pos0`` int64 [B].  Returns (n_accepted, tokens_out)."""
+    lib = library()
+    inp = _kind_input(kind, inp)
+    _dev_tensor(draft, "draft", torch.int32)
+    _dev_tensor(q, "q")
+    _dev_tensor(pos0, "pos0", torch.int64)
+    _dev_tensor(logits_out, "logits_out", torch.float32)
+    if q.dtype == torch.bfloat16:
+        qd = SV_BF16
+    elif q.dtype == torch.float32:
+        qd = SV_F32
+    else:
+        raise ValueError("q must be float32 or bfloat16")
+    n, tok = _outs(B, gamma, inp.device, out)
+    kvs = kv.struct() if kv is not None else None
+    _call_with_ws(lib.spec_verify_sample,
+                  (ctypes.byref(model.struct), kind, _ptr(inp), B, gamma, _ptr(draft), _ptr(q), qd,
+                   float(temperature), ctypes.c_uint64(int(seed)), _ptr(pos0),
+                   ctypes.byref(kvs) if kvs is not None else None, _ptr(n), _ptr(tok), _ptr(logits_out)),
+                  inp.device, ws, stream)
+    return n, tok
+
+
+def timing_enable(on=True):
+    """Start (clearing earlier records) or stop event timing of kernel classes."""
+    _check(library().sv_timing_enable(1 if on else 0))
+
+
+def timing_read(which):
+    """(total milliseconds, launches) recorded for class ``which``
+    (0 LM-head product, 1 decoder layers, 2 acceptance tail)."""
+    ms, cnt = ctypes.c_double(0), ctypes.c_int64(0)
+    _check(library().sv_timing_read(which, ctypes.byref(ms), ctypes.byref(cnt)))
+    return ms.value, cnt.value

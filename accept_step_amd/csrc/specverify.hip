@@ -1,0 +1,604 @@
+// specverify.hip -- host side of the verify-step library: argument checking,
+// workspace planning and the launch sequence behind the C ABI in specverify.h.
+//
+// One call = one verify pass ([Infra-ch8] "why one forward pass can verify several
+// tokens"): logits of all gamma+1 slots (LM-head product, or the full decoder
+// forward), the vocab-wide row statistics fused into the product's epilogue, then
+// the acceptance rule and -- for sampling -- the correction/bonus draw.  Everything
+// is enqueued on the caller's stream; nothing here synchronises or allocates.
+#include "specverify.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "sv_accept.hpp"
+#include "sv_decoder.hpp"
+#include "sv_device.hpp"
+#include "sv_gemm.hpp"
+
+using namespace sv;
+
+namespace {
+
+constexpr int32_t VERSION = 10000;   // 1.0.0
+constexpr size_t ALIGN = 256;
+constexpr int GEMM_WAVES = 4;
+constexpr int GEMM_MAX_WG = 2048;    // upper bound of workgroups along the vocabulary
+constexpr size_t GEMM_LDS_BUDGET = 64 * 1024;
+constexpr int SAMPLE_CHUNK = 4096;
+constexpr int ATT_SPLITS_MAX = 16;
+
+thread_local std::string g_err;
+
+sv_status fail(sv_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+#define SV_HIP(call)                                                                     \
+  do {                                                                                   \
+    hipError_t e_ = (call);                                                              \
+    if (e_ != hipSuccess) return fail(SV_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+// ---------------------------------------------------------------------------
+// device properties (per device, lazily)
+struct DevInfo {
+  int cus = 0;
+};
+std::mutex g_dev_mu;
+std::vector<DevInfo> g_dev;
+
+sv_status dev_info(DevInfo* out) {
+  int dev = 0;
+  SV_HIP(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (int(g_dev.size()) <= dev) g_dev.resize(dev + 1);
+  if (g_dev[dev].cus == 0) {
+    int cus = 0;
+    SV_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    g_dev[dev].cus = cus > 0 ? cus : 1;
+  }
+  *out = g_dev[dev];
+  return SV_OK;
+}
+
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  return v && *v ? atoi(v) : dflt;
+}
+
+// ---------------------------------------------------------------------------
+// timing with events on the caller's stream
+struct Timer {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  struct Rec { int which; hipEvent_t a, b; };
+  std::vector<Rec> recs;
+} g_timer;
+
+struct TimeScope {
+  hipStream_t s;
+  int which;
+  hipEvent_t a = nullptr, b = nullptr;
+  TimeScope(hipStream_t s_, int w) : s(s_), which(w) {
+    std::lock_guard<std::mutex> lk(g_timer.mu);
+    if (!g_timer.on) return;
+    for (hipEvent_t* e : {&a, &b}) {
+      if (!g_timer.pool.empty()) { *e = g_timer.pool.back(); g_timer.pool.pop_back(); }
+      else if (hipEventCreate(e) != hipSuccess) { *e = nullptr; }
+    }
+    if (a && b) (void)hipEventRecord(a, s);
+  }
+  ~TimeScope() {
+    if (!(a && b)) return;
+    (void)hipEventRecord(b, s);
+    std::lock_guard<std::mutex> lk(g_timer.mu);
+    g_timer.recs.push_back({which, a, b});
+  }
+};
+
+// ---------------------------------------------------------------------------
+// argument checks
+
+bool is_aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Shape {
+  int B, gamma, G1, M, V, d;
+  sv_input_kind kind;
+  bool decoder;
+};
+
+sv_status check_common(const sv_model* m, sv_input_kind kind, const void* input, int32_t B, int32_t gamma,
+                       const sv_kv_cache* kv, Shape* sh) {
+  if (!m) return fail(SV_ERR_ARG, "model is NULL");
+  if (!input) return fail(SV_ERR_ARG, "input is NULL");
+  if (B < 1) return fail(SV_ERR_ARG, "B must be >= 1 (got %d)", B);
+  if (gamma < 1 || gamma > 15) return fail(SV_ERR_ARG, "gamma must be in [1, 15] (got %d)", gamma);
+  if (m->vocab < 2) return fail(SV_ERR_ARG, "vocab must be >= 2 (got %d)", m->vocab);
+  if (int64_t(B) * (gamma + 1) > (int64_t(1) << 30)) return fail(SV_ERR_SHAPE, "B * (gamma + 1) too large");
+  if (int64_t(B) * (gamma + 1) * m->vocab > (int64_t(1) << 40)) return fail(SV_ERR_SHAPE, "logits too large");
+  if (int64_t(B) * ((m->vocab + 4095) / 4096) > 0x7fffffffLL) return fail(SV_ERR_SHAPE, "B * V too large");
+  if (kind != SV_IN_LOGITS && int64_t(B) * (gamma + 1) > 64LL * 65535)
+    return fail(SV_ERR_SHAPE, "B * (gamma + 1) must be <= %lld for model inputs", 64LL * 65535);
+  sh->B = B; sh->gamma = gamma; sh->G1 = gamma + 1; sh->M = B * (gamma + 1);
+  sh->V = m->vocab; sh->d = m->d_model; sh->kind = kind; sh->decoder = false;
+  switch (kind) {
+    case SV_IN_LOGITS:
+      if (!is_aligned(input, 4)) return fail(SV_ERR_ARG, "logits input must be 4-byte aligned");
+      break;
+    case SV_IN_HIDDEN:
+      if (m->n_layers != 0) return fail(SV_ERR_ARG, "SV_IN_HIDDEN needs an LM-head-only model (n_layers == 0)");
+      if (!m->lm_head) return fail(SV_ERR_ARG, "lm_head is NULL");
+      if (m->d_model < 1) return fail(SV_ERR_ARG, "d_model must be >= 1");
+      if (m->wdtype == SV_BF16) {
+        if (m->d_model % 32) return fail(SV_ERR_SHAPE, "bf16 LM head needs d_model %% 32 == 0 (got %d)", m->d_model);
+        if (!is_aligned(m->lm_head, 16) || !is_aligned(input, 16))
+          return fail(SV_ERR_ARG, "bf16 lm_head and hidden states must be 16-byte aligned");
+      } else if (m->wdtype == SV_F32) {
+        if (size_t(sh->M) * m->d_model * 4 > 48 * 1024)
+          return fail(SV_ERR_UNSUPPORTED, "float32 LM head supports M * d_model <= 12288 only");
+      } else {
+        return fail(SV_ERR_DTYPE, "unknown wdtype %d", int(m->wdtype));
+      }
+      break;
+    case SV_IN_TOKENS: {
+      if (m->n_layers < 1) return fail(SV_ERR_ARG, "SV_IN_TOKENS needs n_layers >= 1");
+      if (m->wdtype != SV_BF16) return fail(SV_ERR_DTYPE, "decoder weights must be bf16");
+      if (m->head_dim != 64 && m->head_dim != 128) return fail(SV_ERR_SHAPE, "head_dim must be 64 or 128");
+      if (m->n_heads < 1 || m->d_model < 32 || m->d_ff < 32) return fail(SV_ERR_ARG, "bad decoder dimensions");
+      if (m->d_model % 32 || m->d_ff % 32 || (m->n_heads * m->head_dim) % 32)
+        return fail(SV_ERR_SHAPE, "d_model, d_ff and n_heads * head_dim must be multiples of 32");
+      if (!m->embed || !m->layers || !m->final_norm || !m->lm_head) return fail(SV_ERR_ARG, "model pointer is NULL");
+      for (int i = 0; i < m->n_layers * 9; ++i) {
+        if (!m->layers[i]) return fail(SV_ERR_ARG, "layer pointer %d is NULL", i);
+        if (!is_aligned(m->layers[i], 16)) return fail(SV_ERR_ARG, "layer pointer %d is not 16-byte aligned", i);
+      }
+      if (!is_aligned(m->lm_head, 16) || !is_aligned(m->embed, 16)) return fail(SV_ERR_ARG, "weights must be 16-byte aligned");
+      if (!(m->rms_eps >= 0.0f) || !std::isfinite(m->rms_eps)) return fail(SV_ERR_ARG, "rms_eps must be finite and >= 0");
+      if (!(m->rope_theta > 0.0f) || !std::isfinite(m->rope_theta)) return fail(SV_ERR_ARG, "rope_theta must be finite and > 0");
+      if (!kv || !kv->k || !kv->v || !kv->len) return fail(SV_ERR_ARG, "SV_IN_TOKENS needs a KV cache");
+      if (kv->max_len < gamma + 1) return fail(SV_ERR_ARG, "kv max_len must be >= gamma + 1");
+      sh->decoder = true;
+      break;
+    }
+    default:
+      return fail(SV_ERR_ARG, "unknown input kind %d", int(kind));
+  }
+  return SV_OK;
+}
+
+// ---------------------------------------------------------------------------
+// GEMM planning
+struct GemmPlan {
+  int MB, mgroups, KC, grid_x_max;
+  size_t lds;
+};
+
+GemmPlan plan_gemm(int M, int N_total_tiles, int K) {
+  GemmPlan p;
+  const int mblocks = (M + 15) / 16;
+  p.MB = mblocks < 4 ? mblocks : 4;
+  p.mgroups = (mblocks + p.MB - 1) / p.MB;
+  const int rows = std::min(16 * p.MB, M);
+  int KC = K;
+  if (size_t(rows) * (K + 8) * 2 > GEMM_LDS_BUDGET) {
+    KC = int((GEMM_LDS_BUDGET / (size_t(rows) * 2) - 8) / 256 * 256);
+    if (KC < 256) KC = 256;
+  }
+  p.KC = KC;
+  size_t stage = size_t(rows) * (std::min(KC, K) + 8) * 2;
+  size_t stats = size_t(GEMM_WAVES) * 16 * p.MB * 12;
+  p.lds = std::max(stage, stats);
+  const int nblk = (N_total_tiles + GEMM_WAVES - 1) / GEMM_WAVES;
+  p.grid_x_max = std::min(nblk, GEMM_MAX_WG);
+  return p;
+}
+
+int gemm_grid_x(const GemmPlan& p, const DevInfo& di) {
+  const int per_cu = env_int("SV_GEMM_WG_PER_CU", 4);
+  int g = di.cus * (per_cu > 0 ? per_cu : 4);
+  return std::max(1, std::min(g, p.grid_x_max));
+}
+
+template <int MB>
+void launch_gemm_mb(const GemmArgs& a, dim3 grid, size_t lds, hipStream_t s) {
+  hipLaunchKernelGGL((k_gemm_bf16<MB, GEMM_WAVES>), grid, dim3(GEMM_WAVES * 64), lds, s, a);
+}
+
+sv_status launch_gemm(const GemmPlan& p, GemmArgs a, int grid_x, hipStream_t s) {
+  a.KC = p.KC;
+  dim3 grid(grid_x, p.mgroups);
+  switch (p.MB) {
+    case 1: launch_gemm_mb<1>(a, grid, p.lds, s); break;
+    case 2: launch_gemm_mb<2>(a, grid, p.lds, s); break;
+    case 3: launch_gemm_mb<3>(a, grid, p.lds, s); break;
+    default: launch_gemm_mb<4>(a, grid, p.lds, s); break;
+  }
+  SV_HIP(hipGetLastError());
+  return SV_OK;
+}
+
+GemmArgs gemm_args(const bf16_t* X, int M, int K) {
+  GemmArgs a;
+  memset(&a, 0, sizeof a);
+  a.X = X; a.M = M; a.K = K;
+  return a;
+}
+
+void gemm_add_seg(GemmArgs& a, const void* W, float* out, int N) {
+  const int i = a.nseg++;
+  a.W[i] = static_cast<const bf16_t*>(W);
+  a.out[i] = out;
+  a.N[i] = N;
+  a.tile_end[i] = (i ? a.tile_end[i - 1] : 0) + (N + 15) / 16;
+}
+
+// ---------------------------------------------------------------------------
+// workspace layout
+struct Layout {
+  size_t logits = 0, part = 0, state = 0, spart = 0, invalid = 0;
+  size_t rope = 0, x = 0, h = 0, q = 0, k = 0, v = 0, attp = 0, att = 0, gate = 0, up = 0;
+  size_t total = 0;
+  int P = 0;          // row-statistics partials per row
+  int nch = 0;        // sampling chunks per sequence
+  int S = 0;          // attention key splits
+  GemmPlan head;
+};
+
+struct Bump {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    size_t o = off;
+    off = align_up(off + std::max<size_t>(bytes, 1));
+    return o;
+  }
+};
+
+int att_splits(const sv_kv_cache* kv) {
+  int S = (kv->max_len + 255) / 256;
+  return std::max(1, std::min(S, ATT_SPLITS_MAX));
+}
+
+Layout plan(const sv_model* m, const Shape& sh, const sv_kv_cache* kv, bool need_logits_buf, bool sample) {
+  Layout L;
+  Bump b;
+  const int M = sh.M, V = sh.V;
+  if (need_logits_buf) L.logits = b.take(size_t(M) * V * 4);
+  if (sh.kind == SV_IN_LOGITS) {
+    L.P = (V + LCH - 1) / LCH;
+  } else if (sh.kind == SV_IN_HIDDEN && m->wdtype == SV_F32) {
+    L.P = (V + 255) / 256;
+  } else {
+    L.head = plan_gemm(M, (V + 15) / 16, sh.decoder ? m->d_model : sh.d);
+    L.P = L.head.grid_x_max;
+  }
+  L.part = b.take(size_t(L.P) * M * sizeof(RowPart));
+  L.state = b.take(size_t(sh.B) * sizeof(SeqState));
+  L.nch = (V + SAMPLE_CHUNK - 1) / SAMPLE_CHUNK;
+  if (sample) L.spart = b.take(size_t(sh.B) * L.nch * sizeof(SamplePart));
+  L.invalid = b.take(size_t(sh.B) * 4);
+  if (sh.decoder) {
+    const int d = m->d_model, HD = m->n_heads * m->head_dim, ff = m->d_ff;
+    L.S = att_splits(kv);
+    L.rope = b.take(size_t(M) * (m->head_dim / 2) * sizeof(float2));
+    L.x = b.take(size_t(M) * d * 4);
+    L.h = b.take(size_t(M) * std::max(std::max(d, ff), HD) * 2);
+    L.q = b.take(size_t(M) * HD * 4);
+    L.k = b.take(size_t(M) * HD * 4);
+    L.v = b.take(size_t(M) * HD * 4);
+    L.attp = b.take(size_t(sh.B) * m->n_heads * L.S * sh.G1 * (m->head_dim + 2) * 4);
+    L.att = b.take(size_t(M) * HD * 2);
+    L.gate = b.take(size_t(M) * ff * 4);
+    L.up = b.take(size_t(M) * ff * 4);
+  }
+  L.total = b.off;
+  return L;
+}
+
+template <class T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+sv_status check_ws(void* ws, size_t* ws_bytes, const Layout& L, bool* query) {
+  if (!ws_bytes) return fail(SV_ERR_ARG, "ws_bytes is NULL");
+  if (!ws) {
+    *ws_bytes = L.total;
+    *query = true;
+    return SV_OK;
+  }
+  *query = false;
+  if (*ws_bytes < L.total)
+    return fail(SV_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", *ws_bytes, L.total);
+  if (!is_aligned(ws, ALIGN)) return fail(SV_ERR_WORKSPACE, "workspace must be %zu-byte aligned", ALIGN);
+  return SV_OK;
+}
+
+// ---------------------------------------------------------------------------
+// forward passes
+
+// Full decoder up to (and including) the final RMSNorm: leaves bf16 h [M, d] in
+// the workspace.  [Infra-ch8] "why one forward pass can verify several tokens".
+sv_status run_decoder(const sv_model* m, const Shape& sh, const int* tokens, const sv_kv_cache* kv,
+                      const Layout& L, void* ws, const DevInfo& di, hipStream_t s) {
+  TimeScope ts(s, 1);
+  const int M = sh.M, d = m->d_model, H = m->n_heads, hd = m->head_dim, ff = m->d_ff, HD = H * hd;
+  DecArgs da;
+  da.B = sh.B; da.G1 = sh.G1; da.d = d; da.H = H; da.hd = hd; da.ff = ff; da.V = sh.V;
+  da.max_len = kv->max_len; da.n_layers = m->n_layers; da.eps = m->rms_eps;
+  int* invalid = at<int>(ws, L.invalid);
+  float2* rope = at<float2>(ws, L.rope);
+  float* x = at<float>(ws, L.x);
+  bf16_t* h = at<bf16_t>(ws, L.h);
+  float* q = at<float>(ws, L.q);
+  float* k = at<float>(ws, L.k);
+  float* v = at<float>(ws, L.v);
+  float* attp = at<float>(ws, L.attp);
+  bf16_t* att = at<bf16_t>(ws, L.att);
+  float* gate = at<float>(ws, L.gate);
+  float* up = at<float>(ws, L.up);
+  bf16_t* kc = static_cast<bf16_t*>(kv->k);
+  bf16_t* vc = static_cast<bf16_t*>(kv->v);
+
+  const int nprep = std::max(sh.B, M * (hd / 2));
+  hipLaunchKernelGGL(k_prep, dim3((nprep + 255) / 256), dim3(256), 0, s, kv->len, rope, invalid, sh.B, sh.G1, hd,
+                     kv->max_len, m->rope_theta);
+  hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, s, tokens, static_cast<const bf16_t*>(m->embed), x, invalid,
+                     sh.G1, sh.V, d);
+  SV_HIP(hipGetLastError());
+
+  const GemmPlan pqkv = plan_gemm(M, 3 * ((HD + 15) / 16), d);
+  const GemmPlan po = plan_gemm(M, (d + 15) / 16, HD);
+  const GemmPlan pgu = plan_gemm(M, 2 * ((ff + 15) / 16), d);
+  const GemmPlan pd = plan_gemm(M, (d + 15) / 16, ff);
+  const float scale = 1.0f / sqrtf(float(hd));
+  for (int l = 0; l < m->n_layers; ++l) {
+    const void* const* w = m->layers + size_t(l) * 9;
+    hipLaunchKernelGGL(k_rmsnorm, dim3(M), dim3(256), 0, s, x, static_cast<const bf16_t*>(w[0]), h, d, m->rms_eps);
+    GemmArgs a = gemm_args(h, M, d);
+    gemm_add_seg(a, w[1], q, HD);
+    gemm_add_seg(a, w[2], k, HD);
+    gemm_add_seg(a, w[3], v, HD);
+    sv_status st = launch_gemm(pqkv, a, gemm_grid_x(pqkv, di), s);
+    if (st) return st;
+    hipLaunchKernelGGL(k_rope_append, dim3(M, H), dim3(hd / 2), 0, s, q, k, v, rope, kc, vc, kv->len, invalid, da, l);
+    if (hd == 128)
+      hipLaunchKernelGGL((k_attn<128>), dim3(L.S, H, sh.B), dim3(256), 0, s, q, kc, vc, kv->len, invalid, attp, da, l,
+                         L.S, scale);
+    else
+      hipLaunchKernelGGL((k_attn<64>), dim3(L.S, H, sh.B), dim3(256), 0, s, q, kc, vc, kv->len, invalid, attp, da, l,
+                         L.S, scale);
+    hipLaunchKernelGGL(k_attn_merge, dim3(M, H), dim3(hd), 0, s, attp, att, da, L.S);
+    SV_HIP(hipGetLastError());
+    GemmArgs ao = gemm_args(att, M, HD);
+    gemm_add_seg(ao, w[4], x, d);
+    ao.accumulate = 1;
+    if ((st = launch_gemm(po, ao, gemm_grid_x(po, di), s))) return st;
+    hipLaunchKernelGGL(k_rmsnorm, dim3(M), dim3(256), 0, s, x, static_cast<const bf16_t*>(w[5]), h, d, m->rms_eps);
+    GemmArgs agu = gemm_args(h, M, d);
+    gemm_add_seg(agu, w[6], gate, ff);
+    gemm_add_seg(agu, w[7], up, ff);
+    if ((st = launch_gemm(pgu, agu, gemm_grid_x(pgu, di), s))) return st;
+    const int nf = M * ff;
+    hipLaunchKernelGGL(k_silu_mul, dim3((nf + 255) / 256), dim3(256), 0, s, gate, up, h, nf);
+    GemmArgs ad = gemm_args(h, M, ff);
+    gemm_add_seg(ad, w[8], x, d);
+    ad.accumulate = 1;
+    if ((st = launch_gemm(pd, ad, gemm_grid_x(pd, di), s))) return st;
+  }
+  hipLaunchKernelGGL(k_rmsnorm, dim3(M), dim3(256), 0, s, x, static_cast<const bf16_t*>(m->final_norm), h, d,
+                     m->rms_eps);
+  SV_HIP(hipGetLastError());
+  return SV_OK;
+}
+
+// Logits of all slots plus (if part != NULL) the row-statistics partials.
+// Returns the number of partials per row in *P.
+sv_status run_logits(const sv_model* m, const Shape& sh, const void* input, const sv_kv_cache* kv,
+                     const Layout& L, void* ws, float* logits, RowPart* part, float c, int* P, hipStream_t s) {
+  DevInfo di;
+  sv_status st = dev_info(&di);
+  if (st) return st;
+  const int M = sh.M, V = sh.V;
+  if (sh.kind == SV_IN_LOGITS) {
+    if (part) {
+      TimeScope ts(s, 2);
+      const int nch = (V + LCH - 1) / LCH;
+      const long items = long(M) * nch;
+      hipLaunchKernelGGL(k_stats_logits, dim3(unsigned((items + 3) / 4)), dim3(256), 0, s,
+                         static_cast<const float*>(input), part, M, V, c);
+      SV_HIP(hipGetLastError());
+      *P = nch;
+    }
+    return SV_OK;
+  }
+  const bf16_t* hb = nullptr;
+  if (sh.decoder) {
+    if ((st = run_decoder(m, sh, static_cast<const int*>(input), kv, L, ws, di, s))) return st;
+    hb = at<bf16_t>(ws, L.h);
+  } else if (m->wdtype == SV_F32) {
+    TimeScope ts(s, 0);
+    const int d = sh.d;
+    hipLaunchKernelGGL(k_gemm_f32, dim3((V + 255) / 256), dim3(256), size_t(M) * d * 4, s,
+                       static_cast<const float*>(m->lm_head), static_cast<const float*>(input), logits, part, M, V, d,
+                       c, part ? 1 : 0);
+    SV_HIP(hipGetLastError());
+    *P = (V + 255) / 256;
+    return SV_OK;
+  } else {
+    hb = static_cast<const bf16_t*>(input);
+  }
+  TimeScope ts(s, 0);
+  const int K = sh.decoder ? m->d_model : sh.d;
+  GemmArgs a = gemm_args(hb, M, K);
+  gemm_add_seg(a, m->lm_head, logits, V);
+  a.part = part;
+  a.want_stats = part ? 1 : 0;
+  a.c_stat = c;
+  const int gx = gemm_grid_x(L.head, di);
+  if ((st = launch_gemm(L.head, a, gx, s))) return st;
+  *P = gx;
+  return SV_OK;
+}
+
+sv_status verify_common(const sv_model* m, sv_input_kind kind, const void* input, int32_t B, int32_t gamma,
+                        const int32_t* draft, const void* q, sv_dtype q_dtype, float temperature, uint64_t seed,
+                        const int64_t* pos0, const sv_kv_cache* kv, int32_t* n_accepted, int32_t* tokens_out,
+                        float* logits_out, void* ws, size_t* ws_bytes, void* stream, bool sample) {
+  g_err.clear();
+  Shape sh;
+  sv_status st = check_common(m, kind, input, B, gamma, kv, &sh);
+  if (st) return st;
+  if (!n_accepted || !tokens_out) return fail(SV_ERR_ARG, "n_accepted and tokens_out must not be NULL");
+  if (!draft && kind != SV_IN_TOKENS) return fail(SV_ERR_ARG, "draft is NULL");
+  if (sample) {
+    if (!std::isfinite(temperature) || temperature < 0.0f)
+      return fail(SV_ERR_ARG, "temperature must be finite and >= 0");
+    if (temperature == 0.0f) sample = false;   // the greedy rule, exactly
+  }
+  if (sample) {
+    if (!q) return fail(SV_ERR_ARG, "q is NULL");
+    if (!pos0) return fail(SV_ERR_ARG, "pos0 is NULL");
+    if (q_dtype != SV_F32 && q_dtype != SV_BF16) return fail(SV_ERR_DTYPE, "q_dtype must be SV_F32 or SV_BF16");
+  }
+  const bool need_buf = kind != SV_IN_LOGITS && logits_out == nullptr;
+  Layout L = plan(m, sh, kv, need_buf, sample);
+  bool query = false;
+  if ((st = check_ws(ws, ws_bytes, L, &query))) return st;
+  if (query) return SV_OK;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float c = sample ? LOG2E / temperature : 0.0f;
+  float* logits = kind == SV_IN_LOGITS ? const_cast<float*>(static_cast<const float*>(input))
+                                       : (logits_out ? logits_out : at<float>(ws, L.logits));
+  RowPart* part = at<RowPart>(ws, L.part);
+  int* invalid = at<int>(ws, L.invalid);
+  int P = 0;
+  if ((st = run_logits(m, sh, input, kv, L, ws, logits, part, c, &P, s))) return st;
+  if (kind == SV_IN_LOGITS && logits_out)
+    SV_HIP(hipMemcpyAsync(logits_out, input, size_t(sh.M) * sh.V * 4, hipMemcpyDeviceToDevice, s));
+
+  TimeScope ts(s, 2);
+  AcceptArgs aa;
+  memset(&aa, 0, sizeof aa);
+  aa.part = part; aa.P = P; aa.logits = logits;
+  if (draft) { aa.draft = draft; aa.draft_stride = gamma; aa.draft_offset = 0; }
+  else { aa.draft = static_cast<const int*>(input); aa.draft_stride = gamma + 1; aa.draft_offset = 1; }
+  aa.q = q; aa.q_bf16 = q_dtype == SV_BF16; aa.pos0 = pos0; aa.invalid = sh.decoder ? invalid : nullptr;
+  aa.len = kv ? kv->len : nullptr;
+  aa.n_accepted = n_accepted; aa.tokens_out = tokens_out;
+  aa.state = at<SeqState>(ws, L.state);
+  aa.seed = seed; aa.B = sh.B; aa.gamma = gamma; aa.V = sh.V; aa.c = c; aa.sample = sample ? 1 : 0;
+  hipLaunchKernelGGL(k_accept, dim3((sh.B + 3) / 4), dim3(256), 0, s, aa);
+  SV_HIP(hipGetLastError());
+  if (!sample) return SV_OK;
+  SampleArgs sa;
+  memset(&sa, 0, sizeof sa);
+  sa.logits = logits; sa.q = q; sa.q_bf16 = aa.q_bf16; sa.pos0 = pos0; sa.state = aa.state;
+  sa.spart = at<SamplePart>(ws, L.spart); sa.seed = seed; sa.B = sh.B; sa.gamma = gamma; sa.V = sh.V;
+  sa.chunk = SAMPLE_CHUNK; sa.nch = L.nch; sa.c = c;
+  hipLaunchKernelGGL(k_sample, dim3(unsigned(L.nch) * unsigned(sh.B)), dim3(256), 0, s, sa);
+  hipLaunchKernelGGL(k_sample_finish, dim3((sh.B + 255) / 256), dim3(256), 0, s, aa.state, sa.spart, L.nch, sh.B,
+                     gamma, n_accepted, tokens_out, aa.len);
+  SV_HIP(hipGetLastError());
+  return SV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sv_status verify_forward(const sv_model* m, sv_input_kind kind, const void* input, int32_t B, int32_t gamma,
+                         const sv_kv_cache* kv, float* logits, void* ws, size_t* ws_bytes, void* stream) {
+  g_err.clear();
+  Shape sh;
+  sv_status st = check_common(m, kind, input, B, gamma, kv, &sh);
+  if (st) return st;
+  if (!logits) return fail(SV_ERR_ARG, "logits is NULL");
+  Layout L = plan(m, sh, kv, false, false);
+  bool query = false;
+  if ((st = check_ws(ws, ws_bytes, L, &query))) return st;
+  if (query) return SV_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (kind == SV_IN_LOGITS) {
+    if (logits != input) SV_HIP(hipMemcpyAsync(logits, input, size_t(sh.M) * sh.V * 4, hipMemcpyDeviceToDevice, s));
+    return SV_OK;
+  }
+  int P = 0;
+  return run_logits(m, sh, input, kv, L, ws, logits, nullptr, 0.0f, &P, s);
+}
+
+sv_status spec_verify_greedy(const sv_model* m, sv_input_kind kind, const void* input, int32_t B, int32_t gamma,
+                             const int32_t* draft, const sv_kv_cache* kv, int32_t* n_accepted, int32_t* tokens_out,
+                             float* logits_out, void* ws, size_t* ws_bytes, void* stream) {
+  return verify_common(m, kind, input, B, gamma, draft, nullptr, SV_F32, 0.0f, 0, nullptr, kv, n_accepted,
+                       tokens_out, logits_out, ws, ws_bytes, stream, false);
+}
+
+sv_status spec_verify_sample(const sv_model* m, sv_input_kind kind, const void* input, int32_t B, int32_t gamma,
+                             const int32_t* draft, const void* q, sv_dtype q_dtype, float temperature, uint64_t seed,
+                             const int64_t* pos0, const sv_kv_cache* kv, int32_t* n_accepted, int32_t* tokens_out,
+                             float* logits_out, void* ws, size_t* ws_bytes, void* stream) {
+  return verify_common(m, kind, input, B, gamma, draft, q, q_dtype, temperature, seed, pos0, kv, n_accepted,
+                       tokens_out, logits_out, ws, ws_bytes, stream, true);
+}
+
+int32_t sv_version(void) { return VERSION; }
+
+const char* sv_status_string(int32_t status) {
+  switch (status) {
+    case SV_OK: return "SV_OK";
+    case SV_ERR_ARG: return "SV_ERR_ARG";
+    case SV_ERR_DTYPE: return "SV_ERR_DTYPE";
+    case SV_ERR_SHAPE: return "SV_ERR_SHAPE";
+    case SV_ERR_WORKSPACE: return "SV_ERR_WORKSPACE";
+    case SV_ERR_HIP: return "SV_ERR_HIP";
+    case SV_ERR_UNSUPPORTED: return "SV_ERR_UNSUPPORTED";
+    default: return "SV_ERR_UNKNOWN";
+  }
+}
+
+const char* sv_last_error(void) { return g_err.c_str(); }
+
+sv_status sv_timing_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  for (auto& r : g_timer.recs) { g_timer.pool.push_back(r.a); g_timer.pool.push_back(r.b); }
+  g_timer.recs.clear();
+  g_timer.on = on != 0;
+  return SV_OK;
+}
+
+sv_status sv_timing_read(int32_t which, double* total_ms, int64_t* count) {
+  if (!total_ms || !count) return fail(SV_ERR_ARG, "NULL output");
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  double tot = 0.0;
+  int64_t n = 0;
+  for (auto& r : g_timer.recs) {
+    if (r.which != which) continue;
+    SV_HIP(hipEventSynchronize(r.b));
+    float ms = 0.0f;
+    SV_HIP(hipEventElapsedTime(&ms, r.a, r.b));
+    tot += ms;
+    ++n;
+  }
+  *total_ms = tot;
+  *count = n;
+  return SV_OK;
+}
+
+}  // extern "C"

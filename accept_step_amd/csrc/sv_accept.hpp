@@ -1,0 +1,256 @@
+// sv_accept.hpp -- row statistics, the acceptance rules and the correction/bonus
+// sampler of the verify step (gfx950).
+//
+// Greedy rule ([MTP-drafters] 3.2, [Self-spec] 3.1): accept draft i while it equals
+// the argmax of slot i; the first mismatch ends the round with the slot's argmax;
+// all accepted gives slot gamma's argmax as the bonus ([Infra-ch8] "where the extra
+// token comes from").
+// Sampling rule ([MTP-deep-dive] 2.2, [Infra-ch8] "why the output does not change",
+// [Self-spec] 3.2): accept draft x with probability min(1, p(x)/q(x)), tested as
+// u * q(x) < p(x) with a 24-bit Philox uniform per (sequence, position); the first
+// rejected slot draws from max(0, p - q) (from p when that is zero everywhere);
+// all accepted draws the bonus from p_gamma.  Draws use Gumbel-max over Philox noise
+// keyed by (seed, sequence, position, vocab entry), so any partition of the vocabulary
+// over workgroups gives the same token.
+#pragma once
+
+#include "sv_device.hpp"
+
+namespace sv {
+
+// Per-sequence state handed from the accept kernel to the sampler.
+struct SeqState {
+  int n;          // accepted drafts (-1: invalid sequence)
+  float m;        // max logit of slot n
+  float z;        // sum of exp2((l - m) * c) over slot n
+  int pad;
+};
+
+// Best (score, index) of a vocabulary chunk for the residual and for p itself.
+struct SamplePart {
+  float sr;
+  int ir;
+  float sp;
+  int ip;
+  int any_r;      // some r_v > 0 in this chunk
+  int pad[3];
+};
+
+// Row statistics of float32 logits [M, V]: one wavefront per (row, chunk of LCH).
+constexpr int LCH = 4096;
+
+__global__ __launch_bounds__(256) void k_stats_logits(const float* __restrict__ logits, RowPart* __restrict__ part,
+                                                      int M, int V, float c) {
+  const int lane = threadIdx.x & 63;
+  const long item = long(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int nch = (V + LCH - 1) / LCH;
+  if (item >= long(M) * nch) return;
+  const int row = int(item % M), ch = int(item / M);
+  const float* l = logits + size_t(row) * V;
+  const int v0 = ch * LCH, v1 = min(V, v0 + LCH);
+  float m = -INFINITY;
+  int am = 0x7fffffff;
+  for (int v = v0 + lane; v < v1; v += 64) {
+    float x = l[v];
+    if (x > m) { m = x; am = v; }           // ascending v per lane: first max kept
+  }
+  float s = 0.0f;
+  if (c != 0.0f && am != 0x7fffffff)
+    for (int v = v0 + lane; v < v1; v += 64) s += exp2f((l[v] - m) * c);
+  wave_merge_stat(m, s, am, c);
+  if (lane == 0) {
+    RowPart p;
+    p.m = m; p.s = s; p.a = am; p.pad = 0;
+    part[size_t(ch) * M + row] = p;
+  }
+}
+
+struct AcceptArgs {
+  const RowPart* part;    // [P, M]
+  int P;
+  const float* logits;    // [M, V]
+  const int* draft;       // [B, gamma] (or tokens [B, G1] with draft_stride = G1, offset 1)
+  int draft_stride, draft_offset;
+  const void* q;          // [B, gamma, V]
+  int q_bf16;
+  const int64_t* pos0;    // [B]
+  const int* invalid;     // [B] or null: 1 = invalid sequence (bad token id / cache overflow)
+  int* len;               // [B] or null: cache lengths to advance
+  int* n_accepted;        // [B]
+  int* tokens_out;        // [B, G1]
+  SeqState* state;        // [B] (sampling)
+  uint64_t seed;
+  int B, gamma, V;
+  float c;                // log2(e) / T
+  int sample;             // 0 greedy, 1 sampling
+};
+
+// One wavefront per sequence; lane i holds slot i.
+__global__ __launch_bounds__(256) void k_accept(AcceptArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (b >= a.B) return;
+  const int G1 = a.gamma + 1;
+  const int M = a.B * G1;
+  float my_m = -INFINITY, my_s = 0.0f;
+  int my_a = 0x7fffffff;
+  const float cs = a.sample ? a.c : 0.0f;
+  for (int i = 0; i < G1; ++i) {
+    float m = -INFINITY, s = 0.0f;
+    int am = 0x7fffffff;
+    for (int p = lane; p < a.P; p += 64) {
+      const RowPart rp = a.part[size_t(p) * M + b * G1 + i];
+      merge_stat(m, s, am, rp.m, rp.s, rp.a, cs);
+    }
+    wave_merge_stat(m, s, am, cs);
+    if (lane == i) { my_m = m; my_s = s; my_a = am; }
+  }
+  const bool bad = a.invalid && a.invalid[b];
+  if (bad) {
+    if (lane < G1) a.tokens_out[b * G1 + lane] = -1;
+    if (lane == 0) {
+      a.n_accepted[b] = -1;
+      if (a.sample) { SeqState st; st.n = -1; st.m = 0.f; st.z = 0.f; st.pad = 0; a.state[b] = st; }
+    }
+    return;
+  }
+  int x = -1;
+  if (lane < a.gamma) x = a.draft[size_t(b) * a.draft_stride + a.draft_offset + lane];
+  const bool inr = x >= 0 && x < a.V;
+  bool ok;
+  if (!a.sample) {
+    ok = inr && x == my_a;
+  } else {
+    float px = 0.0f, qx = 0.0f;
+    if (inr) {
+      const float l = a.logits[size_t(b * G1 + lane) * a.V + x];
+      px = exp2f((l - my_m) * a.c) / my_s;
+      const size_t qi = (size_t(b) * a.gamma + lane) * a.V + x;
+      qx = a.q_bf16 ? bf16_to_f32(reinterpret_cast<const bf16_t*>(a.q)[qi]) : reinterpret_cast<const float*>(a.q)[qi];
+    }
+    const float u = lane < a.gamma ? accept_uniform(a.seed, uint64_t(b), uint64_t(a.pos0[b] + lane + 1)) : 1.0f;
+    ok = double(u) * double(qx) < double(px);      // exact: 24-bit u times <= 24-bit q
+  }
+  const unsigned long long rej = __ballot(lane < a.gamma && !ok);
+  const int n = rej ? __ffsll(rej) - 1 : a.gamma;
+  const int tok_n = __shfl(my_a, n);
+  const float m_n = __shfl(my_m, n), s_n = __shfl(my_s, n);
+  if (lane < G1) {
+    int t = -1;
+    if (lane < n) t = x;
+    else if (lane == n && !a.sample) t = tok_n;
+    a.tokens_out[b * G1 + lane] = t;
+  }
+  if (lane == 0) {
+    if (!a.sample) {
+      a.n_accepted[b] = n;
+      if (a.len) a.len[b] += n + 1;
+    } else {
+      SeqState st;
+      st.n = n; st.m = m_n; st.z = s_n; st.pad = 0;
+      a.state[b] = st;
+    }
+  }
+}
+
+struct SampleArgs {
+  const float* logits;    // [M, V]
+  const void* q;          // [B, gamma, V]
+  int q_bf16;
+  const int64_t* pos0;
+  const SeqState* state;  // [B]
+  SamplePart* spart;      // [B, nch]
+  uint64_t seed;
+  int B, gamma, V, chunk, nch;
+  float c;
+};
+
+// grid nch * B: Gumbel-max over one chunk of row n_b.  Each thread draws four
+// consecutive vocab entries from one Philox block.
+__global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
+  const int b = int(blockIdx.x / unsigned(a.nch)), ch = int(blockIdx.x % unsigned(a.nch));
+  const SeqState st = a.state[b];
+  SamplePart out;
+  out.sr = -INFINITY; out.ir = 0x7fffffff; out.sp = -INFINITY; out.ip = 0x7fffffff; out.any_r = 0;
+  out.pad[0] = out.pad[1] = out.pad[2] = 0;
+  if (st.n < 0) {
+    if (threadIdx.x == 0) a.spart[size_t(b) * a.nch + ch] = out;
+    return;
+  }
+  const int G1 = a.gamma + 1;
+  const bool resid = st.n < a.gamma;
+  const float* l = a.logits + size_t(b * G1 + st.n) * a.V;
+  const size_t qrow = (size_t(b) * a.gamma + (resid ? st.n : 0)) * a.V;
+  const uint64_t pos = uint64_t(a.pos0[b] + st.n + 1);
+  const int v0 = ch * a.chunk, v1 = min(a.V, v0 + a.chunk);
+  float sr = -INFINITY, sp = -INFINITY;
+  int ir = 0x7fffffff, ip = 0x7fffffff, any_r = 0;
+  for (int vb = v0 + 4 * threadIdx.x; vb < v1; vb += 4 * blockDim.x) {
+    const Philox4 w = philox4x64_10(uint64_t(vb) >> 2, pos, uint64_t(b), TAG_GUMBEL, a.seed, 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int v = vb + e;
+      if (v >= v1) break;
+      const float U = gumbel_uniform_from_word(w.w[e]);
+      const float G = -logf(-logf(U));
+      const float p = exp2f((l[v] - st.m) * a.c) / st.z;
+      if (p > 0.0f) {
+        const float s = logf(p) + G;
+        if (s > sp) { sp = s; ip = v; }
+      }
+      if (resid) {
+        const float qv = a.q_bf16 ? bf16_to_f32(reinterpret_cast<const bf16_t*>(a.q)[qrow + v])
+                                  : reinterpret_cast<const float*>(a.q)[qrow + v];
+        const float r = fmaxf(p - qv, 0.0f);
+        if (r > 0.0f) {
+          any_r = 1;
+          const float s = logf(r) + G;
+          if (s > sr) { sr = s; ir = v; }
+        }
+      }
+    }
+  }
+  wave_merge_best(sr, ir);
+  wave_merge_best(sp, ip);
+  any_r = __any(any_r) ? 1 : 0;
+  __shared__ float s_sr[4], s_sp[4];
+  __shared__ int s_ir[4], s_ip[4], s_any[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) { s_sr[wave] = sr; s_ir[wave] = ir; s_sp[wave] = sp; s_ip[wave] = ip; s_any[wave] = any_r; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 0; w < int(blockDim.x >> 6); ++w) {
+      merge_best(out.sr, out.ir, s_sr[w], s_ir[w]);
+      merge_best(out.sp, out.ip, s_sp[w], s_ip[w]);
+      out.any_r |= s_any[w];
+    }
+    a.spart[size_t(b) * a.nch + ch] = out;
+  }
+}
+
+// One thread per sequence: merge the chunk winners, write the last token, n and len.
+// p itself is used where p is drawn from (bonus) or where the residual is zero
+// everywhere.
+__global__ __launch_bounds__(256) void k_sample_finish(const SeqState* __restrict__ state,
+                                                       const SamplePart* __restrict__ spart, int nch,
+                                                       int B, int gamma, int* __restrict__ n_accepted,
+                                                       int* __restrict__ tokens_out, int* __restrict__ len) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const SeqState st = state[b];
+  if (st.n < 0) return;        // invalid: the accept kernel wrote the outputs
+  float sr = -INFINITY, sp = -INFINITY;
+  int ir = 0x7fffffff, ip = 0x7fffffff, any_r = 0;
+  for (int c = 0; c < nch; ++c) {
+    const SamplePart p = spart[size_t(b) * nch + c];
+    merge_best(sr, ir, p.sr, p.ir);
+    merge_best(sp, ip, p.sp, p.ip);
+    any_r |= p.any_r;
+  }
+  const bool resid = st.n < gamma && any_r;
+  tokens_out[b * (gamma + 1) + st.n] = resid ? ir : ip;
+  n_accepted[b] = st.n;
+  if (len) len[b] += st.n + 1;
+}
+
+}  // namespace sv

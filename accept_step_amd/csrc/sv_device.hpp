@@ -1,0 +1,131 @@
+// sv_device.hpp -- device-side helpers shared by the verify-step kernels (gfx950).
+//
+// bf16 storage, MFMA operand types, wavefront reductions, and the Philox4x64-10
+// counter-based generator (Salmon, Moraes, Dror, Shaw, "Parallel random numbers:
+// as easy as 1, 2, 3", SC'11) that keys every random draw of the sampling rule by
+// (seed, sequence, absolute position, purpose) -- the per-position independent
+// randomness that [Self-spec] section 3.3 requires.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+typedef uint16_t bf16_t;                                              // bf16 bit pattern
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));             // MFMA A/B operand
+typedef float f32x4 __attribute__((ext_vector_type(4)));               // 16x16 MFMA accumulator
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));        // 16-byte load
+
+constexpr int WAVE = 64;
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// float32 -> bf16, round to nearest even (inputs are finite here; NaN maps to a quiet NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return bf16_t(0x7fc0);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return bf16_t(u >> 16);
+}
+
+// 16-byte global load that bypasses cache retention (streamed weights).
+__device__ __forceinline__ u32x4 load_stream16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Row statistics partial: running max, sum of exp((l - max) / T), argmax.
+// The argmax keeps the lowest index on ties.
+struct RowPart {
+  float m;
+  float s;
+  int a;
+  int pad;
+};
+
+// Merge (m2, s2, a2) into (m, s, a); c = log2(e) / T (0 when sums are not needed).
+// The identity element is (-inf, 0, INT_MAX); rescaling is skipped for empty sums so
+// that two identities never form inf - inf.
+__device__ __forceinline__ void merge_stat(float& m, float& s, int& a, float m2, float s2, int a2, float c) {
+  if (m2 > m || (m2 == m && a2 < a)) {
+    if (c != 0.0f) s = (s != 0.0f ? s * exp2f((m - m2) * c) : 0.0f) + s2;
+    m = m2;
+    a = a2;
+  } else if (c != 0.0f && s2 != 0.0f) {
+    s = s + s2 * exp2f((m2 - m) * c);
+  }
+}
+
+__device__ __forceinline__ void wave_merge_stat(float& m, float& s, int& a, float c, int width = WAVE) {
+  for (int o = width / 2; o > 0; o >>= 1) {
+    float m2 = __shfl_xor(m, o);
+    float s2 = __shfl_xor(s, o);
+    int a2 = __shfl_xor(a, o);
+    merge_stat(m, s, a, m2, s2, a2, c);
+  }
+}
+
+// (score, index) argmax with lowest index on ties.
+__device__ __forceinline__ void merge_best(float& s, int& i, float s2, int i2) {
+  if (s2 > s || (s2 == s && i2 < i)) { s = s2; i = i2; }
+}
+
+__device__ __forceinline__ void wave_merge_best(float& s, int& i) {
+  for (int o = WAVE / 2; o > 0; o >>= 1) {
+    float s2 = __shfl_xor(s, o);
+    int i2 = __shfl_xor(i, o);
+    merge_best(s, i, s2, i2);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x64-10.  State: four 64-bit counter words; key: two 64-bit words.  Each
+// round forms the 128-bit products of counter words 0 and 2 with two fixed odd
+// multipliers, then sets (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0); the key is
+// advanced by two Weyl constants between rounds.  Constants as published with the
+// generator.
+struct Philox4 {
+  uint64_t w[4];
+};
+
+__device__ __forceinline__ Philox4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3,
+                                                 uint64_t k0, uint64_t k1) {
+  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) { k0 += W0; k1 += W1; }
+    uint64_t hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
+    uint64_t hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
+    uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+  }
+  Philox4 o;
+  o.w[0] = c0; o.w[1] = c1; o.w[2] = c2; o.w[3] = c3;
+  return o;
+}
+
+constexpr uint64_t TAG_ACCEPT = 0;
+constexpr uint64_t TAG_GUMBEL = 1;
+
+// Acceptance uniform of the token at absolute position ``pos`` of sequence ``seq``:
+// 24 random bits, exact in float32.
+__device__ __forceinline__ float accept_uniform(uint64_t seed, uint64_t seq, uint64_t pos) {
+  Philox4 r = philox4x64_10(0, pos, seq, TAG_ACCEPT, seed, 0);
+  return float(uint32_t(r.w[0] >> 40)) * 5.9604644775390625e-08f;   // 2^-24
+}
+
+// Uniform in (0, 1) with 23 random bits from one Philox word.
+__device__ __forceinline__ float gumbel_uniform_from_word(uint64_t w) {
+  return (float(uint32_t(w >> 41)) + 0.5f) * 1.1920928955078125e-07f;  // 2^-23
+}
+
+}  // namespace sv

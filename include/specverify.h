@@ -1,0 +1,196 @@
+/*
+ * specverify.h -- C ABI of the speculative-decoding verify step on MI355X (gfx950).
+ *
+ * The verify step of speculative / multi-token-prediction decoding: the target
+ * model takes the last accepted token plus gamma drafted tokens, produces
+ * next-token logits at all gamma+1 positions in one pass, and applies the
+ * acceptance rule.
+ *   - [Infra-ch8] AI-infra book, chapter 8 (speculative decoding), sections
+ *     "a concrete example", "why one forward pass can verify several tokens",
+ *     "why the output does not change", "where the extra token comes from".
+ *   - [MTP-deep-dive] "Gemma 4 Multi-Token Prediction (MTP) deep dive", 2.2.
+ *   - [Self-spec] "Self-speculative decoding: layer skip and rejection
+ *     sampling", sections 3.1 (greedy), 3.2 (sampling), 3.3 (per-position
+ *     randomness, KV trim).
+ *   - [MTP-drafters] "Accelerating Gemma 4: faster inference with
+ *     multi-token prediction drafters", sections 3.2 and 4.2.
+ *
+ * Notation.  B sequences, gamma drafts each (1 <= gamma <= 15), G1 = gamma+1
+ * positions ("slots"), M = B*G1 rows, V vocabulary entries, d hidden size.
+ * Slot i's prediction judges draft i (0-based: draft[b*gamma + i] is the token
+ * after input slot i); slot gamma gives the bonus (N+1-th) token.
+ *
+ * Conventions shared by every entry point.
+ *   Memory:   every array argument is a DEVICE pointer allocated and owned by
+ *             the caller, row-major and densely packed, unless marked "host".
+ *             The library never allocates, frees or retains caller memory.
+ *   Workspace: scratch is caller-provided.  Call once with ws == NULL: the
+ *             required size is written to *ws_bytes, nothing is launched, and
+ *             SV_OK is returned.  Then call with ws != NULL and *ws_bytes >= that
+ *             size (256-byte aligned).  The workspace content need not be
+ *             initialised and is undefined afterwards.
+ *   Streams:  stream is a hipStream_t (NULL = the null stream).  All work is
+ *             enqueued on it and the call returns before it completes;
+ *             outputs are valid once the caller synchronises the stream.
+ *             Calls that share a workspace must not overlap in time.
+ *   Errors:   a status code; nothing throws or aborts across the ABI.  Argument
+ *             errors are detected on the host before anything is launched and
+ *             leave the outputs untouched.  sv_last_error() returns a message
+ *             for the calling thread.  Device faults surface at the caller's
+ *             synchronisation as HIP errors.
+ *   Data errors that need device values (out-of-range token or draft ids,
+ *             a KV cache too short for the new positions) never read or write
+ *             out of bounds: an out-of-range draft is rejected; a sequence
+ *             with an out-of-range input token or an overfull cache gets
+ *             n_accepted[b] = -1, tokens_out[b][*] = -1, and its cache length
+ *             is left unchanged.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sv_status {
+  SV_OK = 0,
+  SV_ERR_ARG = 1,          /* null pointer, gamma/B/T out of range, bad struct field */
+  SV_ERR_DTYPE = 2,        /* unsupported dtype combination */
+  SV_ERR_SHAPE = 3,        /* sizes the kernels do not support (e.g. d % 32 != 0) */
+  SV_ERR_WORKSPACE = 4,    /* *ws_bytes smaller than required, or misaligned ws */
+  SV_ERR_HIP = 5,          /* a HIP runtime call failed (no device, launch error) */
+  SV_ERR_UNSUPPORTED = 6   /* valid request this build does not implement */
+} sv_status;
+
+typedef enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+/* What ``input`` holds:
+ *   SV_IN_LOGITS  float32 [B, G1, V] target logits (the forward is skipped);
+ *   SV_IN_HIDDEN  wdtype  [B, G1, d] final hidden states (LM head only);
+ *   SV_IN_TOKENS  int32   [B, G1] token ids, slot 0 = last accepted token,
+ *                 slots 1..gamma = the drafts (full decoder forward). */
+typedef enum sv_input_kind { SV_IN_LOGITS = 0, SV_IN_HIDDEN = 1, SV_IN_TOKENS = 2 } sv_input_kind;
+
+/* Target model; all pointers are device pointers except ``layers``.
+ * n_layers == 0: LM head only (SV_IN_LOGITS / SV_IN_HIDDEN).
+ * n_layers > 0: pre-norm decoder (SV_IN_TOKENS), weights bf16, matrices
+ * row-major [out, in]:  per layer, in this order,
+ *   attn_norm [d], wq [H*hd, d], wk [H*hd, d], wv [H*hd, d], wo [d, H*hd],
+ *   ffn_norm [d], w_gate [d_ff, d], w_up [d_ff, d], w_down [d, d_ff].
+ * RMSNorm x / sqrt(mean(x^2) + rms_eps) * g; rotary embedding (rotate-half
+ * pairs (j, j + hd/2), angle pos * rope_theta^(-2j/hd)); causal softmax
+ * attention with scale 1/sqrt(hd); SwiGLU SiLU(gate) * up. */
+typedef struct sv_model {
+  int32_t n_layers;
+  int32_t d_model;             /* d; multiple of 32 */
+  int32_t n_heads;
+  int32_t head_dim;            /* 64 or 128 when n_layers > 0 */
+  int32_t d_ff;                /* multiple of 32 */
+  int32_t vocab;               /* V >= 2 */
+  sv_dtype wdtype;             /* SV_BF16, or SV_F32 for an LM-head-only model */
+  float rms_eps;
+  float rope_theta;
+  const void* embed;           /* [V, d] (n_layers > 0) */
+  const void* const* layers;   /* HOST array of n_layers * 9 device pointers */
+  const void* final_norm;      /* [d] (n_layers > 0) */
+  const void* lm_head;         /* [V, d]; not read for SV_IN_LOGITS */
+} sv_model;
+
+/* KV cache of the decoder: bf16 [n_layers][B][n_heads][max_len][head_dim]
+ * for K (after the rotary embedding) and V.  len: device int32 [B], the
+ * number of valid positions per sequence.  The verify pass writes K/V of its
+ * G1 new positions at len..len+gamma; see the commit rule of the entry points. */
+typedef struct sv_kv_cache {
+  void* k;
+  void* v;
+  int32_t max_len;
+  int32_t* len;
+} sv_kv_cache;
+
+/* Logits of all G1 slots (steps a1-a3 of the verify pass).
+ *   input/kind: as above.  kv: required for SV_IN_TOKENS (K/V of the new
+ *   positions are written at len..len+gamma; len itself is NOT changed),
+ *   ignored otherwise.  logits: out float32 [B, G1, V].
+ * [Infra-ch8] "why one forward pass can verify several tokens": one pass over
+ * L inputs yields L next-token predictions; the causal mask keeps slot i from
+ * seeing later drafts. */
+sv_status verify_forward(const sv_model* m, sv_input_kind kind, const void* input,
+                         int32_t B, int32_t gamma, const sv_kv_cache* kv,
+                         float* logits, void* ws, size_t* ws_bytes, void* stream);
+
+/* Greedy verify: accept draft i while it equals the argmax of slot i (lowest
+ * index on ties), stop at the first mismatch and emit the slot's argmax in its
+ * place; if all gamma drafts match, emit slot gamma's argmax as the bonus.
+ * [MTP-drafters] 3.2; [Self-spec] 3.1 (compare with the mode, not a
+ * probability threshold); [Infra-ch8] "a concrete example".
+ *   draft:      int32 [B, gamma]; may be NULL for SV_IN_TOKENS (then the
+ *               drafts are input slots 1..gamma).
+ *   kv:         SV_IN_TOKENS: required; after the pass len[b] += n_b + 1 on
+ *               the device (the accepted drafts and the slot-0 token are now
+ *               cached; K/V written beyond the new len are stale and will be
+ *               overwritten next round; [Self-spec] 3.3).  Otherwise may be
+ *               NULL; if given, only len is advanced.
+ *   n_accepted: out int32 [B], accepted drafts 0..gamma (-1: see Data errors).
+ *   tokens_out: out int32 [B, G1], emitted tokens: the n_b accepted drafts,
+ *               then the correction or bonus token; -1 after those n_b + 1.
+ *   logits_out: optional out float32 [B, G1, V] (NULL: kept in workspace). */
+sv_status spec_verify_greedy(const sv_model* m, sv_input_kind kind, const void* input,
+                             int32_t B, int32_t gamma, const int32_t* draft,
+                             const sv_kv_cache* kv, int32_t* n_accepted, int32_t* tokens_out,
+                             float* logits_out, void* ws, size_t* ws_bytes, void* stream);
+
+/* Speculative sampling verify: p_i = softmax(logits_i / T).  Draft i is
+ * accepted iff u_i * q_i(x) < p_i(x), i.e. with probability min(1, p/q); at
+ * the first rejection the slot's token is drawn from max(0, p - q) (from p if
+ * that is zero everywhere); if all drafts are accepted the bonus is drawn
+ * from p_gamma.  The output law equals the target's.
+ * [MTP-deep-dive] 2.2; [Infra-ch8] "why the output does not change";
+ * [Self-spec] 3.2, 3.3.
+ *   q, q_dtype:  draft distributions [B, gamma, V], float32 or bf16, used as
+ *                given (not renormalised).
+ *   temperature: finite, >= 0; 0 applies the greedy rule exactly.
+ *   seed, pos0:  the random stream.  pos0: device int64 [B], absolute position
+ *                of slot 0.  Draws are Philox4x64-10 (Salmon et al., SC'11)
+ *                with key (seed, 0) and counter (block, position, b, tag):
+ *                the acceptance uniform of the token at absolute position P is
+ *                word 0 of block 0, tag 0, u = (w >> 40) * 2^-24; the
+ *                resampling noise of vocab entry v at position P is word v & 3
+ *                of block v >> 2, tag 1, U = ((w >> 41) + 0.5) * 2^-23,
+ *                Gumbel G = -log(-log U), token = argmax_v log r_v + G_v.
+ *                The result is a pure function of (inputs, seed, pos0).
+ *   Other arguments as for spec_verify_greedy. */
+sv_status spec_verify_sample(const sv_model* m, sv_input_kind kind, const void* input,
+                             int32_t B, int32_t gamma, const int32_t* draft,
+                             const void* q, sv_dtype q_dtype, float temperature,
+                             uint64_t seed, const int64_t* pos0,
+                             const sv_kv_cache* kv, int32_t* n_accepted, int32_t* tokens_out,
+                             float* logits_out, void* ws, size_t* ws_bytes, void* stream);
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int32_t sv_version(void);
+
+/* Static string naming a status code. */
+const char* sv_status_string(int32_t status);
+
+/* Message describing the calling thread's most recent error ("" if none). */
+const char* sv_last_error(void);
+
+/* Kernel timing with HIP events recorded on the caller's stream around the
+ * launches of one kernel class.  which: 0 = LM-head product (the dominant
+ * kernel of the LM-head configurations), 1 = decoder layers, 2 = acceptance
+ * tail (statistics merge, accept, resample).  sv_timing_enable(1) starts
+ * recording (and clears what was recorded); sv_timing_read synchronises on the
+ * recorded events and returns the summed milliseconds and launch count of
+ * class ``which``.  Disabled by default; costs two event records per timed
+ * launch while enabled. */
+sv_status sv_timing_enable(int32_t on);
+sv_status sv_timing_read(int32_t which, double* total_ms, int64_t* count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

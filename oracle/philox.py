@@ -128,3 +128,16 @@ def gumbel_uniform(seed, seq, pos, v):
     sel = (v & np.uint64(3)).astype(np.int64)
     w = np.choose(np.broadcast_to(sel, words[0].shape), words)
     return ((w >> np.uint64(41)).astype(np.float64) + 0.5) * 2.0 ** -23
+
+
+def gumbel_uniform_rows(seed, seq, pos, V):
+    """The uniforms of :func:`gumbel_uniform` for entries 0..V-1 of one row per
+    sequence: [B, V] float64 from ``seq``, ``pos`` of shape [B].  Each Philox
+    block is computed once and its four words laid out in vocab order."""
+    seq = np.asarray(seq, dtype=np.int64).astype(np.uint64)[:, None]
+    pos = np.asarray(pos, dtype=np.int64).astype(np.uint64)[:, None]
+    nb = (int(V) + 3) // 4
+    blocks = np.arange(nb, dtype=np.uint64)[None, :]
+    words = philox4x64_10_np(blocks, pos, seq, TAG_GUMBEL, np.uint64(seed), 0)
+    w = np.stack(words, axis=-1).reshape(seq.shape[0], nb * 4)[:, :int(V)]
+    return ((w >> np.uint64(41)).astype(np.float64) + 0.5) * 2.0 ** -23

@@ -237,8 +237,7 @@ def gumbel_scores(r32, seed, seq, pos):
     Philox uniform of (seed, seq, pos, v).
     """
     B, V = r32.shape
-    U = philox.gumbel_uniform(seed, np.asarray(seq)[:, None], np.asarray(pos)[:, None],
-                              np.arange(V)[None, :]).astype(np.float32)
+    U = philox.gumbel_uniform_rows(seed, seq, pos, V).astype(np.float32)
     G = -np.log(-np.log(U))
     with np.errstate(divide="ignore"):
         s = np.where(r32 > 0, np.log(r32) + G, np.float32(-np.inf)).astype(np.float32)

@@ -1,0 +1,114 @@
+"""The C-ABI library loads and exports what include/specverify.h declares; host-side
+argument checks and workspace queries work without a GPU (no compute calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import accept_step_amd as sv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:sv_status|int32_t|const char\s*\*)\s+(\w+)\s*\(", text, flags=re.M)
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sv.library_path()):
+        pytest.fail("libspecverify.so is not built (run python -m accept_step_amd.build)")
+    return sv.library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"verify_forward", "spec_verify_greedy", "spec_verify_sample"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.sv_version() == 10000
+    assert lib.sv_status_string(0) == b"SV_OK"
+    assert lib.sv_status_string(4) == b"SV_ERR_WORKSPACE"
+    assert lib.sv_status_string(99) == b"SV_ERR_UNKNOWN"
+
+
+def _model(vocab=1000, d=64, n_layers=0, wdtype=sv.SV_BF16):
+    m = sv._SvModel()
+    m.n_layers, m.vocab, m.d_model, m.wdtype = n_layers, vocab, d, wdtype
+    m.lm_head = 0x10000            # never dereferenced by the host checks below
+    return m
+
+
+FAKE = ctypes.c_void_p(0x20000)     # 256-byte aligned stand-in pointer, never dereferenced
+
+
+def greedy(lib, m, kind=sv.SV_IN_HIDDEN, inp=FAKE, B=1, gamma=4, draft=FAKE, ws=None, nbytes=0):
+    n = ctypes.c_size_t(nbytes)
+    st = lib.spec_verify_greedy(ctypes.byref(m) if m is not None else None, kind, inp, B, gamma, draft, None,
+                                FAKE, FAKE, None, ws, ctypes.byref(n), None)
+    return st, n.value
+
+
+def test_argument_errors_are_reported_before_any_launch(lib):
+    m = _model()
+    assert greedy(lib, None)[0] == 1
+    assert greedy(lib, m, inp=None)[0] == 1
+    assert greedy(lib, m, B=0)[0] == 1
+    assert greedy(lib, m, gamma=0)[0] == 1
+    assert greedy(lib, m, gamma=16)[0] == 1
+    assert b"gamma" in lib.sv_last_error()
+    assert greedy(lib, m, draft=None)[0] == 1
+    assert greedy(lib, _model(vocab=1))[0] == 1
+    assert greedy(lib, _model(d=48))[0] == 3            # bf16 head needs d % 32 == 0
+    assert greedy(lib, _model(wdtype=7))[0] == 2
+    assert greedy(lib, m, kind=9)[0] == 1
+    assert greedy(lib, _model(n_layers=1), kind=sv.SV_IN_HIDDEN)[0] == 1
+    assert greedy(lib, m, kind=sv.SV_IN_TOKENS)[0] == 1  # no layers / cache
+
+
+def test_sampling_argument_errors(lib):
+    m = _model()
+
+    def sample(T=1.0, q=FAKE, qd=sv.SV_BF16, pos0=FAKE):
+        n = ctypes.c_size_t(0)
+        return lib.spec_verify_sample(ctypes.byref(m), sv.SV_IN_HIDDEN, FAKE, 2, 4, FAKE, q, qd, T, 7, pos0, None,
+                                      FAKE, FAKE, None, None, ctypes.byref(n), None)
+
+    assert sample() == 0
+    assert sample(T=-1.0) == 1
+    assert sample(T=float("nan")) == 1
+    assert sample(T=float("inf")) == 1
+    assert sample(q=None) == 1
+    assert sample(pos0=None) == 1
+    assert sample(qd=5) == 2
+    assert sample(T=0.0, q=None, pos0=None) == 0          # T == 0 is the greedy rule
+
+
+def test_workspace_query_and_size_check(lib):
+    m = _model(vocab=262144, d=1536)
+    st, need = greedy(lib, m)
+    assert st == 0 and need > 262144 * 5 * 4                # holds the float32 logits
+    st, need_b8 = greedy(lib, m, B=8)
+    assert st == 0 and need_b8 > need
+    # too small / misaligned workspace: rejected on the host
+    assert greedy(lib, m, ws=FAKE, nbytes=need - 1)[0] == 4
+    assert greedy(lib, m, ws=ctypes.c_void_p(0x20008), nbytes=need)[0] == 4
+    # logits input needs no logits buffer
+    st, need_l = greedy(lib, sv.logits_model(262144).struct, kind=sv.SV_IN_LOGITS)
+    assert st == 0 and need_l < need
+
+
+def test_timing_api(lib):
+    assert lib.sv_timing_enable(1) == 0
+    ms, cnt = ctypes.c_double(1.0), ctypes.c_int64(5)
+    assert lib.sv_timing_read(0, ctypes.byref(ms), ctypes.byref(cnt)) == 0
+    assert cnt.value == 0 and ms.value == 0.0
+    assert lib.sv_timing_enable(0) == 0

@@ -79,3 +79,11 @@ def test_uniformity():
     exp = len(u) / 20
     chi2 = ((hist - exp) ** 2 / exp).sum()
     assert chi2 < 50  # 19 dof; p ~ 1e-4
+
+
+def test_gumbel_rows_match_elementwise():
+    seq = np.array([0, 5, 1 << 40])
+    pos = np.array([3, 2048, 77])
+    rows = philox.gumbel_uniform_rows(11, seq, pos, 13)
+    ref = philox.gumbel_uniform(11, seq[:, None], pos[:, None], np.arange(13)[None, :])
+    assert np.array_equal(rows, ref)

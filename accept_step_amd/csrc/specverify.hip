@@ -33,7 +33,7 @@ constexpr size_t ALIGN = 256;
 constexpr int GEMM_WAVES = 4;
 constexpr int GEMM_MAX_WG = 2048;    // upper bound of workgroups along the vocabulary
 constexpr size_t GEMM_LDS_BUDGET = 64 * 1024;
-constexpr int SAMPLE_CHUNK = 4096;
+constexpr int SAMPLE_CHUNK = 1024;
 constexpr int ATT_SPLITS_MAX = 16;
 
 thread_local std::string g_err;
@@ -60,6 +60,7 @@ size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 // device properties (per device, lazily)
 struct DevInfo {
   int cus = 0;
+  size_t lds_max = 64 * 1024;   // dynamic LDS per workgroup the streaming product may use
 };
 std::mutex g_dev_mu;
 std::vector<DevInfo> g_dev;
@@ -70,9 +71,11 @@ sv_status dev_info(DevInfo* out) {
   std::lock_guard<std::mutex> lk(g_dev_mu);
   if (int(g_dev.size()) <= dev) g_dev.resize(dev + 1);
   if (g_dev[dev].cus == 0) {
-    int cus = 0;
+    int cus = 0, lds = 0;
     SV_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    SV_HIP(hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev));
     g_dev[dev].cus = cus > 0 ? cus : 1;
+    g_dev[dev].lds_max = lds >= 64 * 1024 ? size_t(lds) : size_t(64 * 1024);
   }
   *out = g_dev[dev];
   return SV_OK;
@@ -188,24 +191,27 @@ sv_status check_common(const sv_model* m, sv_input_kind kind, const void* input,
 // GEMM planning
 struct GemmPlan {
   int MB, mgroups, KC, grid_x_max;
+  bool stream;        // streaming kernel (X fully in LDS, K % 256 == 0)
   size_t lds;
 };
 
-GemmPlan plan_gemm(int M, int N_total_tiles, int K) {
+// ``lds_limit`` = 0 plans without device knowledge (workspace sizing only needs grid_x_max).
+GemmPlan plan_gemm(int M, int N_total_tiles, int K, size_t lds_limit = 0) {
   GemmPlan p;
   const int mblocks = (M + 15) / 16;
   p.MB = mblocks < 4 ? mblocks : 4;
   p.mgroups = (mblocks + p.MB - 1) / p.MB;
   const int rows = std::min(16 * p.MB, M);
+  const size_t stats = size_t(GEMM_WAVES) * 16 * p.MB * 12;
+  const size_t full = size_t(rows) * (K + 8) * 2;
+  p.stream = lds_limit > 0 && K % (32 * GEMM_GRP) == 0 && full <= lds_limit;
   int KC = K;
-  if (size_t(rows) * (K + 8) * 2 > GEMM_LDS_BUDGET) {
+  if (!p.stream && full > GEMM_LDS_BUDGET) {
     KC = int((GEMM_LDS_BUDGET / (size_t(rows) * 2) - 8) / 256 * 256);
     if (KC < 256) KC = 256;
   }
   p.KC = KC;
-  size_t stage = size_t(rows) * (std::min(KC, K) + 8) * 2;
-  size_t stats = size_t(GEMM_WAVES) * 16 * p.MB * 12;
-  p.lds = std::max(stage, stats);
+  p.lds = std::max(size_t(rows) * (std::min(KC, K) + 8) * 2, stats);
   const int nblk = (N_total_tiles + GEMM_WAVES - 1) / GEMM_WAVES;
   p.grid_x_max = std::min(nblk, GEMM_MAX_WG);
   return p;
@@ -218,21 +224,33 @@ int gemm_grid_x(const GemmPlan& p, const DevInfo& di) {
 }
 
 template <int MB>
-void launch_gemm_mb(const GemmArgs& a, dim3 grid, size_t lds, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemm_bf16<MB, GEMM_WAVES>), grid, dim3(GEMM_WAVES * 64), lds, s, a);
-}
-
-sv_status launch_gemm(const GemmPlan& p, GemmArgs a, int grid_x, hipStream_t s) {
-  a.KC = p.KC;
-  dim3 grid(grid_x, p.mgroups);
-  switch (p.MB) {
-    case 1: launch_gemm_mb<1>(a, grid, p.lds, s); break;
-    case 2: launch_gemm_mb<2>(a, grid, p.lds, s); break;
-    case 3: launch_gemm_mb<3>(a, grid, p.lds, s); break;
-    default: launch_gemm_mb<4>(a, grid, p.lds, s); break;
+sv_status launch_gemm_mb(const GemmPlan& p, const GemmArgs& a, dim3 grid, size_t lds_max, hipStream_t s) {
+  if (p.stream) {
+    static bool lds_set = false;      // raising the limit to the device maximum is idempotent
+    if (p.lds > 64 * 1024 && !lds_set) {
+      SV_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_stream<MB, GEMM_WAVES>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(lds_max)));
+      lds_set = true;
+    }
+    hipLaunchKernelGGL((k_gemm_stream<MB, GEMM_WAVES>), grid, dim3(GEMM_WAVES * 64), p.lds, s, a);
+  } else {
+    hipLaunchKernelGGL((k_gemm_chunked<MB, GEMM_WAVES>), grid, dim3(GEMM_WAVES * 64), p.lds, s, a);
   }
   SV_HIP(hipGetLastError());
   return SV_OK;
+}
+
+sv_status launch_gemm(const GemmPlan& p, GemmArgs a, const DevInfo& di, hipStream_t s, int* grid_x_out = nullptr) {
+  a.KC = p.KC;
+  const int gx = gemm_grid_x(p, di);
+  if (grid_x_out) *grid_x_out = gx;
+  dim3 grid(gx, p.mgroups);
+  switch (p.MB) {
+    case 1: return launch_gemm_mb<1>(p, a, grid, di.lds_max, s);
+    case 2: return launch_gemm_mb<2>(p, a, grid, di.lds_max, s);
+    case 3: return launch_gemm_mb<3>(p, a, grid, di.lds_max, s);
+    default: return launch_gemm_mb<4>(p, a, grid, di.lds_max, s);
+  }
 }
 
 GemmArgs gemm_args(const bf16_t* X, int M, int K) {
@@ -306,7 +324,7 @@ Layout plan(const sv_model* m, const Shape& sh, const sv_kv_cache* kv, bool need
     L.attp = b.take(size_t(sh.B) * m->n_heads * L.S * sh.G1 * (m->head_dim + 2) * 4);
     L.att = b.take(size_t(M) * HD * 2);
     L.gate = b.take(size_t(M) * ff * 4);
-    L.up = b.take(size_t(M) * ff * 4);
+    L.up = b.take(size_t(M) * std::max(ff, d) * 4);
   }
   L.total = b.off;
   return L;
@@ -362,19 +380,24 @@ sv_status run_decoder(const sv_model* m, const Shape& sh, const int* tokens, con
                      sh.G1, sh.V, d);
   SV_HIP(hipGetLastError());
 
-  const GemmPlan pqkv = plan_gemm(M, 3 * ((HD + 15) / 16), d);
-  const GemmPlan po = plan_gemm(M, (d + 15) / 16, HD);
-  const GemmPlan pgu = plan_gemm(M, 2 * ((ff + 15) / 16), d);
-  const GemmPlan pd = plan_gemm(M, (d + 15) / 16, ff);
+  const GemmPlan pqkv = plan_gemm(M, 3 * ((HD + 15) / 16), d, di.lds_max);
+  const GemmPlan po = plan_gemm(M, (d + 15) / 16, HD, di.lds_max);
+  const GemmPlan pgu = plan_gemm(M, 2 * ((ff + 15) / 16), d, di.lds_max);
+  const GemmPlan pd = plan_gemm(M, (d + 15) / 16, ff, di.lds_max);
   const float scale = 1.0f / sqrtf(float(hd));
+  // Residual adds are folded into the next RMSNorm: the output projections write
+  // ``delta`` and the following k_add_rmsnorm adds it to x.
+  float* delta = up;    // the up-projection buffer holds [M, max(d, d_ff)] floats
+  const float* pending = nullptr;
   for (int l = 0; l < m->n_layers; ++l) {
     const void* const* w = m->layers + size_t(l) * 9;
-    hipLaunchKernelGGL(k_rmsnorm, dim3(M), dim3(256), 0, s, x, static_cast<const bf16_t*>(w[0]), h, d, m->rms_eps);
+    hipLaunchKernelGGL(k_add_rmsnorm, dim3(M), dim3(256), 0, s, x, pending, static_cast<const bf16_t*>(w[0]), h, d,
+                       m->rms_eps);
     GemmArgs a = gemm_args(h, M, d);
     gemm_add_seg(a, w[1], q, HD);
     gemm_add_seg(a, w[2], k, HD);
     gemm_add_seg(a, w[3], v, HD);
-    sv_status st = launch_gemm(pqkv, a, gemm_grid_x(pqkv, di), s);
+    sv_status st = launch_gemm(pqkv, a, di, s);
     if (st) return st;
     hipLaunchKernelGGL(k_rope_append, dim3(M, H), dim3(hd / 2), 0, s, q, k, v, rope, kc, vc, kv->len, invalid, da, l);
     if (hd == 128)
@@ -386,23 +409,23 @@ sv_status run_decoder(const sv_model* m, const Shape& sh, const int* tokens, con
     hipLaunchKernelGGL(k_attn_merge, dim3(M, H), dim3(hd), 0, s, attp, att, da, L.S);
     SV_HIP(hipGetLastError());
     GemmArgs ao = gemm_args(att, M, HD);
-    gemm_add_seg(ao, w[4], x, d);
-    ao.accumulate = 1;
-    if ((st = launch_gemm(po, ao, gemm_grid_x(po, di), s))) return st;
-    hipLaunchKernelGGL(k_rmsnorm, dim3(M), dim3(256), 0, s, x, static_cast<const bf16_t*>(w[5]), h, d, m->rms_eps);
+    gemm_add_seg(ao, w[4], delta, d);
+    if ((st = launch_gemm(po, ao, di, s))) return st;
+    hipLaunchKernelGGL(k_add_rmsnorm, dim3(M), dim3(256), 0, s, x, delta, static_cast<const bf16_t*>(w[5]), h, d,
+                       m->rms_eps);
     GemmArgs agu = gemm_args(h, M, d);
     gemm_add_seg(agu, w[6], gate, ff);
     gemm_add_seg(agu, w[7], up, ff);
-    if ((st = launch_gemm(pgu, agu, gemm_grid_x(pgu, di), s))) return st;
+    if ((st = launch_gemm(pgu, agu, di, s))) return st;
     const int nf = M * ff;
     hipLaunchKernelGGL(k_silu_mul, dim3((nf + 255) / 256), dim3(256), 0, s, gate, up, h, nf);
     GemmArgs ad = gemm_args(h, M, ff);
-    gemm_add_seg(ad, w[8], x, d);
-    ad.accumulate = 1;
-    if ((st = launch_gemm(pd, ad, gemm_grid_x(pd, di), s))) return st;
+    gemm_add_seg(ad, w[8], delta, d);
+    if ((st = launch_gemm(pd, ad, di, s))) return st;
+    pending = delta;
   }
-  hipLaunchKernelGGL(k_rmsnorm, dim3(M), dim3(256), 0, s, x, static_cast<const bf16_t*>(m->final_norm), h, d,
-                     m->rms_eps);
+  hipLaunchKernelGGL(k_add_rmsnorm, dim3(M), dim3(256), 0, s, x, pending, static_cast<const bf16_t*>(m->final_norm), h,
+                     d, m->rms_eps);
   SV_HIP(hipGetLastError());
   return SV_OK;
 }
@@ -450,8 +473,9 @@ sv_status run_logits(const sv_model* m, const Shape& sh, const void* input, cons
   a.part = part;
   a.want_stats = part ? 1 : 0;
   a.c_stat = c;
-  const int gx = gemm_grid_x(L.head, di);
-  if ((st = launch_gemm(L.head, a, gx, s))) return st;
+  const GemmPlan ph = plan_gemm(M, (V + 15) / 16, K, di.lds_max);
+  int gx = 0;
+  if ((st = launch_gemm(ph, a, di, s, &gx))) return st;
   *P = gx;
   return SV_OK;
 }
@@ -504,7 +528,7 @@ sv_status verify_common(const sv_model* m, sv_input_kind kind, const void* input
   aa.n_accepted = n_accepted; aa.tokens_out = tokens_out;
   aa.state = at<SeqState>(ws, L.state);
   aa.seed = seed; aa.B = sh.B; aa.gamma = gamma; aa.V = sh.V; aa.c = c; aa.sample = sample ? 1 : 0;
-  hipLaunchKernelGGL(k_accept, dim3((sh.B + 3) / 4), dim3(256), 0, s, aa);
+  hipLaunchKernelGGL(k_accept, dim3(sh.B), dim3(256), 0, s, aa);
   SV_HIP(hipGetLastError());
   if (!sample) return SV_OK;
   SampleArgs sa;
@@ -513,7 +537,7 @@ sv_status verify_common(const sv_model* m, sv_input_kind kind, const void* input
   sa.spart = at<SamplePart>(ws, L.spart); sa.seed = seed; sa.B = sh.B; sa.gamma = gamma; sa.V = sh.V;
   sa.chunk = SAMPLE_CHUNK; sa.nch = L.nch; sa.c = c;
   hipLaunchKernelGGL(k_sample, dim3(unsigned(L.nch) * unsigned(sh.B)), dim3(256), 0, s, sa);
-  hipLaunchKernelGGL(k_sample_finish, dim3((sh.B + 255) / 256), dim3(256), 0, s, aa.state, sa.spart, L.nch, sh.B,
+  hipLaunchKernelGGL(k_sample_finish, dim3((sh.B + 3) / 4), dim3(256), 0, s, aa.state, sa.spart, L.nch, sh.B,
                      gamma, n_accepted, tokens_out, aa.len);
   SV_HIP(hipGetLastError());
   return SV_OK;

@@ -85,26 +85,47 @@ struct AcceptArgs {
   int sample;             // 0 greedy, 1 sampling
 };
 
-// One wavefront per sequence; lane i holds slot i.
-__global__ __launch_bounds__(256) void k_accept(AcceptArgs a) {
+// Merge the P partials of one row over a wavefront: independent loads, 8 per lane
+// in flight, then a shuffle reduction.
+__device__ __forceinline__ void merge_row(const RowPart* __restrict__ part, int P, int M, int row, float c, float& m,
+                                          float& s, int& am) {
   const int lane = threadIdx.x & 63;
-  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (b >= a.B) return;
+  m = -INFINITY; s = 0.0f; am = 0x7fffffff;
+  for (int p0 = lane; p0 < P; p0 += 64 * 8) {
+    RowPart rp[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int p = p0 + 64 * u;
+      if (p < P) rp[u] = part[size_t(p) * M + row];
+      else { rp[u].m = -INFINITY; rp[u].s = 0.0f; rp[u].a = 0x7fffffff; rp[u].pad = 0; }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) merge_stat(m, s, am, rp[u].m, rp[u].s, rp[u].a, c);
+  }
+  wave_merge_stat(m, s, am, c);
+}
+
+// One workgroup per sequence.  Wave w merges the statistics of slots w, w+4, ...;
+// wave 0 then applies the rule with lane i holding slot i.
+__global__ __launch_bounds__(256) void k_accept(AcceptArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b = blockIdx.x;
   const int G1 = a.gamma + 1;
   const int M = a.B * G1;
+  const float cs = a.sample ? a.c : 0.0f;
+  __shared__ float s_m[16], s_s[16];
+  __shared__ int s_a[16];
+  for (int i = wave; i < G1; i += 4) {
+    float m, s;
+    int am;
+    merge_row(a.part, a.P, M, b * G1 + i, cs, m, s, am);
+    if (lane == 0) { s_m[i] = m; s_s[i] = s; s_a[i] = am; }
+  }
+  __syncthreads();
+  if (wave != 0) return;
   float my_m = -INFINITY, my_s = 0.0f;
   int my_a = 0x7fffffff;
-  const float cs = a.sample ? a.c : 0.0f;
-  for (int i = 0; i < G1; ++i) {
-    float m = -INFINITY, s = 0.0f;
-    int am = 0x7fffffff;
-    for (int p = lane; p < a.P; p += 64) {
-      const RowPart rp = a.part[size_t(p) * M + b * G1 + i];
-      merge_stat(m, s, am, rp.m, rp.s, rp.a, cs);
-    }
-    wave_merge_stat(m, s, am, cs);
-    if (lane == i) { my_m = m; my_s = s; my_a = am; }
-  }
+  if (lane < G1) { my_m = s_m[lane]; my_s = s_s[lane]; my_a = s_a[lane]; }
   const bool bad = a.invalid && a.invalid[b];
   if (bad) {
     if (lane < G1) a.tokens_out[b * G1 + lane] = -1;
@@ -186,6 +207,16 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
   float sr = -INFINITY, sp = -INFINITY;
   int ir = 0x7fffffff, ip = 0x7fffffff, any_r = 0;
   for (int vb = v0 + 4 * threadIdx.x; vb < v1; vb += 4 * blockDim.x) {
+    float lv[4], qv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int v = min(vb + e, v1 - 1);
+      lv[e] = l[v];
+      qv[e] = 0.0f;
+      if (resid)
+        qv[e] = a.q_bf16 ? bf16_to_f32(reinterpret_cast<const bf16_t*>(a.q)[qrow + v])
+                         : reinterpret_cast<const float*>(a.q)[qrow + v];
+    }
     const Philox4 w = philox4x64_10(uint64_t(vb) >> 2, pos, uint64_t(b), TAG_GUMBEL, a.seed, 0);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -193,19 +224,17 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
       if (v >= v1) break;
       const float U = gumbel_uniform_from_word(w.w[e]);
       const float G = -logf(-logf(U));
-      const float p = exp2f((l[v] - st.m) * a.c) / st.z;
+      const float p = exp2f((lv[e] - st.m) * a.c) / st.z;
       if (p > 0.0f) {
-        const float s = logf(p) + G;
-        if (s > sp) { sp = s; ip = v; }
+        const float sc = logf(p) + G;
+        if (sc > sp) { sp = sc; ip = v; }
       }
       if (resid) {
-        const float qv = a.q_bf16 ? bf16_to_f32(reinterpret_cast<const bf16_t*>(a.q)[qrow + v])
-                                  : reinterpret_cast<const float*>(a.q)[qrow + v];
-        const float r = fmaxf(p - qv, 0.0f);
+        const float r = fmaxf(p - qv[e], 0.0f);
         if (r > 0.0f) {
           any_r = 1;
-          const float s = logf(r) + G;
-          if (s > sr) { sr = s; ir = v; }
+          const float sc = logf(r) + G;
+          if (sc > sr) { sr = sc; ir = v; }
         }
       }
     }
@@ -228,29 +257,35 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
   }
 }
 
-// One thread per sequence: merge the chunk winners, write the last token, n and len.
-// p itself is used where p is drawn from (bonus) or where the residual is zero
+// One wavefront per sequence: merge the chunk winners, write the last token, n and
+// len.  p itself is used where p is drawn from (bonus) or where the residual is zero
 // everywhere.
 __global__ __launch_bounds__(256) void k_sample_finish(const SeqState* __restrict__ state,
                                                        const SamplePart* __restrict__ spart, int nch,
                                                        int B, int gamma, int* __restrict__ n_accepted,
                                                        int* __restrict__ tokens_out, int* __restrict__ len) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (b >= B) return;
   const SeqState st = state[b];
   if (st.n < 0) return;        // invalid: the accept kernel wrote the outputs
   float sr = -INFINITY, sp = -INFINITY;
   int ir = 0x7fffffff, ip = 0x7fffffff, any_r = 0;
-  for (int c = 0; c < nch; ++c) {
+  for (int c = lane; c < nch; c += 64) {
     const SamplePart p = spart[size_t(b) * nch + c];
     merge_best(sr, ir, p.sr, p.ir);
     merge_best(sp, ip, p.sp, p.ip);
     any_r |= p.any_r;
   }
-  const bool resid = st.n < gamma && any_r;
-  tokens_out[b * (gamma + 1) + st.n] = resid ? ir : ip;
-  n_accepted[b] = st.n;
-  if (len) len[b] += st.n + 1;
+  wave_merge_best(sr, ir);
+  wave_merge_best(sp, ip);
+  any_r = __any(any_r) ? 1 : 0;
+  if (lane == 0) {
+    const bool resid = st.n < gamma && any_r;
+    tokens_out[b * (gamma + 1) + st.n] = resid ? ir : ip;
+    n_accepted[b] = st.n;
+    if (len) len[b] += st.n + 1;
+  }
 }
 
 }  // namespace sv

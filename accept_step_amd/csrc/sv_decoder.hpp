@@ -54,13 +54,22 @@ __global__ __launch_bounds__(256) void k_embed(const int* __restrict__ tokens, c
     x[size_t(m) * d + k] = ok ? bf16_to_f32(embed[size_t(tok) * d + k]) : 0.0f;
 }
 
+// Residual add and RMSNorm: x[m, :] += add[m, :] (if add is given), then
 // h[m, :] = bf16(x / sqrt(mean(x^2) + eps) * g).  One workgroup per row.
-__global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, const bf16_t* __restrict__ g,
-                                                 bf16_t* __restrict__ h, int d, float eps) {
+__global__ __launch_bounds__(256) void k_add_rmsnorm(float* __restrict__ x, const float* __restrict__ add,
+                                                     const bf16_t* __restrict__ g, bf16_t* __restrict__ h, int d,
+                                                     float eps) {
   const int m = blockIdx.x;
-  const float* xr = x + size_t(m) * d;
+  float* xr = x + size_t(m) * d;
   float ss = 0.0f;
-  for (int k = threadIdx.x; k < d; k += blockDim.x) ss = fmaf(xr[k], xr[k], ss);
+  for (int k = threadIdx.x; k < d; k += blockDim.x) {
+    float v = xr[k];
+    if (add) {
+      v += add[size_t(m) * d + k];
+      xr[k] = v;
+    }
+    ss = fmaf(v, v, ss);
+  }
   for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
   __shared__ float red[4];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;

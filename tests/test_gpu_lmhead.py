@@ -211,6 +211,13 @@ SMALL = [
     (517, 256, 2, 15, 1.0),     # largest gamma
     (1000, 96, 3, 4, 0.0),      # greedy on ragged shapes
     (4099, 64, 20, 15, 0.0),
+    # K % 256 == 0 with X resident in LDS: the streaming product, 1-4 row blocks
+    (4096, 256, 2, 8, 0.0),     # M = 18
+    (4096, 256, 4, 4, 1.0),     # M = 20
+    (4099, 256, 3, 10, 0.0),    # M = 33
+    (4096, 1536, 8, 4, 0.0),    # M = 40
+    (4096, 1536, 8, 4, 0.7),
+    (4096, 256, 4, 15, 0.0),    # M = 64
 ]
 
 

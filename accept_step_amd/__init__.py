@@ -189,14 +189,16 @@ class KVCache:
 
 
 class Workspace:
-    """Caller-owned scratch for the library, grown on demand (one per device)."""
+    """Caller-owned scratch for the library, grown on demand (one per device).
+    Allocated zero-filled: the library's counters in its first 256 bytes start
+    at zero and every call leaves them zero."""
 
     def __init__(self):
         self.buf = None
 
     def get(self, nbytes, device):
         if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
-            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+            self.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         return self.buf
 
 
@@ -293,9 +295,11 @@ def spec_verify_sample(model, kind, inp, B, gamma, draft, q, temperature, seed, 
     return n, tok
 
 
-def timing_enable(on=True):
-    """Start (clearing earlier records) or stop event timing of kernel classes."""
-    _check(library().sv_timing_enable(1 if on else 0))
+def timing_enable(mask=0b111):
+    """Start event timing of the kernel classes in ``mask`` (bit 0 LM-head
+    product, bit 1 decoder layers, bit 2 acceptance tail), clearing earlier
+    records; ``mask=0`` stops."""
+    _check(library().sv_timing_enable(int(mask)))
 
 
 def timing_read(which):

@@ -35,6 +35,9 @@ constexpr int GEMM_MAX_WG = 2048;    // upper bound of workgroups along the voca
 constexpr size_t GEMM_LDS_BUDGET = 64 * 1024;
 constexpr int SAMPLE_CHUNK = 1024;
 constexpr int ATT_SPLITS_MAX = 16;
+constexpr int FUSE_ACCEPT_MAX_ROWS = 20;   // B * (gamma + 1) merged by the product's last workgroup
+constexpr int FUSE_FINISH_MAX_B = 64;      // sequences finished by the sampler's last workgroup
+constexpr size_t STATIC_LDS_RESERVE = 2048;
 
 thread_local std::string g_err;
 
@@ -90,7 +93,7 @@ int env_int(const char* name, int dflt) {
 // timing with events on the caller's stream
 struct Timer {
   std::mutex mu;
-  bool on = false;
+  unsigned mask = 0;      // bit c: record kernel class c
   std::vector<hipEvent_t> pool;
   struct Rec { int which; hipEvent_t a, b; };
   std::vector<Rec> recs;
@@ -102,7 +105,7 @@ struct TimeScope {
   hipEvent_t a = nullptr, b = nullptr;
   TimeScope(hipStream_t s_, int w) : s(s_), which(w) {
     std::lock_guard<std::mutex> lk(g_timer.mu);
-    if (!g_timer.on) return;
+    if (!(g_timer.mask >> which & 1u)) return;
     for (hipEvent_t* e : {&a, &b}) {
       if (!g_timer.pool.empty()) { *e = g_timer.pool.back(); g_timer.pool.pop_back(); }
       else if (hipEventCreate(e) != hipSuccess) { *e = nullptr; }
@@ -204,7 +207,7 @@ GemmPlan plan_gemm(int M, int N_total_tiles, int K, size_t lds_limit = 0) {
   const int rows = std::min(16 * p.MB, M);
   const size_t stats = size_t(GEMM_WAVES) * 16 * p.MB * 12;
   const size_t full = size_t(rows) * (K + 8) * 2;
-  p.stream = lds_limit > 0 && K % (32 * GEMM_GRP) == 0 && full <= lds_limit;
+  p.stream = lds_limit > STATIC_LDS_RESERVE && K % (32 * GEMM_GRP) == 0 && full <= lds_limit - STATIC_LDS_RESERVE;
   int KC = K;
   if (!p.stream && full > GEMM_LDS_BUDGET) {
     KC = int((GEMM_LDS_BUDGET / (size_t(rows) * 2) - 8) / 256 * 256);
@@ -218,19 +221,24 @@ GemmPlan plan_gemm(int M, int N_total_tiles, int K, size_t lds_limit = 0) {
 }
 
 int gemm_grid_x(const GemmPlan& p, const DevInfo& di) {
-  const int per_cu = env_int("SV_GEMM_WG_PER_CU", 4);
-  int g = di.cus * (per_cu > 0 ? per_cu : 4);
+  const int per_cu = env_int("SV_GEMM_WG_PER_CU", 1);
+  int g = di.cus * (per_cu > 0 ? per_cu : 1);
   return std::max(1, std::min(g, p.grid_x_max));
 }
 
 template <int MB>
-sv_status launch_gemm_mb(const GemmPlan& p, const GemmArgs& a, dim3 grid, size_t lds_max, hipStream_t s) {
+sv_status launch_gemm_mb(const GemmPlan& p, const GemmArgs& a, dim3 grid, hipStream_t s) {
   if (p.stream) {
-    static bool lds_set = false;      // raising the limit to the device maximum is idempotent
-    if (p.lds > 64 * 1024 && !lds_set) {
-      SV_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_stream<MB, GEMM_WAVES>),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(lds_max)));
-      lds_set = true;
+    // raise the kernel's dynamic LDS limit to what this launch needs (monotone)
+    static std::mutex mu;
+    static size_t lds_set = 64 * 1024;
+    {
+      std::lock_guard<std::mutex> lk(mu);
+      if (p.lds > lds_set) {
+        SV_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_stream<MB, GEMM_WAVES>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, int(p.lds)));
+        lds_set = p.lds;
+      }
     }
     hipLaunchKernelGGL((k_gemm_stream<MB, GEMM_WAVES>), grid, dim3(GEMM_WAVES * 64), p.lds, s, a);
   } else {
@@ -246,10 +254,10 @@ sv_status launch_gemm(const GemmPlan& p, GemmArgs a, const DevInfo& di, hipStrea
   if (grid_x_out) *grid_x_out = gx;
   dim3 grid(gx, p.mgroups);
   switch (p.MB) {
-    case 1: return launch_gemm_mb<1>(p, a, grid, di.lds_max, s);
-    case 2: return launch_gemm_mb<2>(p, a, grid, di.lds_max, s);
-    case 3: return launch_gemm_mb<3>(p, a, grid, di.lds_max, s);
-    default: return launch_gemm_mb<4>(p, a, grid, di.lds_max, s);
+    case 1: return launch_gemm_mb<1>(p, a, grid, s);
+    case 2: return launch_gemm_mb<2>(p, a, grid, s);
+    case 3: return launch_gemm_mb<3>(p, a, grid, s);
+    default: return launch_gemm_mb<4>(p, a, grid, s);
   }
 }
 
@@ -271,7 +279,8 @@ void gemm_add_seg(GemmArgs& a, const void* W, float* out, int N) {
 // ---------------------------------------------------------------------------
 // workspace layout
 struct Layout {
-  size_t logits = 0, part = 0, state = 0, spart = 0, invalid = 0;
+  size_t counters = 0;   // 256 bytes of one-shot counters; zero before first use, left zero
+  size_t logits = 0, part = 0, state = 0, spart = 0, invalid = 0, xlogit = 0;
   size_t rope = 0, x = 0, h = 0, q = 0, k = 0, v = 0, attp = 0, att = 0, gate = 0, up = 0;
   size_t total = 0;
   int P = 0;          // row-statistics partials per row
@@ -298,6 +307,7 @@ Layout plan(const sv_model* m, const Shape& sh, const sv_kv_cache* kv, bool need
   Layout L;
   Bump b;
   const int M = sh.M, V = sh.V;
+  L.counters = b.take(256);
   if (need_logits_buf) L.logits = b.take(size_t(M) * V * 4);
   if (sh.kind == SV_IN_LOGITS) {
     L.P = (V + LCH - 1) / LCH;
@@ -309,6 +319,7 @@ Layout plan(const sv_model* m, const Shape& sh, const sv_kv_cache* kv, bool need
   }
   L.part = b.take(size_t(L.P) * M * sizeof(RowPart));
   L.state = b.take(size_t(sh.B) * sizeof(SeqState));
+  L.xlogit = b.take(size_t(M) * 4);
   L.nch = (V + SAMPLE_CHUNK - 1) / SAMPLE_CHUNK;
   if (sample) L.spart = b.take(size_t(sh.B) * L.nch * sizeof(SamplePart));
   L.invalid = b.take(size_t(sh.B) * 4);
@@ -432,8 +443,12 @@ sv_status run_decoder(const sv_model* m, const Shape& sh, const int* tokens, con
 
 // Logits of all slots plus (if part != NULL) the row-statistics partials.
 // Returns the number of partials per row in *P.
+// With ``acc`` non-null, the bf16 LM-head product records each slot's draft-token
+// logit; with ``fuse`` as well, its last workgroup runs the acceptance for all
+// sequences.
 sv_status run_logits(const sv_model* m, const Shape& sh, const void* input, const sv_kv_cache* kv,
-                     const Layout& L, void* ws, float* logits, RowPart* part, float c, int* P, hipStream_t s) {
+                     const Layout& L, void* ws, float* logits, RowPart* part, float c, int* P, hipStream_t s,
+                     const AcceptArgs* acc = nullptr, bool fuse = false) {
   DevInfo di;
   sv_status st = dev_info(&di);
   if (st) return st;
@@ -474,6 +489,14 @@ sv_status run_logits(const sv_model* m, const Shape& sh, const void* input, cons
   a.want_stats = part ? 1 : 0;
   a.c_stat = c;
   const GemmPlan ph = plan_gemm(M, (V + 15) / 16, K, di.lds_max);
+  if (acc) {                              // record the drafts' logits for the rule
+    a.acc = *acc;
+    a.xlogit = at<float>(ws, L.xlogit);
+  }
+  if (acc && fuse) {
+    a.acc.P = gemm_grid_x(ph, di);
+    a.counter = at<unsigned>(ws, L.counters);
+  }
   int gx = 0;
   if ((st = launch_gemm(ph, a, di, s, &gx))) return st;
   *P = gx;
@@ -512,15 +535,9 @@ sv_status verify_common(const sv_model* m, sv_input_kind kind, const void* input
                                        : (logits_out ? logits_out : at<float>(ws, L.logits));
   RowPart* part = at<RowPart>(ws, L.part);
   int* invalid = at<int>(ws, L.invalid);
-  int P = 0;
-  if ((st = run_logits(m, sh, input, kv, L, ws, logits, part, c, &P, s))) return st;
-  if (kind == SV_IN_LOGITS && logits_out)
-    SV_HIP(hipMemcpyAsync(logits_out, input, size_t(sh.M) * sh.V * 4, hipMemcpyDeviceToDevice, s));
-
-  TimeScope ts(s, 2);
   AcceptArgs aa;
   memset(&aa, 0, sizeof aa);
-  aa.part = part; aa.P = P; aa.logits = logits;
+  aa.part = part; aa.logits = logits;
   if (draft) { aa.draft = draft; aa.draft_stride = gamma; aa.draft_offset = 0; }
   else { aa.draft = static_cast<const int*>(input); aa.draft_stride = gamma + 1; aa.draft_offset = 1; }
   aa.q = q; aa.q_bf16 = q_dtype == SV_BF16; aa.pos0 = pos0; aa.invalid = sh.decoder ? invalid : nullptr;
@@ -528,17 +545,31 @@ sv_status verify_common(const sv_model* m, sv_input_kind kind, const void* input
   aa.n_accepted = n_accepted; aa.tokens_out = tokens_out;
   aa.state = at<SeqState>(ws, L.state);
   aa.seed = seed; aa.B = sh.B; aa.gamma = gamma; aa.V = sh.V; aa.c = c; aa.sample = sample ? 1 : 0;
-  hipLaunchKernelGGL(k_accept, dim3(sh.B), dim3(256), 0, s, aa);
-  SV_HIP(hipGetLastError());
+  const bool bf16_head = kind != SV_IN_LOGITS && !(kind == SV_IN_HIDDEN && m->wdtype == SV_F32);
+  const bool fuse = bf16_head && sh.M <= FUSE_ACCEPT_MAX_ROWS;
+  if (bf16_head) aa.xlogit = at<float>(ws, L.xlogit);
+  int P = 0;
+  if ((st = run_logits(m, sh, input, kv, L, ws, logits, part, c, &P, s, bf16_head ? &aa : nullptr, fuse))) return st;
+  if (kind == SV_IN_LOGITS && logits_out)
+    SV_HIP(hipMemcpyAsync(logits_out, input, size_t(sh.M) * sh.V * 4, hipMemcpyDeviceToDevice, s));
+
+  TimeScope ts(s, 2);
+  if (!fuse) {
+    aa.P = P;
+    hipLaunchKernelGGL(k_accept, dim3(sh.B), dim3(256), 0, s, aa);
+    SV_HIP(hipGetLastError());
+  }
   if (!sample) return SV_OK;
   SampleArgs sa;
   memset(&sa, 0, sizeof sa);
   sa.logits = logits; sa.q = q; sa.q_bf16 = aa.q_bf16; sa.pos0 = pos0; sa.state = aa.state;
   sa.spart = at<SamplePart>(ws, L.spart); sa.seed = seed; sa.B = sh.B; sa.gamma = gamma; sa.V = sh.V;
   sa.chunk = SAMPLE_CHUNK; sa.nch = L.nch; sa.c = c;
+  sa.n_accepted = n_accepted; sa.tokens_out = tokens_out; sa.len = aa.len;
+  const bool fuse_finish = sh.B <= FUSE_FINISH_MAX_B;
+  if (fuse_finish) sa.counter = at<unsigned>(ws, L.counters) + 1;
   hipLaunchKernelGGL(k_sample, dim3(unsigned(L.nch) * unsigned(sh.B)), dim3(256), 0, s, sa);
-  hipLaunchKernelGGL(k_sample_finish, dim3((sh.B + 3) / 4), dim3(256), 0, s, aa.state, sa.spart, L.nch, sh.B,
-                     gamma, n_accepted, tokens_out, aa.len);
+  if (!fuse_finish) hipLaunchKernelGGL(k_sample_finish, dim3((sh.B + 3) / 4), dim3(256), 0, s, sa);
   SV_HIP(hipGetLastError());
   return SV_OK;
 }
@@ -599,11 +630,11 @@ const char* sv_status_string(int32_t status) {
 
 const char* sv_last_error(void) { return g_err.c_str(); }
 
-sv_status sv_timing_enable(int32_t on) {
+sv_status sv_timing_enable(int32_t mask) {
   std::lock_guard<std::mutex> lk(g_timer.mu);
   for (auto& r : g_timer.recs) { g_timer.pool.push_back(r.a); g_timer.pool.push_back(r.b); }
   g_timer.recs.clear();
-  g_timer.on = on != 0;
+  g_timer.mask = unsigned(mask) & 7u;
   return SV_OK;
 }
 

@@ -36,6 +36,15 @@ struct SamplePart {
   int pad[3];
 };
 
+__device__ __forceinline__ void store_spart(SamplePart* p, const SamplePart& v) {
+  store_coherent(&p->sr, v.sr);
+  store_coherent(&p->ir, v.ir);
+  store_coherent(&p->sp, v.sp);
+  store_coherent(&p->ip, v.ip);
+  store_coherent(&p->any_r, v.any_r);
+}
+
+
 // Row statistics of float32 logits [M, V]: one wavefront per (row, chunk of LCH).
 constexpr int LCH = 4096;
 
@@ -58,17 +67,14 @@ __global__ __launch_bounds__(256) void k_stats_logits(const float* __restrict__ 
   if (c != 0.0f && am != 0x7fffffff)
     for (int v = v0 + lane; v < v1; v += 64) s += exp2f((l[v] - m) * c);
   wave_merge_stat(m, s, am, c);
-  if (lane == 0) {
-    RowPart p;
-    p.m = m; p.s = s; p.a = am; p.pad = 0;
-    part[size_t(ch) * M + row] = p;
-  }
+  if (lane == 0) store_part(part + size_t(ch) * M + row, m, s, am);
 }
 
 struct AcceptArgs {
   const RowPart* part;    // [P, M]
   int P;
   const float* logits;    // [M, V]
+  const float* xlogit;    // [M] or null: logit of each slot's draft token, stored by the product
   const int* draft;       // [B, gamma] (or tokens [B, G1] with draft_stride = G1, offset 1)
   int draft_stride, draft_offset;
   const void* q;          // [B, gamma, V]
@@ -105,73 +111,100 @@ __device__ __forceinline__ void merge_row(const RowPart* __restrict__ part, int 
   wave_merge_stat(m, s, am, c);
 }
 
-// One workgroup per sequence.  Wave w merges the statistics of slots w, w+4, ...;
-// wave 0 then applies the rule with lane i holding slot i.
-__global__ __launch_bounds__(256) void k_accept(AcceptArgs a) {
+// Acceptance for sequences [b0, b0 + nb) by one workgroup of 256 threads.
+// Phase 1: the four wavefronts merge the statistics partials of the nb * G1 rows
+// (row j by wave j % 4); phase 2: wave w applies the rule to sequences b0 + w,
+// b0 + w + 4, ... with lane i holding slot i.  Requires nb * G1 <= ACC_MAX_ROWS.
+constexpr int ACC_MAX_ROWS = 64;
+
+__device__ __forceinline__ void accept_block(const AcceptArgs& a, int b0, int nb) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int b = blockIdx.x;
   const int G1 = a.gamma + 1;
   const int M = a.B * G1;
   const float cs = a.sample ? a.c : 0.0f;
-  __shared__ float s_m[16], s_s[16];
-  __shared__ int s_a[16];
-  for (int i = wave; i < G1; i += 4) {
+  __shared__ float s_m[ACC_MAX_ROWS], s_s[ACC_MAX_ROWS];
+  __shared__ int s_a[ACC_MAX_ROWS];
+  for (int j = wave; j < nb * G1; j += 4) {
     float m, s;
     int am;
-    merge_row(a.part, a.P, M, b * G1 + i, cs, m, s, am);
-    if (lane == 0) { s_m[i] = m; s_s[i] = s; s_a[i] = am; }
+    merge_row(a.part, a.P, M, b0 * G1 + j, cs, m, s, am);
+    if (lane == 0) { s_m[j] = m; s_s[j] = s; s_a[j] = am; }
   }
   __syncthreads();
-  if (wave != 0) return;
-  float my_m = -INFINITY, my_s = 0.0f;
-  int my_a = 0x7fffffff;
-  if (lane < G1) { my_m = s_m[lane]; my_s = s_s[lane]; my_a = s_a[lane]; }
-  const bool bad = a.invalid && a.invalid[b];
-  if (bad) {
-    if (lane < G1) a.tokens_out[b * G1 + lane] = -1;
-    if (lane == 0) {
-      a.n_accepted[b] = -1;
-      if (a.sample) { SeqState st; st.n = -1; st.m = 0.f; st.z = 0.f; st.pad = 0; a.state[b] = st; }
+  for (int bl = wave; bl < nb; bl += 4) {
+    const int b = b0 + bl;
+    float my_m = -INFINITY, my_s = 0.0f;
+    int my_a = 0x7fffffff;
+    if (lane < G1) { my_m = s_m[bl * G1 + lane]; my_s = s_s[bl * G1 + lane]; my_a = s_a[bl * G1 + lane]; }
+    const bool bad = a.invalid && a.invalid[b];
+    if (bad) {
+      if (lane < G1) a.tokens_out[b * G1 + lane] = -1;
+      if (lane == 0) {
+        a.n_accepted[b] = -1;
+        if (a.sample) { SeqState st; st.n = -1; st.m = 0.f; st.z = 0.f; st.pad = 0; a.state[b] = st; }
+      }
+      continue;
     }
-    return;
-  }
-  int x = -1;
-  if (lane < a.gamma) x = a.draft[size_t(b) * a.draft_stride + a.draft_offset + lane];
-  const bool inr = x >= 0 && x < a.V;
-  bool ok;
-  if (!a.sample) {
-    ok = inr && x == my_a;
-  } else {
-    float px = 0.0f, qx = 0.0f;
-    if (inr) {
-      const float l = a.logits[size_t(b * G1 + lane) * a.V + x];
-      px = exp2f((l - my_m) * a.c) / my_s;
-      const size_t qi = (size_t(b) * a.gamma + lane) * a.V + x;
-      qx = a.q_bf16 ? bf16_to_f32(reinterpret_cast<const bf16_t*>(a.q)[qi]) : reinterpret_cast<const float*>(a.q)[qi];
-    }
-    const float u = lane < a.gamma ? accept_uniform(a.seed, uint64_t(b), uint64_t(a.pos0[b] + lane + 1)) : 1.0f;
-    ok = double(u) * double(qx) < double(px);      // exact: 24-bit u times <= 24-bit q
-  }
-  const unsigned long long rej = __ballot(lane < a.gamma && !ok);
-  const int n = rej ? __ffsll(rej) - 1 : a.gamma;
-  const int tok_n = __shfl(my_a, n);
-  const float m_n = __shfl(my_m, n), s_n = __shfl(my_s, n);
-  if (lane < G1) {
-    int t = -1;
-    if (lane < n) t = x;
-    else if (lane == n && !a.sample) t = tok_n;
-    a.tokens_out[b * G1 + lane] = t;
-  }
-  if (lane == 0) {
+    int x = -1;
+    if (lane < a.gamma) x = a.draft[size_t(b) * a.draft_stride + a.draft_offset + lane];
+    const bool inr = x >= 0 && x < a.V;
+    bool ok;
     if (!a.sample) {
-      a.n_accepted[b] = n;
-      if (a.len) a.len[b] += n + 1;
+      ok = inr && x == my_a;
     } else {
-      SeqState st;
-      st.n = n; st.m = m_n; st.z = s_n; st.pad = 0;
-      a.state[b] = st;
+      float px = 0.0f, qx = 0.0f;
+      if (inr) {
+        const float l = a.xlogit ? a.xlogit[b * G1 + lane] : a.logits[size_t(b * G1 + lane) * a.V + x];
+        px = exp2f((l - my_m) * a.c) / my_s;
+        const size_t qi = (size_t(b) * a.gamma + lane) * a.V + x;
+        qx = a.q_bf16 ? bf16_to_f32(reinterpret_cast<const bf16_t*>(a.q)[qi]) : reinterpret_cast<const float*>(a.q)[qi];
+      }
+      const float u = lane < a.gamma ? accept_uniform(a.seed, uint64_t(b), uint64_t(a.pos0[b] + lane + 1)) : 1.0f;
+      ok = double(u) * double(qx) < double(px);      // exact: 24-bit u times <= 24-bit q
+    }
+    const unsigned long long rej = __ballot(lane < a.gamma && !ok);
+    const int n = rej ? __ffsll(rej) - 1 : a.gamma;
+    const int tok_n = __shfl(my_a, n);
+    const float m_n = __shfl(my_m, n), s_n = __shfl(my_s, n);
+    if (lane < G1) {
+      int t = -1;
+      if (lane < n) t = x;
+      else if (lane == n && !a.sample) t = tok_n;
+      a.tokens_out[b * G1 + lane] = t;
+    }
+    if (lane == 0) {
+      if (!a.sample) {
+        a.n_accepted[b] = n;
+        if (a.len) a.len[b] += n + 1;
+      } else {
+        SeqState st;
+        st.n = n; st.m = m_n; st.z = s_n; st.pad = 0;
+        a.state[b] = st;
+      }
     }
   }
+}
+
+// One workgroup per sequence.
+__global__ __launch_bounds__(256) void k_accept(AcceptArgs a) { accept_block(a, blockIdx.x, 1); }
+
+// Ticket of the calling workgroup on a one-shot counter.  Every thread first waits
+// for its own stores to complete (the data handed over was written with
+// store_coherent, so completion means it reached the coherent memory side); then
+// one thread takes a ticket.  The workgroup that draws the last ticket issues an
+// acquire fence (its caches may hold stale copies from an earlier launch) and can
+// then read the handed-over data with ordinary loads.  It resets the counter for
+// the next launch.
+__device__ __forceinline__ bool last_workgroup(unsigned* counter, unsigned total) {
+  __shared__ unsigned s_ticket;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) s_ticket = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (s_ticket != total - 1) return false;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
 }
 
 struct SampleArgs {
@@ -184,7 +217,13 @@ struct SampleArgs {
   uint64_t seed;
   int B, gamma, V, chunk, nch;
   float c;
+  unsigned* counter;      // non-null: the last workgroup finishes every sequence
+  int* n_accepted;
+  int* tokens_out;
+  int* len;
 };
+
+__device__ __forceinline__ void sample_finish_wave(const SampleArgs& a, int b);
 
 // grid nch * B: Gumbel-max over one chunk of row n_b.  Each thread draws four
 // consecutive vocab entries from one Philox block.
@@ -195,7 +234,10 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
   out.sr = -INFINITY; out.ir = 0x7fffffff; out.sp = -INFINITY; out.ip = 0x7fffffff; out.any_r = 0;
   out.pad[0] = out.pad[1] = out.pad[2] = 0;
   if (st.n < 0) {
-    if (threadIdx.x == 0) a.spart[size_t(b) * a.nch + ch] = out;
+    if (threadIdx.x == 0) store_spart(a.spart + size_t(b) * a.nch + ch, out);
+    if (a.counter && last_workgroup(a.counter, gridDim.x)) {
+      for (int bb = threadIdx.x >> 6; bb < a.B; bb += 4) sample_finish_wave(a, bb);
+    }
     return;
   }
   const int G1 = a.gamma + 1;
@@ -253,26 +295,24 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
       merge_best(out.sp, out.ip, s_sp[w], s_ip[w]);
       out.any_r |= s_any[w];
     }
-    a.spart[size_t(b) * a.nch + ch] = out;
+    store_spart(a.spart + size_t(b) * a.nch + ch, out);
+  }
+  if (a.counter && last_workgroup(a.counter, gridDim.x)) {
+    for (int bb = threadIdx.x >> 6; bb < a.B; bb += 4) sample_finish_wave(a, bb);
   }
 }
 
-// One wavefront per sequence: merge the chunk winners, write the last token, n and
-// len.  p itself is used where p is drawn from (bonus) or where the residual is zero
-// everywhere.
-__global__ __launch_bounds__(256) void k_sample_finish(const SeqState* __restrict__ state,
-                                                       const SamplePart* __restrict__ spart, int nch,
-                                                       int B, int gamma, int* __restrict__ n_accepted,
-                                                       int* __restrict__ tokens_out, int* __restrict__ len) {
+// One wavefront merges the chunk winners of sequence b and writes its last token,
+// n and len.  p itself is used where p is drawn from (bonus) or where the residual
+// is zero everywhere.
+__device__ __forceinline__ void sample_finish_wave(const SampleArgs& a, int b) {
   const int lane = threadIdx.x & 63;
-  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (b >= B) return;
-  const SeqState st = state[b];
-  if (st.n < 0) return;        // invalid: the accept kernel wrote the outputs
+  const SeqState st = a.state[b];
+  if (st.n < 0) return;        // invalid: the accept step wrote the outputs
   float sr = -INFINITY, sp = -INFINITY;
   int ir = 0x7fffffff, ip = 0x7fffffff, any_r = 0;
-  for (int c = lane; c < nch; c += 64) {
-    const SamplePart p = spart[size_t(b) * nch + c];
+  for (int c = lane; c < a.nch; c += 64) {
+    const SamplePart p = a.spart[size_t(b) * a.nch + c];
     merge_best(sr, ir, p.sr, p.ir);
     merge_best(sp, ip, p.sp, p.ip);
     any_r |= p.any_r;
@@ -281,11 +321,18 @@ __global__ __launch_bounds__(256) void k_sample_finish(const SeqState* __restric
   wave_merge_best(sp, ip);
   any_r = __any(any_r) ? 1 : 0;
   if (lane == 0) {
-    const bool resid = st.n < gamma && any_r;
-    tokens_out[b * (gamma + 1) + st.n] = resid ? ir : ip;
-    n_accepted[b] = st.n;
-    if (len) len[b] += st.n + 1;
+    const bool resid = st.n < a.gamma && any_r;
+    a.tokens_out[b * (a.gamma + 1) + st.n] = resid ? ir : ip;
+    a.n_accepted[b] = st.n;
+    if (a.len) a.len[b] += st.n + 1;
   }
+}
+
+// One wavefront per sequence (used when the batch is too large to finish in the
+// sampler's last workgroup).
+__global__ __launch_bounds__(256) void k_sample_finish(SampleArgs a) {
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (b < a.B) sample_finish_wave(a, b);
 }
 
 }  // namespace sv

@@ -42,6 +42,18 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 }
 
 // ---------------------------------------------------------------------------
+// Device-coherent word stores for data one workgroup hands to another inside the
+// same kernel.  The eight XCDs have separate L2 caches; these relaxed agent-scope
+// atomic stores write through to the coherent memory side, so the writer needs no
+// L2 write-back fence (see last_workgroup in sv_accept.hpp).
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<unsigned*>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
 // Row statistics partial: running max, sum of exp((l - max) / T), argmax.
 // The argmax keeps the lowest index on ties.
 struct RowPart {
@@ -50,6 +62,14 @@ struct RowPart {
   int a;
   int pad;
 };
+
+__device__ __forceinline__ void store_part(RowPart* p, float m, float s, int a) {
+  store_coherent(&p->m, m);
+  store_coherent(&p->s, s);
+  store_coherent(&p->a, a);
+}
+
+
 
 // Merge (m2, s2, a2) into (m, s, a); c = log2(e) / T (0 when sums are not needed).
 // The identity element is (-inf, 0, INT_MAX); rescaling is skipped for empty sums so

@@ -25,6 +25,7 @@
 // merge afterwards.
 #pragma once
 
+#include "sv_accept.hpp"
 #include "sv_device.hpp"
 
 namespace sv {
@@ -49,7 +50,19 @@ struct GemmArgs {
   int M, K, KC;          // KC: k-chunk staged in LDS (multiple of 32; the last chunk may be shorter)
   float c_stat;          // log2(e) / T for the sum of exponentials; 0 = argmax/max only
   int want_stats;
+  unsigned* counter;     // non-null: the last workgroup to finish runs the acceptance
+  AcceptArgs acc;        // ... for all acc.B sequences (acc.B * (gamma + 1) <= ACC_MAX_ROWS)
+  float* xlogit;         // non-null: logit of each row's draft token (row m = b*(gamma+1)+i, i < gamma)
 };
+
+// Draft token judged by row m (slot i of sequence b), -1 for the bonus slot.
+__device__ __forceinline__ int row_draft(const GemmArgs& a, int m) {
+  if (!a.xlogit || m >= a.M) return -1;
+  const int G1 = a.acc.gamma + 1;
+  const int b = m / G1, i = m - b * G1;
+  if (i >= a.acc.gamma) return -1;
+  return a.acc.draft[size_t(b) * a.acc.draft_stride + a.acc.draft_offset + i];
+}
 
 // Segment of a tile and its fields, selected without indexing the argument arrays by
 // a runtime value (which would turn into memory loads and waits in the hot loop).
@@ -128,7 +141,7 @@ __device__ __forceinline__ void tile_chunk(const bf16_t* wq, const bf16_t* sX, i
 template <int MB>
 __device__ __forceinline__ void tile_epilogue(const GemmArgs& a, const f32x4 (&acc)[MB], float* outseg, int N, int v0,
                                               int m_base, int rows, int r, int g, float (&rm)[MB], float (&rs)[MB],
-                                              int (&ra)[MB]) {
+                                              int (&ra)[MB], const int (&xd)[MB]) {
   // lane holds out[m = m_base + mb*16 + r][v = v0 + 4g + e], e = 0..3
   const int vb = v0 + 4 * g;
 #pragma unroll
@@ -144,6 +157,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& a, const f32x4 (&a
       for (int e = 0; e < 4; ++e)
         if (vb + e < N) o[e] = val[e];
     }
+    if (xd[mb] >= vb && xd[mb] < vb + 4 && xd[mb] < N) store_coherent(a.xlogit + m, val[xd[mb] - vb]);
     if (a.want_stats) {
       float tm = -INFINITY;
       int ta = 0x7fffffff;
@@ -193,9 +207,7 @@ __device__ __forceinline__ void stats_tail(const GemmArgs& a, unsigned char* sme
       const int idx = w * 16 * MB + t;
       merge_stat(m, s, am, sm[idx], ss[idx], sa[idx], a.c_stat);
     }
-    RowPart p;
-    p.m = m; p.s = s; p.a = am; p.pad = 0;
-    a.part[size_t(blockIdx.x) * a.M + m_base + t] = p;
+    store_part(a.part + size_t(blockIdx.x) * a.M + m_base + t, m, s, am);
   }
 }
 
@@ -217,9 +229,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_chunked(GemmArgs a) {
   const bool one_chunk = a.KC >= a.K;
 
   float rm[MB], rs[MB];
-  int ra[MB];
+  int ra[MB], xd[MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) { rm[mb] = -INFINITY; rs[mb] = 0.0f; ra[mb] = 0x7fffffff; }
+  for (int mb = 0; mb < MB; ++mb) {
+    rm[mb] = -INFINITY; rs[mb] = 0.0f; ra[mb] = 0x7fffffff;
+    xd[mb] = row_draft(a, m_base + mb * 16 + r);
+  }
 
   if (one_chunk) {
     stage_x(a, sX, ld, m_base, rows, 0, a.K);
@@ -246,9 +261,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_chunked(GemmArgs a) {
       if (live) tile_chunk<MB>(Wseg + size_t(vrow) * a.K + k0 + 8 * g, sX, ld, rows, r, 8 * g, kc / 32, acc);
     }
     if (!live) continue;
-    tile_epilogue<MB>(a, acc, outseg, N, v0, m_base, rows, r, g, rm, rs, ra);
+    tile_epilogue<MB>(a, acc, outseg, N, v0, m_base, rows, r, g, rm, rs, ra, xd);
   }
   if (a.want_stats) stats_tail<MB, WAVES>(a, smem, m_base, rows, g, r, wave, rm, rs, ra);
+  if (a.counter && last_workgroup(a.counter, gridDim.x * gridDim.y)) accept_block(a.acc, 0, a.acc.B);
 }
 
 
@@ -278,14 +294,15 @@ __device__ __forceinline__ void stream_load(const bf16_t* p, u32x4 (&buf)[GEMM_G
 template <int MB>
 __device__ __forceinline__ void stream_compute(const GemmArgs& a, const StreamCtx& c, int k, const u32x4 (&buf)[GEMM_GRP],
                                                const bf16_t* sX, int ld, int rows, int r, int g, int m_base,
-                                               f32x4 (&acc)[MB], float (&rm)[MB], float (&rs)[MB], int (&ra)[MB]) {
+                                               f32x4 (&acc)[MB], float (&rm)[MB], float (&rs)[MB], int (&ra)[MB],
+                                               const int (&xd)[MB]) {
   const int i = k / c.gpt, gg = k - i * c.gpt;
   const int kofs = 8 * g + gg * (GEMM_GRP * 32);
 #pragma unroll
   for (int j = 0; j < GEMM_GRP; ++j) mfma_piece<MB>(buf[j], sX, ld, rows, r, kofs + 32 * j, acc);
   if (gg == c.gpt - 1) {
     const TileRef tr = tile_ref(a, c.first + i * c.tstride);
-    tile_epilogue<MB>(a, acc, tr.out, tr.N, tr.v0, m_base, rows, r, g, rm, rs, ra);
+    tile_epilogue<MB>(a, acc, tr.out, tr.N, tr.v0, m_base, rows, r, g, rm, rs, ra, xd);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -303,9 +320,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_stream(GemmArgs a) {
   const int ntiles = a.tile_end[a.nseg - 1];
 
   float rm[MB], rs[MB];
-  int ra[MB];
+  int ra[MB], xd[MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) { rm[mb] = -INFINITY; rs[mb] = 0.0f; ra[mb] = 0x7fffffff; }
+  for (int mb = 0; mb < MB; ++mb) {
+    rm[mb] = -INFINITY; rs[mb] = 0.0f; ra[mb] = 0x7fffffff;
+    xd[mb] = row_draft(a, m_base + mb * 16 + r);
+  }
 
   stage_x(a, sX, ld, m_base, rows, 0, a.K);
   __syncthreads();
@@ -327,19 +347,20 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_stream(GemmArgs a) {
     int k = 0;
     for (; k + 2 < items; k += 2) {
       stream_load(stream_item_ptr(a, c, k + 1, r, g), bufB);
-      stream_compute<MB>(a, c, k, bufA, sX, ld, rows, r, g, m_base, acc, rm, rs, ra);
+      stream_compute<MB>(a, c, k, bufA, sX, ld, rows, r, g, m_base, acc, rm, rs, ra, xd);
       stream_load(stream_item_ptr(a, c, k + 2, r, g), bufA);
-      stream_compute<MB>(a, c, k + 1, bufB, sX, ld, rows, r, g, m_base, acc, rm, rs, ra);
+      stream_compute<MB>(a, c, k + 1, bufB, sX, ld, rows, r, g, m_base, acc, rm, rs, ra, xd);
     }
     if (k + 1 < items) {
       stream_load(stream_item_ptr(a, c, k + 1, r, g), bufB);
-      stream_compute<MB>(a, c, k, bufA, sX, ld, rows, r, g, m_base, acc, rm, rs, ra);
-      stream_compute<MB>(a, c, k + 1, bufB, sX, ld, rows, r, g, m_base, acc, rm, rs, ra);
+      stream_compute<MB>(a, c, k, bufA, sX, ld, rows, r, g, m_base, acc, rm, rs, ra, xd);
+      stream_compute<MB>(a, c, k + 1, bufB, sX, ld, rows, r, g, m_base, acc, rm, rs, ra, xd);
     } else {
-      stream_compute<MB>(a, c, k, bufA, sX, ld, rows, r, g, m_base, acc, rm, rs, ra);
+      stream_compute<MB>(a, c, k, bufA, sX, ld, rows, r, g, m_base, acc, rm, rs, ra, xd);
     }
   }
   if (a.want_stats) stats_tail<MB, WAVES>(a, smem, m_base, rows, g, r, wave, rm, rs, ra);
+  if (a.counter && last_workgroup(a.counter, gridDim.x * gridDim.y)) accept_block(a.acc, 0, a.acc.B);
 }
 
 // float32 LM head (small tables only): one thread per W row, X in LDS.
@@ -374,9 +395,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ W, c
       float M0 = -INFINITY, S0 = 0.0f;
       int A0 = 0x7fffffff;
       for (int w = 0; w < 4; ++w) merge_stat(M0, S0, A0, sm[w], ss[w], sa[w], c_stat);
-      RowPart p;
-      p.m = M0; p.s = S0; p.a = A0; p.pad = 0;
-      part[size_t(blockIdx.x) * M + m] = p;
+      store_part(part + size_t(blockIdx.x) * M + m, M0, S0, A0);
     }
   }
 }

@@ -1,0 +1,214 @@
+"""Benchmark of the verify step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step is one verify pass of the large-vocabulary workload: bf16 LM head
+W[262144, 1536] (about 805 MB), final hidden states [B=1, gamma+1=5, 1536],
+gamma = 4 drafts with a bf16 draft distribution q, temperature 1: logits of
+all five slots, vocab-wide softmax statistics, the min(1, p/q) acceptance
+test, the residual/bonus resample and the commit of n_accepted / tokens.
+Inputs are seeded synthetic arrays resident in HBM before timing starts; the
+step rotates over eight input sets so acceptance varies.
+
+Prints one JSON line: the metric is committed (verified) tokens per second,
+sum over steps of (n_accepted + 1) divided by the timed wall time between two
+device synchronisations.  ``roofline`` reports the LM-head product (the
+dominant kernel): algorithmic bytes per launch (W once plus the hidden
+states) over its average duration measured with HIP events on the stream the
+library launches it on, against the 8 TB/s HBM peak.  ``cpu_baseline`` times
+the CPU oracle (float64 numpy) on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "verified tokens/s + verify-step HBM GB/s (% of MI355X peak), γ=4, V=262144"
+HBM_PEAK_GBS = 8000.0
+N_SETS = 8
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="before timing, copy a buffer of this many MiB five times (a plain copy kernel of known "
+                         "size, used to scale the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--traffic-summary", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                                                              "lmhead_config3_traffic.md"))
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); "
+              "multi-GPU sharding of the verify step is a design note, not a measured path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import accept_step_amd as sv
+    import workloads
+
+    root = os.path.dirname(os.path.abspath(__file__))
+    sys.path.insert(0, root)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---- inputs (resident in HBM before timing)
+    B, gamma, T = 1, 4, 1.0
+    cases = []
+    w = None
+    for s in range(N_SETS):
+        cs = workloads.lm_head_case(262144, 1536, B, gamma, T, 1.0, 3, w=w, pos0=7 * s, variant=s)
+        w = cs.w
+        cases.append(cs)
+    W = to_dev_bf16(w)
+    model = sv.lm_head_model(W)
+    sets = []
+    for cs in cases:
+        sets.append((to_dev_bf16(cs.h), torch.from_numpy(cs.draft.astype(np.int32)).to(dev), to_dev_bf16(cs.q),
+                     torch.from_numpy(cs.pos0).to(dev)))
+    K, Wm = args.steps, args.warmup
+    n_out = torch.empty((K, B), dtype=torch.int32, device=dev)
+    t_out = torch.empty((K, B, gamma + 1), dtype=torch.int32, device=dev)
+    ws = sv.Workspace()
+    seed = cases[0].seed
+
+    def step(i, out=None):
+        h, d, q, p0 = sets[i % N_SETS]
+        return sv.spec_verify_sample(model, sv.SV_IN_HIDDEN, h, B, gamma, d, q, T, seed, p0, out=out, ws=ws)
+
+    if args.calibration_copy_mib:
+        src = torch.empty(args.calibration_copy_mib << 18, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for i in range(Wm):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region
+    sv.timing_enable(0b001)          # events around the LM-head product only
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i, out=(n_out[i], t_out[i]))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    gemm_ms, gemm_n = sv.timing_read(0)
+    sv.timing_enable(0)
+
+    committed = int((n_out.to(torch.int64) + 1).sum().item())
+    value = committed / elapsed
+    ms_per_step = elapsed / K * 1e3
+    gemm_avg_s = gemm_ms / max(gemm_n, 1) * 1e-3
+    algo_bytes = 262144 * 1536 * 2 + B * (gamma + 1) * 1536 * 2
+    achieved = algo_bytes / gemm_avg_s / 1e9
+    traffic = committed_traffic(args.traffic_summary, root)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "verified tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "large-vocab verify: bf16 LM head V=262144 d=1536, B=1, gamma=4, T=1.0 sampling "
+                               "(min(1,p/q) accept, residual/bonus resample)",
+                   "B": B, "gamma": gamma, "V": 262144, "d": 1536, "temperature": T,
+                   "committed_tokens": committed, "candidate_positions_per_s": round(B * (gamma + 1) * K / elapsed, 1),
+                   "verify_steps_per_s": round(K / elapsed, 1),
+                   "step_hbm_gbs": round(algo_bytes / (elapsed / K) / 1e9, 1),
+                   "step_frac_of_peak": round(algo_bytes / (elapsed / K) / 1e9 / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "hbm", "kernel": "k_gemm_stream (LM-head product + row statistics)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": algo_bytes, "avg_launch_us": round(gemm_avg_s * 1e6, 2),
+                     "launches": gemm_n},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cases, args.cpu_seconds, elapsed / K)
+    print(json.dumps(out), flush=True)
+
+
+def committed_traffic(path, root):
+    """HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE summary, or
+    None when the summary is missing or was taken on different kernel sources."""
+    vals = {}
+    try:
+        for line in open(path):
+            if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "kernel_source_hash"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    except OSError:
+        return None
+    if vals.get("kernel_source_hash") != kernel_source_hash(root):
+        return None
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def kernel_source_hash(root):
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("sv_gemm.hpp", "sv_device.hpp"):
+        h.update(open(os.path.join(root, "accept_step_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(cases, budget_s, gpu_step_s):
+    """The oracle as it stands, on a bounded sample of the same workload: whole
+    verify steps (float64 logits from the bf16 table, then the sampling rule),
+    as many as fit in ``budget_s`` seconds (at least one)."""
+    from oracle import bf16 as obf16
+    from oracle import rules
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    steps = committed = 0
+    while True:
+        cs = cases[steps % len(cases)]
+        h = obf16.bf16_to_f64(cs.h)
+        V = cs.w.shape[0]
+        logits = np.empty(h.shape[:-1] + (V,))
+        for v0 in range(0, V, 32768):
+            logits[..., v0:v0 + 32768] = rules.lm_head_logits(h, obf16.bf16_to_f64(cs.w[v0:v0 + 32768]))
+        qf = (cs.q.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+        n, _, _ = rules.verify_sample(logits, cs.draft, qf, cs.temperature, cs.seed, cs.pos0)
+        committed += int((n + 1).sum())
+        steps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(committed / el, 3), "unit": "verified tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{steps} whole verify steps of the same workload (float64 numpy oracle, bf16 table "
+                      f"converted per 32768-row chunk inside the timed region), {el:.1f} s",
+            "ms_per_step": round(el / steps * 1e3, 1), "gpu_speedup": round((el / steps) / gpu_step_s, 1)}
+
+
+if __name__ == "__main__":
+    main()

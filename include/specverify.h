@@ -27,8 +27,11 @@
  *   Workspace: scratch is caller-provided.  Call once with ws == NULL: the
  *             required size is written to *ws_bytes, nothing is launched, and
  *             SV_OK is returned.  Then call with ws != NULL and *ws_bytes >= that
- *             size (256-byte aligned).  The workspace content need not be
- *             initialised and is undefined afterwards.
+ *             size (256-byte aligned).  The first 256 bytes hold one-shot
+ *             counters (the last workgroup of a kernel to finish completes the
+ *             step): a new workspace must be zero-filled once before its first
+ *             use, and every call leaves those bytes zero again.  The rest of the
+ *             workspace need not be initialised and is undefined afterwards.
  *   Streams:  stream is a hipStream_t (NULL = the null stream).  All work is
  *             enqueued on it and the call returns before it completes;
  *             outputs are valid once the caller synchronises the stream.
@@ -179,14 +182,15 @@ const char* sv_status_string(int32_t status);
 const char* sv_last_error(void);
 
 /* Kernel timing with HIP events recorded on the caller's stream around the
- * launches of one kernel class.  which: 0 = LM-head product (the dominant
- * kernel of the LM-head configurations), 1 = decoder layers, 2 = acceptance
- * tail (statistics merge, accept, resample).  sv_timing_enable(1) starts
- * recording (and clears what was recorded); sv_timing_read synchronises on the
- * recorded events and returns the summed milliseconds and launch count of
- * class ``which``.  Disabled by default; costs two event records per timed
- * launch while enabled. */
-sv_status sv_timing_enable(int32_t on);
+ * launches of one kernel class.  Classes: 0 = LM-head product (the dominant
+ * kernel of the LM-head configurations; with a small batch it also runs the
+ * acceptance in its last workgroup), 1 = decoder layers, 2 = acceptance tail
+ * (separate acceptance kernel, resampler).  sv_timing_enable(mask) records the
+ * classes whose bit is set in mask (0 = off) and clears earlier records;
+ * sv_timing_read synchronises on the recorded events and returns the summed
+ * milliseconds and launch count of class ``which``.  Off by default; costs two
+ * event records per timed launch while on. */
+sv_status sv_timing_enable(int32_t mask);
 sv_status sv_timing_read(int32_t which, double* total_ms, int64_t* count);
 
 #ifdef __cplusplus

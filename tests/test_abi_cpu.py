@@ -107,7 +107,7 @@ def test_workspace_query_and_size_check(lib):
 
 
 def test_timing_api(lib):
-    assert lib.sv_timing_enable(1) == 0
+    assert lib.sv_timing_enable(7) == 0
     ms, cnt = ctypes.c_double(1.0), ctypes.c_int64(5)
     assert lib.sv_timing_read(0, ctypes.byref(ms), ctypes.byref(cnt)) == 0
     assert cnt.value == 0 and ms.value == 0.0

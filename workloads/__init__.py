@@ -212,21 +212,22 @@ def tiny_ref(rounds=1000, temperature=1.0, k=1):
     return w, out
 
 
-def lm_head_case(V, d, B, gamma, temperature, noise_std, k, w=None, pos0=0):
+def lm_head_case(V, d, B, gamma, temperature, noise_std, k, w=None, pos0=0, variant=0):
     """Configurations 3 and 4: bf16 W ~ N(0, 0.02^2), hidden ~ N(0, 1).
 
     Draft q = softmax((l + N(0, noise_std^2)) / T) stored as bf16.
-    ``w`` may be passed in to reuse a large table across cases.
+    ``w`` may be passed in to reuse a large table across cases; ``variant``
+    draws an independent set of hidden states, noise and drafts.
     """
     seed = input_seed(k)
     if w is None:
         w = normal_bf16((V, d), 0.02, seed, 0)
-    tag = (B, gamma, int(round(temperature * 1000)))
+    tag = (B, gamma, int(round(temperature * 1000))) + ((variant,) if variant else ())
     h = normal_bf16((B, gamma + 1, d), 1.0, seed, (1,) + tag)
     hf = bf16_bits_to_f32(h)
     lt = _f32_product(hf[:, :gamma], w)
     noise = normal_f32((B, gamma, V), noise_std, seed, (2,) + tag)
-    rng = np.random.default_rng([seed, 7, B, gamma, int(round(temperature * 1000))])
+    rng = np.random.default_rng([seed, 7, B, gamma, int(round(temperature * 1000)), variant])
     x, q = drafter(lt, noise, temperature, rng)
     qb = None if q is None else to_bf16_bits(q)
     return LMHeadCase(w=w, h=h, draft=x, q=qb, temperature=float(temperature),

@@ -1,0 +1,187 @@
+"""GPU parity of the full-model verify path (SV_IN_TOKENS: decoder forward over the
+KV cache, LM head, acceptance, cache-length commit) against the CPU oracle's
+reference decoder, through the C ABI.
+
+Bar: logits within 2e-2 of the row's max |logit| (the bound stated for bf16
+weights; measured values are logged), n_accepted and tokens bit-exact except on
+oracle-flagged sequences, the K/V rows appended for the new positions equal to
+the oracle's up to one bf16 ulp of the row maximum in the first layer and within the same 2e-2
+(relative norm) in every layer, older cache rows untouched, and len advanced by
+n + 1.
+
+Why deeper layers drift: both sides round to bf16 at the same five points per
+layer, but the GPU accumulates in float32 and the oracle in float64.  A 1e-6
+difference before a rounding point either vanishes or becomes a full bf16 ulp
+(0.4%); over 4096-wide vectors those flips compound layer by layer (measured
+logit difference: 3e-3 after one full-width layer, 1.6e-2 after 16, 1.8e-2
+after 32, against 1e-7 for narrow two-layer models).
+"""
+import copy
+
+import numpy as np
+import pytest
+import torch
+
+import accept_step_amd as sv
+import workloads
+from oracle import decoder as dec
+from oracle import rules
+from tests.gpu_util import compare_decisions, dev, dev_bf16, log, row_rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_model(c):
+    wts = dec.DecoderWeights(c.n_layers, c.d_model, c.n_heads, c.head_dim, c.d_ff, c.vocab, c.rms_eps, c.rope_theta,
+                             c.embed, c.layers, c.final_norm, c.lm_head)
+    kv = dec.KVCache(c.k_cache.copy(), c.v_cache.copy(), c.length.astype(np.int64))
+    return wts, kv
+
+
+def gpu_model(c):
+    layers = [{k: dev_bf16(L[k]) for k in sv.LAYER_KEYS} for L in c.layers]
+    model = sv.decoder_model(dev_bf16(c.embed), layers, dev_bf16(c.final_norm), dev_bf16(c.lm_head), c.n_heads,
+                             c.head_dim, c.rms_eps, c.rope_theta)
+    kv = sv.KVCache(dev_bf16(c.k_cache), dev_bf16(c.v_cache), dev(c.length.astype(np.int32)))
+    return model, kv
+
+
+def bf16_ulp_diff(a_bits, b_bits):
+    a = a_bits.astype(np.int32)
+    b = b_bits.astype(np.int32)
+    return np.abs(a - b).max() if a.size else 0
+
+
+def check_case(c, T, label, tol=2e-2):
+    wts, okv = oracle_model(c)
+    model, gkv = gpu_model(c)
+    B, G1 = c.tokens.shape
+    gamma = G1 - 1
+    base = c.length.astype(np.int64).copy()
+    log(f"[{label}] oracle forward")
+    ref = dec.forward(wts, c.tokens, okv)
+    log(f"[{label}] GPU verify T={T}")
+    logits = torch.empty((B, G1, c.vocab), dtype=torch.float32, device="cuda")
+    tok_d = dev(c.tokens.astype(np.int32))
+    if T == 0.0:
+        n, tok = sv.spec_verify_greedy(model, sv.SV_IN_TOKENS, tok_d, B, gamma, None, kv=gkv, logits_out=logits)
+        n0, t0, fl = rules.verify_greedy(ref, c.tokens[:, 1:])
+    else:
+        n, tok = sv.spec_verify_sample(model, sv.SV_IN_TOKENS, tok_d, B, gamma, None, dev(c.q), T, c.seed,
+                                       dev(base), kv=gkv, logits_out=logits)
+        n0, t0, fl = rules.verify_sample(ref, c.tokens[:, 1:], c.q.astype(np.float64), T, c.seed, base)
+    torch.cuda.synchronize()
+    err = row_rel_err(logits.cpu().numpy(), ref)
+    m, f = compare_decisions(n.cpu().numpy(), tok.cpu().numpy(), n0, t0, fl, label)
+    log(f"[{label}] logit rel err max {err.max():.2e} median {np.median(err):.2e}; n={n.cpu().numpy().tolist()} "
+        f"ref n={n0.tolist()} mismatched {m} flagged {f}")
+    assert err.max() <= tol
+    # cache: new rows equal the oracle's up to one bf16 ulp; length advanced by n + 1
+    gk = gkv.k.view(torch.int16).cpu().numpy().view(np.uint16)
+    gv = gkv.v.view(torch.int16).cpu().numpy().view(np.uint16)
+    for b in range(B):
+        sl = slice(int(base[b]), int(base[b]) + G1)
+        # layer 0 sees identical inputs: its new K/V rows agree to one bf16 ulp of
+        # each row's largest value (near-zero elements of a 4096-term sum carry a
+        # larger relative float32 error, so element-wise ulps are not the measure)
+        for got, want in ((gk, okv.k), (gv, okv.v)):
+            g0 = workloads.bf16_bits_to_f32(got[0, b, :, sl]).astype(np.float64)
+            w0 = workloads.bf16_bits_to_f32(want[0, b, :, sl]).astype(np.float64)
+            assert np.all(np.abs(g0 - w0).max(axis=-1) <= 2.0 ** -7 * np.abs(w0).max(axis=-1))
+        # deeper layers inherit the float32-vs-float64 drift amplified by the bf16
+        # rounding points; their new rows agree to the logits' bound
+        for li in range(c.n_layers):
+            for got, want in ((gk, okv.k), (gv, okv.v)):
+                g_ = workloads.bf16_bits_to_f32(got[li, b, :, sl]).astype(np.float64)
+                w_ = workloads.bf16_bits_to_f32(want[li, b, :, sl]).astype(np.float64)
+                assert np.linalg.norm(g_ - w_) <= tol * np.linalg.norm(w_), (li, b)
+        assert np.array_equal(gk[:, b, :, :int(base[b])], c.k_cache[:, b, :, :int(base[b])])
+        assert np.array_equal(gv[:, b, :, :int(base[b])], c.v_cache[:, b, :, :int(base[b])])
+    n_np = n.cpu().numpy()
+    assert np.array_equal(gkv.length.cpu().numpy(), (base + n_np + 1).astype(np.int32))
+    return err.max()
+
+
+@pytest.mark.parametrize("T", [0.0, 1.0])
+@pytest.mark.parametrize("hd,B", [(128, 1), (64, 2)])
+def test_small_decoder(T, hd, B):
+    c = workloads.small_decoder_case(n_layers=2, d_model=256, n_heads=256 // hd, head_dim=hd, d_ff=512, vocab=1000,
+                                     cache_len=100, B=B, gamma=4, std=0.05)
+    check_case(c, T, f"small hd={hd} B={B}")
+
+
+def test_verify_forward_leaves_length():
+    c = workloads.small_decoder_case(n_layers=1, d_model=128, n_heads=2, head_dim=64, d_ff=256, vocab=300,
+                                     cache_len=10, B=2, gamma=3)
+    wts, okv = oracle_model(c)
+    model, gkv = gpu_model(c)
+    ref = dec.forward(wts, c.tokens, okv)
+    out = sv.verify_forward(model, sv.SV_IN_TOKENS, dev(c.tokens.astype(np.int32)), 2, 3, kv=gkv)
+    torch.cuda.synchronize()
+    assert row_rel_err(out.cpu().numpy(), ref).max() <= 2e-2
+    assert np.array_equal(gkv.length.cpu().numpy(), c.length)
+
+
+def test_invalid_tokens_and_full_cache():
+    """An out-of-range token or a cache without room marks the sequence: n = -1,
+    tokens -1, length unchanged, cache untouched; the other sequences are normal."""
+    c = workloads.small_decoder_case(n_layers=1, d_model=128, n_heads=2, head_dim=64, d_ff=256, vocab=300,
+                                     cache_len=10, B=3, gamma=3, max_len=16)
+    c.tokens[0, 2] = 300          # out of range
+    c.length[2] = 13              # 13 + 4 > 16
+    model, gkv = gpu_model(c)
+    n, tok = sv.spec_verify_greedy(model, sv.SV_IN_TOKENS, dev(c.tokens.astype(np.int32)), 3, 3, None, kv=gkv)
+    torch.cuda.synchronize()
+    n = n.cpu().numpy()
+    tok = tok.cpu().numpy()
+    assert n[0] == -1 and n[2] == -1 and np.all(tok[0] == -1) and np.all(tok[2] == -1)
+    assert 0 <= n[1] <= 3
+    assert gkv.length.cpu().numpy().tolist() == [10, 10 + n[1] + 1, 13]
+    gk = gkv.k.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(gk[:, 2], c.k_cache[:, 2])
+    assert np.array_equal(gk[:, 0], c.k_cache[:, 0])
+
+
+def test_greedy_speculative_equals_autoregressive_on_gpu():
+    """Multi-round greedy speculative decoding on the GPU reproduces the oracle's plain
+    greedy autoregressive output token for token, whatever the drafts; the cache
+    length equals the sequence length after every round ([MTP-deep-dive] 2.2,
+    [Self-spec] 3.3)."""
+    gamma, steps = 4, 40
+    c = workloads.small_decoder_case(n_layers=2, d_model=128, n_heads=2, head_dim=64, d_ff=256, vocab=200,
+                                     cache_len=20, B=1, gamma=gamma, max_len=20 + steps + 2 * (gamma + 1), std=0.1)
+    wts, okv = oracle_model(c)
+    first = int(c.tokens[0, 0])
+    ar = dec.greedy_autoregressive(wts, np.array([first]), copy.deepcopy(okv), steps + gamma + 1)[0]
+    model, gkv = gpu_model(c)
+    rng = np.random.default_rng(3)
+    out, last, seen = [], first, set()
+    while len(out) < steps:
+        pos = len(out)
+        cont = np.zeros(gamma, np.int64)
+        avail = ar[pos:pos + gamma]
+        cont[:len(avail)] = avail
+        bad = rng.random(gamma) < 0.3
+        draft = np.where(bad, (cont + 1 + rng.integers(0, 199, gamma)) % 200, cont)
+        toks = np.concatenate([[last], draft]).astype(np.int32)[None]
+        n, tok = sv.spec_verify_greedy(model, sv.SV_IN_TOKENS, dev(toks), 1, gamma, None, kv=gkv)
+        torch.cuda.synchronize()
+        k = int(n.cpu().numpy()[0])
+        emitted = tok.cpu().numpy()[0, :k + 1].tolist()
+        out.extend(emitted)
+        last = emitted[-1]
+        seen.add(k)
+        assert int(gkv.length.cpu().numpy()[0]) == 20 + len(out)
+    assert out[:steps] == ar[:steps].tolist()
+    assert len(seen) >= 3
+
+
+@pytest.mark.timeout(900)
+def test_config5_full_model():
+    """32 layers, d = 4096, 32 heads of 128, FFN 11008, V = 32000, cache 2048, B = 1,
+    gamma = 4: greedy and T = 1 (uniform q)."""
+    log("[config5] generating 13.5 GB of weights")
+    c = workloads.decoder_case()
+    for T in (0.0, 1.0):
+        err = check_case(c, T, f"config5 T={T}")
+        log(f"[config5] T={T} done, max logit rel err {err:.2e}")

@@ -190,7 +190,7 @@ class KVCache:
 
 class Workspace:
     """Caller-owned scratch for the library, grown on demand (one per device).
-    Allocated zero-filled: the library's counters in its first 256 bytes start
+    Allocated zero-filled: the library's counters in its first 4096 bytes start
     at zero and every call leaves them zero."""
 
     def __init__(self):

@@ -23,6 +23,7 @@
 #include "sv_decoder.hpp"
 #include "sv_device.hpp"
 #include "sv_gemm.hpp"
+#include "sv_head.hpp"
 
 using namespace sv;
 
@@ -277,9 +278,148 @@ void gemm_add_seg(GemmArgs& a, const void* W, float* out, int N) {
 }
 
 // ---------------------------------------------------------------------------
+// k-split product (sv_head.hpp) planning
+constexpr size_t HEAD_STATIC_LDS = 8 * 1024;   // the kernel's static LDS (reductions, acceptance)
+
+struct HeadPlan {
+  bool ok = false;
+  int S = 0, NB = 0, GRP = 0, grid = 0, gpt = 0, nloc = 0;
+  size_t lds = 0;
+};
+
+// Largest column-block count instantiated per split factor.
+int head_nb_max(int S) { return S == 4 ? 5 : 3; }
+
+HeadPlan plan_head(int M, int K, const int* N, int nseg, const DevInfo& di) {
+  HeadPlan p;
+  if (M < 1 || M > ACC_MAX_ROWS || K % 8) return p;
+  const int want_s = env_int("SV_HEAD_S", 0), want_grp = env_int("SV_HEAD_GRP", 0);
+  const int per_cu = std::max(1, env_int("SV_HEAD_WG_PER_CU", 1));
+  for (int S : {4, 2}) {
+    if (want_s && S != want_s) continue;
+    const int TR = 16 / S, NB = (M + TR - 1) / TR;
+    if (NB > head_nb_max(S) || K % (32 * S)) continue;
+    const int steps = K / (32 * S);
+    int GRP = 0;
+    for (int gc : {8, 6, 4}) {
+      if (want_grp && gc != want_grp) continue;
+      if (steps % gc == 0) { GRP = gc; break; }
+    }
+    if (!GRP) continue;
+    int ntiles = 0;
+    for (int i = 0; i < nseg; ++i) ntiles += (N[i] + TR - 1) / TR;
+    int grid = std::min(di.cus * per_cu, GEMM_MAX_WG);
+    grid = std::max(1, std::min(grid, (ntiles + HEAD_WAVES - 1) / HEAD_WAVES));
+    const int tpw = (ntiles + grid * HEAD_WAVES - 1) / (grid * HEAD_WAVES) * HEAD_WAVES;
+    const size_t lds = head_lds(M, K, S, tpw * TR);
+    if (lds + HEAD_STATIC_LDS > di.lds_max) continue;
+    p.ok = true; p.S = S; p.NB = NB; p.GRP = GRP; p.grid = grid; p.gpt = steps / GRP; p.nloc = tpw * TR;
+    p.lds = lds;
+    return p;
+  }
+  return p;
+}
+
+template <int S, int NB>
+const void* head_fn_grp(int GRP) {
+  switch (GRP) {
+    case 8: return reinterpret_cast<const void*>(&k_head<S, NB, 8>);
+    case 6: return reinterpret_cast<const void*>(&k_head<S, NB, 6>);
+    default: return reinterpret_cast<const void*>(&k_head<S, NB, 4>);
+  }
+}
+
+const void* head_fn(const HeadPlan& p) {
+  if (p.S == 4) {
+    switch (p.NB) {
+      case 1: return head_fn_grp<4, 1>(p.GRP);
+      case 2: return head_fn_grp<4, 2>(p.GRP);
+      case 3: return head_fn_grp<4, 3>(p.GRP);
+      case 4: return head_fn_grp<4, 4>(p.GRP);
+      default: return head_fn_grp<4, 5>(p.GRP);
+    }
+  }
+  switch (p.NB) {
+    case 1: return head_fn_grp<2, 1>(p.GRP);
+    case 2: return head_fn_grp<2, 2>(p.GRP);
+    default: return head_fn_grp<2, 3>(p.GRP);
+  }
+}
+
+HeadArgs head_args(const bf16_t* X, int M, int K) {
+  HeadArgs a;
+  memset(&a, 0, sizeof a);
+  a.X = X; a.M = M; a.K = K;
+  return a;
+}
+
+void head_add_seg(HeadArgs& a, const void* W, float* out, int N, int TR) {
+  const int i = a.nseg++;
+  a.W[i] = static_cast<const bf16_t*>(W);
+  a.out[i] = out;
+  a.N[i] = N;
+  a.tile_end[i] = (i ? a.tile_end[i - 1] : 0) + (N + TR - 1) / TR;
+}
+
+// Raise the kernel's dynamic LDS limit to what a launch needs (monotone per kernel).
+sv_status head_set_lds(const void* fn, size_t lds) {
+  static std::mutex mu;
+  static std::vector<std::pair<const void*, size_t>> lds_set;
+  std::lock_guard<std::mutex> lk(mu);
+  size_t cur = 64 * 1024;
+  for (auto& e : lds_set) if (e.first == fn) cur = e.second;
+  if (lds <= cur) return SV_OK;
+  SV_HIP(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)));
+  for (auto& e : lds_set) if (e.first == fn) { e.second = lds; return SV_OK; }
+  lds_set.push_back({fn, lds});
+  return SV_OK;
+}
+
+// Whether every workgroup of the plan can be resident at once (the fused sampler's
+// grid barrier needs it).
+sv_status head_all_resident(const HeadPlan& p, const DevInfo& di, bool* yes) {
+  const void* fn = head_fn(p);
+  sv_status st = head_set_lds(fn, p.lds);
+  if (st) return st;
+  int per_cu = 0;
+  SV_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, HEAD_WAVES * 64, p.lds));
+  *yes = int64_t(per_cu) * di.cus >= p.grid && p.grid <= 64 * CNT_GROUPS;   // group merge: a lane per member
+  return SV_OK;
+}
+
+sv_status launch_head(const HeadPlan& p, HeadArgs a, hipStream_t s) {
+  a.gpt = p.gpt;
+  a.nloc = p.nloc;
+  const void* fn = head_fn(p);
+  sv_status st = head_set_lds(fn, p.lds);
+  if (st) return st;
+  void* args[] = {&a};
+  SV_HIP(hipLaunchKernel(fn, dim3(p.grid), dim3(HEAD_WAVES * 64), args, p.lds, s));
+  return SV_OK;
+}
+
+// A product out_s[M, N_s] = X[M, K] W_s^T for up to three weights sharing X: the
+// k-split kernel where it applies, else the 16-row streaming / chunked kernels.
+sv_status run_product(const bf16_t* X, int M, int K, int nseg, const void* const* W, float* const* out, const int* N,
+                      const DevInfo& di, hipStream_t s) {
+  const HeadPlan hp = plan_head(M, K, N, nseg, di);
+  if (hp.ok) {
+    HeadArgs a = head_args(X, M, K);
+    for (int i = 0; i < nseg; ++i) head_add_seg(a, W[i], out[i], N[i], 16 / hp.S);
+    a.write_out = 1;
+    a.mode = HEAD_PRODUCT;
+    return launch_head(hp, a, s);
+  }
+  GemmArgs a = gemm_args(X, M, K);
+  int tiles = 0;
+  for (int i = 0; i < nseg; ++i) { gemm_add_seg(a, W[i], out[i], N[i]); tiles += (N[i] + 15) / 16; }
+  return launch_gemm(plan_gemm(M, tiles, K, di.lds_max), a, di, s);
+}
+
+// ---------------------------------------------------------------------------
 // workspace layout
 struct Layout {
-  size_t counters = 0;   // 256 bytes of one-shot counters; zero before first use, left zero
+  size_t counters = 0;   // CNT_BYTES of one-shot counters; zero before first use, left zero
   size_t logits = 0, part = 0, state = 0, spart = 0, invalid = 0, xlogit = 0;
   size_t rope = 0, x = 0, h = 0, q = 0, k = 0, v = 0, attp = 0, att = 0, gate = 0, up = 0;
   size_t total = 0;
@@ -307,7 +447,7 @@ Layout plan(const sv_model* m, const Shape& sh, const sv_kv_cache* kv, bool need
   Layout L;
   Bump b;
   const int M = sh.M, V = sh.V;
-  L.counters = b.take(256);
+  L.counters = b.take(CNT_BYTES);
   if (need_logits_buf) L.logits = b.take(size_t(M) * V * 4);
   if (sh.kind == SV_IN_LOGITS) {
     L.P = (V + LCH - 1) / LCH;
@@ -317,11 +457,12 @@ Layout plan(const sv_model* m, const Shape& sh, const sv_kv_cache* kv, bool need
     L.head = plan_gemm(M, (V + 15) / 16, sh.decoder ? m->d_model : sh.d);
     L.P = L.head.grid_x_max;
   }
-  L.part = b.take(size_t(L.P) * M * sizeof(RowPart));
+  // per-workgroup partials of either product kernel, then the k-split kernel's group partials
+  L.part = b.take(size_t(std::max(L.P, GEMM_MAX_WG) + CNT_GROUPS) * M * sizeof(RowPart));
   L.state = b.take(size_t(sh.B) * sizeof(SeqState));
   L.xlogit = b.take(size_t(M) * 4);
   L.nch = (V + SAMPLE_CHUNK - 1) / SAMPLE_CHUNK;
-  if (sample) L.spart = b.take(size_t(sh.B) * L.nch * sizeof(SamplePart));
+  if (sample) L.spart = b.take(size_t(sh.B) * std::max(L.nch, GEMM_MAX_WG) * sizeof(SamplePart));   // either sampler
   L.invalid = b.take(size_t(sh.B) * 4);
   if (sh.decoder) {
     const int d = m->d_model, HD = m->n_heads * m->head_dim, ff = m->d_ff;
@@ -391,10 +532,6 @@ sv_status run_decoder(const sv_model* m, const Shape& sh, const int* tokens, con
                      sh.G1, sh.V, d);
   SV_HIP(hipGetLastError());
 
-  const GemmPlan pqkv = plan_gemm(M, 3 * ((HD + 15) / 16), d, di.lds_max);
-  const GemmPlan po = plan_gemm(M, (d + 15) / 16, HD, di.lds_max);
-  const GemmPlan pgu = plan_gemm(M, 2 * ((ff + 15) / 16), d, di.lds_max);
-  const GemmPlan pd = plan_gemm(M, (d + 15) / 16, ff, di.lds_max);
   const float scale = 1.0f / sqrtf(float(hd));
   // Residual adds are folded into the next RMSNorm: the output projections write
   // ``delta`` and the following k_add_rmsnorm adds it to x.
@@ -404,12 +541,13 @@ sv_status run_decoder(const sv_model* m, const Shape& sh, const int* tokens, con
     const void* const* w = m->layers + size_t(l) * 9;
     hipLaunchKernelGGL(k_add_rmsnorm, dim3(M), dim3(256), 0, s, x, pending, static_cast<const bf16_t*>(w[0]), h, d,
                        m->rms_eps);
-    GemmArgs a = gemm_args(h, M, d);
-    gemm_add_seg(a, w[1], q, HD);
-    gemm_add_seg(a, w[2], k, HD);
-    gemm_add_seg(a, w[3], v, HD);
-    sv_status st = launch_gemm(pqkv, a, di, s);
-    if (st) return st;
+    sv_status st;
+    {
+      const void* ws3[3] = {w[1], w[2], w[3]};
+      float* o3[3] = {q, k, v};
+      const int n3[3] = {HD, HD, HD};
+      if ((st = run_product(h, M, d, 3, ws3, o3, n3, di, s))) return st;
+    }
     hipLaunchKernelGGL(k_rope_append, dim3(M, H), dim3(hd / 2), 0, s, q, k, v, rope, kc, vc, kv->len, invalid, da, l);
     if (hd == 128)
       hipLaunchKernelGGL((k_attn<128>), dim3(L.S, H, sh.B), dim3(256), 0, s, q, kc, vc, kv->len, invalid, attp, da, l,
@@ -419,20 +557,28 @@ sv_status run_decoder(const sv_model* m, const Shape& sh, const int* tokens, con
                          L.S, scale);
     hipLaunchKernelGGL(k_attn_merge, dim3(M, H), dim3(hd), 0, s, attp, att, da, L.S);
     SV_HIP(hipGetLastError());
-    GemmArgs ao = gemm_args(att, M, HD);
-    gemm_add_seg(ao, w[4], delta, d);
-    if ((st = launch_gemm(po, ao, di, s))) return st;
+    {
+      const void* w1[1] = {w[4]};
+      float* o1[1] = {delta};
+      const int n1[1] = {d};
+      if ((st = run_product(att, M, HD, 1, w1, o1, n1, di, s))) return st;
+    }
     hipLaunchKernelGGL(k_add_rmsnorm, dim3(M), dim3(256), 0, s, x, delta, static_cast<const bf16_t*>(w[5]), h, d,
                        m->rms_eps);
-    GemmArgs agu = gemm_args(h, M, d);
-    gemm_add_seg(agu, w[6], gate, ff);
-    gemm_add_seg(agu, w[7], up, ff);
-    if ((st = launch_gemm(pgu, agu, di, s))) return st;
+    {
+      const void* w2[2] = {w[6], w[7]};
+      float* o2[2] = {gate, up};
+      const int n2[2] = {ff, ff};
+      if ((st = run_product(h, M, d, 2, w2, o2, n2, di, s))) return st;
+    }
     const int nf = M * ff;
     hipLaunchKernelGGL(k_silu_mul, dim3((nf + 255) / 256), dim3(256), 0, s, gate, up, h, nf);
-    GemmArgs ad = gemm_args(h, M, ff);
-    gemm_add_seg(ad, w[8], delta, d);
-    if ((st = launch_gemm(pd, ad, di, s))) return st;
+    {
+      const void* w1[1] = {w[8]};
+      float* o1[1] = {delta};
+      const int n1[1] = {d};
+      if ((st = run_product(h, M, ff, 1, w1, o1, n1, di, s))) return st;
+    }
     pending = delta;
   }
   hipLaunchKernelGGL(k_add_rmsnorm, dim3(M), dim3(256), 0, s, x, pending, static_cast<const bf16_t*>(m->final_norm), h,
@@ -441,14 +587,28 @@ sv_status run_decoder(const sv_model* m, const Shape& sh, const int* tokens, con
   return SV_OK;
 }
 
+// The rule inside the bf16 LM-head launch (k-split kernel).  Greedy: the whole
+// step.  Sampling: the whole step when every workgroup can be resident at once and
+// the batch fits the counter block's keys (logits stay on chip and are written only
+// to ``logits_out``); otherwise the acceptance, with the logits written to
+// ``logits`` for the separate sampler.
+struct HeadRule {
+  float* logits_out;
+  bool sample;
+  AcceptArgs acc;
+  bool done = false;      // nothing else to launch for the step
+  bool accepted = false;  // the acceptance ran (the sampler still has to)
+};
+
 // Logits of all slots plus (if part != NULL) the row-statistics partials.
 // Returns the number of partials per row in *P.
 // With ``acc`` non-null, the bf16 LM-head product records each slot's draft-token
 // logit; with ``fuse`` as well, its last workgroup runs the acceptance for all
-// sequences.
+// sequences.  With ``rule`` non-null the k-split kernel runs the rule when it fits
+// (rule->fused is then true and nothing else is launched for the step).
 sv_status run_logits(const sv_model* m, const Shape& sh, const void* input, const sv_kv_cache* kv,
                      const Layout& L, void* ws, float* logits, RowPart* part, float c, int* P, hipStream_t s,
-                     const AcceptArgs* acc = nullptr, bool fuse = false) {
+                     const AcceptArgs* acc = nullptr, bool fuse = false, HeadRule* rule = nullptr) {
   DevInfo di;
   sv_status st = dev_info(&di);
   if (st) return st;
@@ -483,6 +643,35 @@ sv_status run_logits(const sv_model* m, const Shape& sh, const void* input, cons
   }
   TimeScope ts(s, 0);
   const int K = sh.decoder ? m->d_model : sh.d;
+  const int Nv[1] = {V};
+  const HeadPlan hp = plan_head(M, K, Nv, 1, di);
+  if (hp.ok && (rule || !part)) {
+    HeadArgs a = head_args(hb, M, K);
+    float* out = rule ? rule->logits_out : logits;
+    a.mode = HEAD_PRODUCT;
+    if (rule) {
+      bool fused = !rule->sample;
+      if (rule->sample && (st = head_all_resident(hp, di, &fused))) return st;
+      a.mode = !rule->sample ? HEAD_ACCEPT : (fused ? HEAD_SAMPLE : HEAD_ACCEPT);
+      if (rule->sample && !fused) out = logits;      // the separate sampler reads them
+      a.part = part;
+      a.c_stat = c;
+      a.xlogit = at<float>(ws, L.xlogit);
+      a.counter = at<unsigned>(ws, L.counters);
+      a.acc = rule->acc;
+      a.acc.P = hp.grid;
+      a.acc.xlogit = a.xlogit;
+      a.spart = at<SamplePart>(ws, L.spart);
+      // SV_HEAD_SPIN_LIMIT lowers the bounded wait (tests force its timeout path with 0)
+      a.spin_limit = unsigned(env_int("SV_HEAD_SPIN_LIMIT", int(HEAD_SPIN_LIMIT)));
+      rule->done = fused;
+      rule->accepted = true;
+    }
+    head_add_seg(a, m->lm_head, out, V, 16 / hp.S);
+    a.write_out = out != nullptr;
+    *P = hp.grid;
+    return launch_head(hp, a, s);
+  }
   GemmArgs a = gemm_args(hb, M, K);
   gemm_add_seg(a, m->lm_head, logits, V);
   a.part = part;
@@ -549,12 +738,19 @@ sv_status verify_common(const sv_model* m, sv_input_kind kind, const void* input
   const bool fuse = bf16_head && sh.M <= FUSE_ACCEPT_MAX_ROWS;
   if (bf16_head) aa.xlogit = at<float>(ws, L.xlogit);
   int P = 0;
-  if ((st = run_logits(m, sh, input, kv, L, ws, logits, part, c, &P, s, bf16_head ? &aa : nullptr, fuse))) return st;
+  HeadRule rule;
+  rule.logits_out = logits_out;
+  rule.sample = sample;
+  rule.acc = aa;
+  if ((st = run_logits(m, sh, input, kv, L, ws, logits, part, c, &P, s, bf16_head ? &aa : nullptr, fuse,
+                       bf16_head ? &rule : nullptr)))
+    return st;
+  if (rule.done) return SV_OK;
   if (kind == SV_IN_LOGITS && logits_out)
     SV_HIP(hipMemcpyAsync(logits_out, input, size_t(sh.M) * sh.V * 4, hipMemcpyDeviceToDevice, s));
 
   TimeScope ts(s, 2);
-  if (!fuse) {
+  if (!fuse && !rule.accepted) {
     aa.P = P;
     hipLaunchKernelGGL(k_accept, dim3(sh.B), dim3(256), 0, s, aa);
     SV_HIP(hipGetLastError());

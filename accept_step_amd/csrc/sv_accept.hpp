@@ -26,6 +26,14 @@ struct SeqState {
   int pad;
 };
 
+// The state is read by other workgroups of the same launch in the fused sampler:
+// written through to the coherent memory side.
+__device__ __forceinline__ void store_state(SeqState* p, int n, float m, float z) {
+  store_coherent(&p->n, n);
+  store_coherent(&p->m, m);
+  store_coherent(&p->z, z);
+}
+
 // Best (score, index) of a vocabulary chunk for the residual and for p itself.
 struct SamplePart {
   float sr;
@@ -108,7 +116,7 @@ __device__ __forceinline__ void merge_row(const RowPart* __restrict__ part, int 
 #pragma unroll
     for (int u = 0; u < 8; ++u) merge_stat(m, s, am, rp[u].m, rp[u].s, rp[u].a, c);
   }
-  wave_merge_stat(m, s, am, c);
+  wave_allmerge_stat(m, s, am, c);
 }
 
 // Acceptance for sequences [b0, b0 + nb) by one workgroup of 256 threads.
@@ -141,7 +149,7 @@ __device__ __forceinline__ void accept_block(const AcceptArgs& a, int b0, int nb
       if (lane < G1) a.tokens_out[b * G1 + lane] = -1;
       if (lane == 0) {
         a.n_accepted[b] = -1;
-        if (a.sample) { SeqState st; st.n = -1; st.m = 0.f; st.z = 0.f; st.pad = 0; a.state[b] = st; }
+        if (a.sample) store_state(a.state + b, -1, 0.0f, 0.0f);
       }
       continue;
     }
@@ -177,9 +185,7 @@ __device__ __forceinline__ void accept_block(const AcceptArgs& a, int b0, int nb
         a.n_accepted[b] = n;
         if (a.len) a.len[b] += n + 1;
       } else {
-        SeqState st;
-        st.n = n; st.m = m_n; st.z = s_n; st.pad = 0;
-        a.state[b] = st;
+        store_state(a.state + b, n, m_n, s_n);
       }
     }
   }

@@ -93,9 +93,51 @@ __device__ __forceinline__ void wave_merge_stat(float& m, float& s, int& a, floa
   }
 }
 
+// DPP lane exchanges within rows of 16 lanes: xor 1, xor 2 (quad permutes), the
+// mirror of each half row and of the whole row.  After xor 1 and xor 2 every quad
+// holds one value, so the two mirrors complete a 16-lane butterfly; xor 16 and
+// xor 32 then go through the LDS crossbar.
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) { return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true); }
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) { return __int_as_float(dpp<CTRL>(__float_as_int(v))); }
+
+template <int CTRL>
+__device__ __forceinline__ void dpp_merge_stat(float& m, float& s, int& a, float c) {
+  merge_stat(m, s, a, dpp<CTRL>(m), dpp<CTRL>(s), dpp<CTRL>(a), c);
+}
+__device__ __forceinline__ void xor_merge_stat(float& m, float& s, int& a, float c, int o) {
+  merge_stat(m, s, a, __shfl_xor(m, o), __shfl_xor(s, o), __shfl_xor(a, o), c);
+}
+
+// Butterfly all-reduce of (max, sum, argmax) over the wavefront; every lane ends with
+// the same bits (each step merges the same two operands on both sides).
+__device__ __forceinline__ void wave_allmerge_stat(float& m, float& s, int& a, float c) {
+  dpp_merge_stat<DPP_XOR1>(m, s, a, c);
+  dpp_merge_stat<DPP_XOR2>(m, s, a, c);
+  dpp_merge_stat<DPP_HALF_MIRROR>(m, s, a, c);
+  dpp_merge_stat<DPP_MIRROR>(m, s, a, c);
+  xor_merge_stat(m, s, a, c, 16);
+  xor_merge_stat(m, s, a, c, 32);
+}
+
 // (score, index) argmax with lowest index on ties.
 __device__ __forceinline__ void merge_best(float& s, int& i, float s2, int i2) {
   if (s2 > s || (s2 == s && i2 < i)) { s = s2; i = i2; }
+}
+
+template <int CTRL>
+__device__ __forceinline__ void dpp_merge_best(float& s, int& i) { merge_best(s, i, dpp<CTRL>(s), dpp<CTRL>(i)); }
+
+__device__ __forceinline__ void wave_allmerge_best(float& s, int& i) {
+  dpp_merge_best<DPP_XOR1>(s, i);
+  dpp_merge_best<DPP_XOR2>(s, i);
+  dpp_merge_best<DPP_HALF_MIRROR>(s, i);
+  dpp_merge_best<DPP_MIRROR>(s, i);
+  merge_best(s, i, __shfl_xor(s, 16), __shfl_xor(i, 16));
+  merge_best(s, i, __shfl_xor(s, 32), __shfl_xor(i, 32));
 }
 
 __device__ __forceinline__ void wave_merge_best(float& s, int& i) {

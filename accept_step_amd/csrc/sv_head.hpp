@@ -1,0 +1,664 @@
+// sv_head.hpp -- the k-split streaming product and the fused verify kernel (gfx950).
+//
+// Same contraction as sv_gemm.hpp, out[m, v] = sum_k X[m, k] W[v, k] with W streamed
+// once from HBM, but with each load instruction covering whole 128-byte lines: HBM
+// reads with non-temporal loads reach about 7.2 TB/s on MI355X when every row
+// segment a wavefront touches is at least 128 contiguous bytes, against about 6.4
+// TB/s for the 64-byte row segments that the plain 16x16x32 operand layout gives.
+//
+// k-split virtual rows.  v_mfma_f32_16x16x32_bf16 multiplies a 16 x 32 operand A by
+// a 32 x 16 operand B.  Here the 16 rows of A are TR = 16 / S rows of W, each split
+// into S interleaved parts of its k range: virtual row r = (W row r / S, part r % S).
+// The 16 columns of B are likewise CPB = 16 / S rows of X times the same S parts.
+// Output entry (r, c) is a partial dot product when the parts of r and c agree and
+// meaningless otherwise; summing the S partials of a (W row, X row) pair over the
+// S lanes that hold them gives the product.  Lane (r, g) of step j reads 16-byte
+// piece 4S*j + S*g + r % S of W row r / S, so the 4S lanes of a W row read 64*S
+// contiguous bytes.  The matrix cores do S times more work per byte than needed,
+// which leaves them far from busy at these shapes (a few rows of X).
+//
+// The products of a workgroup's tiles are kept in LDS.  After the stream, the
+// workgroup writes them out if asked, reduces its share of every row to a
+// statistics partial (max, sum of exp((l - max)/T), lowest-index argmax), and
+// records the draft-token logits it owns.  Then, depending on the mode:
+//   HEAD_PRODUCT  nothing more (decoder projections, verify_forward);
+//   HEAD_ACCEPT   the last workgroup to finish applies the rule (greedy, or the
+//                 acceptance half of sampling);
+//   HEAD_SAMPLE   the whole sampling rule in one launch: after a grid barrier every
+//                 workgroup merges the partials and decides n for every sequence
+//                 (same inputs, same arithmetic, same result), draws the Gumbel-max
+//                 of row n over its own slice of the vocabulary straight from LDS,
+//                 and stores its slice winner; the last workgroup through merges the
+//                 winners and commits.  The barrier needs every workgroup resident at
+//                 once (the host checks the occupancy); its wait is bounded, and a
+//                 timed-out wait marks the step's outputs invalid instead of hanging.
+// The row statistics are folded tile by tile in the product's epilogue, where they
+// overlap the loads in flight.  Counts between workgroups are two-level (one counter
+// per XCD on its own cache line, then one at the top): hundreds of workgroups
+// incrementing one line at the same moment serialise for tens of microseconds.
+// Rule and sampler: [MTP-deep-dive] 2.2, [Infra-ch8] "why the output does not
+// change", [Self-spec] 3.1-3.3; see sv_accept.hpp.
+#pragma once
+
+#include "sv_accept.hpp"
+#include "sv_device.hpp"
+#include "sv_gemm.hpp"
+
+namespace sv {
+
+constexpr int HEAD_WAVES = 4;
+constexpr int HEAD_PRODUCT = 0, HEAD_ACCEPT = 1, HEAD_SAMPLE = 2;
+constexpr unsigned HEAD_SPIN_LIMIT = 1u << 20;   // default polls of the barrier count (about a second)
+
+// The counter block at the start of the workspace (zero between launches), in
+// 32-bit words.  Line 0: the top counts and a sticky error flag; lines 1-8: per-group
+// arrival counts; lines 9-16: per-group finishing counts.
+constexpr int CNT_BYTES = 4096;
+constexpr int CNT_LINE = 32;                      // words per 128-byte line
+constexpr int CNT_GROUPS = 8;                     // workgroups are dispatched round-robin over 8 XCDs
+constexpr int CNT_TOP_ARRIVE = 0, CNT_TOP_DONE = 1, CNT_ERROR = 2;
+constexpr int CNT_GRP_ARRIVE = 1 * CNT_LINE, CNT_GRP_DONE = 9 * CNT_LINE;
+
+struct HeadArgs {
+  const bf16_t* W[MAX_SEG];   // [N_s, K] row-major
+  float* out[MAX_SEG];        // [M, N_s] row-major (written when write_out)
+  int N[MAX_SEG];
+  int tile_end[MAX_SEG];      // cumulative TR-row tile counts
+  int nseg;
+  const bf16_t* X;            // [M, K]
+  int M, K;
+  int gpt;                    // work items per tile (K / (32 * S * GRP))
+  int nloc;                   // LDS products kept per X row: tiles per workgroup * TR
+  int write_out;
+  int mode;
+  // statistics and rule (single segment)
+  RowPart* part;              // [gridDim.x, M]; null: no statistics
+  float c_stat;               // log2(e) / T; 0 = max / argmax only
+  float* xlogit;              // [M] draft-token logits (rule modes)
+  unsigned* counter;          // the counter block
+  AcceptArgs acc;             // acc.P == gridDim.x
+  SamplePart* spart;          // [B, gridDim.x] slice winners (HEAD_SAMPLE)
+  unsigned spin_limit;        // polls of the barrier count before giving up
+};
+
+// Bytes of dynamic LDS: X rows (zero rows up to a whole number of column blocks,
+// each row padded by 16*S bytes so the lanes of a k-group hit distinct banks), then
+// the kept products.
+__host__ __device__ inline int head_rows_pad(int M, int S) { return (M * S + 15) / 16 * (16 / S); }
+__host__ __device__ inline size_t head_lds_x(int M, int K, int S) {
+  return (size_t(head_rows_pad(M, S)) * (K + 8 * S) * 2 + 15) / 16 * 16;
+}
+__host__ __device__ inline size_t head_lds(int M, int K, int S, int nloc) {
+  return head_lds_x(M, K, S) + size_t(M) * nloc * 4;
+}
+
+__device__ __forceinline__ TileRef head_tile(const HeadArgs& a, int tile, int TR) {
+  const int seg = (a.nseg > 1 && tile >= a.tile_end[0]) ? ((a.nseg > 2 && tile >= a.tile_end[1]) ? 2 : 1) : 0;
+  TileRef t;
+  t.W = pick(seg, a.W[0], a.W[1], a.W[2]);
+  t.out = pick(seg, a.out[0], a.out[1], a.out[2]);
+  t.N = pick(seg, a.N[0], a.N[1], a.N[2]);
+  t.v0 = (tile - pick(seg, 0, a.tile_end[0], a.tile_end[1])) * TR;
+  return t;
+}
+
+// Global tile of local tile ``lt`` of workgroup ``wg``: wavefront lt % 4, its (lt / 4)-th tile.
+__device__ __forceinline__ int head_global_tile(int wg, int lt, int grid) {
+  return wg * HEAD_WAVES + (lt % HEAD_WAVES) + (lt / HEAD_WAVES) * grid * HEAD_WAVES;
+}
+
+// W address of the lane's first piece in work item k of a wavefront whose tiles are
+// first, first + tstride, ...
+template <int S>
+__device__ __forceinline__ const bf16_t* head_item_ptr(const HeadArgs& a, int k, int first, int tstride, int r,
+                                                       int lane_ofs, int item_k) {
+  const int i = k / a.gpt, gg = k - i * a.gpt;
+  const TileRef tr = head_tile(a, first + i * tstride, 16 / S);
+  const int vrow = min(tr.v0 + r / S, tr.N - 1);
+  return tr.W + size_t(vrow) * a.K + lane_ofs + gg * item_k;
+}
+
+// Loads of one work item.  The scheduling barrier keeps them issued ahead of the
+// previous item's matrix work (the scheduler would otherwise sink them below it and
+// halve the loads in flight).
+template <int S, int NB, int GRP>
+__device__ __forceinline__ void head_load(const bf16_t* p, u32x4 (&buf)[GRP]) {
+#pragma unroll
+  for (int u = 0; u < GRP; ++u) buf[u] = load_stream16(p + 32 * S * u);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One work item: GRP steps of NB MFMAs.  The X operands of the item are read from
+// LDS in one batch (padding rows are zero, so no read is conditional).
+template <int S, int NB, int GRP>
+__device__ __forceinline__ void head_mfma(const u32x4 (&buf)[GRP], const bf16_t* xp, int xstride, int kofs,
+                                          f32x4 (&acc)[NB]) {
+  u32x4 x[GRP][NB];
+#pragma unroll
+  for (int u = 0; u < GRP; ++u)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      x[u][nb] = *reinterpret_cast<const u32x4*>(xp + nb * xstride + kofs + 32 * S * u);
+#pragma unroll
+  for (int u = 0; u < GRP; ++u)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma16x16x32(buf[u], x[u][nb], acc[nb]);
+}
+
+// Running row statistics of the lane: one (max, sum, argmax) per column block, for
+// X row nb * CPB + r / S (kept by the lanes with r % S == 0).
+template <int NB>
+struct HeadStats {
+  float m[NB], s[NB];
+  int a[NB];
+};
+
+// Finish a tile: sum the S partials of every useful output entry, keep the products
+// in LDS (sL[m * nloc + lt * TR + w]) and fold them into the running statistics.
+// v0: vocab index of the tile's first row (statistics only).
+template <int S, int NB>
+__device__ __forceinline__ void head_tile_done(f32x4 (&acc)[NB], float* sL, int nloc, int M, int lt, int r, int g,
+                                               bool stats, int v0, int N0, float c, HeadStats<NB>& st) {
+  constexpr int TR = 16 / S, CPB = 16 / S;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int m = nb * CPB + r / S;
+#pragma unroll
+    for (int t = 0; t < 4 / S; ++t) {
+      // lane (c = r, g) holds rows 4g + e; entry e is useful when e % S == r % S
+      float v = acc[nb][0];
+      const int e = r % S + S * t;
+#pragma unroll
+      for (int ee = 1; ee < 4; ++ee)
+        if (e == ee) v = acc[nb][ee];
+      if (S >= 2) v += dpp<DPP_XOR1>(v);
+      if (S >= 4) v += dpp<DPP_XOR2>(v);
+      const int w = (4 * g) / S + t;
+      if (r % S == 0 && m < M) {
+        sL[m * nloc + lt * TR + w] = v;
+        if (stats && v0 + w < N0) merge_stat(st.m[nb], st.s[nb], st.a[nb], v, c != 0.0f ? 1.0f : 0.0f, v0 + w, c);
+      }
+    }
+    acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// Local index of vocab entry x in workgroup wg's products, or -1 if another owns it.
+__device__ __forceinline__ int head_local_index(int x, int TR, int grid, int wg) {
+  const int t = x / TR;
+  const int span = grid * HEAD_WAVES;
+  if ((t % span) / HEAD_WAVES != wg) return -1;
+  const int lt = (t / span) * HEAD_WAVES + t % HEAD_WAVES;
+  return lt * TR + x % TR;
+}
+
+__device__ __forceinline__ unsigned atomic_add_agent(unsigned* p, unsigned v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void atomic_store_agent(unsigned* p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned load_coherent(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int load_coherent(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __uint_as_float(load_coherent(reinterpret_cast<const unsigned*>(p)));
+}
+
+// Two-level count, thread 0 only: the workgroup's group counter (blockIdx % groups)
+// and, for the last member of a group, the top counter.  Returns the top count after
+// this workgroup's contribution, or 0 if it did not reach the top.  A group's last
+// member resets its group counter (all members have counted).
+__device__ __forceinline__ unsigned count_two_level(unsigned* cnt, int grp_word, int top_word) {
+  const unsigned G = min(gridDim.x, unsigned(CNT_GROUPS));
+  const unsigned g = blockIdx.x % G;
+  const unsigned gsize = (gridDim.x - g + G - 1) / G;
+  unsigned* gc = cnt + grp_word + g * CNT_LINE;
+  if (atomic_add_agent(gc, 1u) != gsize - 1) return 0u;
+  atomic_store_agent(gc, 0u);
+  return atomic_add_agent(cnt + top_word, 1u) + 1u;
+}
+
+// Whether the calling workgroup is the last of the grid to pass this point (two-level
+// count).  Each workgroup first waits for its own stores (the handed-over data is
+// written with store_coherent, so completion means it reached the coherent side).
+// The last one resets the top counter and issues an acquire fence before reading.
+__device__ __forceinline__ bool last_workgroup_2l(unsigned* cnt, int grp_word, int top_word) {
+  __shared__ unsigned s_last;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned G = min(gridDim.x, unsigned(CNT_GROUPS));
+    const bool last = count_two_level(cnt, grp_word, top_word) == G;
+    if (last) atomic_store_agent(cnt + top_word, 0u);
+    s_last = last;
+  }
+  __syncthreads();
+  if (!s_last) return false;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return true;
+}
+
+// Raw bits of q[qrow + vb + e], e < 4 (bf16 zero-extended or float32), clamped to V - 1.
+__device__ __forceinline__ void load_q4(const AcceptArgs& ac, size_t qrow, int vb, unsigned (&o)[4]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int v = min(vb + e, ac.V - 1);
+    o[e] = ac.q_bf16 ? unsigned(reinterpret_cast<const bf16_t*>(ac.q)[qrow + v])
+                     : __float_as_uint(reinterpret_cast<const float*>(ac.q)[qrow + v]);
+  }
+}
+__device__ __forceinline__ float q_value(const AcceptArgs& ac, unsigned raw) {
+  return ac.q_bf16 ? __uint_as_float(raw << 16) : __uint_as_float(raw);
+}
+
+constexpr int HEAD_QPF = 8;   // (row, group) entries of q a thread prefetches for the draw
+// Vocab index of the first entry of the thread's k-th group of four (or >= V).
+__device__ __forceinline__ int head_group_v(int k, int nloc, int TR) {
+  const int j0 = 4 * (threadIdx.x + k * blockDim.x);
+  if (j0 >= nloc) return 0x7fffffff;
+  const int lt = j0 / TR;
+  return head_global_tile(blockIdx.x, lt, gridDim.x) * TR + (j0 - lt * TR);
+}
+
+// Gumbel noise G = -log(-log U) of the four vocab entries vb .. vb+3 at absolute
+// position pos of sequence b (Philox block vb / 4, tag 1).
+__device__ __forceinline__ void gumbel4(uint64_t seed, int b, uint64_t pos, int vb, float (&G)[4]) {
+  const Philox4 w = philox4x64_10(uint64_t(vb) >> 2, pos, uint64_t(b), TAG_GUMBEL, seed, 0);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) G[e] = -logf(-logf(gumbel_uniform_from_word(w.w[e])));
+}
+
+// Merge the statistics partials of the workgroups of group g (blockIdx % G == g) for
+// every row and store one group partial per row (coherent): wave w takes rows w,
+// w + 4, ...; lane k the k-th member (grids of up to 64 * G workgroups).
+__device__ __forceinline__ void head_group_merge(const RowPart* part, RowPart* gpart, int M, unsigned G, unsigned g,
+                                                 float c) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const unsigned gsize = (gridDim.x - g + G - 1) / G;
+  for (int row = wave; row < M; row += HEAD_WAVES) {
+    float m = -INFINITY, s = 0.0f;
+    int am = 0x7fffffff;
+    if (unsigned(lane) < gsize) {
+      const RowPart* q = part + size_t(g + G * lane) * M + row;
+      m = load_coherent(&q->m); s = load_coherent(&q->s); am = load_coherent(&q->a);
+    }
+    wave_allmerge_stat(m, s, am, c);
+    if (lane == 0) store_part(gpart + size_t(g) * M + row, m, s, am);
+  }
+}
+template <int S, int NB, int GRP>
+__global__ __launch_bounds__(HEAD_WAVES * 64) void k_head(HeadArgs a) {
+  constexpr int TR = 16 / S, CPB = 16 / S;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  bf16_t* sX = reinterpret_cast<bf16_t*>(smem);
+  float* sL = reinterpret_cast<float*>(smem + head_lds_x(a.M, a.K, S));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int ld = a.K + 8 * S;
+  const int ntiles = a.tile_end[a.nseg - 1];
+  const int M = a.M, nloc = a.nloc, N0 = a.N[0];
+  const AcceptArgs& ac = a.acc;
+  const bool rule = a.mode != HEAD_PRODUCT;
+  const bool sample = a.mode == HEAD_SAMPLE;
+  const bool stats = a.part != nullptr;
+  const int G1 = ac.gamma + 1;
+
+  // per-row inputs of the rule, fetched before the stream (their latency would
+  // otherwise land after it, behind the other workgroups' traffic)
+  __shared__ int s_draft[ACC_MAX_ROWS];
+  __shared__ float s_qx[ACC_MAX_ROWS], s_u[ACC_MAX_ROWS];
+  __shared__ int s_bad[ACC_MAX_ROWS];
+  __shared__ long long s_pos0[ACC_MAX_ROWS];
+
+  // stage all of X, zero rows up to NB * CPB; fetch the drafts
+  {
+    const int pieces = a.K / 8;
+    for (int t = threadIdx.x; t < NB * CPB * pieces; t += blockDim.x) {
+      const int row = t / pieces, c = t - row * pieces;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row < M) v = load16(a.X + size_t(row) * a.K + c * 8);
+      *reinterpret_cast<u32x4*>(sX + row * ld + c * 8) = v;
+    }
+    if (rule && threadIdx.x < M) {
+      const int b = threadIdx.x / G1, i = threadIdx.x - b * G1;
+      s_draft[threadIdx.x] = i < ac.gamma ? ac.draft[size_t(b) * ac.draft_stride + ac.draft_offset + i] : -1;
+    }
+    if (sample && threadIdx.x < ac.B) {
+      s_pos0[threadIdx.x] = ac.pos0[threadIdx.x];
+      s_bad[threadIdx.x] = ac.invalid ? ac.invalid[threadIdx.x] : 0;
+    }
+  }
+  __syncthreads();
+
+  const int lane_ofs = 8 * (S * g + r % S);       // element offset of the lane's piece in step 0
+  const bf16_t* xp = sX + (r / S) * ld + lane_ofs; // column block nb adds nb * CPB rows
+  const int xstride = CPB * ld;
+
+  const int first = blockIdx.x * HEAD_WAVES + wave, tstride = gridDim.x * HEAD_WAVES;
+  const int n_my = first < ntiles ? (ntiles - 1 - first) / tstride + 1 : 0;
+  const int items = n_my * a.gpt;
+  const int item_k = 32 * S * GRP;                // elements of a row per work item
+  u32x4 bufA[GRP], bufB[GRP];
+  if (items > 0) head_load<S, NB, GRP>(head_item_ptr<S>(a, 0, first, tstride, r, lane_ofs, item_k), bufA);
+
+  // sampling: q at each draft token and the acceptance uniforms, while the first loads fly
+  float my_qx = 0.0f;
+  if (sample && threadIdx.x < M) {
+    const int t = threadIdx.x, b = t / G1, i = t - b * G1;
+    const int x = s_draft[t];
+    if (x >= 0 && x < ac.V) {
+      const size_t qi = (size_t(b) * ac.gamma + i) * ac.V + x;
+      my_qx = ac.q_bf16 ? bf16_to_f32(reinterpret_cast<const bf16_t*>(ac.q)[qi])
+                        : reinterpret_cast<const float*>(ac.q)[qi];
+    }
+    s_u[t] = i < ac.gamma ? accept_uniform(ac.seed, uint64_t(b), uint64_t(s_pos0[b] + i + 1)) : 1.0f;
+  }
+
+  const int kg = (nloc / 4 + int(blockDim.x) - 1) / int(blockDim.x);   // groups of four per thread
+
+  HeadStats<NB> st;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) { st.m[nb] = -INFINITY; st.s[nb] = 0.0f; st.a[nb] = 0x7fffffff; }
+  const float c = a.c_stat;
+  if (items > 0) {
+    f32x4 acc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int k = 0;
+#define SV_HEAD_ITEM(KK, BUF)                                                                             \
+    {                                                                                                     \
+      const int i_ = (KK) / a.gpt, gg_ = (KK) - i_ * a.gpt;                                               \
+      head_mfma<S, NB, GRP>(BUF, xp, xstride, gg_ * item_k, acc);                                         \
+      if (gg_ == a.gpt - 1) {                                                                             \
+        head_tile_done<S, NB>(acc, sL, nloc, M, i_ * HEAD_WAVES + wave, r, g, stats,                      \
+                              (first + i_ * tstride) * TR, N0, c, st);                                    \
+      }                                                                                                   \
+    }
+    for (; k + 2 < items; k += 2) {
+      head_load<S, NB, GRP>(head_item_ptr<S>(a, k + 1, first, tstride, r, lane_ofs, item_k), bufB);
+      SV_HEAD_ITEM(k, bufA)
+      head_load<S, NB, GRP>(head_item_ptr<S>(a, k + 2, first, tstride, r, lane_ofs, item_k), bufA);
+      SV_HEAD_ITEM(k + 1, bufB)
+    }
+    if (k + 1 < items) {
+      head_load<S, NB, GRP>(head_item_ptr<S>(a, k + 1, first, tstride, r, lane_ofs, item_k), bufB);
+      SV_HEAD_ITEM(k, bufA)
+      SV_HEAD_ITEM(k + 1, bufB)
+    } else {
+      SV_HEAD_ITEM(k, bufA)
+    }
+#undef SV_HEAD_ITEM
+  }
+  if (sample && threadIdx.x < M) s_qx[threadIdx.x] = my_qx;
+
+  // ---- statistics partials: lanes of a row differ in g (xor 16, 32), then the waves
+  __shared__ float s_m[HEAD_WAVES][ACC_MAX_ROWS], s_s[HEAD_WAVES][ACC_MAX_ROWS];
+  __shared__ int s_a[HEAD_WAVES][ACC_MAX_ROWS];
+  if (stats) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      xor_merge_stat(st.m[nb], st.s[nb], st.a[nb], c, 16);
+      xor_merge_stat(st.m[nb], st.s[nb], st.a[nb], c, 32);
+      const int m = nb * CPB + r / S;
+      if (g == 0 && r % S == 0 && m < M) { s_m[wave][m] = st.m[nb]; s_s[wave][m] = st.s[nb]; s_a[wave][m] = st.a[nb]; }
+    }
+  }
+  __syncthreads();
+
+  const int tpw = nloc / TR;                      // local tiles per workgroup
+  // ---- write the products
+  if (a.write_out) {
+    for (int idx = threadIdx.x; idx < M * tpw; idx += blockDim.x) {
+      const int m = idx / tpw, lt = idx - m * tpw;
+      const int t = head_global_tile(blockIdx.x, lt, gridDim.x);
+      if (t >= ntiles) continue;
+      const TileRef tr = head_tile(a, t, TR);
+      const float* src = sL + m * nloc + lt * TR;
+      float* dst = tr.out + size_t(m) * tr.N + tr.v0;
+      if (tr.v0 + TR <= tr.N && (tr.N & 3) == 0 && (reinterpret_cast<uintptr_t>(tr.out) & 15) == 0) {
+#pragma unroll
+        for (int q = 0; q < TR; q += 4) *reinterpret_cast<f32x4*>(dst + q) = *reinterpret_cast<const f32x4*>(src + q);
+      } else {
+        for (int w = 0; w < TR && tr.v0 + w < tr.N; ++w) dst[w] = src[w];
+      }
+    }
+  }
+  if (!stats) return;
+
+  for (int m = threadIdx.x; m < M; m += blockDim.x) {
+    float rm = -INFINITY, rs = 0.0f;
+    int ra = 0x7fffffff;
+#pragma unroll
+    for (int w = 0; w < HEAD_WAVES; ++w) merge_stat(rm, rs, ra, s_m[w][m], s_s[w][m], s_a[w][m], c);
+    store_part(a.part + size_t(blockIdx.x) * M + m, rm, rs, ra);
+    // draft-token logit of this row, if this workgroup holds it
+    if (rule && a.xlogit) {
+      const int x = s_draft[m];
+      if (x >= 0 && x < N0) {
+        const int j = head_local_index(x, TR, gridDim.x, blockIdx.x);
+        if (j >= 0) store_coherent(a.xlogit + m, sL[m * nloc + j]);
+      }
+    }
+  }
+  if (!rule) return;
+  if (a.mode == HEAD_ACCEPT) {
+    if (last_workgroup_2l(a.counter, CNT_GRP_ARRIVE, CNT_TOP_ARRIVE)) accept_block(ac, 0, ac.B);
+    return;
+  }
+
+  // ---- HEAD_SAMPLE
+  // 1. arrive at the grid barrier (own partials and draft logits stored first)
+  const unsigned G = min(gridDim.x, unsigned(CNT_GROUPS));
+  __shared__ int s_ok;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // Two-level count: the last member of each group merges the group's partials
+  // first, so that afterwards every workgroup reads G group partials per row.
+  __shared__ unsigned s_grp_last;
+  RowPart* gpart = a.part + size_t(gridDim.x) * M;
+  if (threadIdx.x == 0) {
+    const unsigned g = blockIdx.x % G, gsize = (gridDim.x - g + G - 1) / G;
+    unsigned* gc = a.counter + CNT_GRP_ARRIVE + g * CNT_LINE;
+    s_grp_last = atomic_add_agent(gc, 1u) == gsize - 1;
+    if (s_grp_last) atomic_store_agent(gc, 0u);
+  }
+  __syncthreads();
+  unsigned seen = 0;
+  if (s_grp_last) {
+    head_group_merge(a.part, gpart, M, G, blockIdx.x % G, c);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) seen = atomic_add_agent(a.counter + CNT_TOP_ARRIVE, 1u) + 1u;
+  }
+
+  // 2. while the others arrive: fetch q over this slice for every drafted slot
+  const int npf = ac.B * ac.gamma * kg;
+  const bool prefetched = npf <= HEAD_QPF;
+  unsigned qpf[HEAD_QPF][4];
+#pragma unroll
+  for (int e = 0; e < HEAD_QPF; ++e) {
+    qpf[e][0] = qpf[e][1] = qpf[e][2] = qpf[e][3] = 0u;
+    if (prefetched && e < npf) {
+      const int rowslot = e / kg, k = e - rowslot * kg;
+      const int vb = head_group_v(k, nloc, TR);
+      if (vb < ac.V) load_q4(ac, size_t(rowslot) * ac.V, vb, qpf[e]);
+    }
+  }
+
+  // 3. wait until every group has arrived (bounded)
+  if (threadIdx.x == 0) {
+    unsigned spins = 0;
+    while (seen < G && spins++ < a.spin_limit) {
+      __builtin_amdgcn_s_sleep(1);
+      seen = load_coherent(a.counter + CNT_TOP_ARRIVE);
+    }
+    s_ok = seen >= G;
+    if (!s_ok) atomic_store_agent(a.counter + CNT_ERROR, 1u);
+  }
+  __syncthreads();
+  const bool ok = s_ok != 0;
+
+  // 4. every workgroup decides n for every sequence (same inputs, same arithmetic)
+  __shared__ int s_n[ACC_MAX_ROWS];
+  __shared__ float s_mn[ACC_MAX_ROWS], s_zn[ACC_MAX_ROWS];
+  if (ok) {
+    // draft logits of this wave's first sequence, in flight with the partials
+    float xl = (wave < ac.B && lane < ac.gamma) ? load_coherent(a.xlogit + wave * G1 + lane) : 0.0f;
+    // eight lanes per row (one per group partial), eight rows per wave and pass
+    for (int row0 = wave * 8; row0 < M; row0 += 8 * HEAD_WAVES) {
+      const int row = row0 + lane / 8, gp = lane % 8;
+      float m = -INFINITY, sm = 0.0f;
+      int am = 0x7fffffff;
+      if (row < M && unsigned(gp) < G) {
+        const RowPart* q = gpart + size_t(gp) * M + row;
+        m = load_coherent(&q->m); sm = load_coherent(&q->s); am = load_coherent(&q->a);
+      }
+      dpp_merge_stat<DPP_XOR1>(m, sm, am, c);
+      dpp_merge_stat<DPP_XOR2>(m, sm, am, c);
+      dpp_merge_stat<DPP_HALF_MIRROR>(m, sm, am, c);
+      if (gp == 0 && row < M) { s_m[0][row] = m; s_s[0][row] = sm; s_a[0][row] = am; }
+    }
+    __syncthreads();
+    for (int b = wave; b < ac.B; b += HEAD_WAVES) {
+      const int row = b * G1 + lane;
+      if (b != wave && lane < ac.gamma) xl = load_coherent(a.xlogit + row);
+      float my_m = -INFINITY, my_s = 0.0f;
+      float px = 0.0f, qx = 0.0f, u = 1.0f;
+      if (lane < G1) { my_m = s_m[0][row]; my_s = s_s[0][row]; }
+      if (lane < ac.gamma) {
+        const int x = s_draft[row];
+        u = s_u[row];
+        if (x >= 0 && x < ac.V) {
+          px = exp2f((xl - my_m) * c) / my_s;
+          qx = s_qx[row];
+        }
+      }
+      const bool acc_ok = double(u) * double(qx) < double(px);   // exact: 24-bit u times <= 24-bit q
+      const unsigned long long rej = __ballot(lane < ac.gamma && !acc_ok);
+      const int n = rej ? __ffsll(rej) - 1 : ac.gamma;
+      const float m_n = __shfl(my_m, n), z_n = __shfl(my_s, n);
+      if (lane == 0) { s_n[b] = s_bad[b] ? -1 : n; s_mn[b] = m_n; s_zn[b] = z_n; }
+    }
+    __syncthreads();
+  }
+
+  // 5. Gumbel-max of row n_b over this slice; one winner per (sequence, workgroup)
+  __shared__ float s_sr[HEAD_WAVES], s_sp[HEAD_WAVES];
+  __shared__ int s_ir[HEAD_WAVES], s_ip[HEAD_WAVES];
+  for (int b = 0; b < ac.B && ok; ++b) {
+    const int n = s_n[b];
+    float sr = -INFINITY, sp = -INFINITY;
+    int ir = 0x7fffffff, ip = 0x7fffffff;
+    if (n >= 0) {
+      const float mx = s_mn[b], z = s_zn[b];
+      const bool resid = n < ac.gamma;
+      const float* l = sL + (b * G1 + n) * nloc;
+      const uint64_t pos = uint64_t(s_pos0[b] + n + 1);
+      for (int k = 0; k < kg; ++k) {
+        const int j0 = 4 * (threadIdx.x + k * blockDim.x);
+        if (j0 >= nloc) break;
+        const int lt = j0 / TR;
+        const int vb = head_global_tile(blockIdx.x, lt, gridDim.x) * TR + (j0 - lt * TR);
+        if (vb >= ac.V) continue;
+        unsigned qr[4] = {0u, 0u, 0u, 0u};
+        if (resid) {
+          if (prefetched) {
+            const int want = (b * ac.gamma + n) * kg + k;
+#pragma unroll
+            for (int e = 0; e < HEAD_QPF; ++e)
+              if (e == want) { qr[0] = qpf[e][0]; qr[1] = qpf[e][1]; qr[2] = qpf[e][2]; qr[3] = qpf[e][3]; }
+          } else {
+            load_q4(ac, (size_t(b) * ac.gamma + n) * ac.V, vb, qr);
+          }
+        }
+        float gn[4];
+        gumbel4(ac.seed, b, pos, vb, gn);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int v = vb + e;
+          if (v >= ac.V) break;
+          const float Gv = gn[e];
+          const float p = exp2f((l[j0 + e] - mx) * ac.c) / z;
+          if (p > 0.0f) {
+            const float sc = logf(p) + Gv;
+            if (sc > sp) { sp = sc; ip = v; }
+          }
+          if (resid) {
+            const float rr = fmaxf(p - q_value(ac, qr[e]), 0.0f);
+            if (rr > 0.0f) {
+              const float sc = logf(rr) + Gv;
+              if (sc > sr) { sr = sc; ir = v; }
+            }
+          }
+        }
+      }
+    }
+    wave_allmerge_best(sr, ir);
+    wave_allmerge_best(sp, ip);
+    if (lane == 0) { s_sr[wave] = sr; s_ir[wave] = ir; s_sp[wave] = sp; s_ip[wave] = ip; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      SamplePart o;
+      o.sr = -INFINITY; o.ir = 0x7fffffff; o.sp = -INFINITY; o.ip = 0x7fffffff;
+      for (int w = 0; w < HEAD_WAVES; ++w) {
+        merge_best(o.sr, o.ir, s_sr[w], s_ir[w]);
+        merge_best(o.sp, o.ip, s_sp[w], s_ip[w]);
+      }
+      o.any_r = o.ir != 0x7fffffff;
+      o.pad[0] = o.pad[1] = o.pad[2] = 0;
+      store_spart(a.spart + size_t(b) * gridDim.x + blockIdx.x, o);
+    }
+    __syncthreads();
+  }
+
+  // 6. the last workgroup through merges the winners, writes the outputs and clears
+  //    the barrier count and the error flag
+  if (last_workgroup_2l(a.counter, CNT_GRP_DONE, CNT_TOP_DONE)) {
+    const bool failed = !ok || load_coherent(a.counter + CNT_ERROR) != 0u;
+    for (int b = wave; b < ac.B; b += HEAD_WAVES) {
+      const int n = failed ? -1 : s_n[b];
+      float sr = -INFINITY, sp = -INFINITY;
+      int ir = 0x7fffffff, ip = 0x7fffffff;
+      if (n >= 0) {
+        for (int p0 = 0; p0 < int(gridDim.x); p0 += 256) {
+          float qs[4], qp[4];
+          int qi[4], qj[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int p = p0 + lane + 64 * u;
+            qs[u] = -INFINITY; qp[u] = -INFINITY; qi[u] = 0x7fffffff; qj[u] = 0x7fffffff;
+            if (p < int(gridDim.x)) {
+              const SamplePart& q = a.spart[size_t(b) * gridDim.x + p];
+              qs[u] = q.sr; qi[u] = q.ir; qp[u] = q.sp; qj[u] = q.ip;
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) { merge_best(sr, ir, qs[u], qi[u]); merge_best(sp, ip, qp[u], qj[u]); }
+        }
+      }
+      wave_allmerge_best(sr, ir);
+      wave_allmerge_best(sp, ip);
+      const int tok = (n < ac.gamma && ir != 0x7fffffff) ? ir : ip;
+      if (lane < G1) {
+        int t = -1;
+        if (n >= 0 && lane < n) t = s_draft[b * G1 + lane];
+        else if (n >= 0 && lane == n) t = tok;
+        ac.tokens_out[b * G1 + lane] = t;
+      }
+      if (lane == 0) {
+        ac.n_accepted[b] = n;
+        if (ac.len && n >= 0) ac.len[b] += n + 1;
+      }
+    }
+    if (threadIdx.x == 0) {
+      atomic_store_agent(a.counter + CNT_TOP_ARRIVE, 0u);
+      atomic_store_agent(a.counter + CNT_ERROR, 0u);
+    }
+  }
+}
+
+}  // namespace sv

@@ -15,7 +15,8 @@ sum over steps of (n_accepted + 1) divided by the timed wall time between two
 device synchronisations.  ``roofline`` reports the LM-head product (the
 dominant kernel): algorithmic bytes per launch (W once plus the hidden
 states) over its average duration measured with HIP events on the stream the
-library launches it on, against the 8 TB/s HBM peak.  ``cpu_baseline`` times
+library launches it on, against the 8 TB/s HBM peak.  At this batch the whole step
+is that one kernel.  ``cpu_baseline`` times
 the CPU oracle (float64 numpy) on a bounded sample of the same workload.
 """
 import argparse
@@ -101,7 +102,7 @@ def main():
     torch.cuda.synchronize()
 
     # ---- timed region
-    sv.timing_enable(0b001)          # events around the LM-head product only
+    sv.timing_enable(0b001)          # events around the LM-head kernel (here the whole fused step)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -111,11 +112,15 @@ def main():
     gemm_ms, gemm_n = sv.timing_read(0)
     sv.timing_enable(0)
 
-    committed = int((n_out.to(torch.int64) + 1).sum().item())
+    n_host = n_out.to(torch.int64).cpu()
+    committed = int((n_host + 1).sum().item())
     value = committed / elapsed
     ms_per_step = elapsed / K * 1e3
     gemm_avg_s = gemm_ms / max(gemm_n, 1) * 1e-3
-    algo_bytes = 262144 * 1536 * 2 + B * (gamma + 1) * 1536 * 2
+    # algorithmic bytes of one step: W once, the hidden states, and the q row of each
+    # rejected sequence (the residual draw); the q gathers at the drafts are negligible
+    rejected = int((n_host < gamma).sum().item())
+    algo_bytes = 262144 * 1536 * 2 + B * (gamma + 1) * 1536 * 2 + rejected * 262144 * 2 / K
     achieved = algo_bytes / gemm_avg_s / 1e9
     traffic = committed_traffic(args.traffic_summary, root)
 
@@ -139,10 +144,11 @@ def main():
                    "verify_steps_per_s": round(K / elapsed, 1),
                    "step_hbm_gbs": round(algo_bytes / (elapsed / K) / 1e9, 1),
                    "step_frac_of_peak": round(algo_bytes / (elapsed / K) / 1e9 / HBM_PEAK_GBS, 4)},
-        "roofline": {"bound": "hbm", "kernel": "k_gemm_stream (LM-head product + row statistics)",
+        "roofline": {"bound": "hbm", "kernel": "k_head (fused verify step: LM-head product, row statistics, "
+                                                "acceptance, residual/bonus draw, commit)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": algo_bytes, "avg_launch_us": round(gemm_avg_s * 1e6, 2),
+                     "algorithmic_bytes_per_launch": round(algo_bytes), "avg_launch_us": round(gemm_avg_s * 1e6, 2),
                      "launches": gemm_n},
     }
     if not args.no_cpu_baseline:
@@ -172,7 +178,7 @@ def committed_traffic(path, root):
 def kernel_source_hash(root):
     import hashlib
     h = hashlib.sha256()
-    for f in ("sv_gemm.hpp", "sv_device.hpp"):
+    for f in ("sv_head.hpp", "sv_accept.hpp", "sv_gemm.hpp", "sv_device.hpp"):
         h.update(open(os.path.join(root, "accept_step_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 

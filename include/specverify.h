@@ -27,9 +27,9 @@
  *   Workspace: scratch is caller-provided.  Call once with ws == NULL: the
  *             required size is written to *ws_bytes, nothing is launched, and
  *             SV_OK is returned.  Then call with ws != NULL and *ws_bytes >= that
- *             size (256-byte aligned).  The first 256 bytes hold one-shot
- *             counters (the last workgroup of a kernel to finish completes the
- *             step): a new workspace must be zero-filled once before its first
+ *             size (256-byte aligned).  The first 4096 bytes hold one-shot
+ *             counters (workgroups of one launch hand work to each other through
+ *             them): a new workspace must be zero-filled once before its first
  *             use, and every call leaves those bytes zero again.  The rest of the
  *             workspace need not be initialised and is undefined afterwards.
  *   Streams:  stream is a hipStream_t (NULL = the null stream).  All work is
@@ -183,9 +183,10 @@ const char* sv_last_error(void);
 
 /* Kernel timing with HIP events recorded on the caller's stream around the
  * launches of one kernel class.  Classes: 0 = LM-head product (the dominant
- * kernel of the LM-head configurations; with a small batch it also runs the
- * acceptance in its last workgroup), 1 = decoder layers, 2 = acceptance tail
- * (separate acceptance kernel, resampler).  sv_timing_enable(mask) records the
+ * kernel of the LM-head configurations; with a small batch it also applies the
+ * rule and, for sampling, draws and commits: the whole step in one kernel),
+ * 1 = decoder layers, 2 = acceptance tail (separate acceptance kernel,
+ * resampler, where the batch is too large for the fused step).  sv_timing_enable(mask) records the
  * classes whose bit is set in mask (0 = off) and clears earlier records;
  * sv_timing_read synchronises on the recorded events and returns the summed
  * milliseconds and launch count of class ``which``.  Off by default; costs two

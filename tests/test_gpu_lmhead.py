@@ -218,6 +218,13 @@ SMALL = [
     (4096, 1536, 8, 4, 0.0),    # M = 40
     (4096, 1536, 8, 4, 0.7),
     (4096, 256, 4, 15, 0.0),    # M = 64
+    # k-split product with split factor 4 (K % 512 == 0 or K = 1536), 1-5 column blocks
+    (777, 1024, 1, 1, 1.0),     # M = 2
+    (3001, 512, 1, 4, 1.0),     # M = 5: two blocks
+    (4099, 512, 3, 3, 0.7),     # M = 12: three blocks
+    (1000, 1024, 4, 3, 0.0),    # M = 16: four blocks, greedy
+    (2503, 512, 4, 4, 1.0),     # M = 20: five blocks
+    (2503, 1536, 2, 4, 1.0),    # M = 10, the large-vocabulary hidden size
 ]
 
 
@@ -267,3 +274,29 @@ def test_fp32_head_ragged():
     n0, t0, fl = rules.verify_greedy(ref, draft)
     compare_decisions(n.cpu().numpy(), tok.cpu().numpy(), n0, t0, fl, "fp32 ragged")
     assert n.cpu().numpy().tolist() == [4, 2]
+
+
+def test_fused_sampler_wait_timeout(monkeypatch):
+    """The fused sampler's grid barrier waits a bounded number of polls.  With the
+    bound forced to zero from the host, every workgroup but the last to arrive gives
+    up: the step must mark every sequence invalid (n = -1, tokens -1) instead of
+    drawing from partial data, and leave the workspace's counters clean, so that the
+    next step on the same workspace matches the oracle."""
+    V, d, B, gamma, T = 65536, 512, 2, 4, 1.0
+    cs = small_case(V, d, B, gamma, T, seed=99)
+    ref = oracle_logits_bf16(cs.h, cs.w)
+    model = sv.lm_head_model(dev_bf16(cs.w))
+    ws = sv.Workspace()
+    args = (model, sv.SV_IN_HIDDEN, dev_bf16(cs.h), B, gamma, dev(cs.draft.astype(np.int32)), dev_bf16(cs.q), T,
+            cs.seed, dev(cs.pos0))
+    monkeypatch.setenv("SV_HEAD_SPIN_LIMIT", "0")
+    n, tok = sv.spec_verify_sample(*args, ws=ws)
+    torch.cuda.synchronize()
+    log(f"[timeout] n={n.cpu().numpy().tolist()}")
+    assert (n.cpu().numpy() == -1).all() and (tok.cpu().numpy() == -1).all()
+    monkeypatch.delenv("SV_HEAD_SPIN_LIMIT")
+    n, tok = sv.spec_verify_sample(*args, ws=ws)
+    torch.cuda.synchronize()
+    n0, t0, fl = oracle_case(cs, ref)
+    compare_decisions(n.cpu().numpy(), tok.cpu().numpy(), n0, t0, fl, "after timeout")
+    assert (ws.buf[:4096] == 0).all()

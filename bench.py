@@ -43,7 +43,7 @@ def parse():
                     help="before timing, copy a buffer of this many MiB five times (a plain copy kernel of known "
                          "size, used to scale the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--traffic-summary", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                                                              "lmhead_config3_traffic.md"))
+                                                              "k_head_vocab262144_d1536_B1_traffic.md"))
     return ap.parse_args()
 
 

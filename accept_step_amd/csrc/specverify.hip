@@ -293,6 +293,8 @@ int head_nb_max(int S) { return S == 4 ? 5 : 3; }
 HeadPlan plan_head(int M, int K, const int* N, int nseg, const DevInfo& di) {
   HeadPlan p;
   if (M < 1 || M > ACC_MAX_ROWS || K % 8) return p;
+  for (int i = 0; i < nseg; ++i)    // weights are addressed with 32-bit byte offsets
+    if (int64_t(N[i]) * K * 2 > int64_t(0xffffffffLL) - 4096) return p;
   const int want_s = env_int("SV_HEAD_S", 0), want_grp = env_int("SV_HEAD_GRP", 0);
   const int per_cu = std::max(1, env_int("SV_HEAD_WG_PER_CU", 1));
   for (int S : {4, 2}) {
@@ -301,7 +303,7 @@ HeadPlan plan_head(int M, int K, const int* N, int nseg, const DevInfo& di) {
     if (NB > head_nb_max(S) || K % (32 * S)) continue;
     const int steps = K / (32 * S);
     int GRP = 0;
-    for (int gc : {8, 6, 4}) {
+    for (int gc : {4, 8, 6}) {   // two items of 4 loads per lane in flight measured best (2, 3, 6, 8 slower)
       if (want_grp && gc != want_grp) continue;
       if (steps % gc == 0) { GRP = gc; break; }
     }

@@ -56,7 +56,7 @@ __device__ __forceinline__ void store_coherent(int* p, int v) {
 // ---------------------------------------------------------------------------
 // Row statistics partial: running max, sum of exp((l - max) / T), argmax.
 // The argmax keeps the lowest index on ties.
-struct RowPart {
+struct alignas(16) RowPart {
   float m;
   float s;
   int a;
@@ -64,8 +64,8 @@ struct RowPart {
 };
 
 __device__ __forceinline__ void store_part(RowPart* p, float m, float s, int a) {
-  store_coherent(&p->m, m);
-  store_coherent(&p->s, s);
+  const unsigned long long ms = (static_cast<unsigned long long>(__float_as_uint(s)) << 32) | __float_as_uint(m);
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), ms, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   store_coherent(&p->a, a);
 }
 

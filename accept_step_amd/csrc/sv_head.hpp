@@ -107,24 +107,47 @@ __device__ __forceinline__ int head_global_tile(int wg, int lt, int grid) {
   return wg * HEAD_WAVES + (lt % HEAD_WAVES) + (lt / HEAD_WAVES) * grid * HEAD_WAVES;
 }
 
-// W address of the lane's first piece in work item k of a wavefront whose tiles are
-// first, first + tstride, ...
-template <int S>
-__device__ __forceinline__ const bf16_t* head_item_ptr(const HeadArgs& a, int k, int first, int tstride, int r,
-                                                       int lane_ofs, int item_k) {
-  const int i = k / a.gpt, gg = k - i * a.gpt;
-  const TileRef tr = head_tile(a, first + i * tstride, 16 / S);
-  const int vrow = min(tr.v0 + r / S, tr.N - 1);
-  return tr.W + size_t(vrow) * a.K + lane_ofs + gg * item_k;
+// Weights are read through buffer descriptors (one per segment, bounded to the
+// segment's bytes): 32-bit offsets from a scalar base leave less vector address work
+// per load than 64-bit global addresses (805 MB streamed in 109 us against 112 us),
+// and reads past the segment's end return zeros, so the rows beyond N of a ragged last
+// tile need no clamping (their products are discarded).
+struct HeadItem {
+  __amdgpu_buffer_rsrc_t rs;
+  unsigned soff;              // byte offset of the item within its segment (uniform)
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const bf16_t* W, int N, int K) {
+  // The tile (hence the segment) is uniform over the wavefront; saying so keeps the
+  // descriptor in scalar registers (otherwise every load becomes a loop over lanes).
+  const uint64_t wp = reinterpret_cast<uint64_t>(W);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(wp)), hi = __builtin_amdgcn_readfirstlane(uint32_t(wp >> 32));
+  void* base = reinterpret_cast<void*>((uint64_t(hi) << 32) | lo);
+  const int bytes = __builtin_amdgcn_readfirstlane(int(unsigned(N) * unsigned(K) * 2u));
+  // raw buffer, no stride; num_records = the segment's bytes (below 4 GB, checked on the host)
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, 0x00020000);
 }
 
-// Loads of one work item.  The scheduling barrier keeps them issued ahead of the
-// previous item's matrix work (the scheduler would otherwise sink them below it and
-// halve the loads in flight).
+// Work item k of a wavefront whose tiles are first, first + tstride, ...: the segment's
+// descriptor and the item's offset.  The lane adds (r / S) * K * 2 + its piece offset.
+template <int S>
+__device__ __forceinline__ HeadItem head_item(const HeadArgs& a, int k, int first, int tstride, int item_k) {
+  const int i = k / a.gpt, gg = k - i * a.gpt;
+  const TileRef tr = head_tile(a, first + i * tstride, 16 / S);
+  HeadItem it;
+  it.rs = head_rsrc(tr.W, tr.N, a.K);
+  it.soff = __builtin_amdgcn_readfirstlane((unsigned(tr.v0) * unsigned(a.K) + unsigned(gg * item_k)) * 2u);
+  return it;
+}
+
+// Loads of one work item (non-temporal: each byte is used once).  The scheduling
+// barrier keeps them issued ahead of the previous item's matrix work (the scheduler
+// would otherwise sink them below it and halve the loads in flight).
 template <int S, int NB, int GRP>
-__device__ __forceinline__ void head_load(const bf16_t* p, u32x4 (&buf)[GRP]) {
+__device__ __forceinline__ void head_load(const HeadItem& it, unsigned voff, u32x4 (&buf)[GRP]) {
 #pragma unroll
-  for (int u = 0; u < GRP; ++u) buf[u] = load_stream16(p + 32 * S * u);
+  for (int u = 0; u < GRP; ++u)
+    buf[u] = __builtin_amdgcn_raw_buffer_load_b128(it.rs, voff + 64u * S * u, it.soff, 2 /* nt */);
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -207,6 +230,14 @@ __device__ __forceinline__ int load_coherent(const int* p) {
 __device__ __forceinline__ float load_coherent(const float* p) {
   return __uint_as_float(load_coherent(reinterpret_cast<const unsigned*>(p)));
 }
+// (m, s, a) of a partial written by another workgroup: (m, s) as one 8-byte load.
+__device__ __forceinline__ void load_part_coherent(const RowPart* q, float& m, float& s, int& a) {
+  const unsigned long long ms =
+      __hip_atomic_load(reinterpret_cast<const unsigned long long*>(q), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  m = __uint_as_float(unsigned(ms));
+  s = __uint_as_float(unsigned(ms >> 32));
+  a = load_coherent(&q->a);
+}
 
 // Two-level count, thread 0 only: the workgroup's group counter (blockIdx % groups)
 // and, for the last member of a group, the top counter.  Returns the top count after
@@ -265,11 +296,12 @@ __device__ __forceinline__ int head_group_v(int k, int nloc, int TR) {
 }
 
 // Gumbel noise G = -log(-log U) of the four vocab entries vb .. vb+3 at absolute
-// position pos of sequence b (Philox block vb / 4, tag 1).
+// position pos of sequence b (Philox block vb / 4, tag 1).  U lies in [2^-24, 1), so
+// both logarithms take normal arguments and the hardware logarithm serves.
 __device__ __forceinline__ void gumbel4(uint64_t seed, int b, uint64_t pos, int vb, float (&G)[4]) {
   const Philox4 w = philox4x64_10(uint64_t(vb) >> 2, pos, uint64_t(b), TAG_GUMBEL, seed, 0);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) G[e] = -logf(-logf(gumbel_uniform_from_word(w.w[e])));
+  for (int e = 0; e < 4; ++e) G[e] = -__logf(-__logf(gumbel_uniform_from_word(w.w[e])));
 }
 
 // Merge the statistics partials of the workgroups of group g (blockIdx % G == g) for
@@ -282,16 +314,13 @@ __device__ __forceinline__ void head_group_merge(const RowPart* part, RowPart* g
   for (int row = wave; row < M; row += HEAD_WAVES) {
     float m = -INFINITY, s = 0.0f;
     int am = 0x7fffffff;
-    if (unsigned(lane) < gsize) {
-      const RowPart* q = part + size_t(g + G * lane) * M + row;
-      m = load_coherent(&q->m); s = load_coherent(&q->s); am = load_coherent(&q->a);
-    }
+    if (unsigned(lane) < gsize) load_part_coherent(part + size_t(g + G * lane) * M + row, m, s, am);
     wave_allmerge_stat(m, s, am, c);
     if (lane == 0) store_part(gpart + size_t(g) * M + row, m, s, am);
   }
 }
 template <int S, int NB, int GRP>
-__global__ __launch_bounds__(HEAD_WAVES * 64) void k_head(HeadArgs a) {
+__global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_head(HeadArgs a) {
   constexpr int TR = 16 / S, CPB = 16 / S;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   bf16_t* sX = reinterpret_cast<bf16_t*>(smem);
@@ -343,7 +372,8 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) void k_head(HeadArgs a) {
   const int items = n_my * a.gpt;
   const int item_k = 32 * S * GRP;                // elements of a row per work item
   u32x4 bufA[GRP], bufB[GRP];
-  if (items > 0) head_load<S, NB, GRP>(head_item_ptr<S>(a, 0, first, tstride, r, lane_ofs, item_k), bufA);
+  const unsigned voff = (unsigned(r / S) * unsigned(a.K) + unsigned(lane_ofs)) * 2u;   // the lane's W bytes
+  if (items > 0) head_load<S, NB, GRP>(head_item<S>(a, 0, first, tstride, item_k), voff, bufA);
 
   // sampling: q at each draft token and the acceptance uniforms, while the first loads fly
   float my_qx = 0.0f;
@@ -379,13 +409,13 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) void k_head(HeadArgs a) {
       }                                                                                                   \
     }
     for (; k + 2 < items; k += 2) {
-      head_load<S, NB, GRP>(head_item_ptr<S>(a, k + 1, first, tstride, r, lane_ofs, item_k), bufB);
+      head_load<S, NB, GRP>(head_item<S>(a, k + 1, first, tstride, item_k), voff, bufB);
       SV_HEAD_ITEM(k, bufA)
-      head_load<S, NB, GRP>(head_item_ptr<S>(a, k + 2, first, tstride, r, lane_ofs, item_k), bufA);
+      head_load<S, NB, GRP>(head_item<S>(a, k + 2, first, tstride, item_k), voff, bufA);
       SV_HEAD_ITEM(k + 1, bufB)
     }
     if (k + 1 < items) {
-      head_load<S, NB, GRP>(head_item_ptr<S>(a, k + 1, first, tstride, r, lane_ofs, item_k), bufB);
+      head_load<S, NB, GRP>(head_item<S>(a, k + 1, first, tstride, item_k), voff, bufB);
       SV_HEAD_ITEM(k, bufA)
       SV_HEAD_ITEM(k + 1, bufB)
     } else {
@@ -475,8 +505,10 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) void k_head(HeadArgs a) {
     if (threadIdx.x == 0) seen = atomic_add_agent(a.counter + CNT_TOP_ARRIVE, 1u) + 1u;
   }
 
-  // 2. while the others arrive: fetch q over this slice for every drafted slot
-  const int npf = ac.B * ac.gamma * kg;
+  // 2. while the others arrive: fetch q over this slice for every drafted slot, for the
+  //    residual draw after the decision (about gamma rows x 2 bytes x V per step;
+  //    issuing it at kernel start instead measured no faster)
+  const int npf = sample ? ac.B * ac.gamma * kg : 0;
   const bool prefetched = npf <= HEAD_QPF;
   unsigned qpf[HEAD_QPF][4];
 #pragma unroll
@@ -513,10 +545,7 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) void k_head(HeadArgs a) {
       const int row = row0 + lane / 8, gp = lane % 8;
       float m = -INFINITY, sm = 0.0f;
       int am = 0x7fffffff;
-      if (row < M && unsigned(gp) < G) {
-        const RowPart* q = gpart + size_t(gp) * M + row;
-        m = load_coherent(&q->m); sm = load_coherent(&q->s); am = load_coherent(&q->a);
-      }
+      if (row < M && unsigned(gp) < G) load_part_coherent(gpart + size_t(gp) * M + row, m, sm, am);
       dpp_merge_stat<DPP_XOR1>(m, sm, am, c);
       dpp_merge_stat<DPP_XOR2>(m, sm, am, c);
       dpp_merge_stat<DPP_HALF_MIRROR>(m, sm, am, c);
@@ -554,7 +583,8 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) void k_head(HeadArgs a) {
     float sr = -INFINITY, sp = -INFINITY;
     int ir = 0x7fffffff, ip = 0x7fffffff;
     if (n >= 0) {
-      const float mx = s_mn[b], z = s_zn[b];
+      // log p = (l - max) * c * ln 2 - ln z exactly; p itself only for the residual
+      const float mx = s_mn[b], z = s_zn[b], lnz = logf(z), inv_z = 1.0f / z;
       const bool resid = n < ac.gamma;
       const float* l = sL + (b * G1 + n) * nloc;
       const uint64_t pos = uint64_t(s_pos0[b] + n + 1);
@@ -582,15 +612,13 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) void k_head(HeadArgs a) {
           const int v = vb + e;
           if (v >= ac.V) break;
           const float Gv = gn[e];
-          const float p = exp2f((l[j0 + e] - mx) * ac.c) / z;
-          if (p > 0.0f) {
-            const float sc = logf(p) + Gv;
-            if (sc > sp) { sp = sc; ip = v; }
-          }
+          const float t = (l[j0 + e] - mx) * ac.c;
+          const float scp = t * LN2 - lnz + Gv;
+          if (scp > sp) { sp = scp; ip = v; }
           if (resid) {
-            const float rr = fmaxf(p - q_value(ac, qr[e]), 0.0f);
+            const float rr = fmaxf(exp2f(t) * inv_z - q_value(ac, qr[e]), 0.0f);
             if (rr > 0.0f) {
-              const float sc = logf(rr) + Gv;
+              const float sc = __logf(rr) + Gv;
               if (sc > sr) { sr = sc; ir = v; }
             }
           }
@@ -631,9 +659,9 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) void k_head(HeadArgs a) {
           for (int u = 0; u < 4; ++u) {
             const int p = p0 + lane + 64 * u;
             qs[u] = -INFINITY; qp[u] = -INFINITY; qi[u] = 0x7fffffff; qj[u] = 0x7fffffff;
-            if (p < int(gridDim.x)) {
-              const SamplePart& q = a.spart[size_t(b) * gridDim.x + p];
-              qs[u] = q.sr; qi[u] = q.ir; qp[u] = q.sp; qj[u] = q.ip;
+            if (p < int(gridDim.x)) {   // (sr, ir, sp, ip) in one 16-byte load
+              const u32x4 q = *reinterpret_cast<const u32x4*>(a.spart + size_t(b) * gridDim.x + p);
+              qs[u] = __uint_as_float(q[0]); qi[u] = int(q[1]); qp[u] = __uint_as_float(q[2]); qj[u] = int(q[3]);
             }
           }
 #pragma unroll

@@ -15,8 +15,9 @@ sum over steps of (n_accepted + 1) divided by the timed wall time between two
 device synchronisations.  ``roofline`` reports the LM-head product (the
 dominant kernel): algorithmic bytes per launch (W once plus the hidden
 states) over its average duration measured with HIP events on the stream the
-library launches it on, against the 8 TB/s HBM peak.  At this batch the whole step
-is that one kernel.  ``cpu_baseline`` times
+library launches it on (one event pair around the timed loop; a step is one launch
+of that kernel here, so this is its duration per launch including launch gaps),
+against the 8 TB/s HBM peak.  ``cpu_baseline`` times
 the CPU oracle (float64 numpy) on a bounded sample of the same workload.
 """
 import argparse
@@ -101,16 +102,22 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # ---- timed region
-    sv.timing_enable(0b001)          # events around the LM-head kernel (here the whole fused step)
+    # ---- timed region.  One pair of HIP events on the stream the library launches on
+    # (torch's current stream) brackets the K launches: at this batch a step is one
+    # launch of the fused kernel, so the event time over K is that kernel's average
+    # duration per launch, launch gaps included (an upper bound on its own duration).
+    # Events around every launch would cost the GPU ~7 us per step on this system.
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(K):
         step(i, out=(n_out[i], t_out[i]))
+    ev1.record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    gemm_ms, gemm_n = sv.timing_read(0)
-    sv.timing_enable(0)
+    gemm_ms, gemm_n = ev0.elapsed_time(ev1), K
 
     n_host = n_out.to(torch.int64).cpu()
     committed = int((n_host + 1).sum().item())
@@ -149,6 +156,7 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": round(algo_bytes), "avg_launch_us": round(gemm_avg_s * 1e6, 2),
+                     "timing": "HIP events around the timed loop on the launch stream (duration per launch, gaps included)",
                      "launches": gemm_n},
     }
     if not args.no_cpu_baseline:

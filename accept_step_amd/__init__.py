@@ -190,11 +190,16 @@ class KVCache:
 
 class Workspace:
     """Caller-owned scratch for the library, grown on demand (one per device).
-    Allocated zero-filled: the library's counters in its first 4096 bytes start
-    at zero and every call leaves them zero."""
+    Allocated zero-filled, as the library requires of a new workspace (it keeps
+    counters and a launch epoch in it between calls).  ``reset()`` zero-fills it
+    again, e.g. after a step that timed out."""
 
     def __init__(self):
         self.buf = None
+
+    def reset(self):
+        if self.buf is not None:
+            self.buf.zero_()
 
     def get(self, nbytes, device):
         if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:

@@ -422,7 +422,7 @@ sv_status run_product(const bf16_t* X, int M, int K, int nseg, const void* const
 // workspace layout
 struct Layout {
   size_t counters = 0;   // CNT_BYTES of one-shot counters; zero before first use, left zero
-  size_t logits = 0, part = 0, state = 0, spart = 0, invalid = 0, xlogit = 0;
+  size_t logits = 0, part = 0, state = 0, spart = 0, invalid = 0, xlogit = 0, recs = 0;
   size_t rope = 0, x = 0, h = 0, q = 0, k = 0, v = 0, attp = 0, att = 0, gate = 0, up = 0;
   size_t total = 0;
   int P = 0;          // row-statistics partials per row
@@ -466,6 +466,11 @@ Layout plan(const sv_model* m, const Shape& sh, const sv_kv_cache* kv, bool need
   L.nch = (V + SAMPLE_CHUNK - 1) / SAMPLE_CHUNK;
   if (sample) L.spart = b.take(size_t(sh.B) * std::max(L.nch, GEMM_MAX_WG) * sizeof(SamplePart));   // either sampler
   L.invalid = b.take(size_t(sh.B) * 4);
+  // the fused sampler's epoch-tagged hand-off records (k-split kernel with a bf16 head and
+  // at most ACC_MAX_ROWS rows; grids up to GEMM_MAX_WG)
+  const bool bf16_head = sh.kind != SV_IN_LOGITS && !(sh.kind == SV_IN_HIDDEN && m->wdtype == SV_F32);
+  if (sample && bf16_head && M <= ACC_MAX_ROWS)
+    L.recs = b.take((size_t(GEMM_MAX_WG + CNT_GROUPS) * M * 4 + M + size_t(sh.B) * GEMM_MAX_WG * 4) * 8);
   if (sh.decoder) {
     const int d = m->d_model, HD = m->n_heads * m->head_dim, ff = m->d_ff;
     L.S = att_splits(kv);
@@ -664,6 +669,8 @@ sv_status run_logits(const sv_model* m, const Shape& sh, const void* input, cons
       a.acc.P = hp.grid;
       a.acc.xlogit = a.xlogit;
       a.spart = at<SamplePart>(ws, L.spart);
+      a.recs = rule->sample ? at<unsigned long long>(ws, L.recs) : nullptr;   // planned whenever this path can run
+      a.rec_grid = GEMM_MAX_WG;
       // SV_HEAD_SPIN_LIMIT lowers the bounded wait (tests force its timeout path with 0)
       a.spin_limit = unsigned(env_int("SV_HEAD_SPIN_LIMIT", int(HEAD_SPIN_LIMIT)));
       rule->done = fused;

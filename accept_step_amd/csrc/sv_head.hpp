@@ -58,6 +58,13 @@ constexpr int CNT_LINE = 32;                      // words per 128-byte line
 constexpr int CNT_GROUPS = 8;                     // workgroups are dispatched round-robin over 8 XCDs
 constexpr int CNT_TOP_ARRIVE = 0, CNT_TOP_DONE = 1, CNT_ERROR = 2;
 constexpr int CNT_GRP_ARRIVE = 1 * CNT_LINE, CNT_GRP_DONE = 9 * CNT_LINE;
+// The fused sampler hands data between workgroups as epoch-tagged 64-bit words (value
+// bits low, launch epoch high) and needs no counter: readers poll until every word they
+// need carries the current epoch.  The epoch lives in the counter block: each launch
+// uses the stored value plus one and its finishing workgroup stores it.  POISON marks a
+// workspace whose step timed out (see HEAD_SAMPLE below).
+constexpr int CNT_EPOCH = 17 * CNT_LINE, CNT_FAIL = 18 * CNT_LINE;
+constexpr unsigned EPOCH_POISON = 0xffffffffu;
 
 struct HeadArgs {
   const bf16_t* W[MAX_SEG];   // [N_s, K] row-major
@@ -77,7 +84,11 @@ struct HeadArgs {
   float* xlogit;              // [M] draft-token logits (rule modes)
   unsigned* counter;          // the counter block
   AcceptArgs acc;             // acc.P == gridDim.x
-  SamplePart* spart;          // [B, gridDim.x] slice winners (HEAD_SAMPLE)
+  SamplePart* spart;          // unused by the k-split kernel
+  // HEAD_SAMPLE hand-off records, 4 tagged words each: statistics partials [grid][M],
+  // group partials [8][M], draft logits [M] (1 word each), slice winners [B][grid]
+  unsigned long long* recs;
+  int rec_grid;               // grid the record regions are sized for
   unsigned spin_limit;        // polls of the barrier count before giving up
 };
 
@@ -239,6 +250,14 @@ __device__ __forceinline__ void load_part_coherent(const RowPart* q, float& m, f
   a = load_coherent(&q->a);
 }
 
+__device__ __forceinline__ void put_tagged(unsigned long long* p, unsigned bits, unsigned ep) {
+  __hip_atomic_store(p, (static_cast<unsigned long long>(ep) << 32) | bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long get_tagged(const unsigned long long* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool tag_is(unsigned long long w, unsigned ep) { return unsigned(w >> 32) == ep; }
+
 // Two-level count, thread 0 only: the workgroup's group counter (blockIdx % groups)
 // and, for the last member of a group, the top counter.  Returns the top count after
 // this workgroup's contribution, or 0 if it did not reach the top.  A group's last
@@ -342,6 +361,7 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   __shared__ float s_qx[ACC_MAX_ROWS], s_u[ACC_MAX_ROWS];
   __shared__ int s_bad[ACC_MAX_ROWS];
   __shared__ long long s_pos0[ACC_MAX_ROWS];
+  __shared__ unsigned s_ep;                       // HEAD_SAMPLE: this launch's epoch
 
   // stage all of X, zero rows up to NB * CPB; fetch the drafts
   {
@@ -359,6 +379,10 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
     if (sample && threadIdx.x < ac.B) {
       s_pos0[threadIdx.x] = ac.pos0[threadIdx.x];
       s_bad[threadIdx.x] = ac.invalid ? ac.invalid[threadIdx.x] : 0;
+    }
+    if (sample && threadIdx.x == 0) {
+      const unsigned e = load_coherent(a.counter + CNT_EPOCH);
+      s_ep = e == EPOCH_POISON ? e : (e + 1u >= EPOCH_POISON ? 1u : e + 1u);   // 0 never tags a record
     }
   }
   __syncthreads();
@@ -459,56 +483,112 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   }
   if (!stats) return;
 
+  if (!sample) {
+    for (int m = threadIdx.x; m < M; m += blockDim.x) {
+      float rm = -INFINITY, rs = 0.0f;
+      int ra = 0x7fffffff;
+#pragma unroll
+      for (int w = 0; w < HEAD_WAVES; ++w) merge_stat(rm, rs, ra, s_m[w][m], s_s[w][m], s_a[w][m], c);
+      store_part(a.part + size_t(blockIdx.x) * M + m, rm, rs, ra);
+      // draft-token logit of this row, if this workgroup holds it
+      if (rule && a.xlogit) {
+        const int x = s_draft[m];
+        if (x >= 0 && x < N0) {
+          const int j = head_local_index(x, TR, gridDim.x, blockIdx.x);
+          if (j >= 0) store_coherent(a.xlogit + m, sL[m * nloc + j]);
+        }
+      }
+    }
+    if (!rule) return;
+    if (last_workgroup_2l(a.counter, CNT_GRP_ARRIVE, CNT_TOP_ARRIVE)) accept_block(ac, 0, ac.B);
+    return;
+  }
+
+  // ---- HEAD_SAMPLE.  Every hand-off is a set of epoch-tagged words that the reader
+  // polls (bounded) until all carry this launch's epoch:
+  //   1. each workgroup publishes its statistics partial (and the draft logits it holds);
+  //   2. the first workgroup of each XCD group merges its group's partials and
+  //      publishes a group partial;
+  //   3. every workgroup reads the G group partials, decides n for every sequence
+  //      (same inputs, same arithmetic, same n), draws the Gumbel-max of row n over its
+  //      slice and publishes its slice winner;
+  //   4. workgroup 0 merges the winners, writes the outputs and stores the epoch.
+  // A wait that times out (the device could not run every workgroup at once) makes the
+  // step report every sequence invalid and poisons the workspace: a workgroup that
+  // started after the step gave up could otherwise leave records that a later launch
+  // takes for its own.  Later calls then report every sequence invalid until the
+  // workspace is zero-filled again.
+  const unsigned ep = s_ep;
+  const unsigned G = min(gridDim.x, unsigned(CNT_GROUPS));
+  const int RG = a.rec_grid;
+  unsigned long long* r_part = a.recs;                                  // [RG][M][4]
+  unsigned long long* r_group = r_part + size_t(RG) * M * 4;            // [8][M][4]
+  unsigned long long* r_xl = r_group + size_t(CNT_GROUPS) * M * 4;      // [M]
+  unsigned long long* r_win = r_xl + M;                                 // [B][RG][4]
+  if (ep == EPOCH_POISON) {
+    if (blockIdx.x == 0)
+      for (int b = threadIdx.x; b < ac.B; b += blockDim.x) {
+        for (int i = 0; i < G1; ++i) ac.tokens_out[b * G1 + i] = -1;
+        ac.n_accepted[b] = -1;
+      }
+    return;
+  }
+  __shared__ int s_ok;
+  if (threadIdx.x == 0) s_ok = 1;
+  __syncthreads();
+
+  // 1. publish the partial and the draft logits this workgroup holds
   for (int m = threadIdx.x; m < M; m += blockDim.x) {
     float rm = -INFINITY, rs = 0.0f;
     int ra = 0x7fffffff;
 #pragma unroll
     for (int w = 0; w < HEAD_WAVES; ++w) merge_stat(rm, rs, ra, s_m[w][m], s_s[w][m], s_a[w][m], c);
-    store_part(a.part + size_t(blockIdx.x) * M + m, rm, rs, ra);
-    // draft-token logit of this row, if this workgroup holds it
-    if (rule && a.xlogit) {
-      const int x = s_draft[m];
-      if (x >= 0 && x < N0) {
-        const int j = head_local_index(x, TR, gridDim.x, blockIdx.x);
-        if (j >= 0) store_coherent(a.xlogit + m, sL[m * nloc + j]);
+    unsigned long long* rec = r_part + (size_t(blockIdx.x) * M + m) * 4;
+    put_tagged(rec + 0, __float_as_uint(rm), ep);
+    put_tagged(rec + 1, __float_as_uint(rs), ep);
+    put_tagged(rec + 2, unsigned(ra), ep);
+    const int x = s_draft[m];
+    if (x >= 0 && x < N0) {
+      const int j = head_local_index(x, TR, gridDim.x, blockIdx.x);
+      if (j >= 0) put_tagged(r_xl + m, __float_as_uint(sL[m * nloc + j]), ep);
+    }
+  }
+
+  // 2. the first workgroup of each group merges its members' partials: wave w takes
+  //    rows w, w + 4, ..., lane k member k; each wave polls its own rows
+  if (blockIdx.x < G) {
+    const unsigned g = blockIdx.x, gsize = (gridDim.x - g + G - 1) / G;
+    for (int m = wave; m < M; m += HEAD_WAVES) {
+      const unsigned long long* rec = r_part + (size_t(g + G * lane) * M + m) * 4;
+      float rm = -INFINITY, rs = 0.0f;
+      int ra = 0x7fffffff;
+      unsigned spins = 0;
+      bool got = false;
+      for (;;) {
+        bool mine = true;
+        if (unsigned(lane) < gsize) {
+          const unsigned long long w0 = get_tagged(rec), w1 = get_tagged(rec + 1), w2 = get_tagged(rec + 2);
+          mine = tag_is(w0, ep) && tag_is(w1, ep) && tag_is(w2, ep);
+          rm = __uint_as_float(unsigned(w0)); rs = __uint_as_float(unsigned(w1)); ra = int(unsigned(w2));
+        }
+        if (__all(mine)) { got = true; break; }
+        if (spins++ >= a.spin_limit) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (!got) { if (lane == 0) s_ok = 0; break; }
+      wave_allmerge_stat(rm, rs, ra, c);
+      if (lane == 0) {
+        unsigned long long* out = r_group + (size_t(g) * M + m) * 4;
+        put_tagged(out + 0, __float_as_uint(rm), ep);
+        put_tagged(out + 1, __float_as_uint(rs), ep);
+        put_tagged(out + 2, unsigned(ra), ep);
       }
     }
   }
-  if (!rule) return;
-  if (a.mode == HEAD_ACCEPT) {
-    if (last_workgroup_2l(a.counter, CNT_GRP_ARRIVE, CNT_TOP_ARRIVE)) accept_block(ac, 0, ac.B);
-    return;
-  }
 
-  // ---- HEAD_SAMPLE
-  // 1. arrive at the grid barrier (own partials and draft logits stored first)
-  const unsigned G = min(gridDim.x, unsigned(CNT_GROUPS));
-  __shared__ int s_ok;
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  // Two-level count: the last member of each group merges the group's partials
-  // first, so that afterwards every workgroup reads G group partials per row.
-  __shared__ unsigned s_grp_last;
-  RowPart* gpart = a.part + size_t(gridDim.x) * M;
-  if (threadIdx.x == 0) {
-    const unsigned g = blockIdx.x % G, gsize = (gridDim.x - g + G - 1) / G;
-    unsigned* gc = a.counter + CNT_GRP_ARRIVE + g * CNT_LINE;
-    s_grp_last = atomic_add_agent(gc, 1u) == gsize - 1;
-    if (s_grp_last) atomic_store_agent(gc, 0u);
-  }
-  __syncthreads();
-  unsigned seen = 0;
-  if (s_grp_last) {
-    head_group_merge(a.part, gpart, M, G, blockIdx.x % G, c);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (threadIdx.x == 0) seen = atomic_add_agent(a.counter + CNT_TOP_ARRIVE, 1u) + 1u;
-  }
-
-  // 2. while the others arrive: fetch q over this slice for every drafted slot, for the
-  //    residual draw after the decision (about gamma rows x 2 bytes x V per step;
-  //    issuing it at kernel start instead measured no faster)
-  const int npf = sample ? ac.B * ac.gamma * kg : 0;
+  // 3a. while the groups merge: fetch q over this slice for every drafted slot, for
+  //     the residual draw after the decision (about gamma rows x 2 bytes x V per step)
+  const int npf = ac.B * ac.gamma * kg;
   const bool prefetched = npf <= HEAD_QPF;
   unsigned qpf[HEAD_QPF][4];
 #pragma unroll
@@ -521,40 +601,52 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
     }
   }
 
-  // 3. wait until every group has arrived (bounded)
-  if (threadIdx.x == 0) {
+  // 3b. read the G group partials (eight lanes per row, merged in a fixed order) and
+  //     the draft logits; each wave polls its own rows
+  __shared__ float s_xl[ACC_MAX_ROWS];
+  for (int row0 = wave * 8; row0 < M; row0 += 8 * HEAD_WAVES) {
+    const int row = row0 + lane / 8, gp = lane % 8;
+    const bool need = row < M && unsigned(gp) < G;
+    const unsigned long long* rec = r_group + (size_t(gp) * M + row) * 4;
+    // the row's first lane also watches the row's draft logit
+    const int x = row < M ? s_draft[row] : -1;
+    const bool need_xl = gp == 0 && x >= 0 && x < N0;
+    float m = -INFINITY, sm = 0.0f, xl = 0.0f;
+    int am = 0x7fffffff;
     unsigned spins = 0;
-    while (seen < G && spins++ < a.spin_limit) {
+    bool got = false;
+    for (;;) {
+      bool mine = true;
+      if (need) {
+        const unsigned long long w0 = get_tagged(rec), w1 = get_tagged(rec + 1), w2 = get_tagged(rec + 2);
+        mine = tag_is(w0, ep) && tag_is(w1, ep) && tag_is(w2, ep);
+        m = __uint_as_float(unsigned(w0)); sm = __uint_as_float(unsigned(w1)); am = int(unsigned(w2));
+      }
+      if (need_xl) {
+        const unsigned long long w = get_tagged(r_xl + row);
+        mine = mine && tag_is(w, ep);
+        xl = __uint_as_float(unsigned(w));
+      }
+      if (__all(mine)) { got = true; break; }
+      if (spins++ >= a.spin_limit) break;
       __builtin_amdgcn_s_sleep(1);
-      seen = load_coherent(a.counter + CNT_TOP_ARRIVE);
     }
-    s_ok = seen >= G;
-    if (!s_ok) atomic_store_agent(a.counter + CNT_ERROR, 1u);
+    if (!got) { if (lane == 0) s_ok = 0; break; }
+    if (!need) { m = -INFINITY; sm = 0.0f; am = 0x7fffffff; }
+    dpp_merge_stat<DPP_XOR1>(m, sm, am, c);
+    dpp_merge_stat<DPP_XOR2>(m, sm, am, c);
+    dpp_merge_stat<DPP_HALF_MIRROR>(m, sm, am, c);
+    if (gp == 0 && row < M) { s_m[0][row] = m; s_s[0][row] = sm; s_a[0][row] = am; s_xl[row] = xl; }
   }
   __syncthreads();
   const bool ok = s_ok != 0;
 
-  // 4. every workgroup decides n for every sequence (same inputs, same arithmetic)
+  // 3c. decide n for every sequence
   __shared__ int s_n[ACC_MAX_ROWS];
   __shared__ float s_mn[ACC_MAX_ROWS], s_zn[ACC_MAX_ROWS];
   if (ok) {
-    // draft logits of this wave's first sequence, in flight with the partials
-    float xl = (wave < ac.B && lane < ac.gamma) ? load_coherent(a.xlogit + wave * G1 + lane) : 0.0f;
-    // eight lanes per row (one per group partial), eight rows per wave and pass
-    for (int row0 = wave * 8; row0 < M; row0 += 8 * HEAD_WAVES) {
-      const int row = row0 + lane / 8, gp = lane % 8;
-      float m = -INFINITY, sm = 0.0f;
-      int am = 0x7fffffff;
-      if (row < M && unsigned(gp) < G) load_part_coherent(gpart + size_t(gp) * M + row, m, sm, am);
-      dpp_merge_stat<DPP_XOR1>(m, sm, am, c);
-      dpp_merge_stat<DPP_XOR2>(m, sm, am, c);
-      dpp_merge_stat<DPP_HALF_MIRROR>(m, sm, am, c);
-      if (gp == 0 && row < M) { s_m[0][row] = m; s_s[0][row] = sm; s_a[0][row] = am; }
-    }
-    __syncthreads();
     for (int b = wave; b < ac.B; b += HEAD_WAVES) {
       const int row = b * G1 + lane;
-      if (b != wave && lane < ac.gamma) xl = load_coherent(a.xlogit + row);
       float my_m = -INFINITY, my_s = 0.0f;
       float px = 0.0f, qx = 0.0f, u = 1.0f;
       if (lane < G1) { my_m = s_m[0][row]; my_s = s_s[0][row]; }
@@ -562,7 +654,7 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
         const int x = s_draft[row];
         u = s_u[row];
         if (x >= 0 && x < ac.V) {
-          px = exp2f((xl - my_m) * c) / my_s;
+          px = exp2f((s_xl[row] - my_m) * c) / my_s;
           qx = s_qx[row];
         }
       }
@@ -575,7 +667,7 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
     __syncthreads();
   }
 
-  // 5. Gumbel-max of row n_b over this slice; one winner per (sequence, workgroup)
+  // 3d. Gumbel-max of row n_b over this slice; publish one winner per (sequence, workgroup)
   __shared__ float s_sr[HEAD_WAVES], s_sp[HEAD_WAVES];
   __shared__ int s_ir[HEAD_WAVES], s_ip[HEAD_WAVES];
   for (int b = 0; b < ac.B && ok; ++b) {
@@ -591,8 +683,7 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
       for (int k = 0; k < kg; ++k) {
         const int j0 = 4 * (threadIdx.x + k * blockDim.x);
         if (j0 >= nloc) break;
-        const int lt = j0 / TR;
-        const int vb = head_global_tile(blockIdx.x, lt, gridDim.x) * TR + (j0 - lt * TR);
+        const int vb = head_group_v(k, nloc, TR);
         if (vb >= ac.V) continue;
         unsigned qr[4] = {0u, 0u, 0u, 0u};
         if (resid) {
@@ -630,63 +721,78 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
     if (lane == 0) { s_sr[wave] = sr; s_ir[wave] = ir; s_sp[wave] = sp; s_ip[wave] = ip; }
     __syncthreads();
     if (threadIdx.x == 0) {
-      SamplePart o;
-      o.sr = -INFINITY; o.ir = 0x7fffffff; o.sp = -INFINITY; o.ip = 0x7fffffff;
+      float osr = -INFINITY, osp = -INFINITY;
+      int oir = 0x7fffffff, oip = 0x7fffffff;
       for (int w = 0; w < HEAD_WAVES; ++w) {
-        merge_best(o.sr, o.ir, s_sr[w], s_ir[w]);
-        merge_best(o.sp, o.ip, s_sp[w], s_ip[w]);
+        merge_best(osr, oir, s_sr[w], s_ir[w]);
+        merge_best(osp, oip, s_sp[w], s_ip[w]);
       }
-      o.any_r = o.ir != 0x7fffffff;
-      o.pad[0] = o.pad[1] = o.pad[2] = 0;
-      store_spart(a.spart + size_t(b) * gridDim.x + blockIdx.x, o);
+      unsigned long long* rec = r_win + (size_t(b) * RG + blockIdx.x) * 4;
+      put_tagged(rec + 0, __float_as_uint(osr), ep);
+      put_tagged(rec + 1, unsigned(oir), ep);
+      put_tagged(rec + 2, __float_as_uint(osp), ep);
+      put_tagged(rec + 3, unsigned(oip), ep);
     }
     __syncthreads();
   }
+  if (!ok && threadIdx.x == 0) atomic_store_agent(a.counter + CNT_FAIL, ep);
 
-  // 6. the last workgroup through merges the winners, writes the outputs and clears
-  //    the barrier count and the error flag
-  if (last_workgroup_2l(a.counter, CNT_GRP_DONE, CNT_TOP_DONE)) {
-    const bool failed = !ok || load_coherent(a.counter + CNT_ERROR) != 0u;
-    for (int b = wave; b < ac.B; b += HEAD_WAVES) {
-      const int n = failed ? -1 : s_n[b];
-      float sr = -INFINITY, sp = -INFINITY;
-      int ir = 0x7fffffff, ip = 0x7fffffff;
-      if (n >= 0) {
-        for (int p0 = 0; p0 < int(gridDim.x); p0 += 256) {
-          float qs[4], qp[4];
-          int qi[4], qj[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int p = p0 + lane + 64 * u;
-            qs[u] = -INFINITY; qp[u] = -INFINITY; qi[u] = 0x7fffffff; qj[u] = 0x7fffffff;
-            if (p < int(gridDim.x)) {   // (sr, ir, sp, ip) in one 16-byte load
-              const u32x4 q = *reinterpret_cast<const u32x4*>(a.spart + size_t(b) * gridDim.x + p);
-              qs[u] = __uint_as_float(q[0]); qi[u] = int(q[1]); qp[u] = __uint_as_float(q[2]); qj[u] = int(q[3]);
-            }
-          }
-#pragma unroll
-          for (int u = 0; u < 4; ++u) { merge_best(sr, ir, qs[u], qi[u]); merge_best(sp, ip, qp[u], qj[u]); }
+  // 4. workgroup 0 merges the winners, writes the outputs and stores the epoch
+  if (blockIdx.x != 0) return;
+  __shared__ int s_tok[ACC_MAX_ROWS];
+  bool done = ok;
+  for (int b = 0; b < ac.B && done; ++b) {
+    if (s_n[b] < 0) continue;
+    float sr = -INFINITY, sp = -INFINITY;
+    int ir = 0x7fffffff, ip = 0x7fffffff;
+    unsigned spins = 0;
+    for (;;) {
+      bool mine = true;
+      float tsr = -INFINITY, tsp = -INFINITY;
+      int tir = 0x7fffffff, tip = 0x7fffffff;
+      for (int p = threadIdx.x; p < int(gridDim.x); p += blockDim.x) {
+        const unsigned long long* rec = r_win + (size_t(b) * RG + p) * 4;
+        const unsigned long long w0 = get_tagged(rec), w1 = get_tagged(rec + 1), w2 = get_tagged(rec + 2),
+                                 w3 = get_tagged(rec + 3);
+        if (tag_is(w0, ep) && tag_is(w1, ep) && tag_is(w2, ep) && tag_is(w3, ep)) {
+          merge_best(tsr, tir, __uint_as_float(unsigned(w0)), int(unsigned(w1)));
+          merge_best(tsp, tip, __uint_as_float(unsigned(w2)), int(unsigned(w3)));
+        } else {
+          mine = false;
         }
       }
-      wave_allmerge_best(sr, ir);
-      wave_allmerge_best(sp, ip);
-      const int tok = (n < ac.gamma && ir != 0x7fffffff) ? ir : ip;
-      if (lane < G1) {
-        int t = -1;
-        if (n >= 0 && lane < n) t = s_draft[b * G1 + lane];
-        else if (n >= 0 && lane == n) t = tok;
-        ac.tokens_out[b * G1 + lane] = t;
-      }
-      if (lane == 0) {
-        ac.n_accepted[b] = n;
-        if (ac.len && n >= 0) ac.len[b] += n + 1;
-      }
+      if (__syncthreads_and(mine)) { sr = tsr; ir = tir; sp = tsp; ip = tip; break; }
+      // a workgroup that gave up never publishes: stop waiting (one uniform answer)
+      const bool failed = __syncthreads_or(threadIdx.x == 0 && load_coherent(a.counter + CNT_FAIL) == ep);
+      if (failed || spins++ >= a.spin_limit) { done = false; break; }
+      __builtin_amdgcn_s_sleep(1);
     }
+    if (!done) break;
+    wave_allmerge_best(sr, ir);
+    wave_allmerge_best(sp, ip);
+    if (lane == 0) { s_sr[wave] = sr; s_ir[wave] = ir; s_sp[wave] = sp; s_ip[wave] = ip; }
+    __syncthreads();
     if (threadIdx.x == 0) {
-      atomic_store_agent(a.counter + CNT_TOP_ARRIVE, 0u);
-      atomic_store_agent(a.counter + CNT_ERROR, 0u);
+      for (int w = 1; w < HEAD_WAVES; ++w) {
+        merge_best(s_sr[0], s_ir[0], s_sr[w], s_ir[w]);
+        merge_best(s_sp[0], s_ip[0], s_sp[w], s_ip[w]);
+      }
+      s_tok[b] = (s_n[b] < ac.gamma && s_ir[0] != 0x7fffffff) ? s_ir[0] : s_ip[0];
     }
+    __syncthreads();
   }
+  for (int b = threadIdx.x; b < ac.B; b += blockDim.x) {
+    const int n = done ? s_n[b] : -1;
+    for (int i = 0; i < G1; ++i) {
+      int t = -1;
+      if (n >= 0 && i < n) t = s_draft[b * G1 + i];
+      else if (n >= 0 && i == n) t = s_tok[b];
+      ac.tokens_out[b * G1 + i] = t;
+    }
+    ac.n_accepted[b] = n;
+    if (ac.len && n >= 0) ac.len[b] += n + 1;
+  }
+  if (threadIdx.x == 0) atomic_store_agent(a.counter + CNT_EPOCH, done ? ep : EPOCH_POISON);
 }
 
 }  // namespace sv

@@ -27,11 +27,16 @@
  *   Workspace: scratch is caller-provided.  Call once with ws == NULL: the
  *             required size is written to *ws_bytes, nothing is launched, and
  *             SV_OK is returned.  Then call with ws != NULL and *ws_bytes >= that
- *             size (256-byte aligned).  The first 4096 bytes hold one-shot
- *             counters (workgroups of one launch hand work to each other through
- *             them): a new workspace must be zero-filled once before its first
- *             use, and every call leaves those bytes zero again.  The rest of the
- *             workspace need not be initialised and is undefined afterwards.
+ *             size (256-byte aligned).  A new workspace must be zero-filled
+ *             (all of it) once before its first use; the library keeps state in
+ *             it between calls (counters through which the workgroups of one
+ *             launch hand work to each other, and a launch epoch), so keep using
+ *             the same workspace or zero-fill a new one.  The sampling step with a
+ *             small batch runs as one kernel whose workgroups wait for each other
+ *             (bounded): if the device cannot run them all at once for about a
+ *             second (e.g. it is shared), the step reports every sequence invalid
+ *             (see Data errors) and so does every later sampling call on that
+ *             workspace until it is zero-filled again.
  *   Streams:  stream is a hipStream_t (NULL = the null stream).  All work is
  *             enqueued on it and the call returns before it completes;
  *             outputs are valid once the caller synchronises the stream.

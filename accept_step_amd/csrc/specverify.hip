@@ -35,7 +35,7 @@ constexpr int GEMM_WAVES = 4;
 constexpr int GEMM_MAX_WG = 2048;    // upper bound of workgroups along the vocabulary
 constexpr size_t GEMM_LDS_BUDGET = 64 * 1024;
 constexpr int SAMPLE_CHUNK = 1024;
-constexpr int ATT_SPLITS_MAX = 16;
+constexpr int ATT_SPLITS_MAX = ATT_SPLITS_CAP;
 constexpr int FUSE_ACCEPT_MAX_ROWS = 20;   // B * (gamma + 1) merged by the product's last workgroup
 constexpr int FUSE_FINISH_MAX_B = 64;      // sequences finished by the sampler's last workgroup
 constexpr size_t STATIC_LDS_RESERVE = 2048;
@@ -177,7 +177,9 @@ sv_status check_common(const sv_model* m, sv_input_kind kind, const void* input,
         if (!m->layers[i]) return fail(SV_ERR_ARG, "layer pointer %d is NULL", i);
         if (!is_aligned(m->layers[i], 16)) return fail(SV_ERR_ARG, "layer pointer %d is not 16-byte aligned", i);
       }
-      if (!is_aligned(m->lm_head, 16) || !is_aligned(m->embed, 16)) return fail(SV_ERR_ARG, "weights must be 16-byte aligned");
+      if (!is_aligned(m->lm_head, 16) || !is_aligned(m->embed, 16) || !is_aligned(m->final_norm, 16))
+        return fail(SV_ERR_ARG, "weights must be 16-byte aligned");
+      if (m->d_model > 256 * 4 * RMS_VEC) return fail(SV_ERR_SHAPE, "d_model must be <= %d", 256 * 4 * RMS_VEC);
       if (!(m->rms_eps >= 0.0f) || !std::isfinite(m->rms_eps)) return fail(SV_ERR_ARG, "rms_eps must be finite and >= 0");
       if (!(m->rope_theta > 0.0f) || !std::isfinite(m->rope_theta)) return fail(SV_ERR_ARG, "rope_theta must be finite and > 0");
       if (!kv || !kv->k || !kv->v || !kv->len) return fail(SV_ERR_ARG, "SV_IN_TOKENS needs a KV cache");
@@ -424,6 +426,7 @@ struct Layout {
   size_t counters = 0;   // CNT_BYTES of one-shot counters; zero before first use, left zero
   size_t logits = 0, part = 0, state = 0, spart = 0, invalid = 0, xlogit = 0, recs = 0;
   size_t rope = 0, x = 0, h = 0, q = 0, k = 0, v = 0, attp = 0, att = 0, gate = 0, up = 0;
+  size_t attcnt = 0;    // [B, n_heads, query groups] split counters of the attention; zeroed by k_prep each call
   size_t total = 0;
   int P = 0;          // row-statistics partials per row
   int nch = 0;        // sampling chunks per sequence
@@ -439,6 +442,14 @@ struct Bump {
     return o;
   }
 };
+
+// Query groups of the attention (at most ATT_QMAX new positions per workgroup) and
+// the query slots of each group's kernel.
+int att_query_groups(int G1) { return (G1 + ATT_QMAX - 1) / ATT_QMAX; }
+int att_query_slots(int G1) {
+  const int per = (G1 + att_query_groups(G1) - 1) / att_query_groups(G1);
+  return per <= 2 ? 2 : per <= 4 ? 4 : per <= 5 ? 5 : 8;
+}
 
 int att_splits(const sv_kv_cache* kv) {
   int S = (kv->max_len + 255) / 256;
@@ -481,6 +492,7 @@ Layout plan(const sv_model* m, const Shape& sh, const sv_kv_cache* kv, bool need
     L.k = b.take(size_t(M) * HD * 4);
     L.v = b.take(size_t(M) * HD * 4);
     L.attp = b.take(size_t(sh.B) * m->n_heads * L.S * sh.G1 * (m->head_dim + 2) * 4);
+    L.attcnt = b.take(size_t(sh.B) * m->n_heads * att_query_groups(sh.G1) * 4);
     L.att = b.take(size_t(M) * HD * 2);
     L.gate = b.take(size_t(M) * ff * 4);
     L.up = b.take(size_t(M) * std::max(ff, d) * 4);
@@ -526,15 +538,17 @@ sv_status run_decoder(const sv_model* m, const Shape& sh, const int* tokens, con
   float* k = at<float>(ws, L.k);
   float* v = at<float>(ws, L.v);
   float* attp = at<float>(ws, L.attp);
+  unsigned* attcnt = at<unsigned>(ws, L.attcnt);
   bf16_t* att = at<bf16_t>(ws, L.att);
   float* gate = at<float>(ws, L.gate);
   float* up = at<float>(ws, L.up);
   bf16_t* kc = static_cast<bf16_t*>(kv->k);
   bf16_t* vc = static_cast<bf16_t*>(kv->v);
 
-  const int nprep = std::max(sh.B, M * (hd / 2));
-  hipLaunchKernelGGL(k_prep, dim3((nprep + 255) / 256), dim3(256), 0, s, kv->len, rope, invalid, sh.B, sh.G1, hd,
-                     kv->max_len, m->rope_theta);
+  const int ncnt = sh.B * H * att_query_groups(sh.G1);
+  const int nprep = std::max(std::max(sh.B, M * (hd / 2)), ncnt);
+  hipLaunchKernelGGL(k_prep, dim3((nprep + 255) / 256), dim3(256), 0, s, kv->len, rope, invalid, attcnt, ncnt, sh.B,
+                     sh.G1, hd, kv->max_len, m->rope_theta);
   hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, s, tokens, static_cast<const bf16_t*>(m->embed), x, invalid,
                      sh.G1, sh.V, d);
   SV_HIP(hipGetLastError());
@@ -556,13 +570,18 @@ sv_status run_decoder(const sv_model* m, const Shape& sh, const int* tokens, con
       if ((st = run_product(h, M, d, 3, ws3, o3, n3, di, s))) return st;
     }
     hipLaunchKernelGGL(k_rope_append, dim3(M, H), dim3(hd / 2), 0, s, q, k, v, rope, kc, vc, kv->len, invalid, da, l);
-    if (hd == 128)
-      hipLaunchKernelGGL((k_attn<128>), dim3(L.S, H, sh.B), dim3(256), 0, s, q, kc, vc, kv->len, invalid, attp, da, l,
-                         L.S, scale);
-    else
-      hipLaunchKernelGGL((k_attn<64>), dim3(L.S, H, sh.B), dim3(256), 0, s, q, kc, vc, kv->len, invalid, attp, da, l,
-                         L.S, scale);
-    hipLaunchKernelGGL(k_attn_merge, dim3(M, H), dim3(hd), 0, s, attp, att, da, L.S);
+    {
+      const int NQ = att_query_groups(sh.G1), QS = att_query_slots(sh.G1);
+      const dim3 ag(L.S, H, sh.B * NQ);
+      const float qscale = scale * 1.4426950408889634f;   // scores in base-2 units
+#define SV_ATTN(HDv, QGv) hipLaunchKernelGGL((k_attn<HDv, QGv>), ag, dim3(256), 0, s, q, kc, vc, kv->len, invalid, attp, \
+                                             att, attcnt, da, l, L.S, NQ, qscale)
+#define SV_ATTN_Q(HDv) do { if (QS == 2) SV_ATTN(HDv, 2); else if (QS == 4) SV_ATTN(HDv, 4); \
+                            else if (QS == 5) SV_ATTN(HDv, 5); else SV_ATTN(HDv, 8); } while (0)
+      if (hd == 128) SV_ATTN_Q(128); else SV_ATTN_Q(64);
+#undef SV_ATTN_Q
+#undef SV_ATTN
+    }
     SV_HIP(hipGetLastError());
     {
       const void* w1[1] = {w[4]};

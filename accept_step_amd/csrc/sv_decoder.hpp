@@ -14,6 +14,7 @@
 // output, SiLU(gate)*up.  Everything else stays float32.
 #pragma once
 
+#include "sv_accept.hpp"
 #include "sv_device.hpp"
 
 namespace sv {
@@ -26,11 +27,14 @@ struct DecArgs {
 // Cache lengths and RoPE table for the G1 new positions of every sequence.
 // invalid[b] = 1 when the cache cannot hold the new positions.  One thread per
 // (row, frequency) pair; angles in float64 (positions reach thousands of radians).
+// Also zeroes the attention's split counters (their place in the workspace depends
+// on the shapes of the call, so it may hold anything from an earlier call).
 __global__ __launch_bounds__(256) void k_prep(const int* __restrict__ len, float2* __restrict__ rope_cs,
-                                              int* __restrict__ invalid, int B, int G1, int hd, int max_len,
-                                              float theta) {
+                                              int* __restrict__ invalid, unsigned* __restrict__ att_cnt, int ncnt,
+                                              int B, int G1, int hd, int max_len, float theta) {
   const int half = hd / 2;
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < ncnt) att_cnt[t] = 0;
   if (t < B) invalid[t] = (len[t] < 0 || len[t] > max_len - G1) ? 1 : 0;
   if (t >= B * G1 * half) return;
   const int m = t / half, j = t - m * half;
@@ -55,29 +59,64 @@ __global__ __launch_bounds__(256) void k_embed(const int* __restrict__ tokens, c
 }
 
 // Residual add and RMSNorm: x[m, :] += add[m, :] (if add is given), then
-// h[m, :] = bf16(x / sqrt(mean(x^2) + eps) * g).  One workgroup per row.
+// h[m, :] = bf16(x / sqrt(mean(x^2) + eps) * g).  One workgroup per row; each thread
+// keeps its float4 groups of the row in registers (d <= 256 * 4 * RMS_VEC).
+constexpr int RMS_VEC = 8;
+
 __global__ __launch_bounds__(256) void k_add_rmsnorm(float* __restrict__ x, const float* __restrict__ add,
                                                      const bf16_t* __restrict__ g, bf16_t* __restrict__ h, int d,
                                                      float eps) {
   const int m = blockIdx.x;
   float* xr = x + size_t(m) * d;
-  float ss = 0.0f;
-  for (int k = threadIdx.x; k < d; k += blockDim.x) {
-    float v = xr[k];
-    if (add) {
-      v += add[size_t(m) * d + k];
-      xr[k] = v;
+  const int n4 = d / 4;                                 // d % 32 == 0
+  f32x4 v[RMS_VEC], ad[RMS_VEC];
+#pragma unroll
+  for (int u = 0; u < RMS_VEC; ++u) {
+    const int k4 = threadIdx.x + u * blockDim.x;
+    v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    ad[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (k4 < n4) {
+      v[u] = reinterpret_cast<const f32x4*>(xr)[k4];
+      if (add) ad[u] = reinterpret_cast<const f32x4*>(add + size_t(m) * d)[k4];
     }
-    ss = fmaf(v, v, ss);
   }
-  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  float ss = 0.0f;
+#pragma unroll
+  for (int u = 0; u < RMS_VEC; ++u) {
+    const int k4 = threadIdx.x + u * blockDim.x;
+    if (k4 < n4) {
+      if (add) {
+        v[u] += ad[u];
+        reinterpret_cast<f32x4*>(xr)[k4] = v[u];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss = fmaf(v[u][e], v[u][e], ss);
+    }
+  }
+  ss += dpp<DPP_XOR1>(ss);
+  ss += dpp<DPP_XOR2>(ss);
+  ss += dpp<DPP_HALF_MIRROR>(ss);
+  ss += dpp<DPP_MIRROR>(ss);
+  ss += __shfl_xor(ss, 16);
+  ss += __shfl_xor(ss, 32);
   __shared__ float red[4];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
   const float tot = red[0] + red[1] + red[2] + red[3];
   const float scale = 1.0f / sqrtf(tot / float(d) + eps);
-  for (int k = threadIdx.x; k < d; k += blockDim.x)
-    h[size_t(m) * d + k] = f32_to_bf16(xr[k] * scale * bf16_to_f32(g[k]));
+#pragma unroll
+  for (int u = 0; u < RMS_VEC; ++u) {
+    const int k4 = threadIdx.x + u * blockDim.x;
+    if (k4 < n4) {
+      const uint2 gw = reinterpret_cast<const uint2*>(g)[k4];
+      const float g0 = __uint_as_float(gw.x << 16), g1 = __uint_as_float(gw.x & 0xffff0000u);
+      const float g2 = __uint_as_float(gw.y << 16), g3 = __uint_as_float(gw.y & 0xffff0000u);
+      uint2 o;
+      o.x = uint32_t(f32_to_bf16(v[u][0] * scale * g0)) | (uint32_t(f32_to_bf16(v[u][1] * scale * g1)) << 16);
+      o.y = uint32_t(f32_to_bf16(v[u][2] * scale * g2)) | (uint32_t(f32_to_bf16(v[u][3] * scale * g3)) << 16);
+      reinterpret_cast<uint2*>(h + size_t(m) * d)[k4] = o;
+    }
+  }
 }
 
 __device__ __forceinline__ size_t cache_index(const DecArgs& a, int layer, int b, int h, int pos, int j) {
@@ -107,167 +146,292 @@ __global__ void k_rope_append(float* __restrict__ q, const float* __restrict__ k
   vc[cache_index(a, layer, b, h, pos, j + half)] = f32_to_bf16(v[base + j + half]);
 }
 
-constexpr int ATT_MAXQ = 16;   // gamma + 1 <= 16
+constexpr int ATT_KEYS = 256;   // keys per workgroup and pass (64 per wavefront)
+constexpr int ATT_SPLITS_CAP = 16;   // key splits per head at most
+constexpr int ATT_QMAX = 8;     // query slots per workgroup; more new positions use several query groups
 
-// Split-K decode attention.  grid (S, H, B), 256 threads; split s covers a range of
-// the len[b] + G1 keys, processed in tiles of 64 keys per wavefront.  Scores: lane =
-// key, dot with the G1 queries from LDS.  Values: lane = dimension pair.  Online
-// softmax per query; the four wavefronts are merged in LDS and one partial
-// (max, sum, unnormalised output) per (b, h, s, query) is written.
-template <int HD>
+// Butterfly all-reduces over the wavefront (DPP within rows of 16, then xor 16 and 32).
+__device__ __forceinline__ float wave_allmax(float v) {
+  v = fmaxf(v, dpp<DPP_XOR1>(v));
+  v = fmaxf(v, dpp<DPP_XOR2>(v));
+  v = fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp<DPP_MIRROR>(v));
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+__device__ __forceinline__ float wave_allsum(float v) {
+  v += dpp<DPP_XOR1>(v);
+  v += dpp<DPP_XOR2>(v);
+  v += dpp<DPP_HALF_MIRROR>(v);
+  v += dpp<DPP_MIRROR>(v);
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+// The same within each row of 16 lanes.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<DPP_XOR1>(v));
+  v = fmaxf(v, dpp<DPP_XOR2>(v));
+  v = fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
+  return fmaxf(v, dpp<DPP_MIRROR>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<DPP_XOR1>(v);
+  v += dpp<DPP_XOR2>(v);
+  v += dpp<DPP_HALF_MIRROR>(v);
+  return v + dpp<DPP_MIRROR>(v);
+}
+
+// float32 -> (hi, lo) bf16 pair with hi + lo = x to about 16 significant bits.
+__device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
+  const bf16_t h = f32_to_bf16(x);
+  hi = h;
+  lo = f32_to_bf16(x - bf16_to_f32(h));
+}
+
+// Split-K decode attention of the new positions, with the merge of the splits.
+// grid (S, H, B * NQ): workgroup (s, h, b, g) handles query slots [g*QG, g*QG + QG)
+// (those below G1) of head h and the keys [256 s, 256 s + 256), then every 256 S
+// further, of the len[b] + G1 keys; wavefront w takes 64 keys from 64 w of each such
+// block.  Scores in base-2 units (the queries carry scale * log2 e):
+//   * Q K^T on the matrix cores, 16x16x32 bf16 tiles.  The key rows are the B operand,
+//     read straight from the cache (16 keys x 64 contiguous bytes per load); each
+//     query is split into bf16 hi + lo parts, two products per tile, so the scores
+//     keep about 16 significant bits of the float32 query.  A lane ends with the
+//     scores of query rows 4 (l/16) + e, e < 4, for key l % 16 of each 16-key block.
+//   * online softmax per query row with DPP reductions inside rows of 16 lanes;
+//   * P V on the vector ALU: the value rows are read fully coalesced (a lane holds 8
+//     dimensions of one key per load) and each lane accumulates its 8 dimensions over
+//     its keys for every query; the weights and rescale factors go through LDS.
+// All loads of a block are issued before the first product.  The four wavefronts are
+// merged in LDS and the workgroup's partial (max, sum, unnormalised output) per query
+// is stored for the other workgroups of the head; the last of the S workgroups to
+// finish combines them and writes the bf16 attention output.  cnt[(b*H + h)*NQ + g]
+// counts the finished workgroups and is reset by the last one.
+template <int HD, int QG>
 __global__ __launch_bounds__(256) void k_attn(const float* __restrict__ q, const bf16_t* __restrict__ kc,
                                               const bf16_t* __restrict__ vc, const int* __restrict__ len,
-                                              const int* __restrict__ invalid, float* __restrict__ part, DecArgs a,
-                                              int layer, int S, float scale) {
-  constexpr int DPL = HD / 64;                 // dimensions per lane in the value phase
-  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+                                              const int* __restrict__ invalid, float* __restrict__ part,
+                                              bf16_t* __restrict__ out, unsigned* __restrict__ cnt, DecArgs a,
+                                              int layer, int S, int NQ, float qscale) {
+  static_assert(HD == 64 || HD == 128, "head_dim 64 or 128");
+  static_assert(QG >= 1 && QG <= ATT_QMAX, "query slots per workgroup");
+  constexpr int KC = HD / 32;          // 32-dimension chunks of a score product
+  constexpr int LPK = HD / 8;          // lanes per value row in the coalesced value loads
+  constexpr int KPI = 64 / LPK;        // value rows per load
+  constexpr int NV = HD / 8;           // value loads per 64 keys
+  const int s = blockIdx.x, h = blockIdx.y;
+  const int b = blockIdx.z / NQ, qg = blockIdx.z - b * NQ;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int G1 = a.G1;
-  __shared__ float sq[ATT_MAXQ][HD];
-  __shared__ float sp[4][ATT_MAXQ][64];
-  __shared__ float sm[4][ATT_MAXQ], sl[4][ATT_MAXQ];
-  __shared__ float so[4][ATT_MAXQ][HD];
+  const int q0 = qg * QG;
+  const int nq = min(QG, G1 - q0);
+  __shared__ u32x4 sqa[KC][2][64];                           // query hi / lo in A-operand order
+  __shared__ __attribute__((aligned(16))) float sp[4][QG][64];  // weights, [r][c] order per query
+  __shared__ __attribute__((aligned(16))) float scorr[4][ATT_QMAX];
+  __shared__ float sm[4][QG], sl[4][QG];
+  __shared__ float so[4][QG][HD];
   const size_t psz = size_t(HD + 2);
-  float* out = part + ((((size_t(b) * a.H + h) * S + s) * G1) * psz);
-  if (invalid[b]) {
-    for (int t = threadIdx.x; t < G1 * int(psz); t += blockDim.x) out[t] = (t % psz == 0) ? -INFINITY : 0.0f;
-    return;
-  }
-  for (int t = threadIdx.x; t < G1 * HD; t += blockDim.x) {
-    const int i = t / HD, j = t - i * HD;
-    sq[i][j] = q[(size_t(b) * G1 + i) * a.H * HD + size_t(h) * HD + j] * scale;
-  }
-  __syncthreads();
+  bf16_t* outp = out + (size_t(b) * G1 + q0) * a.H * HD + size_t(h) * HD;
   const int L = len[b];
   const int nk = L + G1;
-  const int per = (nk + S - 1) / S;
-  const int k_beg = s * per, k_end = min(nk, k_beg + per);
-  float mi[ATT_MAXQ], li[ATT_MAXQ], oi[ATT_MAXQ][DPL];
-#pragma unroll
-  for (int i = 0; i < ATT_MAXQ; ++i) {
-    mi[i] = -INFINITY; li[i] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) oi[i][e] = 0.0f;
-  }
+  const int g = lane >> 4, col = lane & 15;        // score layout: query rows 4g + e, key col
+  const int r = lane / LPK, j = lane % LPK;        // value layout: key r of each load, dims 8j..8j+7
   const bf16_t* kbase = kc + cache_index(a, layer, b, h, 0, 0);
   const bf16_t* vbase = vc + cache_index(a, layer, b, h, 0, 0);
-  for (int t0 = k_beg + wave * 64; t0 < k_end; t0 += 4 * 64) {
-    const int key = t0 + lane;
-    float sc[ATT_MAXQ];
+  // Rows past the last key are clamped to it (loaded, then masked); the clamp also
+  // keeps a sequence whose new positions do not fit the cache inside it (its result
+  // is discarded below).
+  const int klast = max(0, min(nk, a.max_len) - 1);
+  u32x4 kb[4][KC], vb[NV];
+  auto load_block = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < ATT_MAXQ; ++i) sc[i] = 0.0f;
-    if (key < k_end) {
-      const bf16_t* kr = kbase + size_t(key) * HD;
-      for (int j0 = 0; j0 < HD; j0 += 8) {
-        const u32x4 w = load16(kr + j0);
-        float kf[8];
+    for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kf[2 * e] = __uint_as_float(w[e] << 16);
-          kf[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-        }
+      for (int c = 0; c < KC; ++c)
+        kb[blk][c] = load16(kbase + size_t(min(k0 + 16 * blk + col, klast)) * HD + 32 * c + 8 * g);
 #pragma unroll
-        for (int i = 0; i < ATT_MAXQ; ++i) {
-          if (i < G1) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sc[i] = fmaf(sq[i][j0 + e], kf[e], sc[i]);
-          }
-        }
-      }
-    }
-    // causal mask: query i sees keys <= L + i
-#pragma unroll
-    for (int i = 0; i < ATT_MAXQ; ++i) {
-      if (i >= G1) break;
-      const float sv_ = (key < k_end && key <= L + i) ? sc[i] : -INFINITY;
-      float tmax = sv_;
-      for (int o = 32; o > 0; o >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o));
-      const float mnew = fmaxf(mi[i], tmax);
-      float p = 0.0f, corr = 1.0f;
-      if (mnew != -INFINITY) {
-        p = (sv_ == -INFINITY) ? 0.0f : expf(sv_ - mnew);
-        corr = (mi[i] == -INFINITY) ? 0.0f : expf(mi[i] - mnew);
-      }
-      float psum = p;
-      for (int o = 32; o > 0; o >>= 1) psum += __shfl_xor(psum, o);
-      li[i] = li[i] * corr + psum;
-      mi[i] = mnew;
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) oi[i][e] *= corr;
-      sp[wave][i][lane] = p;
-    }
-    __builtin_amdgcn_wave_barrier();
-    const int nkt = min(64, k_end - t0);
-    for (int kk = 0; kk < nkt; ++kk) {
-      const bf16_t* vr = vbase + size_t(t0 + kk) * HD + lane * DPL;
-      float vf[DPL];
-      if (DPL == 2) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(vr);
-        vf[0] = __uint_as_float(w << 16);
-        vf[DPL - 1] = __uint_as_float(w & 0xffff0000u);
-      } else {
-        vf[0] = bf16_to_f32(vr[0]);
-      }
-#pragma unroll
-      for (int i = 0; i < ATT_MAXQ; ++i) {
-        if (i < G1) {
-          const float p = sp[wave][i][kk];
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) oi[i][e] = fmaf(p, vf[e], oi[i][e]);
-        }
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
+    for (int c = 0; c < NV; ++c) vb[c] = load16(vbase + size_t(min(k0 + KPI * c + r, klast)) * HD + 8 * j);
+  };
+  // The query loads go out first (staged below), then the first block's keys and
+  // values, unconditionally (a wave without keys loads the last row), so that the
+  // waits before the staging and the scores count only the loads they need.
+  const int tq = threadIdx.x;                       // KC * 64 <= 256 staging threads
+  const int qkc = tq >> 6, ql = tq & 63, qm = ql & 15;
+  const int qd0 = 32 * qkc + 8 * (ql >> 4);
+  f32x4 x0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f}, x1 = x0;
+  if (tq < KC * 64) {
+    const float* qr = q + (size_t(b) * G1 + q0 + min(qm, nq - 1)) * a.H * HD + size_t(h) * HD + qd0;
+    x0 = *reinterpret_cast<const f32x4*>(qr);
+    x1 = *reinterpret_cast<const f32x4*>(qr + 4);
   }
-  // merge the four wavefronts
+  int k0 = s * ATT_KEYS + wave * 64;
+  load_block(k0);
+  __builtin_amdgcn_sched_barrier(0);
+  if (invalid[b]) {   // same for every workgroup of the sequence: no counting, zero output
+    if (s == 0)
+      for (int t = threadIdx.x; t < nq * HD; t += blockDim.x) outp[size_t(t / HD) * a.H * HD + t % HD] = 0;
+    return;
+  }
+  if (tq < KC * 64) {
+    const float f = qm < nq ? qscale : 0.0f;
+    uint32_t hi[8], lo[8];
 #pragma unroll
-  for (int i = 0; i < ATT_MAXQ; ++i) {
-    if (i < G1) {
-      if (lane == 0) { sm[wave][i] = mi[i]; sl[wave][i] = li[i]; }
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) so[wave][i][lane * DPL + e] = oi[i][e];
+    for (int e = 0; e < 4; ++e) {
+      split_bf16(x0[e] * f, hi[e], lo[e]);
+      split_bf16(x1[e] * f, hi[4 + e], lo[4 + e]);
     }
+    u32x4 vh, vl;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) { vh[w] = hi[2 * w] | (hi[2 * w + 1] << 16); vl[w] = lo[2 * w] | (lo[2 * w + 1] << 16); }
+    sqa[qkc][0][ql] = vh;
+    sqa[qkc][1][ql] = vl;
   }
   __syncthreads();
-  for (int t = threadIdx.x; t < G1 * HD; t += blockDim.x) {
-    const int i = t / HD, j = t - i * HD;
+  float mi[4], li[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { mi[e] = -INFINITY; li[e] = 0.0f; }
+  float o[QG][8];
+#pragma unroll
+  for (int i = 0; i < QG; ++i)
+#pragma unroll
+    for (int d = 0; d < 8; ++d) o[i][d] = 0.0f;
+  auto process = [&](int k0) {
+    f32x4 sc[4];
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) sc[blk] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const u32x4 ah = sqa[c][0][lane], al = sqa[c][1][lane];
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        sc[blk] = mfma16x16x32(ah, kb[blk][c], sc[blk]);
+        sc[blk] = mfma16x16x32(al, kb[blk][c], sc[blk]);
+      }
+    }
+    // online softmax; query row 4g + e sees keys <= L + q0 + 4g + e
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int qi = 4 * g + e;
+      float sv[4], mloc = -INFINITY;
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        const int key = k0 + 16 * blk + col;
+        sv[blk] = (key < nk && key <= L + q0 + qi) ? sc[blk][e] : -INFINITY;
+        mloc = fmaxf(mloc, sv[blk]);
+      }
+      const float mnew = fmaxf(mi[e], row16_max(mloc));
+      const float corr = mi[e] == -INFINITY ? 0.0f : exp2f(mi[e] - mnew);
+      float psum = 0.0f;
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        const float p = sv[blk] == -INFINITY ? 0.0f : exp2f(sv[blk] - mnew);
+        psum += p;
+        const int kl = 16 * blk + col;
+        if (qi < QG) sp[wave][qi < QG ? qi : 0][(kl % KPI) * NV + kl / KPI] = p;
+      }
+      li[e] = li[e] * corr + row16_sum(psum);
+      mi[e] = mnew;
+      if (col == 0 && qi < QG) scorr[wave][qi] = corr;
+    }
+    __builtin_amdgcn_wave_barrier();
+    // weighted values: lane (r, j) takes key KPI c + r of load c, dimensions 8j..8j+7
+#pragma unroll
+    for (int i = 0; i < QG; ++i) {
+      const float cf = scorr[wave][i];
+#pragma unroll
+      for (int d = 0; d < 8; ++d) o[i][d] *= cf;
+    }
+#pragma unroll
+    for (int c4 = 0; c4 < NV; c4 += 4) {
+      f32x4 pw[QG];
+#pragma unroll
+      for (int i = 0; i < QG; ++i) pw[i] = *reinterpret_cast<const f32x4*>(&sp[wave][i][r * NV + c4]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float v[8];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          v[2 * w] = __uint_as_float(vb[c4 + u][w] << 16);
+          v[2 * w + 1] = __uint_as_float(vb[c4 + u][w] & 0xffff0000u);
+        }
+#pragma unroll
+        for (int i = 0; i < QG; ++i)
+#pragma unroll
+          for (int d = 0; d < 8; ++d) o[i][d] = fmaf(pw[i][u], v[d], o[i][d]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+  // first block (loaded above), then the rest with each block's loads issued together
+  if (k0 < nk) process(k0);
+  for (k0 += S * ATT_KEYS; k0 < nk; k0 += S * ATT_KEYS) {
+    load_block(k0);
+    __builtin_amdgcn_sched_barrier(0);
+    process(k0);
+  }
+  // sum the KPI key lanes of each dimension group, then merge the four wavefronts
+#pragma unroll
+  for (int x = LPK; x < 64; x <<= 1)
+#pragma unroll
+    for (int i = 0; i < QG; ++i)
+#pragma unroll
+      for (int d = 0; d < 8; ++d) o[i][d] += __shfl_xor(o[i][d], x);
+  if (lane < LPK) {
+#pragma unroll
+    for (int i = 0; i < QG; ++i)
+#pragma unroll
+      for (int d = 0; d < 8; ++d) so[wave][i][8 * lane + d] = o[i][d];
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int qi = 4 * g + e;
+    if (col == 0 && qi < QG) { sm[wave][qi] = mi[e]; sl[wave][qi] = li[e]; }
+  }
+  __syncthreads();
+  float* pout = part + (((size_t(b) * a.H + h) * S + s) * G1 + q0) * psz;
+  for (int t = threadIdx.x; t < nq * HD; t += blockDim.x) {
+    const int i = t / HD, d = t - i * HD;
     float M = -INFINITY;
     for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w][i]);
-    float l = 0.0f, o = 0.0f;
+    float l = 0.0f, ov = 0.0f;
     if (M != -INFINITY) {
       for (int w = 0; w < 4; ++w) {
         if (sm[w][i] == -INFINITY) continue;
-        const float f = expf(sm[w][i] - M);
+        const float f = exp2f(sm[w][i] - M);
         l += sl[w][i] * f;
-        o += so[w][i][j] * f;
+        ov += so[w][i][d] * f;
       }
     }
-    float* po = out + size_t(i) * psz;
-    if (j == 0) { po[0] = M; po[1] = l; }
-    po[2 + j] = o;
+    float* po = pout + size_t(i) * psz;
+    if (d == 0) { store_coherent(po, M); store_coherent(po + 1, l); }
+    store_coherent(po + 2 + d, ov);
   }
-}
-
-// Merge the S partials of every (row, head) and store bf16 attention output
-// [M, H*hd].  grid (M, H), hd threads.
-__global__ void k_attn_merge(const float* __restrict__ part, bf16_t* __restrict__ out, DecArgs a, int S) {
-  const int m = blockIdx.x, h = blockIdx.y, j = threadIdx.x;
-  if (j >= a.hd) return;
-  const int b = m / a.G1, i = m - b * a.G1;
-  const size_t psz = size_t(a.hd + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, part[((((size_t(b) * a.H + h) * S + s) * a.G1) + i) * psz]);
-  float l = 0.0f, o = 0.0f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < S; ++s) {
-      const float* p = part + ((((size_t(b) * a.H + h) * S + s) * a.G1) + i) * psz;
-      if (p[0] == -INFINITY) continue;
-      const float f = expf(p[0] - M);
-      l += p[1] * f;
-      o += p[2 + j] * f;
+  if (!last_workgroup(cnt + (size_t(b) * a.H + h) * NQ + qg, unsigned(S))) return;
+  // last workgroup of the head: combine the S partials of every query (all loads of an
+  // output issued together)
+  const float* pb = part + ((size_t(b) * a.H + h) * S * G1 + q0) * psz;
+  for (int t = threadIdx.x; t < nq * HD; t += blockDim.x) {
+    const int i = t / HD, d = t - i * HD;
+    float pm[ATT_SPLITS_CAP], pl[ATT_SPLITS_CAP], pv[ATT_SPLITS_CAP];
+#pragma unroll
+    for (int u = 0; u < ATT_SPLITS_CAP; ++u) {
+      const float* pp = pb + (size_t(min(u, S - 1)) * G1 + i) * psz;
+      pm[u] = pp[0];
+      pl[u] = pp[1];
+      pv[u] = pp[2 + d];
     }
+    float M = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < ATT_SPLITS_CAP; ++u) M = fmaxf(M, pm[u]);
+    float l = 0.0f, ov = 0.0f;
+#pragma unroll
+    for (int u = 0; u < ATT_SPLITS_CAP; ++u) {
+      const float f = (u >= S || M == -INFINITY || pm[u] == -INFINITY) ? 0.0f : exp2f(pm[u] - M);
+      l += pl[u] * f;
+      ov += pv[u] * f;
+    }
+    outp[size_t(i) * a.H * HD + d] = f32_to_bf16(l > 0.0f ? ov / l : 0.0f);
   }
-  out[size_t(m) * a.H * a.hd + size_t(h) * a.hd + j] = f32_to_bf16(l > 0.0f ? o / l : 0.0f);
 }
 
 // f[m, j] = bf16(SiLU(gate) * up).

@@ -92,12 +92,11 @@ struct HeadArgs {
   unsigned spin_limit;        // polls of the barrier count before giving up
 };
 
-// Bytes of dynamic LDS: X rows (zero rows up to a whole number of column blocks,
-// each row padded by 16*S bytes so the lanes of a k-group hit distinct banks), then
-// the kept products.
-__host__ __device__ inline int head_rows_pad(int M, int S) { return (M * S + 15) / 16 * (16 / S); }
+// Bytes of dynamic LDS: the M rows of X plus one zero row that the lanes of padding
+// rows (past M in the last column block) read, each row padded by 16*S bytes so the
+// lanes of a k-group hit distinct banks; then the kept products.
 __host__ __device__ inline size_t head_lds_x(int M, int K, int S) {
-  return (size_t(head_rows_pad(M, S)) * (K + 8 * S) * 2 + 15) / 16 * 16;
+  return (size_t(M + 1) * (K + 8 * S) * 2 + 15) / 16 * 16;
 }
 __host__ __device__ inline size_t head_lds(int M, int K, int S, int nloc) {
   return head_lds_x(M, K, S) + size_t(M) * nloc * 4;
@@ -163,16 +162,16 @@ __device__ __forceinline__ void head_load(const HeadItem& it, unsigned voff, u32
 }
 
 // One work item: GRP steps of NB MFMAs.  The X operands of the item are read from
-// LDS in one batch (padding rows are zero, so no read is conditional).
+// LDS in one batch (lanes of padding rows read the zero row, so no read is conditional).
 template <int S, int NB, int GRP>
-__device__ __forceinline__ void head_mfma(const u32x4 (&buf)[GRP], const bf16_t* xp, int xstride, int kofs,
+__device__ __forceinline__ void head_mfma(const u32x4 (&buf)[GRP], const bf16_t* const (&xp)[NB], int kofs,
                                           f32x4 (&acc)[NB]) {
   u32x4 x[GRP][NB];
 #pragma unroll
   for (int u = 0; u < GRP; ++u)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      x[u][nb] = *reinterpret_cast<const u32x4*>(xp + nb * xstride + kofs + 32 * S * u);
+      x[u][nb] = *reinterpret_cast<const u32x4*>(xp[nb] + kofs + 32 * S * u);
 #pragma unroll
   for (int u = 0; u < GRP; ++u)
 #pragma unroll
@@ -363,10 +362,10 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   __shared__ long long s_pos0[ACC_MAX_ROWS];
   __shared__ unsigned s_ep;                       // HEAD_SAMPLE: this launch's epoch
 
-  // stage all of X, zero rows up to NB * CPB; fetch the drafts
+  // stage all of X and the zero row; fetch the drafts
   {
     const int pieces = a.K / 8;
-    for (int t = threadIdx.x; t < NB * CPB * pieces; t += blockDim.x) {
+    for (int t = threadIdx.x; t < (M + 1) * pieces; t += blockDim.x) {
       const int row = t / pieces, c = t - row * pieces;
       u32x4 v = {0u, 0u, 0u, 0u};
       if (row < M) v = load16(a.X + size_t(row) * a.K + c * 8);
@@ -388,8 +387,9 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   __syncthreads();
 
   const int lane_ofs = 8 * (S * g + r % S);       // element offset of the lane's piece in step 0
-  const bf16_t* xp = sX + (r / S) * ld + lane_ofs; // column block nb adds nb * CPB rows
-  const int xstride = CPB * ld;
+  const bf16_t* xp[NB];                           // the lane's X row in each column block
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) xp[nb] = sX + min(nb * CPB + r / S, M) * ld + lane_ofs;
 
   const int first = blockIdx.x * HEAD_WAVES + wave, tstride = gridDim.x * HEAD_WAVES;
   const int n_my = first < ntiles ? (ntiles - 1 - first) / tstride + 1 : 0;
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
 #define SV_HEAD_ITEM(KK, BUF)                                                                             \
     {                                                                                                     \
       const int i_ = (KK) / a.gpt, gg_ = (KK) - i_ * a.gpt;                                               \
-      head_mfma<S, NB, GRP>(BUF, xp, xstride, gg_ * item_k, acc);                                         \
+      head_mfma<S, NB, GRP>(BUF, xp, gg_ * item_k, acc);                                                  \
       if (gg_ == a.gpt - 1) {                                                                             \
         head_tile_done<S, NB>(acc, sL, nloc, M, i_ * HEAD_WAVES + wave, r, g, stats,                      \
                               (first + i_ * tstride) * TR, N0, c, st);                                    \

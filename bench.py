@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB five times (a plain copy kernel of known "
                          "size, used to scale the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--workload", choices=("large-vocab", "full-model"), default="large-vocab",
+                    help="large-vocab (default, the headline metric) or full-model: the 32-layer decoder verify")
     ap.add_argument("--traffic-summary", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                                               "k_head_vocab262144_d1536_B1_traffic.md"))
     return ap.parse_args()
@@ -58,6 +60,8 @@ def main():
     import accept_step_amd as sv
     import workloads
 
+    if args.workload == "full-model":
+        return full_model(args, torch, sv)
     root = os.path.dirname(os.path.abspath(__file__))
     sys.path.insert(0, root)
     dev = torch.device("cuda:0")
@@ -161,6 +165,92 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cases, args.cpu_seconds, elapsed / K)
+    print(json.dumps(out), flush=True)
+
+
+def full_model(args, torch, sv):
+    """The full-model verify: a 32-layer decoder (d 4096, 32 heads x 128, FFN 11008,
+    vocabulary 32000, bf16 weights N(0, 0.02), norm gains 1), a KV cache of 2048
+    positions, B = 1, gamma = 4, T = 1 sampling with a uniform draft distribution.
+    Weights and cache are drawn on the GPU from a seeded generator.  One step = embed,
+    32 layers, final norm, LM head, rule, draw, commit; the cache length is reset to
+    2048 before each step so every step does the same work."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L, d, H, hd, ff, V, C, B, gamma, T = 32, 4096, 32, 128, 11008, 32000, 2048, 1, 4, 1.0
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1005)
+
+    def normal(shape, std):
+        return (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * std).to(torch.bfloat16)
+
+    ones = torch.ones(d, dtype=torch.bfloat16, device=dev)
+    layers = []
+    for _ in range(L):
+        layers.append({"attn_norm": ones, "wq": normal((H * hd, d), 0.02), "wk": normal((H * hd, d), 0.02),
+                       "wv": normal((H * hd, d), 0.02), "wo": normal((d, H * hd), 0.02), "ffn_norm": ones,
+                       "w_gate": normal((ff, d), 0.02), "w_up": normal((ff, d), 0.02), "w_down": normal((d, ff), 0.02)})
+    embed, lm_head = normal((V, d), 0.02), normal((V, d), 0.02)
+    model = sv.decoder_model(embed, layers, ones, lm_head, H, hd)
+    max_len = C + gamma + 1
+    kc = torch.zeros((L, B, H, max_len, hd), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    kc[:, :, :, :C] = normal((L, B, H, C, hd), 1.0)
+    vc[:, :, :, :C] = normal((L, B, H, C, hd), 1.0)
+    length = torch.full((B,), C, dtype=torch.int32, device=dev)
+    kv = sv.KVCache(kc, vc, length)
+    tokens = torch.randint(0, V, (B, gamma + 1), generator=gen, device=dev, dtype=torch.int32)
+    q = torch.full((B, gamma, V), 1.0 / V, dtype=torch.float32, device=dev)
+    pos0 = torch.full((B,), C, dtype=torch.int64, device=dev)
+    ws = sv.Workspace()
+    K, Wm = max(1, args.steps // 10), max(1, args.warmup // 4)
+    n_out = torch.empty((K, B), dtype=torch.int32, device=dev)
+    t_out = torch.empty((K, B, gamma + 1), dtype=torch.int32, device=dev)
+
+    def step(out):
+        length.fill_(C)
+        return sv.spec_verify_sample(model, sv.SV_IN_TOKENS, tokens, B, gamma, None, q, T, 0x5EED0005, pos0, kv=kv,
+                                     out=out, ws=ws)
+
+    for _ in range(Wm):
+        step(None)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(K):
+        step((n_out[i], t_out[i]))
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / K
+    # per-part split from a separate run with per-launch events (decoder layers / LM-head step)
+    sv.timing_enable(0b011)
+    for _ in range(3):
+        step(None)
+    dec_ms, dec_n = sv.timing_read(1)
+    head_ms, head_n = sv.timing_read(0)
+    sv.timing_enable(0)
+    weight_bytes = L * (4 * H * hd * d + 3 * ff * d) * 2
+    kv_read = 2 * L * B * H * C * hd * 2
+    kv_write = 2 * L * B * H * (gamma + 1) * hd * 2
+    with_kv = weight_bytes + V * d * 2 + kv_read + kv_write + B * (gamma + 1) * d * 2
+    params_bytes = weight_bytes + 2 * V * d * 2          # the 6.74B parameters incl. the embedding table
+    committed = int((n_out.to(torch.int64) + 1).sum().item())
+    out = {
+        "metric": "full-model verify step latency (ms/step) and HBM GB/s",
+        "value": round(ms, 4), "unit": "ms/step", "n_gpus": 1, "steps": K, "warmup": Wm,
+        "ms_per_step": round(elapsed / K * 1e3, 4), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "full-model verify: 32-layer decoder d=4096, 32x128 heads, FFN 11008, V=32000, "
+                               "KV cache 2048, B=1, gamma=4, T=1.0 sampling",
+                   "verified_tokens_per_s": round(committed / elapsed, 1),
+                   "bytes_weights_lm_head_kv": with_kv, "gbs_weights_lm_head_kv": round(with_kv / (ms * 1e-3) / 1e9, 1),
+                   "frac_of_peak": round(with_kv / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                   "bytes_params": params_bytes, "gbs_params": round(params_bytes / (ms * 1e-3) / 1e9, 1),
+                   "decoder_ms": round(dec_ms / max(dec_n, 1), 4), "lm_head_step_ms": round(head_ms / max(head_n, 1), 4)},
+    }
     print(json.dumps(out), flush=True)
 
 

@@ -72,10 +72,11 @@ def check_case(c, T, label, tol=2e-2):
         n0, t0, fl = rules.verify_sample(ref, c.tokens[:, 1:], c.q.astype(np.float64), T, c.seed, base)
     torch.cuda.synchronize()
     err = row_rel_err(logits.cpu().numpy(), ref)
+    log(f"[{label}] logit rel err per row {np.array2string(err.reshape(-1), precision=2)}")
+    assert err.max() <= tol
     m, f = compare_decisions(n.cpu().numpy(), tok.cpu().numpy(), n0, t0, fl, label)
     log(f"[{label}] logit rel err max {err.max():.2e} median {np.median(err):.2e}; n={n.cpu().numpy().tolist()} "
         f"ref n={n0.tolist()} mismatched {m} flagged {f}")
-    assert err.max() <= tol
     # cache: new rows equal the oracle's up to one bf16 ulp; length advanced by n + 1
     gk = gkv.k.view(torch.int16).cpu().numpy().view(np.uint16)
     gv = gkv.v.view(torch.int16).cpu().numpy().view(np.uint16)
@@ -108,6 +109,43 @@ def test_small_decoder(T, hd, B):
     c = workloads.small_decoder_case(n_layers=2, d_model=256, n_heads=256 // hd, head_dim=hd, d_ff=512, vocab=1000,
                                      cache_len=100, B=B, gamma=4, std=0.05)
     check_case(c, T, f"small hd={hd} B={B}")
+
+
+@pytest.mark.parametrize("hd", [64, 128])
+@pytest.mark.parametrize("gamma", [1, 2, 5, 8, 15])
+def test_attention_query_groups_ragged_lengths(hd, gamma):
+    """New positions per sequence from 2 to 16 (one or two query groups of the
+    attention, every query-slot count the kernel is built for), a cache long enough
+    for three key splits, and two sequences of different lengths whose cache rows
+    past their length hold stale values that must not be attended to."""
+    import dataclasses
+    c = workloads.small_decoder_case(n_layers=1, d_model=256, n_heads=256 // hd, head_dim=hd, d_ff=256, vocab=500,
+                                     cache_len=600, B=2, gamma=gamma, std=0.05)
+    short = np.array([600, 451], dtype=np.int32)
+    c = dataclasses.replace(c, length=short, pos0=short.astype(np.int64))
+    check_case(c, 0.0, f"attn groups hd={hd} gamma={gamma}")
+
+
+def test_workspace_reused_across_shapes():
+    """One workspace, calls of different shapes, with everything past the fixed
+    counter block filled with garbage before each (the attention's split counters
+    sit at a shape-dependent offset, so the library must not rely on their old
+    contents).  The larger call goes first so the smaller one reuses its buffer."""
+    ws = sv.Workspace()
+    big = workloads.small_decoder_case(n_layers=1, d_model=256, n_heads=2, head_dim=128, d_ff=256, vocab=500,
+                                       cache_len=600, B=2, gamma=3)
+    small = workloads.small_decoder_case(n_layers=1, d_model=128, n_heads=2, head_dim=64, d_ff=256, vocab=300,
+                                         cache_len=40, B=1, gamma=2)
+    for c in (big, small, big):
+        wts, okv = oracle_model(c)
+        model, gkv = gpu_model(c)
+        ref = dec.forward(wts, c.tokens, okv)
+        B, G1 = c.tokens.shape
+        if ws.buf is not None:
+            ws.buf[4096:].fill_(0x7F)
+        out = sv.verify_forward(model, sv.SV_IN_TOKENS, dev(c.tokens.astype(np.int32)), B, G1 - 1, kv=gkv, ws=ws)
+        torch.cuda.synchronize()
+        assert row_rel_err(out.cpu().numpy(), ref).max() <= 2e-2
 
 
 def test_verify_forward_leaves_length():

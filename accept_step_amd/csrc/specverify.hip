@@ -309,15 +309,16 @@ HeadPlan plan_head(int M, int K, const int* N, int nseg, const DevInfo& di) {
       if (want_grp && gc != want_grp) continue;
       if (steps % gc == 0) { GRP = gc; break; }
     }
-    if (!GRP) continue;
+    if (!GRP) GRP = want_grp ? want_grp : 4;   // the last item of a tile runs past K over zeros in X
+    const int gpt = (steps + GRP - 1) / GRP, Kp = gpt * GRP * 32 * S;
     int ntiles = 0;
     for (int i = 0; i < nseg; ++i) ntiles += (N[i] + TR - 1) / TR;
     int grid = std::min(di.cus * per_cu, GEMM_MAX_WG);
     grid = std::max(1, std::min(grid, (ntiles + HEAD_WAVES - 1) / HEAD_WAVES));
     const int tpw = (ntiles + grid * HEAD_WAVES - 1) / (grid * HEAD_WAVES) * HEAD_WAVES;
-    const size_t lds = head_lds(M, K, S, tpw * TR);
+    const size_t lds = head_lds(M, Kp, S, tpw * TR);
     if (lds + HEAD_STATIC_LDS > di.lds_max) continue;
-    p.ok = true; p.S = S; p.NB = NB; p.GRP = GRP; p.grid = grid; p.gpt = steps / GRP; p.nloc = tpw * TR;
+    p.ok = true; p.S = S; p.NB = NB; p.GRP = GRP; p.grid = grid; p.gpt = gpt; p.nloc = tpw * TR;
     p.lds = lds;
     return p;
   }
@@ -402,6 +403,44 @@ sv_status launch_head(const HeadPlan& p, HeadArgs a, hipStream_t s) {
   return SV_OK;
 }
 
+// Decoder fusions of a k-split product: X normalised from float32 rows while it is
+// staged (norm_w set), and the products added into out with per-workgroup sums of
+// squares of the updated rows (residual).
+struct ProductFuse {
+  const float* Xf = nullptr;
+  const bf16_t* norm_w = nullptr;
+  const float* ss_in = nullptr;
+  int ss_parts = 0;
+  float eps = 0.0f;
+  bool residual = false;
+  float* ss_out = nullptr;
+};
+
+// Whether the decoder's fused sequence applies: every product of a layer runs on the
+// k-split kernel.
+bool fused_products_ok(int M, int d, int HD, int ff, const DevInfo& di) {
+  const int n3[3] = {HD, HD, HD}, n1[1] = {d}, n2[2] = {ff, ff};
+  return plan_head(M, d, n3, 3, di).ok && plan_head(M, HD, n1, 1, di).ok && plan_head(M, d, n2, 2, di).ok &&
+         plan_head(M, ff, n1, 1, di).ok && M <= ACC_MAX_ROWS;
+}
+
+// A k-split product with decoder fusions; *grid_out receives the launch's grid (the
+// number of sums-of-squares partials it leaves).
+sv_status run_product_fused(const bf16_t* X, int M, int K, int nseg, const void* const* W, float* const* out,
+                            const int* N, const ProductFuse& f, int* grid_out, const DevInfo& di, hipStream_t s) {
+  const HeadPlan hp = plan_head(M, K, N, nseg, di);
+  if (!hp.ok) return fail(SV_ERR_UNSUPPORTED, "fused decoder product does not fit the k-split kernel");
+  HeadArgs a = head_args(X, M, K);
+  for (int i = 0; i < nseg; ++i) head_add_seg(a, W[i], out[i], N[i], 16 / hp.S);
+  a.write_out = 1;
+  a.mode = HEAD_PRODUCT;
+  a.Xf = f.Xf; a.norm_w = f.norm_w; a.ss_in = f.ss_in; a.ss_parts = f.ss_parts; a.eps = f.eps;
+  a.residual = f.residual ? 1 : 0;
+  a.ss_out = f.ss_out;
+  if (grid_out) *grid_out = hp.grid;
+  return launch_head(hp, a, s);
+}
+
 // A product out_s[M, N_s] = X[M, K] W_s^T for up to three weights sharing X: the
 // k-split kernel where it applies, else the 16-row streaming / chunked kernels.
 sv_status run_product(const bf16_t* X, int M, int K, int nseg, const void* const* W, float* const* out, const int* N,
@@ -427,6 +466,7 @@ struct Layout {
   size_t logits = 0, part = 0, state = 0, spart = 0, invalid = 0, xlogit = 0, recs = 0;
   size_t rope = 0, x = 0, h = 0, q = 0, k = 0, v = 0, attp = 0, att = 0, gate = 0, up = 0;
   size_t attcnt = 0;    // [B, n_heads, query groups] split counters of the attention; zeroed by k_prep each call
+  size_t ss = 0;        // [GEMM_MAX_WG, M] partial sums of squares of the residual stream's rows
   size_t total = 0;
   int P = 0;          // row-statistics partials per row
   int nch = 0;        // sampling chunks per sequence
@@ -493,6 +533,7 @@ Layout plan(const sv_model* m, const Shape& sh, const sv_kv_cache* kv, bool need
     L.v = b.take(size_t(M) * HD * 4);
     L.attp = b.take(size_t(sh.B) * m->n_heads * L.S * sh.G1 * (m->head_dim + 2) * 4);
     L.attcnt = b.take(size_t(sh.B) * m->n_heads * att_query_groups(sh.G1) * 4);
+    L.ss = b.take(size_t(GEMM_MAX_WG) * M * 4);
     L.att = b.take(size_t(M) * HD * 2);
     L.gate = b.take(size_t(M) * ff * 4);
     L.up = b.take(size_t(M) * std::max(ff, d) * 4);
@@ -549,63 +590,113 @@ sv_status run_decoder(const sv_model* m, const Shape& sh, const int* tokens, con
   const int nprep = std::max(std::max(sh.B, M * (hd / 2)), ncnt);
   hipLaunchKernelGGL(k_prep, dim3((nprep + 255) / 256), dim3(256), 0, s, kv->len, rope, invalid, attcnt, ncnt, sh.B,
                      sh.G1, hd, kv->max_len, m->rope_theta);
+  const bool fused = fused_products_ok(M, d, HD, ff, di);
+  float* ss = at<float>(ws, L.ss);
   hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, s, tokens, static_cast<const bf16_t*>(m->embed), x, invalid,
-                     sh.G1, sh.V, d);
+                     fused ? ss : nullptr, sh.G1, sh.V, d);
   SV_HIP(hipGetLastError());
 
   const float scale = 1.0f / sqrtf(float(hd));
-  // Residual adds are folded into the next RMSNorm: the output projections write
-  // ``delta`` and the following k_add_rmsnorm adds it to x.
-  float* delta = up;    // the up-projection buffer holds [M, max(d, d_ff)] floats
-  const float* pending = nullptr;
-  for (int l = 0; l < m->n_layers; ++l) {
-    const void* const* w = m->layers + size_t(l) * 9;
-    hipLaunchKernelGGL(k_add_rmsnorm, dim3(M), dim3(256), 0, s, x, pending, static_cast<const bf16_t*>(w[0]), h, d,
-                       m->rms_eps);
-    sv_status st;
-    {
-      const void* ws3[3] = {w[1], w[2], w[3]};
-      float* o3[3] = {q, k, v};
-      const int n3[3] = {HD, HD, HD};
-      if ((st = run_product(h, M, d, 3, ws3, o3, n3, di, s))) return st;
-    }
+  // RoPE and the cache append of the new positions, then attention (the last
+  // workgroup of each head merges the key splits).
+  auto attention = [&](int l) -> sv_status {
     hipLaunchKernelGGL(k_rope_append, dim3(M, H), dim3(hd / 2), 0, s, q, k, v, rope, kc, vc, kv->len, invalid, da, l);
-    {
-      const int NQ = att_query_groups(sh.G1), QS = att_query_slots(sh.G1);
-      const dim3 ag(L.S, H, sh.B * NQ);
-      const float qscale = scale * 1.4426950408889634f;   // scores in base-2 units
+    const int NQ = att_query_groups(sh.G1), QS = att_query_slots(sh.G1);
+    const dim3 ag(L.S, H, sh.B * NQ);
+    const float qscale = scale * 1.4426950408889634f;   // scores in base-2 units
 #define SV_ATTN(HDv, QGv) hipLaunchKernelGGL((k_attn<HDv, QGv>), ag, dim3(256), 0, s, q, kc, vc, kv->len, invalid, attp, \
                                              att, attcnt, da, l, L.S, NQ, qscale)
 #define SV_ATTN_Q(HDv) do { if (QS == 2) SV_ATTN(HDv, 2); else if (QS == 4) SV_ATTN(HDv, 4); \
                             else if (QS == 5) SV_ATTN(HDv, 5); else SV_ATTN(HDv, 8); } while (0)
-      if (hd == 128) SV_ATTN_Q(128); else SV_ATTN_Q(64);
+    if (hd == 128) SV_ATTN_Q(128); else SV_ATTN_Q(64);
 #undef SV_ATTN_Q
 #undef SV_ATTN
-    }
     SV_HIP(hipGetLastError());
-    {
-      const void* w1[1] = {w[4]};
-      float* o1[1] = {delta};
-      const int n1[1] = {d};
-      if ((st = run_product(att, M, HD, 1, w1, o1, n1, di, s))) return st;
+    return SV_OK;
+  };
+  const int nf = M * ff;
+  sv_status st;
+  const float* pending = nullptr;
+  if (fused) {
+    // Every RMSNorm happens while the next product stages X from the float32 residual
+    // stream, with the row scales from the sums of squares that the producer of the
+    // rows left (k_embed: one per row; the output projections: one per workgroup, as
+    // they add their products into x).
+    int parts = 1;
+    for (int l = 0; l < m->n_layers; ++l) {
+      const void* const* w = m->layers + size_t(l) * 9;
+      ProductFuse fn;
+      fn.Xf = x; fn.ss_in = ss; fn.ss_parts = parts; fn.eps = m->rms_eps;
+      ProductFuse fr;
+      fr.residual = true; fr.ss_out = ss;
+      {
+        const void* ws3[3] = {w[1], w[2], w[3]};
+        float* o3[3] = {q, k, v};
+        const int n3[3] = {HD, HD, HD};
+        fn.norm_w = static_cast<const bf16_t*>(w[0]);
+        if ((st = run_product_fused(nullptr, M, d, 3, ws3, o3, n3, fn, nullptr, di, s))) return st;
+      }
+      if ((st = attention(l))) return st;
+      {
+        const void* w1[1] = {w[4]};
+        float* o1[1] = {x};
+        const int n1[1] = {d};
+        if ((st = run_product_fused(att, M, HD, 1, w1, o1, n1, fr, &parts, di, s))) return st;
+      }
+      {
+        const void* w2[2] = {w[6], w[7]};
+        float* o2[2] = {gate, up};
+        const int n2[2] = {ff, ff};
+        fn.ss_parts = parts;
+        fn.norm_w = static_cast<const bf16_t*>(w[5]);
+        if ((st = run_product_fused(nullptr, M, d, 2, w2, o2, n2, fn, nullptr, di, s))) return st;
+      }
+      hipLaunchKernelGGL(k_silu_mul, dim3((nf + 255) / 256), dim3(256), 0, s, gate, up, h, nf);
+      {
+        const void* w1[1] = {w[8]};
+        float* o1[1] = {x};
+        const int n1[1] = {d};
+        if ((st = run_product_fused(h, M, ff, 1, w1, o1, n1, fr, &parts, di, s))) return st;
+      }
     }
-    hipLaunchKernelGGL(k_add_rmsnorm, dim3(M), dim3(256), 0, s, x, delta, static_cast<const bf16_t*>(w[5]), h, d,
-                       m->rms_eps);
-    {
-      const void* w2[2] = {w[6], w[7]};
-      float* o2[2] = {gate, up};
-      const int n2[2] = {ff, ff};
-      if ((st = run_product(h, M, d, 2, w2, o2, n2, di, s))) return st;
+  } else {
+    // Residual adds are folded into the next RMSNorm: the output projections write
+    // ``delta`` and the following k_add_rmsnorm adds it to x.
+    float* delta = up;    // the up-projection buffer holds [M, max(d, d_ff)] floats
+    for (int l = 0; l < m->n_layers; ++l) {
+      const void* const* w = m->layers + size_t(l) * 9;
+      hipLaunchKernelGGL(k_add_rmsnorm, dim3(M), dim3(256), 0, s, x, pending, static_cast<const bf16_t*>(w[0]), h, d,
+                         m->rms_eps);
+      {
+        const void* ws3[3] = {w[1], w[2], w[3]};
+        float* o3[3] = {q, k, v};
+        const int n3[3] = {HD, HD, HD};
+        if ((st = run_product(h, M, d, 3, ws3, o3, n3, di, s))) return st;
+      }
+      if ((st = attention(l))) return st;
+      {
+        const void* w1[1] = {w[4]};
+        float* o1[1] = {delta};
+        const int n1[1] = {d};
+        if ((st = run_product(att, M, HD, 1, w1, o1, n1, di, s))) return st;
+      }
+      hipLaunchKernelGGL(k_add_rmsnorm, dim3(M), dim3(256), 0, s, x, delta, static_cast<const bf16_t*>(w[5]), h, d,
+                         m->rms_eps);
+      {
+        const void* w2[2] = {w[6], w[7]};
+        float* o2[2] = {gate, up};
+        const int n2[2] = {ff, ff};
+        if ((st = run_product(h, M, d, 2, w2, o2, n2, di, s))) return st;
+      }
+      hipLaunchKernelGGL(k_silu_mul, dim3((nf + 255) / 256), dim3(256), 0, s, gate, up, h, nf);
+      {
+        const void* w1[1] = {w[8]};
+        float* o1[1] = {delta};
+        const int n1[1] = {d};
+        if ((st = run_product(h, M, ff, 1, w1, o1, n1, di, s))) return st;
+      }
+      pending = delta;
     }
-    const int nf = M * ff;
-    hipLaunchKernelGGL(k_silu_mul, dim3((nf + 255) / 256), dim3(256), 0, s, gate, up, h, nf);
-    {
-      const void* w1[1] = {w[8]};
-      float* o1[1] = {delta};
-      const int n1[1] = {d};
-      if ((st = run_product(h, M, ff, 1, w1, o1, n1, di, s))) return st;
-    }
-    pending = delta;
   }
   hipLaunchKernelGGL(k_add_rmsnorm, dim3(M), dim3(256), 0, s, x, pending, static_cast<const bf16_t*>(m->final_norm), h,
                      d, m->rms_eps);

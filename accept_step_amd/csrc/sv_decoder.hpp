@@ -47,15 +47,27 @@ __global__ __launch_bounds__(256) void k_prep(const int* __restrict__ len, float
 
 // x[m, :] = embed[tokens[m], :] (float32 residual stream).  Out-of-range ids give
 // a zero row and mark the sequence invalid.
+// Also stores the row's sum of squares in ss_out[m] (if given) for the RMSNorm that the
+// next product applies while staging the row.
 __global__ __launch_bounds__(256) void k_embed(const int* __restrict__ tokens, const bf16_t* __restrict__ embed,
-                                               float* __restrict__ x, int* __restrict__ invalid, int G1, int V,
-                                               int d) {
+                                               float* __restrict__ x, int* __restrict__ invalid,
+                                               float* __restrict__ ss_out, int G1, int V, int d) {
   const int m = blockIdx.x;
   const int tok = tokens[m];
   const bool ok = tok >= 0 && tok < V;
   if (!ok && threadIdx.x == 0) invalid[m / G1] = 1;
-  for (int k = threadIdx.x; k < d; k += blockDim.x)
-    x[size_t(m) * d + k] = ok ? bf16_to_f32(embed[size_t(tok) * d + k]) : 0.0f;
+  float ss = 0.0f;
+  for (int k = threadIdx.x; k < d; k += blockDim.x) {
+    const float v = ok ? bf16_to_f32(embed[size_t(tok) * d + k]) : 0.0f;
+    x[size_t(m) * d + k] = v;
+    ss = fmaf(v, v, ss);
+  }
+  if (!ss_out) return;
+  ss = wave_allsum(ss);
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) ss_out[m] = red[0] + red[1] + red[2] + red[3];
 }
 
 // Residual add and RMSNorm: x[m, :] += add[m, :] (if add is given), then
@@ -149,37 +161,6 @@ __global__ void k_rope_append(float* __restrict__ q, const float* __restrict__ k
 constexpr int ATT_KEYS = 256;   // keys per workgroup and pass (64 per wavefront)
 constexpr int ATT_SPLITS_CAP = 16;   // key splits per head at most
 constexpr int ATT_QMAX = 8;     // query slots per workgroup; more new positions use several query groups
-
-// Butterfly all-reduces over the wavefront (DPP within rows of 16, then xor 16 and 32).
-__device__ __forceinline__ float wave_allmax(float v) {
-  v = fmaxf(v, dpp<DPP_XOR1>(v));
-  v = fmaxf(v, dpp<DPP_XOR2>(v));
-  v = fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
-  v = fmaxf(v, dpp<DPP_MIRROR>(v));
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
-}
-__device__ __forceinline__ float wave_allsum(float v) {
-  v += dpp<DPP_XOR1>(v);
-  v += dpp<DPP_XOR2>(v);
-  v += dpp<DPP_HALF_MIRROR>(v);
-  v += dpp<DPP_MIRROR>(v);
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
-}
-// The same within each row of 16 lanes.
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp<DPP_XOR1>(v));
-  v = fmaxf(v, dpp<DPP_XOR2>(v));
-  v = fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
-  return fmaxf(v, dpp<DPP_MIRROR>(v));
-}
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp<DPP_XOR1>(v);
-  v += dpp<DPP_XOR2>(v);
-  v += dpp<DPP_HALF_MIRROR>(v);
-  return v + dpp<DPP_MIRROR>(v);
-}
 
 // float32 -> (hi, lo) bf16 pair with hi + lo = x to about 16 significant bits.
 __device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {

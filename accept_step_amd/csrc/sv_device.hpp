@@ -123,6 +123,37 @@ __device__ __forceinline__ void wave_allmerge_stat(float& m, float& s, int& a, f
   xor_merge_stat(m, s, a, c, 32);
 }
 
+// Butterfly all-reduces over the wavefront (DPP within rows of 16, then xor 16 and 32).
+__device__ __forceinline__ float wave_allmax(float v) {
+  v = fmaxf(v, dpp<DPP_XOR1>(v));
+  v = fmaxf(v, dpp<DPP_XOR2>(v));
+  v = fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp<DPP_MIRROR>(v));
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+__device__ __forceinline__ float wave_allsum(float v) {
+  v += dpp<DPP_XOR1>(v);
+  v += dpp<DPP_XOR2>(v);
+  v += dpp<DPP_HALF_MIRROR>(v);
+  v += dpp<DPP_MIRROR>(v);
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+// The same within each row of 16 lanes.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<DPP_XOR1>(v));
+  v = fmaxf(v, dpp<DPP_XOR2>(v));
+  v = fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
+  return fmaxf(v, dpp<DPP_MIRROR>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<DPP_XOR1>(v);
+  v += dpp<DPP_XOR2>(v);
+  v += dpp<DPP_HALF_MIRROR>(v);
+  return v + dpp<DPP_MIRROR>(v);
+}
+
 // (score, index) argmax with lowest index on ties.
 __device__ __forceinline__ void merge_best(float& s, int& i, float s2, int i2) {
   if (s2 > s || (s2 == s && i2 < i)) { s = s2; i = i2; }

@@ -90,16 +90,25 @@ struct HeadArgs {
   unsigned long long* recs;
   int rec_grid;               // grid the record regions are sized for
   unsigned spin_limit;        // polls of the barrier count before giving up
+  // decoder fusions (product mode)
+  const float* Xf;            // non-null: X = bf16(Xf * rsqrt(mean(Xf^2) + eps) * norm_w) per row, Xf [M, K]
+  const bf16_t* norm_w;       // [K]
+  const float* ss_in;         // [ss_parts, M] partial sums of squares of the Xf rows
+  int ss_parts;
+  float eps;
+  int residual;               // the products are added into out (out[m, n] += ...)
+  float* ss_out;              // residual: [gridDim.x, M] sums of squares of the updated rows per workgroup
 };
 
 // Bytes of dynamic LDS: the M rows of X plus one zero row that the lanes of padding
 // rows (past M in the last column block) read, each row padded by 16*S bytes so the
-// lanes of a k-group hit distinct banks; then the kept products.
-__host__ __device__ inline size_t head_lds_x(int M, int K, int S) {
-  return (size_t(M + 1) * (K + 8 * S) * 2 + 15) / 16 * 16;
+// lanes of a k-group hit distinct banks; then the kept products.  Kp is K rounded up
+// to whole work items (zeros past K: see k_head).
+__host__ __device__ inline size_t head_lds_x(int M, int Kp, int S) {
+  return (size_t(M + 1) * (Kp + 8 * S) * 2 + 15) / 16 * 16;
 }
-__host__ __device__ inline size_t head_lds(int M, int K, int S, int nloc) {
-  return head_lds_x(M, K, S) + size_t(M) * nloc * 4;
+__host__ __device__ inline size_t head_lds(int M, int Kp, int S, int nloc) {
+  return head_lds_x(M, Kp, S) + size_t(M) * nloc * 4;
 }
 
 __device__ __forceinline__ TileRef head_tile(const HeadArgs& a, int tile, int TR) {
@@ -305,6 +314,8 @@ __device__ __forceinline__ float q_value(const AcceptArgs& ac, unsigned raw) {
 }
 
 constexpr int HEAD_QPF = 8;   // (row, group) entries of q a thread prefetches for the draw
+constexpr int HEAD_STAGE = 16;   // X pieces per thread in flight while staging
+constexpr int HEAD_STAGE_F = 8;  // the same when X is normalised from float32 rows
 // Vocab index of the first entry of the thread's k-th group of four (or >= V).
 __device__ __forceinline__ int head_group_v(int k, int nloc, int TR) {
   const int j0 = 4 * (threadIdx.x + k * blockDim.x);
@@ -337,15 +348,70 @@ __device__ __forceinline__ void head_group_merge(const RowPart* part, RowPart* g
     if (lane == 0) store_part(gpart + size_t(g) * M + row, m, s, am);
   }
 }
+// X staged from float32 rows with RMSNorm: each row's scale 1 / sqrt(sum(x^2) / K + eps)
+// comes from the ss_parts partial sums the producer of the rows left (wavefront w takes
+// rows w, w + 4, ...; fixed summation order), then every piece is normalised, scaled by
+// the gain and rounded to bf16 as it is written to LDS (zeros past K and in the extra
+// row).  The arithmetic matches a separate RMSNorm pass: bf16((x * scale) * g).
+__device__ __forceinline__ void head_stage_norm(const HeadArgs& a, bf16_t* sX, int ld, int Kp) {
+  __shared__ float s_scale[ACC_MAX_ROWS];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int M = a.M;
+  for (int m = wave; m < M; m += HEAD_WAVES) {
+    float ss = 0.0f;
+    for (int p = lane; p < a.ss_parts; p += 64) ss += a.ss_in[size_t(p) * M + m];
+    ss = wave_allsum(ss);
+    if (lane == 0) s_scale[m] = 1.0f / sqrtf(ss / float(a.K) + a.eps);
+  }
+  __syncthreads();
+  const int pieces = Kp / 8, kpieces = a.K / 8, total = (M + 1) * pieces;
+  for (int t0 = threadIdx.x; t0 < total; t0 += HEAD_STAGE_F * int(blockDim.x)) {
+    f32x4 x0[HEAD_STAGE_F], x1[HEAD_STAGE_F];
+    u32x4 gw[HEAD_STAGE_F];
+#pragma unroll
+    for (int u = 0; u < HEAD_STAGE_F; ++u) {
+      const int t = t0 + u * int(blockDim.x), row = t / pieces, c = t - row * pieces;
+      x0[u] = x1[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      gw[u] = u32x4{0u, 0u, 0u, 0u};
+      if (t < total && row < M && c < kpieces) {
+        const float* xr = a.Xf + size_t(row) * a.K + c * 8;
+        x0[u] = *reinterpret_cast<const f32x4*>(xr);
+        x1[u] = *reinterpret_cast<const f32x4*>(xr + 4);
+        gw[u] = load16(a.norm_w + c * 8);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < HEAD_STAGE_F; ++u) {
+      const int t = t0 + u * int(blockDim.x), row = t / pieces, c = t - row * pieces;
+      if (t < total) {
+        const float sc = row < M ? s_scale[row] : 0.0f;
+        u32x4 o;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float xa = w < 2 ? x0[u][2 * w] : x1[u][2 * w - 4];
+          const float xb = w < 2 ? x0[u][2 * w + 1] : x1[u][2 * w - 3];
+          const float ga = __uint_as_float(gw[u][w] << 16), gb = __uint_as_float(gw[u][w] & 0xffff0000u);
+          o[w] = uint32_t(f32_to_bf16(xa * sc * ga)) | (uint32_t(f32_to_bf16(xb * sc * gb)) << 16);
+        }
+        *reinterpret_cast<u32x4*>(sX + row * ld + c * 8) = o;
+      }
+    }
+  }
+}
+
 template <int S, int NB, int GRP>
 __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_head(HeadArgs a) {
   constexpr int TR = 16 / S, CPB = 16 / S;
+  // K need not be a multiple of the work item: the last item of a tile runs past the
+  // row into the next row's bytes (or past the segment's end, read as zeros), and X
+  // holds zeros there, so those products add nothing.
+  const int Kp = a.gpt * GRP * 32 * S;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   bf16_t* sX = reinterpret_cast<bf16_t*>(smem);
-  float* sL = reinterpret_cast<float*>(smem + head_lds_x(a.M, a.K, S));
+  float* sL = reinterpret_cast<float*>(smem + head_lds_x(a.M, Kp, S));
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
-  const int ld = a.K + 8 * S;
+  const int ld = Kp + 8 * S;
   const int ntiles = a.tile_end[a.nseg - 1];
   const int M = a.M, nloc = a.nloc, N0 = a.N[0];
   const AcceptArgs& ac = a.acc;
@@ -362,15 +428,40 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   __shared__ long long s_pos0[ACC_MAX_ROWS];
   __shared__ unsigned s_ep;                       // HEAD_SAMPLE: this launch's epoch
 
-  // stage all of X and the zero row; fetch the drafts
-  {
-    const int pieces = a.K / 8;
-    for (int t = threadIdx.x; t < (M + 1) * pieces; t += blockDim.x) {
-      const int row = t / pieces, c = t - row * pieces;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row < M) v = load16(a.X + size_t(row) * a.K + c * 8);
-      *reinterpret_cast<u32x4*>(sX + row * ld + c * 8) = v;
+  // The wavefront's first work item is requested before X is staged: the two
+  // latencies overlap instead of adding up.
+  const int first = blockIdx.x * HEAD_WAVES + wave, tstride = gridDim.x * HEAD_WAVES;
+  const int n_my = first < ntiles ? (ntiles - 1 - first) / tstride + 1 : 0;
+  const int items = n_my * a.gpt;
+  const int item_k = 32 * S * GRP;                // elements of a row per work item
+  const int lane_ofs = 8 * (S * g + r % S);       // element offset of the lane's piece in step 0
+  u32x4 bufA[GRP], bufB[GRP];
+  const unsigned voff = (unsigned(r / S) * unsigned(a.K) + unsigned(lane_ofs)) * 2u;   // the lane's W bytes
+  if (items > 0) head_load<S, NB, GRP>(head_item<S>(a, 0, first, tstride, item_k), voff, bufA);
+
+  // stage all of X (zeros from K to Kp) and the zero row, HEAD_STAGE pieces per thread
+  // in flight at a time (one load and store at a time would chain the L2 round trips);
+  // fetch the drafts
+  if (a.Xf) {
+    head_stage_norm(a, sX, ld, Kp);
+  } else {
+    const int pieces = Kp / 8, kpieces = a.K / 8, total = (M + 1) * pieces;
+    for (int t0 = threadIdx.x; t0 < total; t0 += HEAD_STAGE * int(blockDim.x)) {
+      u32x4 v[HEAD_STAGE];
+#pragma unroll
+      for (int u = 0; u < HEAD_STAGE; ++u) {
+        const int t = t0 + u * int(blockDim.x), row = t / pieces, c = t - row * pieces;
+        v[u] = u32x4{0u, 0u, 0u, 0u};
+        if (t < total && row < M && c < kpieces) v[u] = load16(a.X + size_t(row) * a.K + c * 8);
+      }
+#pragma unroll
+      for (int u = 0; u < HEAD_STAGE; ++u) {
+        const int t = t0 + u * int(blockDim.x), row = t / pieces, c = t - row * pieces;
+        if (t < total) *reinterpret_cast<u32x4*>(sX + row * ld + c * 8) = v[u];
+      }
     }
+  }
+  {
     if (rule && threadIdx.x < M) {
       const int b = threadIdx.x / G1, i = threadIdx.x - b * G1;
       s_draft[threadIdx.x] = i < ac.gamma ? ac.draft[size_t(b) * ac.draft_stride + ac.draft_offset + i] : -1;
@@ -386,18 +477,9 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   }
   __syncthreads();
 
-  const int lane_ofs = 8 * (S * g + r % S);       // element offset of the lane's piece in step 0
   const bf16_t* xp[NB];                           // the lane's X row in each column block
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) xp[nb] = sX + min(nb * CPB + r / S, M) * ld + lane_ofs;
-
-  const int first = blockIdx.x * HEAD_WAVES + wave, tstride = gridDim.x * HEAD_WAVES;
-  const int n_my = first < ntiles ? (ntiles - 1 - first) / tstride + 1 : 0;
-  const int items = n_my * a.gpt;
-  const int item_k = 32 * S * GRP;                // elements of a row per work item
-  u32x4 bufA[GRP], bufB[GRP];
-  const unsigned voff = (unsigned(r / S) * unsigned(a.K) + unsigned(lane_ofs)) * 2u;   // the lane's W bytes
-  if (items > 0) head_load<S, NB, GRP>(head_item<S>(a, 0, first, tstride, item_k), voff, bufA);
 
   // sampling: q at each draft token and the acceptance uniforms, while the first loads fly
   float my_qx = 0.0f;
@@ -464,20 +546,48 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   __syncthreads();
 
   const int tpw = nloc / TR;                      // local tiles per workgroup
-  // ---- write the products
+  // ---- write the products (residual: add them into out, and leave each tile's sum of
+  // squares of the updated entries in its first LDS slot, summed per row below in
+  // tile order)
   if (a.write_out) {
+    const bool res = a.residual != 0;
     for (int idx = threadIdx.x; idx < M * tpw; idx += blockDim.x) {
       const int m = idx / tpw, lt = idx - m * tpw;
       const int t = head_global_tile(blockIdx.x, lt, gridDim.x);
-      if (t >= ntiles) continue;
+      float* src = sL + m * nloc + lt * TR;
+      if (t >= ntiles) {
+        if (res) src[0] = 0.0f;
+        continue;
+      }
       const TileRef tr = head_tile(a, t, TR);
-      const float* src = sL + m * nloc + lt * TR;
       float* dst = tr.out + size_t(m) * tr.N + tr.v0;
+      float ssq = 0.0f;
       if (tr.v0 + TR <= tr.N && (tr.N & 3) == 0 && (reinterpret_cast<uintptr_t>(tr.out) & 15) == 0) {
 #pragma unroll
-        for (int q = 0; q < TR; q += 4) *reinterpret_cast<f32x4*>(dst + q) = *reinterpret_cast<const f32x4*>(src + q);
+        for (int q = 0; q < TR; q += 4) {
+          f32x4 v = *reinterpret_cast<const f32x4*>(src + q);
+          if (res) {
+            v += *reinterpret_cast<const f32x4*>(dst + q);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ssq = fmaf(v[e], v[e], ssq);
+          }
+          *reinterpret_cast<f32x4*>(dst + q) = v;
+        }
       } else {
-        for (int w = 0; w < TR && tr.v0 + w < tr.N; ++w) dst[w] = src[w];
+        for (int w = 0; w < TR && tr.v0 + w < tr.N; ++w) {
+          float v = src[w];
+          if (res) { v += dst[w]; ssq = fmaf(v, v, ssq); }
+          dst[w] = v;
+        }
+      }
+      if (res) src[0] = ssq;
+    }
+    if (res && a.ss_out) {
+      __syncthreads();
+      for (int m = threadIdx.x; m < M; m += blockDim.x) {
+        float ss = 0.0f;
+        for (int lt = 0; lt < tpw; ++lt) ss += sL[m * nloc + lt * TR];
+        a.ss_out[size_t(blockIdx.x) * M + m] = ss;
       }
     }
   }

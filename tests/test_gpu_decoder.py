@@ -104,11 +104,14 @@ def check_case(c, T, label, tol=2e-2):
 
 
 @pytest.mark.parametrize("T", [0.0, 1.0])
-@pytest.mark.parametrize("hd,B", [(128, 1), (64, 2)])
-def test_small_decoder(T, hd, B):
-    c = workloads.small_decoder_case(n_layers=2, d_model=256, n_heads=256 // hd, head_dim=hd, d_ff=512, vocab=1000,
+@pytest.mark.parametrize("hd,B,ff", [(128, 1, 512), (64, 2, 512), (128, 2, 640), (64, 1, 704), (64, 5, 512)])
+def test_small_decoder(T, hd, B, ff):
+    """d_ff 640 and 704: the down projection's K is not a whole number of work items.
+    B = 5 (25 rows): the products exceed the k-split kernel's rows, so the layers run
+    unfused (separate RMSNorm passes, fallback products)."""
+    c = workloads.small_decoder_case(n_layers=2, d_model=256, n_heads=256 // hd, head_dim=hd, d_ff=ff, vocab=1000,
                                      cache_len=100, B=B, gamma=4, std=0.05)
-    check_case(c, T, f"small hd={hd} B={B}")
+    check_case(c, T, f"small hd={hd} B={B} ff={ff}")
 
 
 @pytest.mark.parametrize("hd", [64, 128])

@@ -225,6 +225,11 @@ SMALL = [
     (1000, 1024, 4, 3, 0.0),    # M = 16: four blocks, greedy
     (2503, 512, 4, 4, 1.0),     # M = 20: five blocks
     (2503, 1536, 2, 4, 1.0),    # M = 10, the large-vocabulary hidden size
+    # K not a whole number of work items: the last item of each tile runs over zeros
+    (1500, 640, 1, 4, 1.0),     # 5 steps of 128: items of 4, tail of 1
+    (2001, 1408, 2, 4, 0.0),    # 11 steps: tail of 3, greedy
+    (3000, 192, 1, 2, 1.0),     # split factor 2, 3 steps in one item of 4
+    (999, 2304, 1, 4, 0.7),     # 18 steps: items of 6, no tail
 ]
 
 

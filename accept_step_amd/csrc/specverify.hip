@@ -287,6 +287,8 @@ struct HeadPlan {
   bool ok = false;
   int S = 0, NB = 0, GRP = 0, grid = 0, gpt = 0, nloc = 0;
   size_t lds = 0;
+  bool helpers = false;     // sampling launch with helper wavefronts (k_head_h)
+  int threads = HEAD_WAVES * 64;
 };
 
 // Largest column-block count instantiated per split factor.
@@ -334,7 +336,30 @@ const void* head_fn_grp(int GRP) {
   }
 }
 
+template <int S, int NB>
+const void* head_fn_grp_h(int GRP) {
+  switch (GRP) {
+    case 8: return reinterpret_cast<const void*>(&k_head_h<S, NB, 8>);
+    case 6: return reinterpret_cast<const void*>(&k_head_h<S, NB, 6>);
+    default: return reinterpret_cast<const void*>(&k_head_h<S, NB, 4>);
+  }
+}
+
+// Column-block counts with a helper-wavefront instantiation (the noise table of
+// B * (gamma + 1) rows must fit in LDS beside X and the kept products).
+bool head_helpers_instantiated(int S, int NB) { return S == 4 ? NB <= 3 : NB <= 2; }
+
 const void* head_fn(const HeadPlan& p) {
+  if (p.helpers) {
+    if (p.S == 4) {
+      switch (p.NB) {
+        case 1: return head_fn_grp_h<4, 1>(p.GRP);
+        case 2: return head_fn_grp_h<4, 2>(p.GRP);
+        default: return head_fn_grp_h<4, 3>(p.GRP);
+      }
+    }
+    return p.NB == 1 ? head_fn_grp_h<2, 1>(p.GRP) : head_fn_grp_h<2, 2>(p.GRP);
+  }
   if (p.S == 4) {
     switch (p.NB) {
       case 1: return head_fn_grp<4, 1>(p.GRP);
@@ -382,12 +407,23 @@ sv_status head_set_lds(const void* fn, size_t lds) {
 
 // Whether every workgroup of the plan can be resident at once (the fused sampler's
 // grid barrier needs it).
+// The sampling launch's helper wavefronts: when the noise table of ``rows`` rows fits in
+// LDS (SV_HEAD_HELPERS=0 turns them off).
+void head_plan_helpers(HeadPlan& p, int rows, const DevInfo& di) {
+  if (!p.ok || !head_helpers_instantiated(p.S, p.NB) || !env_int("SV_HEAD_HELPERS", 1)) return;
+  const size_t noise = size_t(rows) * p.nloc * 4;
+  if (p.lds + noise + HEAD_STATIC_LDS > di.lds_max) return;
+  p.helpers = true;
+  p.threads = (HEAD_WAVES + HEAD_HELPERS) * 64;
+  p.lds += noise;
+}
+
 sv_status head_all_resident(const HeadPlan& p, const DevInfo& di, bool* yes) {
   const void* fn = head_fn(p);
   sv_status st = head_set_lds(fn, p.lds);
   if (st) return st;
   int per_cu = 0;
-  SV_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, HEAD_WAVES * 64, p.lds));
+  SV_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, p.threads, p.lds));
   *yes = int64_t(per_cu) * di.cus >= p.grid && p.grid <= 64 * CNT_GROUPS;   // group merge: a lane per member
   return SV_OK;
 }
@@ -399,7 +435,7 @@ sv_status launch_head(const HeadPlan& p, HeadArgs a, hipStream_t s) {
   sv_status st = head_set_lds(fn, p.lds);
   if (st) return st;
   void* args[] = {&a};
-  SV_HIP(hipLaunchKernel(fn, dim3(p.grid), dim3(HEAD_WAVES * 64), args, p.lds, s));
+  SV_HIP(hipLaunchKernel(fn, dim3(p.grid), dim3(p.threads), args, p.lds, s));
   return SV_OK;
 }
 
@@ -761,7 +797,8 @@ sv_status run_logits(const sv_model* m, const Shape& sh, const void* input, cons
   TimeScope ts(s, 0);
   const int K = sh.decoder ? m->d_model : sh.d;
   const int Nv[1] = {V};
-  const HeadPlan hp = plan_head(M, K, Nv, 1, di);
+  HeadPlan hp = plan_head(M, K, Nv, 1, di);
+  if (hp.ok && rule && rule->sample) head_plan_helpers(hp, M, di);
   if (hp.ok && (rule || !part)) {
     HeadArgs a = head_args(hb, M, K);
     float* out = rule ? rule->logits_out : logits;
@@ -769,6 +806,10 @@ sv_status run_logits(const sv_model* m, const Shape& sh, const void* input, cons
     if (rule) {
       bool fused = !rule->sample;
       if (rule->sample && (st = head_all_resident(hp, di, &fused))) return st;
+      if (rule->sample && !fused && hp.helpers) {   // helper wavefronts only in the fused sampling launch
+        hp = plan_head(M, K, Nv, 1, di);
+        if ((st = head_all_resident(hp, di, &fused))) return st;
+      }
       a.mode = !rule->sample ? HEAD_ACCEPT : (fused ? HEAD_SAMPLE : HEAD_ACCEPT);
       if (rule->sample && !fused) out = logits;      // the separate sampler reads them
       a.part = part;

@@ -324,6 +324,31 @@ __device__ __forceinline__ int head_group_v(int k, int nloc, int TR) {
   return head_global_tile(blockIdx.x, lt, gridDim.x) * TR + (j0 - lt * TR);
 }
 
+// The thread's q entries for the residual draw: entry e < npf = (drafted row e / kg,
+// the thread's group e % kg of four).  The loads issue as one batch: every index is
+// clamped into the q array (groups past the slice or past V read a valid word that the
+// draw never uses) and each entry has registers of its own, so none waits for another.
+template <bool BF16>
+__device__ __forceinline__ void head_prefetch_q(const AcceptArgs& ac, unsigned (&qpf)[HEAD_QPF][4], int npf, int kg,
+                                                int nloc, int TR) {
+#pragma unroll
+  for (int e = 0; e < HEAD_QPF; ++e) {
+    qpf[e][0] = qpf[e][1] = qpf[e][2] = qpf[e][3] = 0u;
+    if (e >= npf) continue;
+    const int rowslot = e / kg, k = e - rowslot * kg;
+    const int j0 = 4 * (int(threadIdx.x) + k * int(blockDim.x));
+    const int lt = min(j0, nloc - 4) / TR;
+    const int vb = min(head_global_tile(blockIdx.x, lt, gridDim.x) * TR + (min(j0, nloc - 4) - lt * TR), ac.V - 1);
+    const size_t row = size_t(rowslot) * ac.V;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t idx = row + min(vb + i, ac.V - 1);
+      qpf[e][i] = BF16 ? unsigned(reinterpret_cast<const unsigned short*>(ac.q)[idx])
+                       : __float_as_uint(reinterpret_cast<const float*>(ac.q)[idx]);
+    }
+  }
+}
+
 // Gumbel noise G = -log(-log U) of the four vocab entries vb .. vb+3 at absolute
 // position pos of sequence b (Philox block vb / 4, tag 1).  U lies in [2^-24, 1), so
 // both logarithms take normal arguments and the hardware logarithm serves.
@@ -333,21 +358,6 @@ __device__ __forceinline__ void gumbel4(uint64_t seed, int b, uint64_t pos, int 
   for (int e = 0; e < 4; ++e) G[e] = -__logf(-__logf(gumbel_uniform_from_word(w.w[e])));
 }
 
-// Merge the statistics partials of the workgroups of group g (blockIdx % G == g) for
-// every row and store one group partial per row (coherent): wave w takes rows w,
-// w + 4, ...; lane k the k-th member (grids of up to 64 * G workgroups).
-__device__ __forceinline__ void head_group_merge(const RowPart* part, RowPart* gpart, int M, unsigned G, unsigned g,
-                                                 float c) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const unsigned gsize = (gridDim.x - g + G - 1) / G;
-  for (int row = wave; row < M; row += HEAD_WAVES) {
-    float m = -INFINITY, s = 0.0f;
-    int am = 0x7fffffff;
-    if (unsigned(lane) < gsize) load_part_coherent(part + size_t(g + G * lane) * M + row, m, s, am);
-    wave_allmerge_stat(m, s, am, c);
-    if (lane == 0) store_part(gpart + size_t(g) * M + row, m, s, am);
-  }
-}
 // X staged from float32 rows with RMSNorm: each row's scale 1 / sqrt(sum(x^2) / K + eps)
 // comes from the ss_parts partial sums the producer of the rows left (wavefront w takes
 // rows w, w + 4, ...; fixed summation order), then every piece is normalised, scaled by
@@ -355,9 +365,9 @@ __device__ __forceinline__ void head_group_merge(const RowPart* part, RowPart* g
 // row).  The arithmetic matches a separate RMSNorm pass: bf16((x * scale) * g).
 __device__ __forceinline__ void head_stage_norm(const HeadArgs& a, bf16_t* sX, int ld, int Kp) {
   __shared__ float s_scale[ACC_MAX_ROWS];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int M = a.M;
-  for (int m = wave; m < M; m += HEAD_WAVES) {
+  for (int m = wave; m < M; m += nw) {
     float ss = 0.0f;
     for (int p = lane; p < a.ss_parts; p += 64) ss += a.ss_in[size_t(p) * M + m];
     ss = wave_allsum(ss);
@@ -399,9 +409,133 @@ __device__ __forceinline__ void head_stage_norm(const HeadArgs& a, bf16_t* sX, i
   }
 }
 
-template <int S, int NB, int GRP>
-__global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_head(HeadArgs a) {
+// Merge of (max, sum of exp2((l - max) * c), lowest argmax) partials over groups of W
+// aligned lanes (W = 8 or 64) in two passes: the group maximum, then every lane rescales
+// its own sum once, and the group adds the rescaled sums and keeps the lowest index among
+// the lanes holding the maximum.  Each step combines the same two operands on both
+// sides, so every lane of a group ends with the same bits; the result does not depend
+// on which lane holds which partial beyond the fixed butterfly order.
+// Wave-wide all-reduces in two stages: DPP butterflies within each row of 16 lanes,
+// then the four row values read into scalar registers and combined in a fixed order
+// ((row 0, row 1), (row 2, row 3)), so every lane ends with the same bits.  Cheaper than
+// lane shuffles through the LDS crossbar.  All 64 lanes must be active.
+__device__ __forceinline__ float readlane_f(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
+__device__ __forceinline__ float wave_max_rl(float v) {
+  v = fmaxf(v, dpp<DPP_XOR1>(v));
+  v = fmaxf(v, dpp<DPP_XOR2>(v));
+  v = fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp<DPP_MIRROR>(v));
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
+}
+__device__ __forceinline__ float wave_sum_rl(float v) {
+  v += dpp<DPP_XOR1>(v);
+  v += dpp<DPP_XOR2>(v);
+  v += dpp<DPP_HALF_MIRROR>(v);
+  v += dpp<DPP_MIRROR>(v);
+  return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+}
+__device__ __forceinline__ int wave_min_rl(int v) {
+  v = min(v, dpp<DPP_XOR1>(v));
+  v = min(v, dpp<DPP_XOR2>(v));
+  v = min(v, dpp<DPP_HALF_MIRROR>(v));
+  v = min(v, dpp<DPP_MIRROR>(v));
+  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+// Merge of (max, sum of exp2((l - max) * c), lowest argmax) partials over groups of W
+// aligned lanes (W = 8 or 64) in two passes: the group maximum, then every lane rescales
+// its own sum once, and the group adds the rescaled sums and keeps the lowest index among
+// the lanes holding the maximum.  Every lane of a group ends with the same bits; the
+// result does not depend on the order the partials arrived in, only on their lanes.
+template <int W>
+__device__ __forceinline__ void group_merge_stat(float& m, float& s, int& a, float c) {
+  static_assert(W == 8 || W == 64, "group of 8 lanes or the whole wave");
+  float mx;
+  if (W == 64) {
+    mx = wave_max_rl(m);
+  } else {
+    mx = fmaxf(m, dpp<DPP_XOR1>(m));
+    mx = fmaxf(mx, dpp<DPP_XOR2>(mx));
+    mx = fmaxf(mx, dpp<DPP_HALF_MIRROR>(mx));
+  }
+  float t = (c != 0.0f && s != 0.0f) ? s * exp2f((m - mx) * c) : 0.0f;
+  int ai = m == mx ? a : 0x7fffffff;
+  if (W == 64) {
+    t = wave_sum_rl(t);
+    ai = wave_min_rl(ai);
+  } else {
+    t += dpp<DPP_XOR1>(t);
+    ai = min(ai, dpp<DPP_XOR1>(ai));
+    t += dpp<DPP_XOR2>(t);
+    ai = min(ai, dpp<DPP_XOR2>(ai));
+    t += dpp<DPP_HALF_MIRROR>(t);
+    ai = min(ai, dpp<DPP_HALF_MIRROR>(ai));
+  }
+  m = mx;
+  s = t;
+  a = ai;
+}
+
+// Slice winners of the sampling launch as one orderable 64-bit key: bit 63 the class
+// (1: a winner of the residual max(0, p - q), 0: a winner under p), bits 62..31 the
+// score mapped to an unsigned order (-0 taken as +0), bits 30..0 the complement of the
+// index, so that the largest key is the best class, then the highest score, then the
+// lowest index.  Every real score maps above zero, so key 0 means "none".
+__device__ __forceinline__ unsigned long long win_key(bool cls, float score, int idx) {
+  const unsigned u = __float_as_uint(score + 0.0f);
+  const unsigned o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<unsigned long long>(cls) << 63) | (static_cast<unsigned long long>(o) << 31) |
+         static_cast<unsigned long long>(0x7fffffffu - unsigned(idx));
+}
+__device__ __forceinline__ int win_index(unsigned long long key) { return int(0x7fffffffu - unsigned(key & 0x7fffffffu)); }
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_max_u64(unsigned long long k) {
+  const unsigned lo = unsigned(dpp<CTRL>(int(unsigned(k)))), hi = unsigned(dpp<CTRL>(int(unsigned(k >> 32))));
+  const unsigned long long k2 = (static_cast<unsigned long long>(hi) << 32) | lo;
+  return k2 > k ? k2 : k;
+}
+__device__ __forceinline__ unsigned long long readlane_u64(unsigned long long k, int l) {
+  const unsigned lo = unsigned(__builtin_amdgcn_readlane(int(unsigned(k)), l));
+  const unsigned hi = unsigned(__builtin_amdgcn_readlane(int(unsigned(k >> 32)), l));
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+__device__ __forceinline__ unsigned long long max_u64(unsigned long long a, unsigned long long b) { return a > b ? a : b; }
+__device__ __forceinline__ unsigned long long wave_allmax_u64(unsigned long long k) {
+  k = dpp_max_u64<DPP_XOR1>(k);
+  k = dpp_max_u64<DPP_XOR2>(k);
+  k = dpp_max_u64<DPP_HALF_MIRROR>(k);
+  k = dpp_max_u64<DPP_MIRROR>(k);
+  return max_u64(max_u64(readlane_u64(k, 0), readlane_u64(k, 16)), max_u64(readlane_u64(k, 32), readlane_u64(k, 48)));
+}
+
+// Helper wavefronts of the sampling launch: the Gumbel noise of every row the draw may
+// use (slot i of sequence b, absolute position pos0[b] + i + 1) over the workgroup's
+// slice, sG[(b * G1 + i) * nloc + j], computed while the other wavefronts stream W.
+template <int HW>
+__device__ __forceinline__ void head_noise(const AcceptArgs& ac, const long long* pos0, float* sG, int nloc, int TR,
+                                           int G1) {
+  const int ht = int(threadIdx.x) - HEAD_WAVES * 64;
+  const int rows = ac.B * G1;
+  for (int row = 0; row < rows; ++row) {
+    const int b = row / G1, i = row - b * G1;
+    const uint64_t pos = uint64_t(pos0[b] + i + 1);
+    for (int j0 = 4 * ht; j0 < nloc; j0 += 4 * 64 * HW) {
+      const int lt = j0 / TR;
+      const int vb = head_global_tile(blockIdx.x, lt, gridDim.x) * TR + (j0 - lt * TR);
+      float G[4] = {0.f, 0.f, 0.f, 0.f};
+      if (vb < ac.V) gumbel4(ac.seed, b, pos, vb, G);
+      *reinterpret_cast<f32x4*>(sG + size_t(row) * nloc + j0) = f32x4{G[0], G[1], G[2], G[3]};
+    }
+  }
+}
+
+// The kernel body.  HW = 0: four wavefronts stream W (every mode).  HW > 0 (sampling
+// only): HW more wavefronts fill the noise table in LDS during the stream.
+template <int S, int NB, int GRP, int HW>
+__device__ __forceinline__ void head_body(const HeadArgs& a) {
   constexpr int TR = 16 / S, CPB = 16 / S;
+  constexpr int NW = HEAD_WAVES + HW;
   // K need not be a multiple of the work item: the last item of a tile runs past the
   // row into the next row's bytes (or past the segment's end, read as zeros), and X
   // holds zeros there, so those products add nothing.
@@ -409,6 +543,7 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   bf16_t* sX = reinterpret_cast<bf16_t*>(smem);
   float* sL = reinterpret_cast<float*>(smem + head_lds_x(a.M, Kp, S));
+  float* sG = reinterpret_cast<float*>(smem + head_lds(a.M, Kp, S, a.nloc));   // HW > 0: the noise table
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int ld = Kp + 8 * S;
@@ -430,8 +565,10 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
 
   // The wavefront's first work item is requested before X is staged: the two
   // latencies overlap instead of adding up.
+  const bool streamer = wave < HEAD_WAVES;
+  if (HW > 0 && streamer) __builtin_amdgcn_s_setprio(2);   // loads first; the helpers take idle issue slots
   const int first = blockIdx.x * HEAD_WAVES + wave, tstride = gridDim.x * HEAD_WAVES;
-  const int n_my = first < ntiles ? (ntiles - 1 - first) / tstride + 1 : 0;
+  const int n_my = streamer && first < ntiles ? (ntiles - 1 - first) / tstride + 1 : 0;
   const int items = n_my * a.gpt;
   const int item_k = 32 * S * GRP;                // elements of a row per work item
   const int lane_ofs = 8 * (S * g + r % S);       // element offset of the lane's piece in step 0
@@ -495,6 +632,18 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   }
 
   const int kg = (nloc / 4 + int(blockDim.x) - 1) / int(blockDim.x);   // groups of four per thread
+  // sampling: q over this slice for every drafted slot, for the residual draw after the
+  // decision (about gamma rows x 2 bytes x V per step).  Fetched here so the loads have
+  // long completed when the draw needs them: issued after the stream, they would sit in
+  // front of the polls of the hand-off records (a poll waits for every older load).
+  const int npf = sample ? ac.B * ac.gamma * kg : 0;
+  const bool prefetched = npf <= HEAD_QPF;
+  unsigned qpf[HEAD_QPF][4];
+  if (sample && prefetched) {
+    if (ac.q_bf16) head_prefetch_q<true>(ac, qpf, npf, kg, nloc, TR);
+    else head_prefetch_q<false>(ac, qpf, npf, kg, nloc, TR);
+  }
+  if (HW > 0 && sample && !streamer) head_noise<HW>(ac, s_pos0, sG, nloc, TR, G1);
 
   HeadStats<NB> st;
 #pragma unroll
@@ -534,7 +683,7 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   // ---- statistics partials: lanes of a row differ in g (xor 16, 32), then the waves
   __shared__ float s_m[HEAD_WAVES][ACC_MAX_ROWS], s_s[HEAD_WAVES][ACC_MAX_ROWS];
   __shared__ int s_a[HEAD_WAVES][ACC_MAX_ROWS];
-  if (stats) {
+  if (stats && streamer) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       xor_merge_stat(st.m[nb], st.s[nb], st.a[nb], c, 16);
@@ -665,56 +814,53 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   }
 
   // 2. the first workgroup of each group merges its members' partials: wave w takes
-  //    rows w, w + 4, ..., lane k member k; each wave polls its own rows
+  //    rows w, w + NW, ... (all polled together), lane k member k
   if (blockIdx.x < G) {
+    constexpr int RPW = (24 + NW - 1) / NW;        // rows per wave (M <= 24, checked on the host)
     const unsigned g = blockIdx.x, gsize = (gridDim.x - g + G - 1) / G;
-    for (int m = wave; m < M; m += HEAD_WAVES) {
-      const unsigned long long* rec = r_part + (size_t(g + G * lane) * M + m) * 4;
-      float rm = -INFINITY, rs = 0.0f;
-      int ra = 0x7fffffff;
-      unsigned spins = 0;
-      bool got = false;
-      for (;;) {
-        bool mine = true;
-        if (unsigned(lane) < gsize) {
-          const unsigned long long w0 = get_tagged(rec), w1 = get_tagged(rec + 1), w2 = get_tagged(rec + 2);
-          mine = tag_is(w0, ep) && tag_is(w1, ep) && tag_is(w2, ep);
-          rm = __uint_as_float(unsigned(w0)); rs = __uint_as_float(unsigned(w1)); ra = int(unsigned(w2));
-        }
-        if (__all(mine)) { got = true; break; }
-        if (spins++ >= a.spin_limit) break;
-        __builtin_amdgcn_s_sleep(1);
-      }
-      if (!got) { if (lane == 0) s_ok = 0; break; }
-      wave_allmerge_stat(rm, rs, ra, c);
-      if (lane == 0) {
-        unsigned long long* out = r_group + (size_t(g) * M + m) * 4;
-        put_tagged(out + 0, __float_as_uint(rm), ep);
-        put_tagged(out + 1, __float_as_uint(rs), ep);
-        put_tagged(out + 2, unsigned(ra), ep);
-      }
-    }
-  }
-
-  // 3a. while the groups merge: fetch q over this slice for every drafted slot, for
-  //     the residual draw after the decision (about gamma rows x 2 bytes x V per step)
-  const int npf = ac.B * ac.gamma * kg;
-  const bool prefetched = npf <= HEAD_QPF;
-  unsigned qpf[HEAD_QPF][4];
+    float rm[RPW], rs[RPW];
+    int ra[RPW];
+    unsigned spins = 0;
+    bool got = false;
+    for (;;) {
+      bool mine = true;
 #pragma unroll
-  for (int e = 0; e < HEAD_QPF; ++e) {
-    qpf[e][0] = qpf[e][1] = qpf[e][2] = qpf[e][3] = 0u;
-    if (prefetched && e < npf) {
-      const int rowslot = e / kg, k = e - rowslot * kg;
-      const int vb = head_group_v(k, nloc, TR);
-      if (vb < ac.V) load_q4(ac, size_t(rowslot) * ac.V, vb, qpf[e]);
+      for (int j = 0; j < RPW; ++j) {
+        const int m = wave + NW * j;
+        rm[j] = -INFINITY; rs[j] = 0.0f; ra[j] = 0x7fffffff;
+        if (m < M && unsigned(lane) < gsize) {
+          const unsigned long long* rec = r_part + (size_t(g + G * lane) * M + m) * 4;
+          const unsigned long long w0 = get_tagged(rec), w1 = get_tagged(rec + 1), w2 = get_tagged(rec + 2);
+          mine = mine && tag_is(w0, ep) && tag_is(w1, ep) && tag_is(w2, ep);
+          rm[j] = __uint_as_float(unsigned(w0)); rs[j] = __uint_as_float(unsigned(w1)); ra[j] = int(unsigned(w2));
+        }
+      }
+      if (__all(mine)) { got = true; break; }
+      if (spins++ >= a.spin_limit) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (!got) {
+      if (lane == 0) s_ok = 0;
+    } else {
+#pragma unroll
+      for (int j = 0; j < RPW; ++j) group_merge_stat<64>(rm[j], rs[j], ra[j], c);
+#pragma unroll
+      for (int j = 0; j < RPW; ++j) {
+        const int m = wave + NW * j;
+        if (lane == 0 && m < M) {
+          unsigned long long* out = r_group + (size_t(g) * M + m) * 4;
+          put_tagged(out + 0, __float_as_uint(rm[j]), ep);
+          put_tagged(out + 1, __float_as_uint(rs[j]), ep);
+          put_tagged(out + 2, unsigned(ra[j]), ep);
+        }
+      }
     }
   }
 
   // 3b. read the G group partials (eight lanes per row, merged in a fixed order) and
   //     the draft logits; each wave polls its own rows
   __shared__ float s_xl[ACC_MAX_ROWS];
-  for (int row0 = wave * 8; row0 < M; row0 += 8 * HEAD_WAVES) {
+  for (int row0 = wave * 8; row0 < M; row0 += 8 * NW) {
     const int row = row0 + lane / 8, gp = lane % 8;
     const bool need = row < M && unsigned(gp) < G;
     const unsigned long long* rec = r_group + (size_t(gp) * M + row) * 4;
@@ -743,9 +889,7 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
     }
     if (!got) { if (lane == 0) s_ok = 0; break; }
     if (!need) { m = -INFINITY; sm = 0.0f; am = 0x7fffffff; }
-    dpp_merge_stat<DPP_XOR1>(m, sm, am, c);
-    dpp_merge_stat<DPP_XOR2>(m, sm, am, c);
-    dpp_merge_stat<DPP_HALF_MIRROR>(m, sm, am, c);
+    group_merge_stat<8>(m, sm, am, c);
     if (gp == 0 && row < M) { s_m[0][row] = m; s_s[0][row] = sm; s_a[0][row] = am; s_xl[row] = xl; }
   }
   __syncthreads();
@@ -755,7 +899,7 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   __shared__ int s_n[ACC_MAX_ROWS];
   __shared__ float s_mn[ACC_MAX_ROWS], s_zn[ACC_MAX_ROWS];
   if (ok) {
-    for (int b = wave; b < ac.B; b += HEAD_WAVES) {
+    for (int b = wave; b < ac.B; b += NW) {
       const int row = b * G1 + lane;
       float my_m = -INFINITY, my_s = 0.0f;
       float px = 0.0f, qx = 0.0f, u = 1.0f;
@@ -778,10 +922,9 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   }
 
   // 3d. Gumbel-max of row n_b over this slice; publish one winner per (sequence, workgroup)
-  __shared__ float s_sr[HEAD_WAVES], s_sp[HEAD_WAVES];
-  __shared__ int s_ir[HEAD_WAVES], s_ip[HEAD_WAVES];
+  __shared__ unsigned long long s_key[NW];
   for (int b = 0; b < ac.B && ok; ++b) {
-    const int n = s_n[b];
+    const int n = __builtin_amdgcn_readfirstlane(s_n[b]);   // the same for every thread
     float sr = -INFINITY, sp = -INFINITY;
     int ir = 0x7fffffff, ip = 0x7fffffff;
     if (n >= 0) {
@@ -807,7 +950,12 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
           }
         }
         float gn[4];
-        gumbel4(ac.seed, b, pos, vb, gn);
+        if (HW > 0) {
+          const f32x4 g4 = *reinterpret_cast<const f32x4*>(sG + size_t(b * G1 + n) * nloc + j0);
+          gn[0] = g4[0]; gn[1] = g4[1]; gn[2] = g4[2]; gn[3] = g4[3];
+        } else {
+          gumbel4(ac.seed, b, pos, vb, gn);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int v = vb + e;
@@ -826,22 +974,16 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
         }
       }
     }
-    wave_allmerge_best(sr, ir);
-    wave_allmerge_best(sp, ip);
-    if (lane == 0) { s_sr[wave] = sr; s_ir[wave] = ir; s_sp[wave] = sp; s_ip[wave] = ip; }
+    // the slice's residual winner if it has one (class 1), else its winner under p
+    unsigned long long key = ir != 0x7fffffff ? win_key(true, sr, ir) : ip != 0x7fffffff ? win_key(false, sp, ip) : 0ull;
+    key = wave_allmax_u64(key);
+    if (lane == 0) s_key[wave] = key;
     __syncthreads();
     if (threadIdx.x == 0) {
-      float osr = -INFINITY, osp = -INFINITY;
-      int oir = 0x7fffffff, oip = 0x7fffffff;
-      for (int w = 0; w < HEAD_WAVES; ++w) {
-        merge_best(osr, oir, s_sr[w], s_ir[w]);
-        merge_best(osp, oip, s_sp[w], s_ip[w]);
-      }
-      unsigned long long* rec = r_win + (size_t(b) * RG + blockIdx.x) * 4;
-      put_tagged(rec + 0, __float_as_uint(osr), ep);
-      put_tagged(rec + 1, unsigned(oir), ep);
-      put_tagged(rec + 2, __float_as_uint(osp), ep);
-      put_tagged(rec + 3, unsigned(oip), ep);
+      for (int w = 1; w < NW; ++w) key = s_key[w] > key ? s_key[w] : key;
+      unsigned long long* rec = r_win + (size_t(b) * RG + blockIdx.x) * 2;
+      put_tagged(rec + 0, unsigned(key >> 32), ep);
+      put_tagged(rec + 1, unsigned(key), ep);
     }
     __syncthreads();
   }
@@ -853,41 +995,36 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   bool done = ok;
   for (int b = 0; b < ac.B && done; ++b) {
     if (s_n[b] < 0) continue;
-    float sr = -INFINITY, sp = -INFINITY;
-    int ir = 0x7fffffff, ip = 0x7fffffff;
+    // the largest slice-winner key: the residual's winner when any slice has one, else
+    // the winner under p
+    unsigned long long key = 0ull;
     unsigned spins = 0;
     for (;;) {
       bool mine = true;
-      float tsr = -INFINITY, tsp = -INFINITY;
-      int tir = 0x7fffffff, tip = 0x7fffffff;
+      unsigned long long tk = 0ull;
       for (int p = threadIdx.x; p < int(gridDim.x); p += blockDim.x) {
-        const unsigned long long* rec = r_win + (size_t(b) * RG + p) * 4;
-        const unsigned long long w0 = get_tagged(rec), w1 = get_tagged(rec + 1), w2 = get_tagged(rec + 2),
-                                 w3 = get_tagged(rec + 3);
-        if (tag_is(w0, ep) && tag_is(w1, ep) && tag_is(w2, ep) && tag_is(w3, ep)) {
-          merge_best(tsr, tir, __uint_as_float(unsigned(w0)), int(unsigned(w1)));
-          merge_best(tsp, tip, __uint_as_float(unsigned(w2)), int(unsigned(w3)));
+        const unsigned long long* rec = r_win + (size_t(b) * RG + p) * 2;
+        const unsigned long long w0 = get_tagged(rec), w1 = get_tagged(rec + 1);
+        if (tag_is(w0, ep) && tag_is(w1, ep)) {
+          const unsigned long long k2 = (static_cast<unsigned long long>(unsigned(w0)) << 32) | unsigned(w1);
+          tk = k2 > tk ? k2 : tk;
         } else {
           mine = false;
         }
       }
-      if (__syncthreads_and(mine)) { sr = tsr; ir = tir; sp = tsp; ip = tip; break; }
+      if (__syncthreads_and(mine)) { key = tk; break; }
       // a workgroup that gave up never publishes: stop waiting (one uniform answer)
       const bool failed = __syncthreads_or(threadIdx.x == 0 && load_coherent(a.counter + CNT_FAIL) == ep);
       if (failed || spins++ >= a.spin_limit) { done = false; break; }
       __builtin_amdgcn_s_sleep(1);
     }
     if (!done) break;
-    wave_allmerge_best(sr, ir);
-    wave_allmerge_best(sp, ip);
-    if (lane == 0) { s_sr[wave] = sr; s_ir[wave] = ir; s_sp[wave] = sp; s_ip[wave] = ip; }
+    key = wave_allmax_u64(key);
+    if (lane == 0) s_key[wave] = key;
     __syncthreads();
     if (threadIdx.x == 0) {
-      for (int w = 1; w < HEAD_WAVES; ++w) {
-        merge_best(s_sr[0], s_ir[0], s_sr[w], s_ir[w]);
-        merge_best(s_sp[0], s_ip[0], s_sp[w], s_ip[w]);
-      }
-      s_tok[b] = (s_n[b] < ac.gamma && s_ir[0] != 0x7fffffff) ? s_ir[0] : s_ip[0];
+      for (int w = 1; w < NW; ++w) key = s_key[w] > key ? s_key[w] : key;
+      s_tok[b] = win_index(key);
     }
     __syncthreads();
   }
@@ -903,6 +1040,19 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
     if (ac.len && n >= 0) ac.len[b] += n + 1;
   }
   if (threadIdx.x == 0) atomic_store_agent(a.counter + CNT_EPOCH, done ? ep : EPOCH_POISON);
+}
+
+constexpr int HEAD_HELPERS = 4;   // helper wavefronts of the sampling launch
+
+template <int S, int NB, int GRP>
+__global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_head(HeadArgs a) {
+  head_body<S, NB, GRP, 0>(a);
+}
+
+template <int S, int NB, int GRP>
+__global__ __launch_bounds__((HEAD_WAVES + HEAD_HELPERS) * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_head_h(
+    HeadArgs a) {
+  head_body<S, NB, GRP, HEAD_HELPERS>(a);
 }
 
 }  // namespace sv

@@ -287,27 +287,35 @@ struct HeadPlan {
   bool ok = false;
   int S = 0, NB = 0, GRP = 0, grid = 0, gpt = 0, nloc = 0;
   size_t lds = 0;
-  bool helpers = false;     // sampling launch with helper wavefronts (k_head_h)
-  int threads = HEAD_WAVES * 64;
 };
 
 // Largest column-block count instantiated per split factor.
 int head_nb_max(int S) { return S == 4 ? 5 : 3; }
 
-HeadPlan plan_head(int M, int K, const int* N, int nseg, const DevInfo& di) {
+// Plan of the k-split kernel.  Products (decoder linears, verify_forward): one
+// workgroup per CU, loads per lane per work item tried in the order 4, 8, 6.  The
+// LM-head launch that applies the rule (rule = true): two workgroups per CU and the
+// order 6, 4, 8 (805 MB head, K = 1536: 126.1 us against 137.1 us for one workgroup
+// and items of 4; the decoder's products measured slower with two).  only_s != 0
+// admits that split factor alone.  SV_HEAD_S, SV_HEAD_GRP, SV_HEAD_WG_PER_CU and
+// SV_HEAD_RULE_WG_PER_CU override the choices.
+HeadPlan plan_head(int M, int K, const int* N, int nseg, const DevInfo& di, bool rule = false, int only_s = 0) {
   HeadPlan p;
-  if (M < 1 || M > ACC_MAX_ROWS || K % 8) return p;
+  if (M < 1 || M > HEAD_MAX_ROWS || K % 8) return p;
   for (int i = 0; i < nseg; ++i)    // weights are addressed with 32-bit byte offsets
     if (int64_t(N[i]) * K * 2 > int64_t(0xffffffffLL) - 4096) return p;
   const int want_s = env_int("SV_HEAD_S", 0), want_grp = env_int("SV_HEAD_GRP", 0);
-  const int per_cu = std::max(1, env_int("SV_HEAD_WG_PER_CU", 1));
+  const int per_cu = std::max(1, rule ? env_int("SV_HEAD_RULE_WG_PER_CU", 2) : env_int("SV_HEAD_WG_PER_CU", 1));
+  const int order_product[3] = {4, 8, 6}, order_rule[3] = {6, 4, 8};
+  const int* order = rule ? order_rule : order_product;
   for (int S : {4, 2}) {
-    if (want_s && S != want_s) continue;
+    if ((want_s && S != want_s) || (only_s && S != only_s)) continue;
     const int TR = 16 / S, NB = (M + TR - 1) / TR;
     if (NB > head_nb_max(S) || K % (32 * S)) continue;
     const int steps = K / (32 * S);
     int GRP = 0;
-    for (int gc : {4, 8, 6}) {   // two items of 4 loads per lane in flight measured best (2, 3, 6, 8 slower)
+    for (int i = 0; i < 3; ++i) {
+      const int gc = order[i];
       if (want_grp && gc != want_grp) continue;
       if (steps % gc == 0) { GRP = gc; break; }
     }
@@ -327,6 +335,16 @@ HeadPlan plan_head(int M, int K, const int* N, int nseg, const DevInfo& di) {
   return p;
 }
 
+// The plan of an LM-head launch that applies the rule, on the split factor of the
+// product plan: the split fixes the summation order, so the logits are the same bits
+// as verify_forward's.
+HeadPlan plan_head_rule(int M, int K, const int* N, const DevInfo& di) {
+  HeadPlan hp = plan_head(M, K, N, 1, di);
+  if (!hp.ok) return hp;
+  const HeadPlan r = plan_head(M, K, N, 1, di, true, hp.S);
+  return r.ok ? r : hp;
+}
+
 template <int S, int NB>
 const void* head_fn_grp(int GRP) {
   switch (GRP) {
@@ -336,30 +354,7 @@ const void* head_fn_grp(int GRP) {
   }
 }
 
-template <int S, int NB>
-const void* head_fn_grp_h(int GRP) {
-  switch (GRP) {
-    case 8: return reinterpret_cast<const void*>(&k_head_h<S, NB, 8>);
-    case 6: return reinterpret_cast<const void*>(&k_head_h<S, NB, 6>);
-    default: return reinterpret_cast<const void*>(&k_head_h<S, NB, 4>);
-  }
-}
-
-// Column-block counts with a helper-wavefront instantiation (the noise table of
-// B * (gamma + 1) rows must fit in LDS beside X and the kept products).
-bool head_helpers_instantiated(int S, int NB) { return S == 4 ? NB <= 3 : NB <= 2; }
-
 const void* head_fn(const HeadPlan& p) {
-  if (p.helpers) {
-    if (p.S == 4) {
-      switch (p.NB) {
-        case 1: return head_fn_grp_h<4, 1>(p.GRP);
-        case 2: return head_fn_grp_h<4, 2>(p.GRP);
-        default: return head_fn_grp_h<4, 3>(p.GRP);
-      }
-    }
-    return p.NB == 1 ? head_fn_grp_h<2, 1>(p.GRP) : head_fn_grp_h<2, 2>(p.GRP);
-  }
   if (p.S == 4) {
     switch (p.NB) {
       case 1: return head_fn_grp<4, 1>(p.GRP);
@@ -407,23 +402,12 @@ sv_status head_set_lds(const void* fn, size_t lds) {
 
 // Whether every workgroup of the plan can be resident at once (the fused sampler's
 // grid barrier needs it).
-// The sampling launch's helper wavefronts: when the noise table of ``rows`` rows fits in
-// LDS (SV_HEAD_HELPERS=0 turns them off).
-void head_plan_helpers(HeadPlan& p, int rows, const DevInfo& di) {
-  if (!p.ok || !head_helpers_instantiated(p.S, p.NB) || !env_int("SV_HEAD_HELPERS", 1)) return;
-  const size_t noise = size_t(rows) * p.nloc * 4;
-  if (p.lds + noise + HEAD_STATIC_LDS > di.lds_max) return;
-  p.helpers = true;
-  p.threads = (HEAD_WAVES + HEAD_HELPERS) * 64;
-  p.lds += noise;
-}
-
 sv_status head_all_resident(const HeadPlan& p, const DevInfo& di, bool* yes) {
   const void* fn = head_fn(p);
   sv_status st = head_set_lds(fn, p.lds);
   if (st) return st;
   int per_cu = 0;
-  SV_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, p.threads, p.lds));
+  SV_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, HEAD_WAVES * 64, p.lds));
   *yes = int64_t(per_cu) * di.cus >= p.grid && p.grid <= 64 * CNT_GROUPS;   // group merge: a lane per member
   return SV_OK;
 }
@@ -435,7 +419,7 @@ sv_status launch_head(const HeadPlan& p, HeadArgs a, hipStream_t s) {
   sv_status st = head_set_lds(fn, p.lds);
   if (st) return st;
   void* args[] = {&a};
-  SV_HIP(hipLaunchKernel(fn, dim3(p.grid), dim3(p.threads), args, p.lds, s));
+  SV_HIP(hipLaunchKernel(fn, dim3(p.grid), dim3(HEAD_WAVES * 64), args, p.lds, s));
   return SV_OK;
 }
 
@@ -797,8 +781,7 @@ sv_status run_logits(const sv_model* m, const Shape& sh, const void* input, cons
   TimeScope ts(s, 0);
   const int K = sh.decoder ? m->d_model : sh.d;
   const int Nv[1] = {V};
-  HeadPlan hp = plan_head(M, K, Nv, 1, di);
-  if (hp.ok && rule && rule->sample) head_plan_helpers(hp, M, di);
+  HeadPlan hp = rule ? plan_head_rule(M, K, Nv, di) : plan_head(M, K, Nv, 1, di);
   if (hp.ok && (rule || !part)) {
     HeadArgs a = head_args(hb, M, K);
     float* out = rule ? rule->logits_out : logits;
@@ -806,7 +789,7 @@ sv_status run_logits(const sv_model* m, const Shape& sh, const void* input, cons
     if (rule) {
       bool fused = !rule->sample;
       if (rule->sample && (st = head_all_resident(hp, di, &fused))) return st;
-      if (rule->sample && !fused && hp.helpers) {   // helper wavefronts only in the fused sampling launch
+      if (rule->sample && !fused && hp.grid > di.cus) {   // one workgroup per CU, else the separate sampler
         hp = plan_head(M, K, Nv, 1, di);
         if ((st = head_all_resident(hp, di, &fused))) return st;
       }

@@ -119,10 +119,10 @@ __device__ __forceinline__ void merge_row(const RowPart* __restrict__ part, int 
   wave_allmerge_stat(m, s, am, c);
 }
 
-// Acceptance for sequences [b0, b0 + nb) by one workgroup of 256 threads.
-// Phase 1: the four wavefronts merge the statistics partials of the nb * G1 rows
-// (row j by wave j % 4); phase 2: wave w applies the rule to sequences b0 + w,
-// b0 + w + 4, ... with lane i holding slot i.  Requires nb * G1 <= ACC_MAX_ROWS.
+// Acceptance for sequences [b0, b0 + nb) by one workgroup (of four or more wavefronts).
+// Phase 1: the wavefronts merge the statistics partials of the nb * G1 rows
+// (row j by wave j % waves); phase 2: wave w applies the rule to sequences b0 + w,
+// b0 + w + waves, ... with lane i holding slot i.  Requires nb * G1 <= ACC_MAX_ROWS.
 constexpr int ACC_MAX_ROWS = 64;
 
 __device__ __forceinline__ void accept_block(const AcceptArgs& a, int b0, int nb) {
@@ -132,14 +132,14 @@ __device__ __forceinline__ void accept_block(const AcceptArgs& a, int b0, int nb
   const float cs = a.sample ? a.c : 0.0f;
   __shared__ float s_m[ACC_MAX_ROWS], s_s[ACC_MAX_ROWS];
   __shared__ int s_a[ACC_MAX_ROWS];
-  for (int j = wave; j < nb * G1; j += 4) {
+  for (int j = wave; j < nb * G1; j += int(blockDim.x >> 6)) {
     float m, s;
     int am;
     merge_row(a.part, a.P, M, b0 * G1 + j, cs, m, s, am);
     if (lane == 0) { s_m[j] = m; s_s[j] = s; s_a[j] = am; }
   }
   __syncthreads();
-  for (int bl = wave; bl < nb; bl += 4) {
+  for (int bl = wave; bl < nb; bl += int(blockDim.x >> 6)) {
     const int b = b0 + bl;
     float my_m = -INFINITY, my_s = 0.0f;
     int my_a = 0x7fffffff;

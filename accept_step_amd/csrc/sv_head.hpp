@@ -46,7 +46,8 @@
 
 namespace sv {
 
-constexpr int HEAD_WAVES = 4;
+constexpr int HEAD_WAVES = 4;      // wavefronts per workgroup
+constexpr int HEAD_MAX_ROWS = 24;  // most rows of X (M) the k-split kernel takes
 constexpr int HEAD_PRODUCT = 0, HEAD_ACCEPT = 1, HEAD_SAMPLE = 2;
 constexpr unsigned HEAD_SPIN_LIMIT = 1u << 20;   // default polls of the barrier count (about a second)
 
@@ -509,33 +510,10 @@ __device__ __forceinline__ unsigned long long wave_allmax_u64(unsigned long long
   return max_u64(max_u64(readlane_u64(k, 0), readlane_u64(k, 16)), max_u64(readlane_u64(k, 32), readlane_u64(k, 48)));
 }
 
-// Helper wavefronts of the sampling launch: the Gumbel noise of every row the draw may
-// use (slot i of sequence b, absolute position pos0[b] + i + 1) over the workgroup's
-// slice, sG[(b * G1 + i) * nloc + j], computed while the other wavefronts stream W.
-template <int HW>
-__device__ __forceinline__ void head_noise(const AcceptArgs& ac, const long long* pos0, float* sG, int nloc, int TR,
-                                           int G1) {
-  const int ht = int(threadIdx.x) - HEAD_WAVES * 64;
-  const int rows = ac.B * G1;
-  for (int row = 0; row < rows; ++row) {
-    const int b = row / G1, i = row - b * G1;
-    const uint64_t pos = uint64_t(pos0[b] + i + 1);
-    for (int j0 = 4 * ht; j0 < nloc; j0 += 4 * 64 * HW) {
-      const int lt = j0 / TR;
-      const int vb = head_global_tile(blockIdx.x, lt, gridDim.x) * TR + (j0 - lt * TR);
-      float G[4] = {0.f, 0.f, 0.f, 0.f};
-      if (vb < ac.V) gumbel4(ac.seed, b, pos, vb, G);
-      *reinterpret_cast<f32x4*>(sG + size_t(row) * nloc + j0) = f32x4{G[0], G[1], G[2], G[3]};
-    }
-  }
-}
-
-// The kernel body.  HW = 0: four wavefronts stream W (every mode).  HW > 0 (sampling
-// only): HW more wavefronts fill the noise table in LDS during the stream.
-template <int S, int NB, int GRP, int HW>
-__device__ __forceinline__ void head_body(const HeadArgs& a) {
+template <int S, int NB, int GRP>
+__global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_head(HeadArgs a) {
   constexpr int TR = 16 / S, CPB = 16 / S;
-  constexpr int NW = HEAD_WAVES + HW;
+  constexpr int NW = HEAD_WAVES;
   // K need not be a multiple of the work item: the last item of a tile runs past the
   // row into the next row's bytes (or past the segment's end, read as zeros), and X
   // holds zeros there, so those products add nothing.
@@ -543,7 +521,6 @@ __device__ __forceinline__ void head_body(const HeadArgs& a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   bf16_t* sX = reinterpret_cast<bf16_t*>(smem);
   float* sL = reinterpret_cast<float*>(smem + head_lds_x(a.M, Kp, S));
-  float* sG = reinterpret_cast<float*>(smem + head_lds(a.M, Kp, S, a.nloc));   // HW > 0: the noise table
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int ld = Kp + 8 * S;
@@ -557,18 +534,16 @@ __device__ __forceinline__ void head_body(const HeadArgs& a) {
 
   // per-row inputs of the rule, fetched before the stream (their latency would
   // otherwise land after it, behind the other workgroups' traffic)
-  __shared__ int s_draft[ACC_MAX_ROWS];
-  __shared__ float s_qx[ACC_MAX_ROWS], s_u[ACC_MAX_ROWS];
-  __shared__ int s_bad[ACC_MAX_ROWS];
-  __shared__ long long s_pos0[ACC_MAX_ROWS];
+  __shared__ int s_draft[HEAD_MAX_ROWS];
+  __shared__ float s_qx[HEAD_MAX_ROWS], s_u[HEAD_MAX_ROWS];
+  __shared__ int s_bad[HEAD_MAX_ROWS];
+  __shared__ long long s_pos0[HEAD_MAX_ROWS];
   __shared__ unsigned s_ep;                       // HEAD_SAMPLE: this launch's epoch
 
   // The wavefront's first work item is requested before X is staged: the two
   // latencies overlap instead of adding up.
-  const bool streamer = wave < HEAD_WAVES;
-  if (HW > 0 && streamer) __builtin_amdgcn_s_setprio(2);   // loads first; the helpers take idle issue slots
   const int first = blockIdx.x * HEAD_WAVES + wave, tstride = gridDim.x * HEAD_WAVES;
-  const int n_my = streamer && first < ntiles ? (ntiles - 1 - first) / tstride + 1 : 0;
+  const int n_my = first < ntiles ? (ntiles - 1 - first) / tstride + 1 : 0;
   const int items = n_my * a.gpt;
   const int item_k = 32 * S * GRP;                // elements of a row per work item
   const int lane_ofs = 8 * (S * g + r % S);       // element offset of the lane's piece in step 0
@@ -643,7 +618,6 @@ __device__ __forceinline__ void head_body(const HeadArgs& a) {
     if (ac.q_bf16) head_prefetch_q<true>(ac, qpf, npf, kg, nloc, TR);
     else head_prefetch_q<false>(ac, qpf, npf, kg, nloc, TR);
   }
-  if (HW > 0 && sample && !streamer) head_noise<HW>(ac, s_pos0, sG, nloc, TR, G1);
 
   HeadStats<NB> st;
 #pragma unroll
@@ -681,9 +655,9 @@ __device__ __forceinline__ void head_body(const HeadArgs& a) {
   if (sample && threadIdx.x < M) s_qx[threadIdx.x] = my_qx;
 
   // ---- statistics partials: lanes of a row differ in g (xor 16, 32), then the waves
-  __shared__ float s_m[HEAD_WAVES][ACC_MAX_ROWS], s_s[HEAD_WAVES][ACC_MAX_ROWS];
-  __shared__ int s_a[HEAD_WAVES][ACC_MAX_ROWS];
-  if (stats && streamer) {
+  __shared__ float s_m[HEAD_WAVES][HEAD_MAX_ROWS], s_s[HEAD_WAVES][HEAD_MAX_ROWS];
+  __shared__ int s_a[HEAD_WAVES][HEAD_MAX_ROWS];
+  if (stats) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       xor_merge_stat(st.m[nb], st.s[nb], st.a[nb], c, 16);
@@ -816,7 +790,7 @@ __device__ __forceinline__ void head_body(const HeadArgs& a) {
   // 2. the first workgroup of each group merges its members' partials: wave w takes
   //    rows w, w + NW, ... (all polled together), lane k member k
   if (blockIdx.x < G) {
-    constexpr int RPW = (24 + NW - 1) / NW;        // rows per wave (M <= 24, checked on the host)
+    constexpr int RPW = (HEAD_MAX_ROWS + NW - 1) / NW;   // rows per wave
     const unsigned g = blockIdx.x, gsize = (gridDim.x - g + G - 1) / G;
     float rm[RPW], rs[RPW];
     int ra[RPW];
@@ -859,7 +833,7 @@ __device__ __forceinline__ void head_body(const HeadArgs& a) {
 
   // 3b. read the G group partials (eight lanes per row, merged in a fixed order) and
   //     the draft logits; each wave polls its own rows
-  __shared__ float s_xl[ACC_MAX_ROWS];
+  __shared__ float s_xl[HEAD_MAX_ROWS];
   for (int row0 = wave * 8; row0 < M; row0 += 8 * NW) {
     const int row = row0 + lane / 8, gp = lane % 8;
     const bool need = row < M && unsigned(gp) < G;
@@ -896,8 +870,8 @@ __device__ __forceinline__ void head_body(const HeadArgs& a) {
   const bool ok = s_ok != 0;
 
   // 3c. decide n for every sequence
-  __shared__ int s_n[ACC_MAX_ROWS];
-  __shared__ float s_mn[ACC_MAX_ROWS], s_zn[ACC_MAX_ROWS];
+  __shared__ int s_n[HEAD_MAX_ROWS];
+  __shared__ float s_mn[HEAD_MAX_ROWS], s_zn[HEAD_MAX_ROWS];
   if (ok) {
     for (int b = wave; b < ac.B; b += NW) {
       const int row = b * G1 + lane;
@@ -950,12 +924,7 @@ __device__ __forceinline__ void head_body(const HeadArgs& a) {
           }
         }
         float gn[4];
-        if (HW > 0) {
-          const f32x4 g4 = *reinterpret_cast<const f32x4*>(sG + size_t(b * G1 + n) * nloc + j0);
-          gn[0] = g4[0]; gn[1] = g4[1]; gn[2] = g4[2]; gn[3] = g4[3];
-        } else {
-          gumbel4(ac.seed, b, pos, vb, gn);
-        }
+        gumbel4(ac.seed, b, pos, vb, gn);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int v = vb + e;
@@ -991,7 +960,7 @@ __device__ __forceinline__ void head_body(const HeadArgs& a) {
 
   // 4. workgroup 0 merges the winners, writes the outputs and stores the epoch
   if (blockIdx.x != 0) return;
-  __shared__ int s_tok[ACC_MAX_ROWS];
+  __shared__ int s_tok[HEAD_MAX_ROWS];
   bool done = ok;
   for (int b = 0; b < ac.B && done; ++b) {
     if (s_n[b] < 0) continue;
@@ -1040,19 +1009,6 @@ __device__ __forceinline__ void head_body(const HeadArgs& a) {
     if (ac.len && n >= 0) ac.len[b] += n + 1;
   }
   if (threadIdx.x == 0) atomic_store_agent(a.counter + CNT_EPOCH, done ? ep : EPOCH_POISON);
-}
-
-constexpr int HEAD_HELPERS = 4;   // helper wavefronts of the sampling launch
-
-template <int S, int NB, int GRP>
-__global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_head(HeadArgs a) {
-  head_body<S, NB, GRP, 0>(a);
-}
-
-template <int S, int NB, int GRP>
-__global__ __launch_bounds__((HEAD_WAVES + HEAD_HELPERS) * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_head_h(
-    HeadArgs a) {
-  head_body<S, NB, GRP, HEAD_HELPERS>(a);
 }
 
 }  // namespace sv

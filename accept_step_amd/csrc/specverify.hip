@@ -292,20 +292,18 @@ struct HeadPlan {
 // Largest column-block count instantiated per split factor.
 int head_nb_max(int S) { return S == 4 ? 5 : 3; }
 
-// Plan of the k-split kernel.  Products (decoder linears, verify_forward): one
-// workgroup per CU, loads per lane per work item tried in the order 4, 8, 6.  The
-// LM-head launch that applies the rule (rule = true): two workgroups per CU and the
-// order 6, 4, 8 (805 MB head, K = 1536: 126.1 us against 137.1 us for one workgroup
-// and items of 4; the decoder's products measured slower with two).  only_s != 0
-// admits that split factor alone.  SV_HEAD_S, SV_HEAD_GRP, SV_HEAD_WG_PER_CU and
-// SV_HEAD_RULE_WG_PER_CU override the choices.
+// Plan of the k-split kernel, one workgroup per CU.  Loads per lane per work item are
+// tried in the order 4, 8, 6 for products (decoder linears, verify_forward) and 6, 4, 8
+// for the LM-head launch that applies the rule (rule = true; 805 MB head, K = 1536:
+// 130.6 us against 137.1 us with items of 4).  only_s != 0 admits that split factor
+// alone.  SV_HEAD_S, SV_HEAD_GRP and SV_HEAD_WG_PER_CU override the choices.
 HeadPlan plan_head(int M, int K, const int* N, int nseg, const DevInfo& di, bool rule = false, int only_s = 0) {
   HeadPlan p;
   if (M < 1 || M > HEAD_MAX_ROWS || K % 8) return p;
   for (int i = 0; i < nseg; ++i)    // weights are addressed with 32-bit byte offsets
     if (int64_t(N[i]) * K * 2 > int64_t(0xffffffffLL) - 4096) return p;
   const int want_s = env_int("SV_HEAD_S", 0), want_grp = env_int("SV_HEAD_GRP", 0);
-  const int per_cu = std::max(1, rule ? env_int("SV_HEAD_RULE_WG_PER_CU", 2) : env_int("SV_HEAD_WG_PER_CU", 1));
+  const int per_cu = std::max(1, env_int("SV_HEAD_WG_PER_CU", 1));
   const int order_product[3] = {4, 8, 6}, order_rule[3] = {6, 4, 8};
   const int* order = rule ? order_rule : order_product;
   for (int S : {4, 2}) {
@@ -408,7 +406,10 @@ sv_status head_all_resident(const HeadPlan& p, const DevInfo& di, bool* yes) {
   if (st) return st;
   int per_cu = 0;
   SV_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, HEAD_WAVES * 64, p.lds));
-  *yes = int64_t(per_cu) * di.cus >= p.grid && p.grid <= 64 * CNT_GROUPS;   // group merge: a lane per member
+  // One workgroup per CU at most: with two per CU the occupancy query allowed the grid,
+  // yet back-to-back launches did not always have every workgroup resident and the
+  // bounded waits timed out.  The group merge takes a lane per member.
+  *yes = per_cu >= 1 && p.grid <= di.cus && p.grid <= 64 * CNT_GROUPS;
   return SV_OK;
 }
 
@@ -789,10 +790,6 @@ sv_status run_logits(const sv_model* m, const Shape& sh, const void* input, cons
     if (rule) {
       bool fused = !rule->sample;
       if (rule->sample && (st = head_all_resident(hp, di, &fused))) return st;
-      if (rule->sample && !fused && hp.grid > di.cus) {   // one workgroup per CU, else the separate sampler
-        hp = plan_head(M, K, Nv, 1, di);
-        if ((st = head_all_resident(hp, di, &fused))) return st;
-      }
       a.mode = !rule->sample ? HEAD_ACCEPT : (fused ? HEAD_SAMPLE : HEAD_ACCEPT);
       if (rule->sample && !fused) out = logits;      // the separate sampler reads them
       a.part = part;

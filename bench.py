@@ -124,6 +124,7 @@ def main():
     gemm_ms, gemm_n = ev0.elapsed_time(ev1), K
 
     n_host = n_out.to(torch.int64).cpu()
+    require_valid(n_host, "large-vocab")
     committed = int((n_host + 1).sum().item())
     value = committed / elapsed
     ms_per_step = elapsed / K * 1e3
@@ -237,6 +238,7 @@ def full_model(args, torch, sv):
     kv_write = 2 * L * B * H * (gamma + 1) * hd * 2
     with_kv = weight_bytes + V * d * 2 + kv_read + kv_write + B * (gamma + 1) * d * 2
     params_bytes = weight_bytes + 2 * V * d * 2          # the 6.74B parameters incl. the embedding table
+    require_valid(n_out.to(torch.int64).cpu(), "full-model")
     committed = int((n_out.to(torch.int64) + 1).sum().item())
     out = {
         "metric": "full-model verify step latency (ms/step) and HBM GB/s",
@@ -252,6 +254,16 @@ def full_model(args, torch, sv):
                    "decoder_ms": round(dec_ms / max(dec_n, 1), 4), "lm_head_step_ms": round(head_ms / max(head_n, 1), 4)},
     }
     print(json.dumps(out), flush=True)
+
+
+def require_valid(n_host, what):
+    """Every timed step must have produced a valid result (n_accepted >= 0): a step the
+    library reports invalid did not run the whole path, so its time is not a measurement."""
+    bad = int((n_host < 0).sum().item())
+    if bad:
+        print(f"bench.py: {bad} of {n_host.numel()} sequences in the timed {what} steps came back invalid "
+              "(n_accepted = -1); no measurement is reported", file=sys.stderr)
+        sys.exit(3)
 
 
 def committed_traffic(path, root):

@@ -316,7 +316,7 @@ __device__ __forceinline__ float q_value(const AcceptArgs& ac, unsigned raw) {
 
 constexpr int HEAD_QPF = 8;   // (row, group) entries of q a thread prefetches for the draw
 constexpr int HEAD_STAGE = 16;   // X pieces per thread in flight while staging
-constexpr int HEAD_STAGE_F = 8;  // the same when X is normalised from float32 rows
+constexpr int HEAD_STAGE_F = 12; // the same when X is normalised from float32 rows (K = 4096: one round)
 // Vocab index of the first entry of the thread's k-th group of four (or >= V).
 __device__ __forceinline__ int head_group_v(int k, int nloc, int TR) {
   const int j0 = 4 * (threadIdx.x + k * blockDim.x);
@@ -359,38 +359,64 @@ __device__ __forceinline__ void gumbel4(uint64_t seed, int b, uint64_t pos, int 
   for (int e = 0; e < 4; ++e) G[e] = -__logf(-__logf(gumbel_uniform_from_word(w.w[e])));
 }
 
+// Loads of one staging round of head_stage_norm: HEAD_STAGE_F pieces of 8 values per
+// thread (the rows of Xf and the gain), zeros outside the rows and past K.
+__device__ __forceinline__ void head_norm_issue(const HeadArgs& a, int t0, int pieces, int kpieces, int total,
+                                                f32x4 (&x0)[HEAD_STAGE_F], f32x4 (&x1)[HEAD_STAGE_F],
+                                                u32x4 (&gw)[HEAD_STAGE_F]) {
+#pragma unroll
+  for (int u = 0; u < HEAD_STAGE_F; ++u) {
+    const int t = t0 + u * int(blockDim.x), row = t / pieces, c = t - row * pieces;
+    x0[u] = x1[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    gw[u] = u32x4{0u, 0u, 0u, 0u};
+    if (t < total && row < a.M && c < kpieces) {
+      const float* xr = a.Xf + size_t(row) * a.K + c * 8;
+      x0[u] = *reinterpret_cast<const f32x4*>(xr);
+      x1[u] = *reinterpret_cast<const f32x4*>(xr + 4);
+      gw[u] = load16(a.norm_w + c * 8);
+    }
+  }
+}
+
 // X staged from float32 rows with RMSNorm: each row's scale 1 / sqrt(sum(x^2) / K + eps)
-// comes from the ss_parts partial sums the producer of the rows left (wavefront w takes
-// rows w, w + 4, ...; fixed summation order), then every piece is normalised, scaled by
-// the gain and rounded to bf16 as it is written to LDS (zeros past K and in the extra
-// row).  The arithmetic matches a separate RMSNorm pass: bf16((x * scale) * g).
+// comes from the ss_parts partial sums the producer of the rows left, summed in a fixed
+// order (thread t adds parts t, t + 256, ...; then the wavefronts, then the four wave
+// sums in order); every piece is normalised, scaled by the gain and rounded to bf16 as it
+// is written to LDS (zeros past K and in the extra row).  The arithmetic matches a
+// separate RMSNorm pass: bf16((x * scale) * g).  The first round of X loads goes out
+// before the partial sums are read, so the two round trips overlap.
 __device__ __forceinline__ void head_stage_norm(const HeadArgs& a, bf16_t* sX, int ld, int Kp) {
-  __shared__ float s_scale[ACC_MAX_ROWS];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __shared__ float s_scale[HEAD_MAX_ROWS];
+  __shared__ float s_red[HEAD_WAVES][HEAD_MAX_ROWS];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int M = a.M;
-  for (int m = wave; m < M; m += nw) {
-    float ss = 0.0f;
-    for (int p = lane; p < a.ss_parts; p += 64) ss += a.ss_in[size_t(p) * M + m];
-    ss = wave_allsum(ss);
-    if (lane == 0) s_scale[m] = 1.0f / sqrtf(ss / float(a.K) + a.eps);
+  const int pieces = Kp / 8, kpieces = a.K / 8, total = (M + 1) * pieces;
+  f32x4 x0[HEAD_STAGE_F], x1[HEAD_STAGE_F];
+  u32x4 gw[HEAD_STAGE_F];
+  head_norm_issue(a, threadIdx.x, pieces, kpieces, total, x0, x1, gw);
+  float part[HEAD_MAX_ROWS];
+#pragma unroll
+  for (int m = 0; m < HEAD_MAX_ROWS; ++m) part[m] = 0.0f;
+  for (int p0 = 0; p0 < a.ss_parts; p0 += int(blockDim.x)) {
+    const int p = p0 + int(threadIdx.x);
+#pragma unroll
+    for (int m = 0; m < HEAD_MAX_ROWS; ++m)
+      if (m < M && p < a.ss_parts) part[m] += a.ss_in[size_t(p) * M + m];
+  }
+#pragma unroll
+  for (int m = 0; m < HEAD_MAX_ROWS; ++m) {
+    if (m >= M) break;
+    const float v = wave_allsum(part[m]);
+    if (lane == 0) s_red[wave][m] = v;
   }
   __syncthreads();
-  const int pieces = Kp / 8, kpieces = a.K / 8, total = (M + 1) * pieces;
-  for (int t0 = threadIdx.x; t0 < total; t0 += HEAD_STAGE_F * int(blockDim.x)) {
-    f32x4 x0[HEAD_STAGE_F], x1[HEAD_STAGE_F];
-    u32x4 gw[HEAD_STAGE_F];
-#pragma unroll
-    for (int u = 0; u < HEAD_STAGE_F; ++u) {
-      const int t = t0 + u * int(blockDim.x), row = t / pieces, c = t - row * pieces;
-      x0[u] = x1[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      gw[u] = u32x4{0u, 0u, 0u, 0u};
-      if (t < total && row < M && c < kpieces) {
-        const float* xr = a.Xf + size_t(row) * a.K + c * 8;
-        x0[u] = *reinterpret_cast<const f32x4*>(xr);
-        x1[u] = *reinterpret_cast<const f32x4*>(xr + 4);
-        gw[u] = load16(a.norm_w + c * 8);
-      }
-    }
+  if (int(threadIdx.x) < M) {
+    const int m = threadIdx.x;
+    const float ss = ((s_red[0][m] + s_red[1][m]) + s_red[2][m]) + s_red[3][m];
+    s_scale[m] = 1.0f / sqrtf(ss / float(a.K) + a.eps);
+  }
+  __syncthreads();
+  for (int t0 = threadIdx.x;;) {
 #pragma unroll
     for (int u = 0; u < HEAD_STAGE_F; ++u) {
       const int t = t0 + u * int(blockDim.x), row = t / pieces, c = t - row * pieces;
@@ -407,6 +433,9 @@ __device__ __forceinline__ void head_stage_norm(const HeadArgs& a, bf16_t* sX, i
         *reinterpret_cast<u32x4*>(sX + row * ld + c * 8) = o;
       }
     }
+    t0 += HEAD_STAGE_F * int(blockDim.x);
+    if (t0 >= total) break;
+    head_norm_issue(a, t0, pieces, kpieces, total, x0, x1, gw);
   }
 }
 
@@ -540,8 +569,8 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   __shared__ long long s_pos0[HEAD_MAX_ROWS];
   __shared__ unsigned s_ep;                       // HEAD_SAMPLE: this launch's epoch
 
-  // The wavefront's first work item is requested before X is staged: the two
-  // latencies overlap instead of adding up.
+  // The wavefront's first two work items are requested before X is staged: the
+  // latencies overlap instead of adding up, and the stream starts two items deep.
   const int first = blockIdx.x * HEAD_WAVES + wave, tstride = gridDim.x * HEAD_WAVES;
   const int n_my = first < ntiles ? (ntiles - 1 - first) / tstride + 1 : 0;
   const int items = n_my * a.gpt;
@@ -550,6 +579,7 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   u32x4 bufA[GRP], bufB[GRP];
   const unsigned voff = (unsigned(r / S) * unsigned(a.K) + unsigned(lane_ofs)) * 2u;   // the lane's W bytes
   if (items > 0) head_load<S, NB, GRP>(head_item<S>(a, 0, first, tstride, item_k), voff, bufA);
+  if (items > 1) head_load<S, NB, GRP>(head_item<S>(a, 1, first, tstride, item_k), voff, bufB);
 
   // stage all of X (zeros from K to Kp) and the zero row, HEAD_STAGE pieces per thread
   // in flight at a time (one load and store at a time would chain the L2 round trips);
@@ -637,14 +667,19 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
                               (first + i_ * tstride) * TR, N0, c, st);                                    \
       }                                                                                                   \
     }
-    for (; k + 2 < items; k += 2) {
-      head_load<S, NB, GRP>(head_item<S>(a, k + 1, first, tstride, item_k), voff, bufB);
+    // items k (bufA) and k + 1 (bufB) are in flight at the top of each iteration
+    for (; k + 3 < items; k += 2) {
       SV_HEAD_ITEM(k, bufA)
       head_load<S, NB, GRP>(head_item<S>(a, k + 2, first, tstride, item_k), voff, bufA);
       SV_HEAD_ITEM(k + 1, bufB)
+      head_load<S, NB, GRP>(head_item<S>(a, k + 3, first, tstride, item_k), voff, bufB);
     }
-    if (k + 1 < items) {
-      head_load<S, NB, GRP>(head_item<S>(a, k + 1, first, tstride, item_k), voff, bufB);
+    if (k + 2 < items) {
+      SV_HEAD_ITEM(k, bufA)
+      head_load<S, NB, GRP>(head_item<S>(a, k + 2, first, tstride, item_k), voff, bufA);
+      SV_HEAD_ITEM(k + 1, bufB)
+      SV_HEAD_ITEM(k + 2, bufA)
+    } else if (k + 1 < items) {
       SV_HEAD_ITEM(k, bufA)
       SV_HEAD_ITEM(k + 1, bufB)
     } else {

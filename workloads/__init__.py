@@ -357,3 +357,38 @@ def small_decoder_case(**kw):
                 cache_len=100, B=1, gamma=4, k=5, std=0.05)
     args.update(kw)
     return decoder_case(**args)
+
+
+# ----------------------------------------------------------------------------
+# the drafter's centroid-masked LM head
+
+@dataclass
+class MaskedHeadCase:
+    w: np.ndarray          # bf16 bits [V, d], cluster-ordered token table
+    centroids: np.ndarray  # bf16 bits [C, d], one representative per cluster
+    h: np.ndarray          # bf16 bits [M, d], drafter hidden states
+    top_k: int
+
+
+def masked_head_case(V=262144, d=1536, C=2048, M=1, top_k=32, k=6, spread=0.01, variant=0):
+    """Synthetic cluster-ordered embeddings: cluster c has a centre mu_c ~ N(0, 0.02^2)
+    and its cs = V / C member tokens are mu_c + N(0, spread^2) (rounded to bf16), so that
+    members are close to their cluster's representative; the representative table is
+    the bf16-rounded mean of the member rows (the classic k-means centre).  Hidden
+    states ~ N(0, 1).  These stand in for a trained drafter's clustered embeddings."""
+    seed = input_seed(k)
+    cs = V // C
+    mu = normal_f32((C, d), 0.02, seed, (10, C, d))
+    eps = normal_f32((V, d), spread, seed, (11, V, d))
+    wf = (eps.reshape(C, cs, d) + mu[:, None, :]).reshape(V, d)
+    del eps
+    w = to_bf16_bits(wf)
+    del wf
+    cent = np.zeros((C, d), dtype=np.float64)
+    wb = bf16_bits_to_f32(w).reshape(C, cs, d)
+    for c0 in range(0, C, 256):
+        cent[c0:c0 + 256] = wb[c0:c0 + 256].astype(np.float64).mean(axis=1)
+    del wb
+    centroids = to_bf16_bits(cent.astype(np.float32))
+    h = normal_bf16((M, d), 1.0, seed, (12, M, variant))
+    return MaskedHeadCase(w=w, centroids=centroids, h=h, top_k=top_k)

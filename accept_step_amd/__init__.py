@@ -7,7 +7,8 @@ device memory and streams.  The binding fails loudly when the library is
 missing or a call returns an error; it has no fallback path.
 
 Functions mirror the C entry points: :func:`verify_forward`,
-:func:`spec_verify_greedy`, :func:`spec_verify_sample`.
+:func:`spec_verify_greedy`, :func:`spec_verify_sample`, and the drafter's
+centroid-masked LM head :func:`draft_masked_logits`.
 """
 import ctypes
 import os
@@ -19,7 +20,7 @@ import torch
 __all__ = ["SV_F32", "SV_BF16", "SV_IN_LOGITS", "SV_IN_HIDDEN", "SV_IN_TOKENS", "VerifyError",
            "Model", "KVCache", "Workspace", "lm_head_model", "logits_model", "decoder_model",
            "verify_forward", "spec_verify_greedy", "spec_verify_sample", "library", "library_path",
-           "timing_enable", "timing_read", "LAYER_KEYS"]
+           "timing_enable", "timing_read", "LAYER_KEYS", "MaskedHead", "masked_head", "draft_masked_logits"]
 
 SV_F32, SV_BF16 = 0, 1
 SV_IN_LOGITS, SV_IN_HIDDEN, SV_IN_TOKENS = 0, 1, 2
@@ -48,6 +49,11 @@ class _SvModel(ctypes.Structure):
                 ("final_norm", ctypes.c_void_p), ("lm_head", ctypes.c_void_p)]
 
 
+class _SvMaskedHead(ctypes.Structure):
+    _fields_ = [("vocab", ctypes.c_int32), ("d_model", ctypes.c_int32), ("n_clusters", ctypes.c_int32),
+                ("wdtype", ctypes.c_int32), ("embed", ctypes.c_void_p), ("centroids", ctypes.c_void_p)]
+
+
 class _SvKV(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("max_len", ctypes.c_int32),
                 ("len", ctypes.c_void_p)]
@@ -71,8 +77,9 @@ def library():
     lib.spec_verify_greedy.argtypes = [M, i32, vp, i32, i32, vp, KV, vp, vp, vp, vp, sz, vp]
     lib.spec_verify_sample.argtypes = [M, i32, vp, i32, i32, vp, vp, i32, ctypes.c_float, ctypes.c_uint64, vp,
                                        KV, vp, vp, vp, vp, sz, vp]
+    lib.draft_masked_logits.argtypes = [ctypes.POINTER(_SvMaskedHead), vp, i32, i32, vp, vp, vp, vp, sz, vp]
     for f in (lib.verify_forward, lib.spec_verify_greedy, lib.spec_verify_sample, lib.sv_timing_enable,
-              lib.sv_timing_read):
+              lib.sv_timing_read, lib.draft_masked_logits):
         f.restype = i32
     lib.sv_version.restype = i32
     lib.sv_status_string.restype = ctypes.c_char_p
@@ -313,3 +320,47 @@ def timing_read(which):
     ms, cnt = ctypes.c_double(0), ctypes.c_int64(0)
     _check(library().sv_timing_read(which, ctypes.byref(ms), ctypes.byref(cnt)))
     return ms.value, cnt.value
+
+
+@dataclass
+class MaskedHead:
+    """The drafter's centroid-masked LM head: the C struct plus the tensors it points to."""
+    struct: _SvMaskedHead
+    keep: list = field(default_factory=list)
+
+    @property
+    def cluster_size(self):
+        return self.struct.vocab // self.struct.n_clusters
+
+
+def masked_head(embed, centroids):
+    """Masked head from bf16 device tensors: cluster-ordered token table [V, d] and one
+    representative embedding per cluster [C, d] (cluster c = tokens [c*V/C, (c+1)*V/C))."""
+    _dev_tensor(embed, "embed", torch.bfloat16)
+    _dev_tensor(centroids, "centroids", torch.bfloat16)
+    s = _SvMaskedHead()
+    s.vocab, s.d_model = int(embed.shape[0]), int(embed.shape[1])
+    s.n_clusters = int(centroids.shape[0])
+    s.wdtype = SV_BF16
+    s.embed, s.centroids = embed.data_ptr(), centroids.data_ptr()
+    return MaskedHead(s, [embed, centroids])
+
+
+def draft_masked_logits(head, hidden, top_k, clusters=None, logits=None, cluster_logits=None, ws=None, stream=None):
+    """(clusters int32 [M, top_k], logits float32 [M, top_k * cs]) of the masked head
+    (C: draft_masked_logits); ``hidden`` bf16 [M, d]."""
+    lib = library()
+    _dev_tensor(hidden, "hidden", torch.bfloat16)
+    M, dev = int(hidden.shape[0]), hidden.device
+    if clusters is None:
+        clusters = torch.empty((M, top_k), dtype=torch.int32, device=dev)
+    if logits is None:
+        logits = torch.empty((M, top_k * head.cluster_size), dtype=torch.float32, device=dev)
+    _dev_tensor(clusters, "clusters", torch.int32)
+    _dev_tensor(logits, "logits", torch.float32)
+    _dev_tensor(cluster_logits, "cluster_logits", torch.float32)
+    st = head.struct
+    _call_with_ws(lib.draft_masked_logits,
+                  (ctypes.byref(st), _ptr(hidden), M, int(top_k), _ptr(clusters), _ptr(logits), _ptr(cluster_logits)),
+                  dev, ws, stream)
+    return clusters, logits

@@ -24,6 +24,7 @@
 #include "sv_device.hpp"
 #include "sv_gemm.hpp"
 #include "sv_head.hpp"
+#include "sv_masked.hpp"
 
 using namespace sv;
 
@@ -947,6 +948,47 @@ sv_status spec_verify_sample(const sv_model* m, sv_input_kind kind, const void* 
                              float* logits_out, void* ws, size_t* ws_bytes, void* stream) {
   return verify_common(m, kind, input, B, gamma, draft, q, q_dtype, temperature, seed, pos0, kv, n_accepted,
                        tokens_out, logits_out, ws, ws_bytes, stream, true);
+}
+
+sv_status draft_masked_logits(const sv_masked_head* head, const void* hidden, int32_t M, int32_t top_k,
+                              int32_t* clusters, float* logits, float* cluster_logits, void* ws, size_t* ws_bytes,
+                              void* stream) {
+  g_err.clear();
+  if (!head || !hidden || !clusters || !logits) return fail(SV_ERR_ARG, "NULL argument");
+  if (!head->embed || !head->centroids) return fail(SV_ERR_ARG, "embed or centroids is NULL");
+  if (head->wdtype != SV_BF16) return fail(SV_ERR_DTYPE, "the masked head takes bf16 tables");
+  const int V = head->vocab, d = head->d_model, C = head->n_clusters;
+  if (C < 1 || V < 2 || V % C) return fail(SV_ERR_SHAPE, "vocab must be a positive multiple of n_clusters");
+  if (C > MASK_MAX_CLUSTERS) return fail(SV_ERR_UNSUPPORTED, "at most %d clusters", MASK_MAX_CLUSTERS);
+  if (d < 32 || d % 32 || d > 16384) return fail(SV_ERR_SHAPE, "d_model must be a multiple of 32 in [32, 16384]");
+  if (M < 1 || M > HEAD_MAX_ROWS) return fail(SV_ERR_ARG, "M must be in [1, %d]", HEAD_MAX_ROWS);
+  if (top_k < 1 || top_k > C) return fail(SV_ERR_ARG, "top_k must be in [1, n_clusters]");
+  if (!is_aligned(hidden, 16) || !is_aligned(head->embed, 16) || !is_aligned(head->centroids, 16))
+    return fail(SV_ERR_ARG, "hidden, embed and centroids must be 16-byte aligned");
+  Bump b;
+  const size_t cl_off = cluster_logits ? 0 : b.take(size_t(M) * C * 4);
+  Layout L;
+  L.total = b.off;
+  bool query = false;
+  sv_status st = check_ws(ws, ws_bytes, L, &query);
+  if (st || query) return st;
+  DevInfo di;
+  if ((st = dev_info(&di))) return st;
+  const int N1[1] = {C};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* cl = cluster_logits ? cluster_logits : at<float>(ws, cl_off);
+  const void* W1[1] = {head->centroids};
+  float* O1[1] = {cl};
+  if ((st = run_product(static_cast<const bf16_t*>(hidden), M, d, 1, W1, O1, N1, di, s))) return st;
+  int P = 1;
+  while (P < C) P <<= 1;
+  hipLaunchKernelGGL(k_select_clusters, dim3(M), dim3(256), 0, s, cl, C, P, top_k, clusters);
+  const int cs = V / C;
+  hipLaunchKernelGGL(k_gather_logits, dim3(top_k, (cs + MASK_ROWS_PER_WG - 1) / MASK_ROWS_PER_WG, M), dim3(256),
+                     size_t(d) * 4, s, static_cast<const bf16_t*>(head->embed), static_cast<const bf16_t*>(hidden),
+                     clusters, d, cs, top_k, logits);
+  SV_HIP(hipGetLastError());
+  return SV_OK;
 }
 
 int32_t sv_version(void) { return VERSION; }

@@ -177,6 +177,38 @@ sv_status spec_verify_sample(const sv_model* m, sv_input_kind kind, const void* 
                              const sv_kv_cache* kv, int32_t* n_accepted, int32_t* tokens_out,
                              float* logits_out, void* ws, size_t* ws_bytes, void* stream);
 
+/* The drafter's centroid-masked LM head ([MTP-drafters] "efficient embedder";
+ * [MTP-deep-dive] 3.4 "centroids masking"): token embeddings grouped into clusters of
+ * similar tokens, one representative embedding per cluster.  The hidden state scores
+ * the clusters, the top_k clusters are kept, and exact token logits are computed only
+ * for their member tokens (the pages quote 2048 clusters, 32 kept: about 4K of 262,144
+ * tokens scored).  Ordered embeddings: cluster c holds the contiguous tokens
+ * [c * cs, (c + 1) * cs), cs = vocab / n_clusters. */
+typedef struct sv_masked_head {
+  int32_t vocab;               /* V, a positive multiple of n_clusters */
+  int32_t d_model;             /* d; multiple of 32 */
+  int32_t n_clusters;          /* C, 1 .. 4096 */
+  sv_dtype wdtype;             /* SV_BF16 */
+  const void* embed;           /* [V, d] token embeddings (the tied LM head), cluster-ordered */
+  const void* centroids;       /* [C, d] one representative embedding per cluster */
+} sv_masked_head;
+
+/* Masked drafter logits for M hidden states.
+ *   hidden:         bf16 [M, d], 1 <= M <= 24.
+ *   top_k:          clusters kept per row, 1 <= top_k <= C.
+ *   clusters:       out int32 [M, top_k], the kept cluster ids in descending order of
+ *                   their float32 cluster score, the lower id first on equal scores.
+ *   logits:         out float32 [M, top_k * cs]; block j holds the logits of tokens
+ *                   clusters[m, j] * cs + [0, cs).  Every other token is masked (not
+ *                   scored).
+ *   cluster_logits: optional out float32 [M, C] cluster scores (NULL: kept in the
+ *                   workspace).
+ * Workspace, streams and errors as above.  The result is a pure function of the
+ * inputs. */
+sv_status draft_masked_logits(const sv_masked_head* head, const void* hidden, int32_t M, int32_t top_k,
+                              int32_t* clusters, float* logits, float* cluster_logits,
+                              void* ws, size_t* ws_bytes, void* stream);
+
 /* Library version (major * 10000 + minor * 100 + patch). */
 int32_t sv_version(void);
 

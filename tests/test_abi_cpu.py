@@ -112,3 +112,27 @@ def test_timing_api(lib):
     assert lib.sv_timing_read(0, ctypes.byref(ms), ctypes.byref(cnt)) == 0
     assert cnt.value == 0 and ms.value == 0.0
     assert lib.sv_timing_enable(0) == 0
+
+
+def test_masked_head_argument_errors_and_query(lib):
+    def call(V=262144, d=1536, C=2048, wd=sv.SV_BF16, M=1, k=32, hidden=FAKE, clusters=FAKE, cl=None, ws=None,
+             nbytes=0):
+        h = sv._SvMaskedHead()
+        h.vocab, h.d_model, h.n_clusters, h.wdtype = V, d, C, wd
+        h.embed, h.centroids = 0x10000, 0x30000
+        n = ctypes.c_size_t(nbytes)
+        st = lib.draft_masked_logits(ctypes.byref(h), hidden, M, k, clusters, FAKE, cl, ws, ctypes.byref(n), None)
+        return st, n.value
+
+    st, need = call()
+    assert st == 0 and need >= 2048 * 4                 # the cluster scores live in the workspace
+    assert call(cl=FAKE) == (0, 0)                       # caller keeps them: no workspace
+    assert call(hidden=None)[0] == 1
+    assert call(clusters=None)[0] == 1
+    assert call(wd=sv.SV_F32)[0] == 2
+    assert call(V=262145)[0] == 3                        # not a multiple of the cluster count
+    assert call(C=8192, V=8192 * 4)[0] == 6             # more clusters than the selection sorts
+    assert call(d=48)[0] == 3
+    assert call(M=0)[0] == 1 and call(M=25)[0] == 1
+    assert call(k=0)[0] == 1 and call(k=2049)[0] == 1
+    assert call(ws=FAKE, nbytes=need - 1)[0] == 4

@@ -980,9 +980,13 @@ sv_status draft_masked_logits(const sv_masked_head* head, const void* hidden, in
   const void* W1[1] = {head->centroids};
   float* O1[1] = {cl};
   if ((st = run_product(static_cast<const bf16_t*>(hidden), M, d, 1, W1, O1, N1, di, s))) return st;
-  int P = 1;
-  while (P < C) P <<= 1;
-  hipLaunchKernelGGL(k_select_clusters, dim3(M), dim3(256), 0, s, cl, C, P, top_k, clusters);
+  if (top_k <= MASK_FAST_K) {
+    hipLaunchKernelGGL(k_select_topk, dim3(M), dim3(256), 0, s, cl, C, top_k, clusters);
+  } else {
+    int P = 1;
+    while (P < C) P <<= 1;
+    hipLaunchKernelGGL(k_select_clusters, dim3(M), dim3(256), 0, s, cl, C, P, top_k, clusters);
+  }
   const int cs = V / C;
   hipLaunchKernelGGL(k_gather_logits, dim3(top_k, (cs + MASK_ROWS_PER_WG - 1) / MASK_ROWS_PER_WG, M), dim3(256),
                      size_t(d) * 4, s, static_cast<const bf16_t*>(head->embed), static_cast<const bf16_t*>(hidden),

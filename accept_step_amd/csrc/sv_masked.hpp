@@ -13,8 +13,9 @@
 
 namespace sv {
 
-constexpr int MASK_MAX_CLUSTERS = 4096;   // bitonic sort of the cluster keys in LDS
-constexpr int MASK_ROWS_PER_WG = 32;      // gathered token rows per workgroup (8 per wavefront)
+constexpr int MASK_MAX_CLUSTERS = 4096;   // cluster keys of one row held in LDS / registers
+constexpr int MASK_FAST_K = 64;           // top_k up to this: radix selection (else a full bitonic sort)
+constexpr int MASK_ROWS_PER_WG = 16;      // gathered token rows per workgroup (4 per wavefront)
 
 // Orderable key of a cluster score: the float mapped to an unsigned order (-0 as +0)
 // in the high word, the complemented cluster id in the low word, so that the larger
@@ -25,9 +26,10 @@ __device__ __forceinline__ unsigned long long cluster_key(float v, int c) {
   return (static_cast<unsigned long long>(o) << 32) | (0xffffffffu - unsigned(c));
 }
 
-// Kept clusters of row blockIdx.x: the C cluster scores become keys in LDS (zeros pad
-// to P, a power of two), a bitonic network sorts them in descending order, and the
-// first top_k ids are written to clusters[m, 0..top_k).  256 threads.
+// Kept clusters of row blockIdx.x for top_k > MASK_FAST_K: the C cluster scores become
+// keys in LDS (zeros pad to P, a power of two), a bitonic network sorts them in
+// descending order, and the first top_k ids are written to clusters[m, 0..top_k).
+// 256 threads.
 __global__ __launch_bounds__(256) void k_select_clusters(const float* __restrict__ cl, int C, int P, int top_k,
                                                          int32_t* __restrict__ clusters) {
   __shared__ unsigned long long key[MASK_MAX_CLUSTERS];
@@ -51,12 +53,112 @@ __global__ __launch_bounds__(256) void k_select_clusters(const float* __restrict
     clusters[size_t(m) * top_k + j] = int32_t(0xffffffffu - unsigned(key[j]));
 }
 
+__device__ __forceinline__ unsigned score_order(float v) {
+  const unsigned u = __float_as_uint(v + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Kept clusters of row blockIdx.x for top_k <= MASK_FAST_K, 256 threads.  Thread t holds
+// the score orders of clusters t, t + 256, ...  (1) The exact 32-bit order T of the
+// top_k-th largest score by radix selection, four 8-bit digits from the top: per digit
+// an LDS histogram of the candidates that match the prefix so far, and wavefront 0
+// finds the digit at which the count from the top reaches the rank still needed.  (2)
+// The kept set: every cluster scoring above T, and of those scoring exactly T the
+// lowest ids (a cluster's rank among the ties counts the tied ids below it in an LDS
+// bitmap).  (3) Wavefront 0 sorts the top_k keys (order, complemented id) in descending
+// order with a bitonic network across its lanes and writes the ids.
+__global__ __launch_bounds__(256) void k_select_topk(const float* __restrict__ cl, int C, int top_k,
+                                                     int32_t* __restrict__ clusters) {
+  constexpr int PER = MASK_MAX_CLUSTERS / 256;
+  __shared__ unsigned hist[256];
+  __shared__ unsigned s_digit, s_need, s_cnt;
+  __shared__ unsigned tie_bits[MASK_MAX_CLUSTERS / 32];
+  __shared__ unsigned long long s_sel[MASK_FAST_K];
+  const int m = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  unsigned o[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int c = t + 256 * u;
+    o[u] = c < C ? score_order(cl[size_t(m) * C + c]) : 0u;   // 0: no cluster (every real order is larger)
+  }
+  unsigned prefix = 0u, mask = 0u, need = unsigned(top_k);
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist[t] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+      if (t + 256 * u < C && (o[u] & mask) == prefix) atomicAdd(&hist[(o[u] >> shift) & 255u], 1u);
+    __syncthreads();
+    if (wave == 0) {
+      // lane l covers digits 255 - 4l .. 252 - 4l (from the top); exclusive prefix of the
+      // counts above its first digit, then the lane whose range holds rank ``need`` reports
+      unsigned c4[4], tot = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { c4[j] = hist[255 - 4 * lane - j]; tot += c4[j]; }
+      unsigned incl = tot;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const unsigned v = unsigned(__shfl_up(int(incl), off));
+        if (lane >= off) incl += v;
+      }
+      unsigned above = incl - tot;
+      if (above < need && need <= incl) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (above < need && need <= above + c4[j]) { s_digit = unsigned(255 - 4 * lane - j); s_need = need - above; }
+          above += c4[j];
+        }
+      }
+    }
+    __syncthreads();
+    prefix |= s_digit << shift;
+    mask |= 255u << shift;
+    need = s_need;
+  }
+  // prefix = T; ``need`` clusters scoring exactly T are kept, top_k - need score above it
+  if (t < MASK_MAX_CLUSTERS / 32) tie_bits[t] = 0u;
+  if (t == 0) s_cnt = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int c = t + 256 * u;
+    if (c < C && o[u] > prefix) s_sel[atomicAdd(&s_cnt, 1u)] = (static_cast<unsigned long long>(o[u]) << 32) | (0xffffffffu - unsigned(c));
+    if (c < C && o[u] == prefix) atomicOr(&tie_bits[c >> 5], 1u << (c & 31));
+  }
+  __syncthreads();
+  const unsigned above = unsigned(top_k) - need;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int c = t + 256 * u;
+    if (c < C && o[u] == prefix) {
+      unsigned rank = __popc(tie_bits[c >> 5] & ((1u << (c & 31)) - 1u));
+      for (int wd = 0; wd < (c >> 5); ++wd) rank += __popc(tie_bits[wd]);
+      if (rank < need) s_sel[above + rank] = (static_cast<unsigned long long>(prefix) << 32) | (0xffffffffu - unsigned(c));
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    unsigned long long k = lane < top_k ? s_sel[lane] : 0ull;
+    for (int size = 2; size <= 64; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        const unsigned lo = unsigned(__shfl_xor(int(unsigned(k)), stride));
+        const unsigned hi = unsigned(__shfl_xor(int(unsigned(k >> 32)), stride));
+        const unsigned long long other = (static_cast<unsigned long long>(hi) << 32) | lo;
+        const bool desc = (lane & size) == 0;          // all of it at size 64
+        const bool keep_max = ((lane & stride) == 0) == desc;
+        k = keep_max ? (other > k ? other : k) : (other < k ? other : k);
+      }
+    }
+    if (lane < top_k) clusters[size_t(m) * top_k + lane] = int32_t(0xffffffffu - unsigned(k));
+  }
+}
+
 // Token logits of the kept clusters: workgroup (j, chunk, m) computes rows
-// chunk * 32 .. chunk * 32 + 31 of cluster clusters[m, j] (row r = token c * cs + r):
+// chunk * 16 .. chunk * 16 + 15 of cluster clusters[m, j] (row r = token c * cs + r):
 // out[m, j * cs + r] = W[c * cs + r] . h[m].  Each group of 16 lanes takes one row, 16
 // bytes per lane per step (256 contiguous bytes of the row), accumulates in float32
-// and sums its 16 lanes with DPP; a wavefront takes two groups of four rows.  h is
-// staged in LDS as float32.  Rows past cs read the last row and are not stored.
+// and sums its 16 lanes with DPP; a wavefront takes four rows.  h is staged in LDS as
+// float32.  Rows past cs read the last row and are not stored.
 __global__ __launch_bounds__(256) void k_gather_logits(const bf16_t* __restrict__ W, const bf16_t* __restrict__ h,
                                                        const int32_t* __restrict__ clusters, int d, int cs, int top_k,
                                                        float* __restrict__ out) {
@@ -68,12 +170,11 @@ __global__ __launch_bounds__(256) void k_gather_logits(const bf16_t* __restrict_
   for (int i = threadIdx.x; i < d; i += blockDim.x) sh[i] = bf16_to_f32(h[size_t(m) * d + i]);
   __syncthreads();
   const int steps = (d + 127) / 128;
-#pragma unroll
-  for (int grp = 0; grp < 2; ++grp) {
-    const int r = chunk * MASK_ROWS_PER_WG + wave * 8 + grp * 4 + g;
+  {
+    const int r = chunk * MASK_ROWS_PER_WG + wave * 4 + g;
     const bf16_t* wr = W + (size_t(c) * cs + min(r, cs - 1)) * d;
     float acc = 0.0f;
-#pragma unroll 4
+#pragma unroll 12
     for (int s = 0; s < steps; ++s) {
       const int k0 = s * 128 + l16 * 8;
       if (k0 < d) {

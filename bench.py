@@ -43,8 +43,10 @@ def parse():
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB five times (a plain copy kernel of known "
                          "size, used to scale the FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--workload", choices=("large-vocab", "full-model"), default="large-vocab",
-                    help="large-vocab (default, the headline metric) or full-model: the 32-layer decoder verify")
+    ap.add_argument("--workload", choices=("large-vocab", "full-model", "masked-head"), default="large-vocab",
+                    help="large-vocab (default, the headline metric), full-model (the 32-layer decoder verify) or "
+                         "masked-head (the drafter's centroid-masked LM head)")
+    ap.add_argument("--rows", type=int, default=1, help="masked-head: hidden states per call")
     ap.add_argument("--traffic-summary", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                                               "k_head_vocab262144_d1536_B1_traffic.md"))
     return ap.parse_args()
@@ -62,6 +64,8 @@ def main():
 
     if args.workload == "full-model":
         return full_model(args, torch, sv)
+    if args.workload == "masked-head":
+        return masked_head(args, torch, sv, workloads)
     root = os.path.dirname(os.path.abspath(__file__))
     sys.path.insert(0, root)
     dev = torch.device("cuda:0")
@@ -252,6 +256,55 @@ def full_model(args, torch, sv):
                    "frac_of_peak": round(with_kv / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                    "bytes_params": params_bytes, "gbs_params": round(params_bytes / (ms * 1e-3) / 1e9, 1),
                    "decoder_ms": round(dec_ms / max(dec_n, 1), 4), "lm_head_step_ms": round(head_ms / max(head_n, 1), 4)},
+    }
+    print(json.dumps(out), flush=True)
+
+
+def masked_head(args, torch, sv, workloads):
+    """The drafter's centroid-masked LM head: V = 262144 token embeddings (d = 1536) in
+    2048 clusters of 128, 32 clusters kept, ``--rows`` hidden states per call.  One step
+    = one call (cluster scores, selection, member-token logits).  Algorithmic bytes: the
+    cluster table once plus the kept clusters' rows of the token table per hidden state."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    V, d, C, top_k, M = 262144, 1536, 2048, 32, args.rows
+    case = workloads.masked_head_case(V=V, d=d, C=C, M=M, top_k=top_k)
+
+    def to_dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    head = sv.masked_head(to_dev_bf16(case.w), to_dev_bf16(case.centroids))
+    hs = [to_dev_bf16(workloads.normal_bf16((M, d), 1.0, 77, (M, i))) for i in range(8)]
+    cs = V // C
+    sel = torch.empty((M, top_k), dtype=torch.int32, device=dev)
+    logits = torch.empty((M, top_k * cs), dtype=torch.float32, device=dev)
+    ws = sv.Workspace()
+    K, Wm = args.steps, args.warmup
+    for i in range(Wm):
+        sv.draft_masked_logits(head, hs[i % 8], top_k, clusters=sel, logits=logits, ws=ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(K):
+        sv.draft_masked_logits(head, hs[i % 8], top_k, clusters=sel, logits=logits, ws=ws)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    us = ev0.elapsed_time(ev1) / K * 1e3
+    algo = C * d * 2 + M * top_k * cs * d * 2 + M * d * 2
+    out = {
+        "metric": "drafter masked LM-head latency (us/call) and HBM GB/s",
+        "value": round(us, 2), "unit": "us/call", "n_gpus": 1, "steps": K, "warmup": Wm,
+        "ms_per_step": round(elapsed / K * 1e3, 4), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"centroid-masked LM head: V={V} d={d}, {C} clusters of {cs}, top {top_k} kept, "
+                               f"{M} hidden state(s) per call",
+                   "scored_tokens_per_row": top_k * cs, "algorithmic_bytes": algo,
+                   "gbs": round(algo / (us * 1e-6) / 1e9, 1),
+                   "frac_of_peak": round(algo / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                   "full_head_bytes": V * d * 2, "full_head_us_at_peak": round(V * d * 2 / (HBM_PEAK_GBS * 1e3), 2)},
     }
     print(json.dumps(out), flush=True)
 

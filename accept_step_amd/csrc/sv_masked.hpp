@@ -53,88 +53,79 @@ __global__ __launch_bounds__(256) void k_select_clusters(const float* __restrict
     clusters[size_t(m) * top_k + j] = int32_t(0xffffffffu - unsigned(key[j]));
 }
 
-__device__ __forceinline__ unsigned score_order(float v) {
-  const unsigned u = __float_as_uint(v + 0.0f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
 // Kept clusters of row blockIdx.x for top_k <= MASK_FAST_K, 256 threads.  Thread t holds
-// the score orders of clusters t, t + 256, ...  (1) The exact 32-bit order T of the
-// top_k-th largest score by radix selection, four 8-bit digits from the top: per digit
-// an LDS histogram of the candidates that match the prefix so far, and wavefront 0
-// finds the digit at which the count from the top reaches the rank still needed.  (2)
-// The kept set: every cluster scoring above T, and of those scoring exactly T the
-// lowest ids (a cluster's rank among the ties counts the tied ids below it in an LDS
-// bitmap).  (3) Wavefront 0 sorts the top_k keys (order, complemented id) in descending
+// the keys (score order, complemented id) of clusters t, t + 256, ...  (1) An LDS
+// histogram of the top 12 bits of the score orders (sign, exponent and three mantissa
+// bits spread typical scores over many bins), scanned from the top by the four
+// wavefronts (a quarter of the bins each), gives the bin B that holds the top_k-th
+// largest key and the number ``need`` of keys still to take from it.  (2) Every key in a
+// bin above B is kept; the keys of bin B are gathered in LDS and each ranks itself by
+// counting the larger ones (few keys in practice; every key in the worst case), and the
+// ``need`` largest are kept.  (3) Wavefront 0 sorts the top_k kept keys in descending
 // order with a bitonic network across its lanes and writes the ids.
 __global__ __launch_bounds__(256) void k_select_topk(const float* __restrict__ cl, int C, int top_k,
                                                      int32_t* __restrict__ clusters) {
   constexpr int PER = MASK_MAX_CLUSTERS / 256;
-  __shared__ unsigned hist[256];
-  __shared__ unsigned s_digit, s_need, s_cnt;
-  __shared__ unsigned tie_bits[MASK_MAX_CLUSTERS / 32];
+  constexpr int NBINS = 4096, SHIFT = 20, BPL = NBINS / 256;   // bins per lane in the scan
+  __shared__ unsigned hist[NBINS];
+  __shared__ unsigned s_bin, s_need, s_cnt, s_nb, s_wt[4];
   __shared__ unsigned long long s_sel[MASK_FAST_K];
+  __shared__ unsigned long long s_cand[MASK_MAX_CLUSTERS];
   const int m = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  unsigned o[PER];
+  unsigned long long key[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int c = t + 256 * u;
-    o[u] = c < C ? score_order(cl[size_t(m) * C + c]) : 0u;   // 0: no cluster (every real order is larger)
+    key[u] = c < C ? cluster_key(cl[size_t(m) * C + c], c) : 0ull;   // 0: no cluster (every real key is larger)
   }
-  unsigned prefix = 0u, mask = 0u, need = unsigned(top_k);
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    hist[t] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < PER; ++u)
-      if (t + 256 * u < C && (o[u] & mask) == prefix) atomicAdd(&hist[(o[u] >> shift) & 255u], 1u);
-    __syncthreads();
-    if (wave == 0) {
-      // lane l covers digits 255 - 4l .. 252 - 4l (from the top); exclusive prefix of the
-      // counts above its first digit, then the lane whose range holds rank ``need`` reports
-      unsigned c4[4], tot = 0u;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) { c4[j] = hist[255 - 4 * lane - j]; tot += c4[j]; }
-      unsigned incl = tot;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const unsigned v = unsigned(__shfl_up(int(incl), off));
-        if (lane >= off) incl += v;
-      }
-      unsigned above = incl - tot;
-      if (above < need && need <= incl) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (above < need && need <= above + c4[j]) { s_digit = unsigned(255 - 4 * lane - j); s_need = need - above; }
-          above += c4[j];
-        }
-      }
-    }
-    __syncthreads();
-    prefix |= s_digit << shift;
-    mask |= 255u << shift;
-    need = s_need;
-  }
-  // prefix = T; ``need`` clusters scoring exactly T are kept, top_k - need score above it
-  if (t < MASK_MAX_CLUSTERS / 32) tie_bits[t] = 0u;
-  if (t == 0) s_cnt = 0u;
+  for (int b = t; b < NBINS; b += 256) hist[b] = 0u;
+  if (t == 0) { s_cnt = 0u; s_nb = 0u; }
   __syncthreads();
 #pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int c = t + 256 * u;
-    if (c < C && o[u] > prefix) s_sel[atomicAdd(&s_cnt, 1u)] = (static_cast<unsigned long long>(o[u]) << 32) | (0xffffffffu - unsigned(c));
-    if (c < C && o[u] == prefix) atomicOr(&tie_bits[c >> 5], 1u << (c & 31));
+  for (int u = 0; u < PER; ++u)
+    if (t + 256 * u < C) atomicAdd(&hist[unsigned(key[u] >> 32) >> SHIFT], 1u);
+  __syncthreads();
+  // wavefront w scans bins NBINS - 1 - w * NBINS / 4 downwards; lane l takes BPL of them
+  const int top = NBINS - 1 - wave * (NBINS / 4) - lane * BPL;
+  unsigned tot = 0u;
+#pragma unroll
+  for (int j = 0; j < BPL; ++j) tot += hist[top - j];
+  unsigned incl = tot;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned v = unsigned(__shfl_up(int(incl), off));
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) s_wt[wave] = incl;
+  __syncthreads();
+  unsigned base = 0u;
+  for (int w = 0; w < wave; ++w) base += s_wt[w];
+  const unsigned kk = unsigned(top_k);
+  unsigned above = base + incl - tot;
+  if (above < kk && kk <= base + incl) {
+#pragma unroll
+    for (int j = 0; j < BPL; ++j) {
+      const unsigned cj = hist[top - j];
+      if (above < kk && kk <= above + cj) { s_bin = unsigned(top - j); s_need = kk - above; }
+      above += cj;
+    }
   }
   __syncthreads();
-  const unsigned above = unsigned(top_k) - need;
+  const unsigned bin = s_bin, need = s_need, n_above = kk - need;
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
-    const int c = t + 256 * u;
-    if (c < C && o[u] == prefix) {
-      unsigned rank = __popc(tie_bits[c >> 5] & ((1u << (c & 31)) - 1u));
-      for (int wd = 0; wd < (c >> 5); ++wd) rank += __popc(tie_bits[wd]);
-      if (rank < need) s_sel[above + rank] = (static_cast<unsigned long long>(prefix) << 32) | (0xffffffffu - unsigned(c));
-    }
+    if (t + 256 * u >= C) continue;
+    const unsigned kb = unsigned(key[u] >> 32) >> SHIFT;
+    if (kb > bin) s_sel[atomicAdd(&s_cnt, 1u)] = key[u];
+    else if (kb == bin) s_cand[atomicAdd(&s_nb, 1u)] = key[u];
+  }
+  __syncthreads();
+  const unsigned nb = s_nb;
+  for (unsigned i = t; i < nb; i += 256) {
+    const unsigned long long x = s_cand[i];
+    unsigned rank = 0u;
+    for (unsigned j = 0; j < nb; ++j) rank += s_cand[j] > x ? 1u : 0u;
+    if (rank < need) s_sel[n_above + rank] = x;
   }
   __syncthreads();
   if (wave == 0) {

@@ -1,6 +1,6 @@
 // sv_masked.hpp -- the drafter's centroid-masked LM head (gfx950).
 //
-// [MTP-drafters] "efficient embedder", [MTP-deep-dive] 3.4: the hidden state scores
+// [X-thread] "Gemma 4's MTP", efficient embedder, [MTP-deep-dive] 3.4: the hidden state scores
 // clusters of tokens through a table of one representative embedding per cluster; the
 // top_k clusters are kept and exact logits are computed only for their member tokens.
 // With ordered embeddings cluster c is the contiguous token block [c * cs, (c+1) * cs).

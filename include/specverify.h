@@ -177,7 +177,7 @@ sv_status spec_verify_sample(const sv_model* m, sv_input_kind kind, const void* 
                              const sv_kv_cache* kv, int32_t* n_accepted, int32_t* tokens_out,
                              float* logits_out, void* ws, size_t* ws_bytes, void* stream);
 
-/* The drafter's centroid-masked LM head ([MTP-drafters] "efficient embedder";
+/* The drafter's centroid-masked LM head ([X-thread] "Gemma 4's MTP", efficient embedder;
  * [MTP-deep-dive] 3.4 "centroids masking"): token embeddings grouped into clusters of
  * similar tokens, one representative embedding per cluster.  The hidden state scores
  * the clusters, the top_k clusters are kept, and exact token logits are computed only

@@ -2,7 +2,7 @@
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).
 
-[MTP-drafters], section "efficient embedder", and [MTP-deep-dive] 3.4
+[X-thread], section "Gemma 4's MTP", part "efficient embedder", and [MTP-deep-dive] 3.4
 ("centroids masking"): the token embeddings are grouped into clusters of tokens
 with similar meaning and each cluster gets one representative embedding.  The
 drafter's hidden state is multiplied by the table of representatives, which
@@ -37,7 +37,7 @@ def cluster_size(V, C):
 
 
 def cluster_logits(h, centroids):
-    """Cluster scores h . centroid_c^T in float64 ([MTP-drafters] "efficient embedder":
+    """Cluster scores h . centroid_c^T in float64 ([X-thread] "Gemma 4's MTP", efficient embedder:
     the hidden state times the new lookup table gives cluster logits instead of token
     logits).  ``h`` [M, d], ``centroids`` [C, d], float64 holding exact bf16 values.
 

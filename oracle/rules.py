@@ -308,6 +308,108 @@ def verify_sample(logits64, draft, q, temperature, seed, pos0, seq0=0):
     return sample_rule(f32_logits(logits64), draft, q, temperature, seed, pos0, seq0)
 
 
+def filtered_probs(l32, temperature, top_k, top_p):
+    """Target probabilities after the top-k and top-p filters, float32, zero outside the
+    kept tokens, together with the kept masks and boundary flags.
+
+    [Infra-ch8] "why the output does not change" and [MTP-drafters] 5.2 (problem 2):
+    temperature, top-k and top-p must be handled by one rule in drafting and verifying,
+    or the distribution drifts; the deployment example runs temperature 1.0, top_p 0.95,
+    top_k 64 ([MTP-deep-dive] 5.1); top-k samples among the k most probable tokens and
+    top-p among the smallest set whose cumulative probability exceeds p ([MTP-drafters]
+    3.1, draft-token strategies).
+
+    Readings: the filters apply in the order temperature, top-k, top-p; the k kept
+    tokens are the k largest float32 logits, the lower index first on equal values
+    (exactly k are kept); top-p walks the kept tokens in that order with their
+    probabilities renormalised over the top-k set and keeps every token whose
+    predecessors' cumulative probability is still below top_p (the smallest prefix whose
+    sum reaches top_p); the result is renormalised over the kept tokens, computed in
+    float64 from the float32 logits and rounded once to float32.
+
+    ``l32``: [..., V]; returns (p float32 [..., V], kept bool [..., V], flags [...]);
+    a flag marks a row whose top-k cut falls between logits closer than 1e-3, or whose
+    top-p cut has a cumulative probability within 1e-3 of top_p on either side.
+
+    Pinned by: a hand-checked fixture with a tie at the top-k cut; top_k = V and
+    top_p = 1 give target_probs exactly; kept sets are prefixes of the descending
+    order with the stated top-p property.
+    """
+    l = np.asarray(l32, dtype=np.float32)
+    t = float(temperature)
+    if not (t > 0.0 and np.isfinite(t)):
+        raise ValueError("filtered_probs: temperature must be finite and > 0")
+    if not 1 <= int(top_k):
+        raise ValueError("filtered_probs: top_k must be >= 1")
+    if not 0.0 < float(top_p) <= 1.0:
+        raise ValueError("filtered_probs: top_p must be in (0, 1]")
+    shape = l.shape
+    V = shape[-1]
+    rows = l.reshape(-1, V)
+    out = np.zeros(rows.shape, dtype=np.float32)
+    kept = np.zeros(rows.shape, dtype=bool)
+    flags = np.zeros(rows.shape[0], dtype=bool)
+    k = min(int(top_k), V)
+    for r in range(rows.shape[0]):
+        x = rows[r].astype(np.float64)
+        order = np.lexsort((np.arange(V), -x))          # descending logit, lower index first
+        top = order[:k]
+        if k < V and x[order[k - 1]] - x[order[k]] < FLAG_MARGIN:
+            flags[r] = True
+        e = np.exp((x[top] - x[top[0]]) / t)
+        pk = e / e.sum()
+        keep = 0
+        cum = 0.0
+        for j in range(k):
+            if cum >= float(top_p):
+                break
+            keep += 1
+            cum += pk[j]
+        if keep < k:
+            before = cum - pk[keep - 1]
+            if abs(cum - float(top_p)) < FLAG_MARGIN or abs(before - float(top_p)) < FLAG_MARGIN:
+                flags[r] = True
+        sel = top[:keep]
+        out[r, sel] = (pk[:keep] / pk[:keep].sum()).astype(np.float32)
+        kept[r, sel] = True
+    return out.reshape(shape), kept.reshape(shape), flags.reshape(shape[:-1])
+
+
+def sample_rule_filtered(l32, draft, q, temperature, top_k, top_p, seed, pos0, seq0=0):
+    """The sampling rule of :func:`sample_rule` on the filtered target distribution of
+    :func:`filtered_probs` (the same top-k / top-p the drafter applied to q): accept with
+    probability min(1, p~/q), resample the first rejected slot from max(0, p~ - q), the
+    bonus from p~_gamma.  The output law is p~ ([Infra-ch8] "why the output does not
+    change": the rule preserves whatever target distribution it is given).  q is used as
+    given.  Returns (n_accepted [B], tokens [B, gamma+1], flagged [B]).
+
+    Pinned by: top_k = V, top_p = 1 reproduces sample_rule bit for bit; the rule's law
+    is pinned through accept_slots / resample_rows (exact enumeration)."""
+    l32 = np.asarray(l32, dtype=np.float32)
+    draft = np.asarray(draft, dtype=np.int64)
+    q = np.asarray(q, dtype=np.float64)
+    B, G1, V = l32.shape
+    gamma = G1 - 1
+    pos0 = np.broadcast_to(np.asarray(pos0, dtype=np.int64), (B,))
+    seq = seq0 + np.arange(B, dtype=np.int64)
+    p32, _, fflags = filtered_probs(l32, temperature, top_k, top_p)
+    u = np.stack([philox.accept_uniform(seed, seq, pos0 + i + 1) for i in range(gamma)], axis=1) \
+        if gamma else np.zeros((B, 0))
+    n, flagged = accept_slots(p32, q, draft, u)
+    y, gflag = resample(p32, q, n, seed, pos0, seq0)
+    reached = np.arange(G1)[None, :] <= n[:, None]
+    flagged |= gflag | np.any(reached & fflags, axis=1)
+    return n, assemble_tokens(draft, n, y), flagged
+
+
+def verify_sample_filtered(logits64, draft, q, temperature, top_k, top_p, seed, pos0, seq0=0):
+    """Aligned-filter sampling verify from exact logits; T == 0 is the greedy rule (the
+    filters always keep the argmax)."""
+    if float(temperature) == 0.0:
+        return verify_greedy(logits64, draft)
+    return sample_rule_filtered(f32_logits(logits64), draft, q, temperature, top_k, top_p, seed, pos0, seq0)
+
+
 def acceptance_rate(p, q):
     """alpha = sum_v min(p_v, q_v): the probability that a draft x ~ q is
     accepted ([Infra-ch8] "how the benefit is computed"; [Self-spec] 4.1)."""

@@ -1,5 +1,5 @@
 """GPU parity of the drafter's centroid-masked LM head against the CPU oracle, through
-the C ABI ([MTP-drafters] "efficient embedder"; [MTP-deep-dive] 3.4).
+the C ABI ([X-thread] "Gemma 4's MTP", efficient embedder; [MTP-deep-dive] 3.4).
 
 Bar: the kept clusters bit-exact as a set and in order, except where the oracle flags
 a near tie (score gap below 1e-3: at the top_k cut the set may differ; inside the kept

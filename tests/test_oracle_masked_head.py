@@ -1,6 +1,6 @@
 """Pins of the oracle's centroid-masked drafter LM head (CPU only).
 
-[MTP-drafters] "efficient embedder"; [MTP-deep-dive] 3.4.  The selection is pinned by a
+[X-thread] "Gemma 4's MTP", efficient embedder; [MTP-deep-dive] 3.4.  The selection is pinned by a
 hand-checked fixture with ties and by the top-k set property; the cluster scores by
 linearity against the plain LM head; the token logits by the all-clusters case (a
 reordering of the full LM head) and a brute-force loop.

@@ -77,9 +77,11 @@ def library():
     lib.spec_verify_greedy.argtypes = [M, i32, vp, i32, i32, vp, KV, vp, vp, vp, vp, sz, vp]
     lib.spec_verify_sample.argtypes = [M, i32, vp, i32, i32, vp, vp, i32, ctypes.c_float, ctypes.c_uint64, vp,
                                        KV, vp, vp, vp, vp, sz, vp]
+    lib.spec_verify_sample_filtered.argtypes = [M, i32, vp, i32, i32, vp, vp, i32, ctypes.c_float, i32,
+                                                ctypes.c_float, ctypes.c_uint64, vp, KV, vp, vp, vp, vp, sz, vp]
     lib.draft_masked_logits.argtypes = [ctypes.POINTER(_SvMaskedHead), vp, i32, i32, vp, vp, vp, vp, sz, vp]
     for f in (lib.verify_forward, lib.spec_verify_greedy, lib.spec_verify_sample, lib.sv_timing_enable,
-              lib.sv_timing_read, lib.draft_masked_logits):
+              lib.sv_timing_read, lib.draft_masked_logits, lib.spec_verify_sample_filtered):
         f.restype = i32
     lib.sv_version.restype = i32
     lib.sv_status_string.restype = ctypes.c_char_p
@@ -302,6 +304,34 @@ def spec_verify_sample(model, kind, inp, B, gamma, draft, q, temperature, seed, 
     _call_with_ws(lib.spec_verify_sample,
                   (ctypes.byref(model.struct), kind, _ptr(inp), B, gamma, _ptr(draft), _ptr(q), qd,
                    float(temperature), ctypes.c_uint64(int(seed)), _ptr(pos0),
+                   ctypes.byref(kvs) if kvs is not None else None, _ptr(n), _ptr(tok), _ptr(logits_out)),
+                  inp.device, ws, stream)
+    return n, tok
+
+
+def spec_verify_sample_filtered(model, kind, inp, B, gamma, draft, q, temperature, top_k, top_p, seed, pos0,
+                                kv=None, logits_out=None, out=None, ws=None, stream=None):
+    """Speculative-sampling verify with the drafter's top-k / top-p filters applied to
+    the target alike (C: spec_verify_sample_filtered).  ``q`` is the drafter's filtered
+    distributions, float32 or bfloat16 [B, gamma, V]; ``pos0`` int64 [B]; ``top_k`` in
+    1..64, ``top_p`` in (0, 1].  Returns (n_accepted, tokens_out)."""
+    lib = library()
+    inp = _kind_input(kind, inp)
+    _dev_tensor(draft, "draft", torch.int32)
+    _dev_tensor(q, "q")
+    _dev_tensor(pos0, "pos0", torch.int64)
+    _dev_tensor(logits_out, "logits_out", torch.float32)
+    if q.dtype == torch.bfloat16:
+        qd = SV_BF16
+    elif q.dtype == torch.float32:
+        qd = SV_F32
+    else:
+        raise ValueError("q must be float32 or bfloat16")
+    n, tok = _outs(B, gamma, inp.device, out)
+    kvs = kv.struct() if kv is not None else None
+    _call_with_ws(lib.spec_verify_sample_filtered,
+                  (ctypes.byref(model.struct), kind, _ptr(inp), B, gamma, _ptr(draft), _ptr(q), qd,
+                   float(temperature), int(top_k), float(top_p), ctypes.c_uint64(int(seed)), _ptr(pos0),
                    ctypes.byref(kvs) if kvs is not None else None, _ptr(n), _ptr(tok), _ptr(logits_out)),
                   inp.device, ws, stream)
     return n, tok

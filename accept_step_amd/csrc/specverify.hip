@@ -25,6 +25,7 @@
 #include "sv_gemm.hpp"
 #include "sv_head.hpp"
 #include "sv_masked.hpp"
+#include "sv_filter.hpp"
 
 using namespace sv;
 
@@ -991,6 +992,71 @@ sv_status draft_masked_logits(const sv_masked_head* head, const void* hidden, in
   hipLaunchKernelGGL(k_gather_logits, dim3(top_k, (cs + MASK_ROWS_PER_WG - 1) / MASK_ROWS_PER_WG, M), dim3(256),
                      size_t(d) * 4, s, static_cast<const bf16_t*>(head->embed), static_cast<const bf16_t*>(hidden),
                      clusters, d, cs, top_k, logits);
+  SV_HIP(hipGetLastError());
+  return SV_OK;
+}
+
+sv_status spec_verify_sample_filtered(const sv_model* m, sv_input_kind kind, const void* input, int32_t B,
+                                      int32_t gamma, const int32_t* draft, const void* q, sv_dtype q_dtype,
+                                      float temperature, int32_t top_k, float top_p, uint64_t seed, const int64_t* pos0,
+                                      const sv_kv_cache* kv, int32_t* n_accepted, int32_t* tokens_out,
+                                      float* logits_out, void* ws, size_t* ws_bytes, void* stream) {
+  g_err.clear();
+  if (!std::isfinite(temperature) || temperature < 0.0f) return fail(SV_ERR_ARG, "temperature must be finite and >= 0");
+  if (top_k < 1 || top_k > MASK_FAST_K) return fail(SV_ERR_UNSUPPORTED, "top_k must be in [1, %d]", MASK_FAST_K);
+  if (!(top_p > 0.0f && top_p <= 1.0f)) return fail(SV_ERR_ARG, "top_p must be in (0, 1]");
+  if (temperature == 0.0f)   // the greedy rule: the filters always keep the argmax
+    return verify_common(m, kind, input, B, gamma, draft, nullptr, SV_F32, 0.0f, 0, nullptr, kv, n_accepted,
+                         tokens_out, logits_out, ws, ws_bytes, stream, false);
+  Shape sh;
+  sv_status st = check_common(m, kind, input, B, gamma, kv, &sh);
+  if (st) return st;
+  if (!n_accepted || !tokens_out) return fail(SV_ERR_ARG, "n_accepted and tokens_out must not be NULL");
+  if (!draft && kind != SV_IN_TOKENS) return fail(SV_ERR_ARG, "draft is NULL");
+  if (!q) return fail(SV_ERR_ARG, "q is NULL");
+  if (!pos0) return fail(SV_ERR_ARG, "pos0 is NULL");
+  if (q_dtype != SV_F32 && q_dtype != SV_BF16) return fail(SV_ERR_DTYPE, "q_dtype must be SV_F32 or SV_BF16");
+  const int nch = (sh.V + FILT_CHUNK - 1) / FILT_CHUNK;
+  if (int64_t(nch) * top_k > MASK_MAX_CLUSTERS)
+    return fail(SV_ERR_UNSUPPORTED, "vocabulary too large for top_k %d (at most %d entries)", int(top_k),
+                MASK_MAX_CLUSTERS / top_k * FILT_CHUNK);
+  const bool need_buf = kind != SV_IN_LOGITS && logits_out == nullptr;
+  Layout L = plan(m, sh, kv, need_buf, false);
+  Bump b;
+  b.off = L.total;
+  const size_t o_cand = b.take(size_t(sh.M) * nch * top_k * 8);
+  const size_t o_n = b.take(size_t(sh.M) * 4);
+  const size_t o_id = b.take(size_t(sh.M) * top_k * 4);
+  const size_t o_p = b.take(size_t(sh.M) * top_k * 4);
+  L.total = b.off;
+  bool query = false;
+  if ((st = check_ws(ws, ws_bytes, L, &query))) return st;
+  if (query) return SV_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* logits = kind == SV_IN_LOGITS ? const_cast<float*>(static_cast<const float*>(input))
+                                       : (logits_out ? logits_out : at<float>(ws, L.logits));
+  if (kind != SV_IN_LOGITS) {
+    int P = 0;
+    if ((st = run_logits(m, sh, input, kv, L, ws, logits, nullptr, 0.0f, &P, s))) return st;
+  } else if (logits_out && logits_out != input) {
+    SV_HIP(hipMemcpyAsync(logits_out, input, size_t(sh.M) * sh.V * 4, hipMemcpyDeviceToDevice, s));
+  }
+  FiltArgs fa;
+  memset(&fa, 0, sizeof fa);
+  fa.logits = logits; fa.M = sh.M; fa.V = sh.V; fa.G1 = sh.G1; fa.gamma = gamma; fa.B = sh.B;
+  fa.top_k = top_k; fa.nch = nch; fa.inv_t = 1.0 / double(temperature); fa.top_p = double(top_p);
+  fa.cand = at<unsigned long long>(ws, o_cand); fa.kept_n = at<int>(ws, o_n);
+  fa.kept_id = at<int>(ws, o_id); fa.kept_p = at<float>(ws, o_p);
+  if (draft) { fa.draft = draft; fa.draft_stride = gamma; fa.draft_offset = 0; }
+  else { fa.draft = static_cast<const int*>(input); fa.draft_stride = gamma + 1; fa.draft_offset = 1; }
+  fa.q = q; fa.q_bf16 = q_dtype == SV_BF16 ? 1 : 0; fa.pos0 = pos0;
+  fa.invalid = sh.decoder ? at<int>(ws, L.invalid) : nullptr;
+  fa.len = kv ? kv->len : nullptr;
+  fa.seed = seed; fa.n_accepted = n_accepted; fa.tokens_out = tokens_out;
+  TimeScope ts(s, 2);
+  hipLaunchKernelGGL(k_chunk_topk, dim3(nch, sh.M), dim3(256), 0, s, fa);
+  hipLaunchKernelGGL(k_row_filter, dim3(sh.M), dim3(256), 0, s, fa);
+  hipLaunchKernelGGL(k_filtered_rule, dim3(sh.B), dim3(64), 0, s, fa);
   SV_HIP(hipGetLastError());
   return SV_OK;
 }

@@ -53,38 +53,37 @@ __global__ __launch_bounds__(256) void k_select_clusters(const float* __restrict
     clusters[size_t(m) * top_k + j] = int32_t(0xffffffffu - unsigned(key[j]));
 }
 
-// Kept clusters of row blockIdx.x for top_k <= MASK_FAST_K, 256 threads.  Thread t holds
-// the keys (score order, complemented id) of clusters t, t + 256, ...  (1) An LDS
-// histogram of the top 12 bits of the score orders (sign, exponent and three mantissa
-// bits spread typical scores over many bins), scanned from the top by the four
-// wavefronts (a quarter of the bins each), gives the bin B that holds the top_k-th
-// largest key and the number ``need`` of keys still to take from it.  (2) Every key in a
-// bin above B is kept; the keys of bin B are gathered in LDS and each ranks itself by
-// counting the larger ones (few keys in practice; every key in the worst case), and the
-// ``need`` largest are kept.  (3) Wavefront 0 sorts the top_k kept keys in descending
-// order with a bitonic network across its lanes and writes the ids.
-__global__ __launch_bounds__(256) void k_select_topk(const float* __restrict__ cl, int C, int top_k,
-                                                     int32_t* __restrict__ clusters) {
+// The k (<= MASK_FAST_K) largest of up to MASK_MAX_CLUSTERS distinct 64-bit keys held by
+// a workgroup of 256 threads (thread t: key[u] of entry t + 256 u; 0 = no entry, smaller
+// than every real key), left in descending order in wavefront 0's lanes (lane j: the
+// j-th largest, 0 past the number of real keys).  (1) An LDS histogram of the top 12
+// bits of the keys (for a float score: sign, exponent and three mantissa bits, which
+// spread typical scores over many bins), scanned from the top by the four wavefronts (a
+// quarter of the bins each), gives the bin B that holds the k-th largest key and the
+// number ``need`` of keys still to take from it.  (2) Every key in a bin above B is
+// kept; the keys of bin B are gathered in LDS and each ranks itself by counting the
+// larger ones (few keys in practice; all of them in the worst case), and the ``need``
+// largest are kept.  (3) Wavefront 0 sorts the kept keys with a bitonic network across
+// its lanes.  Every thread of the workgroup must call it.
+__device__ unsigned long long block_top_keys(const unsigned long long (&key)[MASK_MAX_CLUSTERS / 256], int k) {
   constexpr int PER = MASK_MAX_CLUSTERS / 256;
-  constexpr int NBINS = 4096, SHIFT = 20, BPL = NBINS / 256;   // bins per lane in the scan
+  constexpr int NBINS = 4096, SHIFT = 52, BPL = NBINS / 256;   // bins per lane in the scan
   __shared__ unsigned hist[NBINS];
-  __shared__ unsigned s_bin, s_need, s_cnt, s_nb, s_wt[4];
+  __shared__ unsigned s_bin, s_need, s_cnt, s_nb, s_nreal, s_wt[4];
   __shared__ unsigned long long s_sel[MASK_FAST_K];
   __shared__ unsigned long long s_cand[MASK_MAX_CLUSTERS];
-  const int m = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  unsigned long long key[PER];
-#pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int c = t + 256 * u;
-    key[u] = c < C ? cluster_key(cl[size_t(m) * C + c], c) : 0ull;   // 0: no cluster (every real key is larger)
-  }
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   for (int b = t; b < NBINS; b += 256) hist[b] = 0u;
-  if (t == 0) { s_cnt = 0u; s_nb = 0u; }
+  if (t == 0) { s_cnt = 0u; s_nb = 0u; s_nreal = 0u; }
+  if (t < MASK_FAST_K) s_sel[t] = 0ull;
   __syncthreads();
+  unsigned nreal = 0u;
 #pragma unroll
   for (int u = 0; u < PER; ++u)
-    if (t + 256 * u < C) atomicAdd(&hist[unsigned(key[u] >> 32) >> SHIFT], 1u);
+    if (key[u]) { atomicAdd(&hist[unsigned(key[u] >> SHIFT)], 1u); ++nreal; }
+  atomicAdd(&s_nreal, nreal);
   __syncthreads();
+  const unsigned kk = min(unsigned(k), s_nreal);
   // wavefront w scans bins NBINS - 1 - w * NBINS / 4 downwards; lane l takes BPL of them
   const int top = NBINS - 1 - wave * (NBINS / 4) - lane * BPL;
   unsigned tot = 0u;
@@ -100,9 +99,8 @@ __global__ __launch_bounds__(256) void k_select_topk(const float* __restrict__ c
   __syncthreads();
   unsigned base = 0u;
   for (int w = 0; w < wave; ++w) base += s_wt[w];
-  const unsigned kk = unsigned(top_k);
   unsigned above = base + incl - tot;
-  if (above < kk && kk <= base + incl) {
+  if (kk > 0u && above < kk && kk <= base + incl) {
 #pragma unroll
     for (int j = 0; j < BPL; ++j) {
       const unsigned cj = hist[top - j];
@@ -111,37 +109,56 @@ __global__ __launch_bounds__(256) void k_select_topk(const float* __restrict__ c
     }
   }
   __syncthreads();
-  const unsigned bin = s_bin, need = s_need, n_above = kk - need;
+  if (kk > 0u) {
+    const unsigned bin = s_bin, need = s_need, n_above = kk - need;
 #pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    if (t + 256 * u >= C) continue;
-    const unsigned kb = unsigned(key[u] >> 32) >> SHIFT;
-    if (kb > bin) s_sel[atomicAdd(&s_cnt, 1u)] = key[u];
-    else if (kb == bin) s_cand[atomicAdd(&s_nb, 1u)] = key[u];
+    for (int u = 0; u < PER; ++u) {
+      if (!key[u]) continue;
+      const unsigned kb = unsigned(key[u] >> SHIFT);
+      if (kb > bin) s_sel[atomicAdd(&s_cnt, 1u)] = key[u];
+      else if (kb == bin) s_cand[atomicAdd(&s_nb, 1u)] = key[u];
+    }
+    __syncthreads();
+    const unsigned nb = s_nb;
+    for (unsigned i = t; i < nb; i += 256) {
+      const unsigned long long x = s_cand[i];
+      unsigned rank = 0u;
+      for (unsigned j = 0; j < nb; ++j) rank += s_cand[j] > x ? 1u : 0u;
+      if (rank < need) s_sel[n_above + rank] = x;
+    }
   }
   __syncthreads();
-  const unsigned nb = s_nb;
-  for (unsigned i = t; i < nb; i += 256) {
-    const unsigned long long x = s_cand[i];
-    unsigned rank = 0u;
-    for (unsigned j = 0; j < nb; ++j) rank += s_cand[j] > x ? 1u : 0u;
-    if (rank < need) s_sel[n_above + rank] = x;
-  }
-  __syncthreads();
+  unsigned long long kv = 0ull;
   if (wave == 0) {
-    unsigned long long k = lane < top_k ? s_sel[lane] : 0ull;
+    kv = lane < int(kk) ? s_sel[lane] : 0ull;
     for (int size = 2; size <= 64; size <<= 1) {
       for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        const unsigned lo = unsigned(__shfl_xor(int(unsigned(k)), stride));
-        const unsigned hi = unsigned(__shfl_xor(int(unsigned(k >> 32)), stride));
+        const unsigned lo = unsigned(__shfl_xor(int(unsigned(kv)), stride));
+        const unsigned hi = unsigned(__shfl_xor(int(unsigned(kv >> 32)), stride));
         const unsigned long long other = (static_cast<unsigned long long>(hi) << 32) | lo;
         const bool desc = (lane & size) == 0;          // all of it at size 64
         const bool keep_max = ((lane & stride) == 0) == desc;
-        k = keep_max ? (other > k ? other : k) : (other < k ? other : k);
+        kv = keep_max ? (other > kv ? other : kv) : (other < kv ? other : kv);
       }
     }
-    if (lane < top_k) clusters[size_t(m) * top_k + lane] = int32_t(0xffffffffu - unsigned(k));
   }
+  return kv;
+}
+
+// Kept clusters of row blockIdx.x for top_k <= MASK_FAST_K (256 threads): the keys of the
+// C cluster scores through block_top_keys; wavefront 0 writes the ids.
+__global__ __launch_bounds__(256) void k_select_topk(const float* __restrict__ cl, int C, int top_k,
+                                                     int32_t* __restrict__ clusters) {
+  constexpr int PER = MASK_MAX_CLUSTERS / 256;
+  const int m = blockIdx.x, t = threadIdx.x;
+  unsigned long long key[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int c = t + 256 * u;
+    key[u] = c < C ? cluster_key(cl[size_t(m) * C + c], c) : 0ull;
+  }
+  const unsigned long long kv = block_top_keys(key, top_k);
+  if (t < top_k) clusters[size_t(m) * top_k + t] = int32_t(0xffffffffu - unsigned(kv));
 }
 
 // Token logits of the kept clusters: workgroup (j, chunk, m) computes rows

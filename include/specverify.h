@@ -177,6 +177,34 @@ sv_status spec_verify_sample(const sv_model* m, sv_input_kind kind, const void* 
                              const sv_kv_cache* kv, int32_t* n_accepted, int32_t* tokens_out,
                              float* logits_out, void* ws, size_t* ws_bytes, void* stream);
 
+/* Speculative sampling verify with the drafter's top-k / top-p filters applied alike to
+ * the target ([Infra-ch8] "why the output does not change", [MTP-drafters] 5.2: the
+ * sampling parameters must be handled by one rule in drafting and verifying;
+ * [MTP-drafters] 3.1 for the filters; [MTP-deep-dive] 5.1 deploys with top_k 64,
+ * top_p 0.95).  The target distribution of every slot becomes p~: softmax(logits / T)
+ * restricted to the top_k largest logits (the lower index first on equal values), then
+ * to the smallest prefix of those (in descending order) whose probability, renormalised
+ * over the top_k set, reaches top_p, renormalised over the kept tokens (computed in
+ * double precision, rounded once to float32).  The rule of spec_verify_sample then runs
+ * on p~: accept iff u * q(x) < p~(x) (a filtered-out draft is rejected), the first
+ * rejection draws from max(0, p~ - q) (p~ if that is zero), all accepted draws the
+ * bonus from p~_gamma, with the same random stream.  The output law is p~.
+ *   top_k: 1 .. 64 (SV_ERR_UNSUPPORTED otherwise); the vocabulary may hold at most
+ *          4096 * floor(4096 / top_k) entries (262,144 at top_k 64).
+ *   top_p: in (0, 1]; 1 keeps the whole top-k set.
+ *   temperature: finite, >= 0; 0 applies the greedy rule exactly (the filters keep the
+ *          argmax).
+ *   q:     the drafter's distributions, filtered by the drafter with the same rule, used
+ *          as given.
+ *   Other arguments as for spec_verify_sample; logits_out, if given, receives the
+ *   unfiltered float32 logits. */
+sv_status spec_verify_sample_filtered(const sv_model* m, sv_input_kind kind, const void* input,
+                                      int32_t B, int32_t gamma, const int32_t* draft,
+                                      const void* q, sv_dtype q_dtype, float temperature,
+                                      int32_t top_k, float top_p, uint64_t seed, const int64_t* pos0,
+                                      const sv_kv_cache* kv, int32_t* n_accepted, int32_t* tokens_out,
+                                      float* logits_out, void* ws, size_t* ws_bytes, void* stream);
+
 /* The drafter's centroid-masked LM head ([X-thread] "Gemma 4's MTP", efficient embedder;
  * [MTP-deep-dive] 3.4 "centroids masking"): token embeddings grouped into clusters of
  * similar tokens, one representative embedding per cluster.  The hidden state scores

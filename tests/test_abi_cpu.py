@@ -136,3 +136,26 @@ def test_masked_head_argument_errors_and_query(lib):
     assert call(M=0)[0] == 1 and call(M=25)[0] == 1
     assert call(k=0)[0] == 1 and call(k=2049)[0] == 1
     assert call(ws=FAKE, nbytes=need - 1)[0] == 4
+
+
+def test_filtered_sampling_argument_errors_and_query(lib):
+    m = _model(vocab=262144, d=1536)
+
+    def call(T=1.0, k=64, p=0.95, q=FAKE, pos0=FAKE, V=None, ws=None, nbytes=0):
+        mm = _model(vocab=V, d=1536) if V else m
+        n = ctypes.c_size_t(nbytes)
+        st = lib.spec_verify_sample_filtered(ctypes.byref(mm), sv.SV_IN_HIDDEN, FAKE, 2, 4, FAKE, q, sv.SV_BF16, T,
+                                             k, p, 7, pos0, None, FAKE, FAKE, None, ws, ctypes.byref(n), None)
+        return st, n.value
+
+    st, need = call()
+    st_plain, need_plain = greedy(lib, m, B=2)
+    assert st == 0 and st_plain == 0 and need > need_plain   # plus the candidate and kept lists
+    assert call(T=-1.0)[0] == 1 and call(T=float("nan"))[0] == 1
+    assert call(k=0)[0] == 6 and call(k=65)[0] == 6
+    assert call(p=0.0)[0] == 1 and call(p=1.5)[0] == 1 and call(p=float("nan"))[0] == 1
+    assert call(q=None)[0] == 1 and call(pos0=None)[0] == 1
+    assert call(V=262144 + 4096)[0] == 6                       # 65 chunks x 64 candidates
+    assert call(V=262144 + 4096, k=32)[0] == 0
+    assert call(T=0.0, q=None, pos0=None)[0] == 0             # T == 0 is the greedy rule
+    assert call(ws=FAKE, nbytes=need - 1)[0] == 4

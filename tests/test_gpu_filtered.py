@@ -1,0 +1,141 @@
+"""GPU parity of spec_verify_sample_filtered (speculative sampling with the drafter's
+top-k / top-p filters applied alike to the target) against the oracle's
+verify_sample_filtered: n and tokens bit-exact except on sequences the oracle flags
+(a filter cut or a sampling decision within its rounding margin).  q is the drafter's
+distribution filtered with the same parameters, as a drafter that follows the rule
+would send it; the drafts are drawn from it."""
+import numpy as np
+import pytest
+import torch
+
+import accept_step_amd as sv
+import workloads
+from oracle import rules
+from tests.gpu_util import (check_token_structure, compare_decisions, dev, dev_bf16, log, oracle_logits_bf16,
+                            row_rel_err)
+
+pytestmark = pytest.mark.gpu
+
+
+def filtered_drafter(target_f32, noise, T, top_k, top_p, rng):
+    """Drafter logits = target + noise; q = the filtered distribution (the same filters);
+    drafts x ~ q by inverse CDF.  Returns (draft int32 [B, gamma], q bf16 bits)."""
+    z = (target_f32 + noise).astype(np.float32)
+    q, _, _ = rules.filtered_probs(z, T, top_k, top_p)
+    qb = workloads.to_bf16_bits(q)
+    qf = workloads.bf16_bits_to_f32(qb).astype(np.float64)
+    B, g, V = q.shape
+    cdf = np.cumsum(qf, axis=-1)
+    u = rng.random((B, g)) * cdf[..., -1]
+    x = np.empty((B, g), dtype=np.int32)
+    for b in range(B):
+        for i in range(g):
+            j = min(int(np.searchsorted(cdf[b, i], u[b, i], side="right")), V - 1)
+            while qf[b, i, j] == 0.0:           # never land on a zero of the rounded q
+                j -= 1
+            x[b, i] = j
+    return x, qb
+
+
+def case(V, d, B, gamma, T, top_k, top_p, seed, noise_std=0.7, w=None, bad_drafts=True):
+    rng = np.random.default_rng(seed)
+    if w is None:
+        w = workloads.to_bf16_bits((rng.standard_normal((V, d)) * 0.3).astype(np.float32))
+    h = workloads.to_bf16_bits(rng.standard_normal((B, gamma + 1, d)).astype(np.float32))
+    ref = oracle_logits_bf16(h, w)
+    lt = rules.f32_logits(ref[:, :gamma])
+    noise = rng.standard_normal((B, gamma, V)).astype(np.float32) * noise_std
+    draft, qb = filtered_drafter(lt, noise, T, top_k, top_p, rng)
+    if bad_drafts:
+        bad = rng.random((B, gamma)) < 0.05
+        draft = np.where(bad, np.where(rng.random((B, gamma)) < 0.5, -3, V + 7), draft).astype(np.int32)
+    pos0 = rng.integers(0, 5000, B).astype(np.int64)
+    return dict(w=w, h=h, ref=ref, draft=draft, qb=qb, pos0=pos0, seed=777 + seed, T=T, k=top_k, p=top_p)
+
+
+def run(model, c, B, gamma, logits_out=None, kind=sv.SV_IN_HIDDEN, inp=None):
+    inp = dev_bf16(c["h"]) if inp is None else inp
+    return sv.spec_verify_sample_filtered(model, kind, inp, B, gamma, dev(c["draft"]), dev_bf16(c["qb"]), c["T"],
+                                          c["k"], c["p"], c["seed"], dev(c["pos0"]), logits_out=logits_out)
+
+
+def oracle(c):
+    qf = workloads.bf16_bits_to_f32(c["qb"]).astype(np.float64)
+    return rules.verify_sample_filtered(c["ref"], c["draft"], qf, c["T"], c["k"], c["p"], c["seed"], c["pos0"])
+
+
+SMALL = [
+    # (V, d, B, gamma, T, top_k, top_p)
+    (1000, 96, 3, 4, 1.0, 64, 0.95),     # one ragged chunk
+    (9000, 64, 5, 4, 0.7, 20, 0.9),      # three chunks, the last ragged
+    (4096, 256, 4, 3, 1.0, 64, 1.0),     # top_p = 1: the whole top-k set
+    (4099, 128, 2, 15, 1.0, 8, 0.5),     # largest gamma, a 3-logit last chunk
+    (30, 32, 4, 4, 1.0, 64, 0.95),       # fewer tokens than top_k
+    (2, 32, 3, 1, 1.0, 64, 1.0),         # smallest vocabulary and gamma
+    (5000, 64, 3, 4, 1.0, 1, 0.95),      # top_k 1: the argmax only
+    (5000, 64, 3, 4, 1.0, 64, 0.01),     # top_p below the largest probability: one token
+    (20000, 64, 2, 4, 2.0, 64, 0.95),    # flat distribution at high temperature
+]
+
+
+@pytest.mark.parametrize("V,d,B,gamma,T,top_k,top_p", SMALL)
+def test_small_and_ragged(V, d, B, gamma, T, top_k, top_p):
+    log(f"[filtered] V={V} d={d} B={B} gamma={gamma} T={T} top_k={top_k} top_p={top_p}")
+    c = case(V, d, B, gamma, T, top_k, top_p, seed=V + d + B + gamma + top_k)
+    model = sv.lm_head_model(dev_bf16(c["w"]))
+    logits = torch.empty((B, gamma + 1, V), dtype=torch.float32, device="cuda")
+    n, tok = run(model, c, B, gamma, logits)
+    torch.cuda.synchronize()
+    assert row_rel_err(logits.cpu().numpy(), c["ref"]).max() <= 1e-4
+    n0, t0, fl = oracle(c)
+    check_token_structure(n.cpu().numpy(), tok.cpu().numpy(), gamma)
+    m, f = compare_decisions(n.cpu().numpy(), tok.cpu().numpy(), n0, t0, fl, f"V={V} k={top_k} p={top_p}")
+    log(f"[filtered] n={n.cpu().numpy().tolist()} mismatched {m} flagged {f}")
+    # every emitted token lies in the kept set of its slot
+    p32, kept, _ = rules.filtered_probs(rules.f32_logits(c["ref"]), T, top_k, top_p)
+    nh, th = n.cpu().numpy(), tok.cpu().numpy()
+    for b in range(B):
+        y = int(th[b, nh[b]])
+        assert kept[b, nh[b], y], (b, y)
+
+
+def test_greedy_limit_and_logits_input():
+    """T = 0 takes the greedy rule; the logits input path gives the same decisions."""
+    V, d, B, gamma = 4099, 128, 4, 4
+    c = case(V, d, B, gamma, 1.0, 64, 0.9, seed=11)
+    model = sv.lm_head_model(dev_bf16(c["w"]))
+    c0 = dict(c, T=0.0)
+    n, tok = run(model, c0, B, gamma)
+    torch.cuda.synchronize()
+    n0, t0, fl = rules.verify_sample_filtered(c["ref"], c["draft"], None, 0.0, 64, 0.9, 0, c["pos0"])
+    compare_decisions(n.cpu().numpy(), tok.cpu().numpy(), n0, t0, fl, "greedy")
+    l32 = rules.f32_logits(c["ref"])
+    n, tok = run(sv.logits_model(V), c, B, gamma, kind=sv.SV_IN_LOGITS, inp=dev(l32))
+    torch.cuda.synchronize()
+    n0, t0, fl = oracle(c)
+    compare_decisions(n.cpu().numpy(), tok.cpu().numpy(), n0, t0, fl, "logits input")
+
+
+LARGE = [(1, 1.0), (4, 1.0), (4, 0.7)]
+
+
+@pytest.fixture(scope="module")
+def large_w():
+    log("[filtered large] generating the 262144 x 1536 table")
+    return workloads.large_vocab(B=1, temperature=1.0).w
+
+
+@pytest.mark.parametrize("B,T", LARGE)
+def test_large_vocab_deployment_filters(large_w, B, T):
+    """V = 262144, d = 1536, gamma = 4 with top_k 64, top_p 0.95, the deployment's filters."""
+    log(f"[filtered large] B={B} T={T}")
+    c = case(262144, 1536, B, 4, T, 64, 0.95, seed=100 + B, noise_std=1.0, w=large_w, bad_drafts=False)
+    model = sv.lm_head_model(dev_bf16(large_w))
+    n, tok = run(model, c, B, 4)
+    torch.cuda.synchronize()
+    n0, t0, fl = oracle(c)
+    m, f = compare_decisions(n.cpu().numpy(), tok.cpu().numpy(), n0, t0, fl, f"B={B} T={T}")
+    log(f"[filtered large] B={B} T={T} n={n.cpu().numpy().tolist()} mismatched {m} flagged {f}")
+    n2, tok2 = run(model, c, B, 4)
+    torch.cuda.synchronize()
+    assert torch.equal(n, n2) and torch.equal(tok, tok2)

@@ -1025,9 +1025,11 @@ sv_status spec_verify_sample_filtered(const sv_model* m, sv_input_kind kind, con
   Bump b;
   b.off = L.total;
   const size_t o_cand = b.take(size_t(sh.M) * nch * top_k * 8);
-  const size_t o_n = b.take(size_t(sh.M) * 4);
   const size_t o_id = b.take(size_t(sh.M) * top_k * 4);
   const size_t o_p = b.take(size_t(sh.M) * top_k * 4);
+  const size_t o_q = b.take(size_t(sh.M) * top_k * 4);
+  const size_t o_dpx = b.take(size_t(sh.M) * 4);
+  const size_t o_dqx = b.take(size_t(sh.M) * 4);
   L.total = b.off;
   bool query = false;
   if ((st = check_ws(ws, ws_bytes, L, &query))) return st;
@@ -1045,8 +1047,10 @@ sv_status spec_verify_sample_filtered(const sv_model* m, sv_input_kind kind, con
   memset(&fa, 0, sizeof fa);
   fa.logits = logits; fa.M = sh.M; fa.V = sh.V; fa.G1 = sh.G1; fa.gamma = gamma; fa.B = sh.B;
   fa.top_k = top_k; fa.nch = nch; fa.inv_t = 1.0 / double(temperature); fa.top_p = double(top_p);
-  fa.cand = at<unsigned long long>(ws, o_cand); fa.kept_n = at<int>(ws, o_n);
-  fa.kept_id = at<int>(ws, o_id); fa.kept_p = at<float>(ws, o_p);
+  fa.cand = at<unsigned long long>(ws, o_cand);
+  fa.kept_id = at<int>(ws, o_id); fa.kept_p = at<float>(ws, o_p); fa.kept_q = at<float>(ws, o_q);
+  fa.dpx = at<float>(ws, o_dpx); fa.dqx = at<float>(ws, o_dqx);
+  fa.counters = at<unsigned>(ws, L.counters);
   if (draft) { fa.draft = draft; fa.draft_stride = gamma; fa.draft_offset = 0; }
   else { fa.draft = static_cast<const int*>(input); fa.draft_stride = gamma + 1; fa.draft_offset = 1; }
   fa.q = q; fa.q_bf16 = q_dtype == SV_BF16 ? 1 : 0; fa.pos0 = pos0;
@@ -1054,9 +1058,7 @@ sv_status spec_verify_sample_filtered(const sv_model* m, sv_input_kind kind, con
   fa.len = kv ? kv->len : nullptr;
   fa.seed = seed; fa.n_accepted = n_accepted; fa.tokens_out = tokens_out;
   TimeScope ts(s, 2);
-  hipLaunchKernelGGL(k_chunk_topk, dim3(nch, sh.M), dim3(256), 0, s, fa);
-  hipLaunchKernelGGL(k_row_filter, dim3(sh.M), dim3(256), 0, s, fa);
-  hipLaunchKernelGGL(k_filtered_rule, dim3(sh.B), dim3(64), 0, s, fa);
+  hipLaunchKernelGGL(k_filter_tail, dim3(nch, sh.M), dim3(256), 0, s, fa);
   SV_HIP(hipGetLastError());
   return SV_OK;
 }

@@ -53,96 +53,137 @@ __global__ __launch_bounds__(256) void k_select_clusters(const float* __restrict
     clusters[size_t(m) * top_k + j] = int32_t(0xffffffffu - unsigned(key[j]));
 }
 
+// LDS of block_top_keys, declared __shared__ by the calling kernel.  Between calls the
+// histogram and the candidate slots are zero and nc is 0; sel_prepare establishes that
+// at kernel start (no barrier needed: the selection begins with one).
+constexpr int SEL_RANK_MAX = 128;                            // bin keys ranked directly
+constexpr int SEL_CAND = MASK_FAST_K + SEL_RANK_MAX;         // gathered candidates, at most
+struct SelScratch {
+  alignas(16) unsigned hist[4096];
+  alignas(16) unsigned long long cand[SEL_CAND];
+  unsigned long long out[MASK_FAST_K];
+  unsigned wt[4], bin, need, nb, nc;
+};
+
+__device__ __forceinline__ void sel_prepare(SelScratch& S) {
+  const int t = threadIdx.x;
+  reinterpret_cast<uint4*>(S.hist)[t * 4 + 0] = make_uint4(0u, 0u, 0u, 0u);
+  reinterpret_cast<uint4*>(S.hist)[t * 4 + 1] = make_uint4(0u, 0u, 0u, 0u);
+  reinterpret_cast<uint4*>(S.hist)[t * 4 + 2] = make_uint4(0u, 0u, 0u, 0u);
+  reinterpret_cast<uint4*>(S.hist)[t * 4 + 3] = make_uint4(0u, 0u, 0u, 0u);
+  if (t < SEL_CAND) S.cand[t] = 0ull;
+  if (t == 0) S.nc = 0u;
+}
+
 // The k (<= MASK_FAST_K) largest of up to MASK_MAX_CLUSTERS distinct 64-bit keys held by
-// a workgroup of 256 threads (thread t: key[u] of entry t + 256 u; 0 = no entry, smaller
-// than every real key), left in descending order in wavefront 0's lanes (lane j: the
-// j-th largest, 0 past the number of real keys).  (1) An LDS histogram of the top 12
-// bits of the keys (for a float score: sign, exponent and three mantissa bits, which
-// spread typical scores over many bins), scanned from the top by the four wavefronts (a
-// quarter of the bins each), gives the bin B that holds the k-th largest key and the
-// number ``need`` of keys still to take from it.  (2) Every key in a bin above B is
-// kept; the keys of bin B are gathered in LDS and each ranks itself by counting the
-// larger ones (few keys in practice; all of them in the worst case), and the ``need``
-// largest are kept.  (3) Wavefront 0 sorts the kept keys with a bitonic network across
-// its lanes.  Every thread of the workgroup must call it.
-__device__ unsigned long long block_top_keys(const unsigned long long (&key)[MASK_MAX_CLUSTERS / 256], int k) {
+// a workgroup of 256 threads (16 per thread, in any order; 0 = no entry, smaller than
+// every real key), returned in descending order in wavefront 0's lanes (lane j: the
+// j-th largest, 0 past the number of real keys).  Every thread must call it.
+//   (1) Radix refinement from the top: an LDS histogram of 12 key bits (bits 52..63
+//       first: for a float score the sign, exponent and three mantissa bits) over the
+//       keys that share the prefix fixed so far; a block scan from the top bin finds the
+//       bin holding the k-th largest key and how many keys are still needed from it.
+//       The bin joins the prefix and the next 12 bits are examined while the bin holds
+//       more than SEL_RANK_MAX keys (keys are distinct, so five passes always suffice).
+//       Each thread owns 16 bins of the scan and clears them once it has read them.
+//   (2) Every key at or above the final prefix (at most k - 1 above it plus the bin's
+//       keys) is gathered in LDS (one LDS atomic per wavefront) and ranks itself by
+//       counting the larger ones in 32-key blocks; the key of rank r < k is stored at
+//       position r, which leaves them sorted.
+__device__ unsigned long long block_top_keys(SelScratch& S, const unsigned long long (&key)[MASK_MAX_CLUSTERS / 256],
+                                             int k) {
   constexpr int PER = MASK_MAX_CLUSTERS / 256;
-  constexpr int NBINS = 4096, SHIFT = 52, BPL = NBINS / 256;   // bins per lane in the scan
-  __shared__ unsigned hist[NBINS];
-  __shared__ unsigned s_bin, s_need, s_cnt, s_nb, s_nreal, s_wt[4];
-  __shared__ unsigned long long s_sel[MASK_FAST_K];
-  __shared__ unsigned long long s_cand[MASK_MAX_CLUSTERS];
+  constexpr int NBINS = 4096, BPT = NBINS / 256;   // bins per thread in the scan
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  for (int b = t; b < NBINS; b += 256) hist[b] = 0u;
-  if (t == 0) { s_cnt = 0u; s_nb = 0u; s_nreal = 0u; }
-  if (t < MASK_FAST_K) s_sel[t] = 0ull;
-  __syncthreads();
-  unsigned nreal = 0u;
+  uint4* h4 = reinterpret_cast<uint4*>(S.hist + NBINS - BPT * (t + 1));   // bins NBINS-16(t+1) .. NBINS-16t-1
+  unsigned long long prefix = 0ull, pmask = 0ull;
+  unsigned need = 0u, kk = 0u;
+  __syncthreads();                                   // the scratch is clear, the keys are loaded
+  for (int shift = 52;; shift -= 12) {
 #pragma unroll
-  for (int u = 0; u < PER; ++u)
-    if (key[u]) { atomicAdd(&hist[unsigned(key[u] >> SHIFT)], 1u); ++nreal; }
-  atomicAdd(&s_nreal, nreal);
-  __syncthreads();
-  const unsigned kk = min(unsigned(k), s_nreal);
-  // wavefront w scans bins NBINS - 1 - w * NBINS / 4 downwards; lane l takes BPL of them
-  const int top = NBINS - 1 - wave * (NBINS / 4) - lane * BPL;
-  unsigned tot = 0u;
-#pragma unroll
-  for (int j = 0; j < BPL; ++j) tot += hist[top - j];
-  unsigned incl = tot;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const unsigned v = unsigned(__shfl_up(int(incl), off));
-    if (lane >= off) incl += v;
-  }
-  if (lane == 63) s_wt[wave] = incl;
-  __syncthreads();
-  unsigned base = 0u;
-  for (int w = 0; w < wave; ++w) base += s_wt[w];
-  unsigned above = base + incl - tot;
-  if (kk > 0u && above < kk && kk <= base + incl) {
-#pragma unroll
-    for (int j = 0; j < BPL; ++j) {
-      const unsigned cj = hist[top - j];
-      if (above < kk && kk <= above + cj) { s_bin = unsigned(top - j); s_need = kk - above; }
-      above += cj;
-    }
-  }
-  __syncthreads();
-  if (kk > 0u) {
-    const unsigned bin = s_bin, need = s_need, n_above = kk - need;
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      if (!key[u]) continue;
-      const unsigned kb = unsigned(key[u] >> SHIFT);
-      if (kb > bin) s_sel[atomicAdd(&s_cnt, 1u)] = key[u];
-      else if (kb == bin) s_cand[atomicAdd(&s_nb, 1u)] = key[u];
-    }
+    for (int u = 0; u < PER; ++u)
+      if (key[u] && (key[u] & pmask) == prefix) atomicAdd(&S.hist[unsigned(key[u] >> shift) & 0xfffu], 1u);
     __syncthreads();
-    const unsigned nb = s_nb;
-    for (unsigned i = t; i < nb; i += 256) {
-      const unsigned long long x = s_cand[i];
-      unsigned rank = 0u;
-      for (unsigned j = 0; j < nb; ++j) rank += s_cand[j] > x ? 1u : 0u;
-      if (rank < need) s_sel[n_above + rank] = x;
+    unsigned c[BPT];
+#pragma unroll
+    for (int j = 0; j < BPT / 4; ++j) {
+      const uint4 v = h4[j];
+      c[4 * j] = v.x; c[4 * j + 1] = v.y; c[4 * j + 2] = v.z; c[4 * j + 3] = v.w;
+      h4[j] = make_uint4(0u, 0u, 0u, 0u);
     }
-  }
-  __syncthreads();
-  unsigned long long kv = 0ull;
-  if (wave == 0) {
-    kv = lane < int(kk) ? s_sel[lane] : 0ull;
-    for (int size = 2; size <= 64; size <<= 1) {
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        const unsigned lo = unsigned(__shfl_xor(int(unsigned(kv)), stride));
-        const unsigned hi = unsigned(__shfl_xor(int(unsigned(kv >> 32)), stride));
-        const unsigned long long other = (static_cast<unsigned long long>(hi) << 32) | lo;
-        const bool desc = (lane & size) == 0;          // all of it at size 64
-        const bool keep_max = ((lane & stride) == 0) == desc;
-        kv = keep_max ? (other > kv ? other : kv) : (other < kv ? other : kv);
+    unsigned tot = 0u;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) tot += c[j];
+    unsigned incl = tot;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const unsigned v = unsigned(__shfl_up(int(incl), off));
+      if (lane >= off) incl += v;
+    }
+    if (lane == 63) S.wt[wave] = incl;
+    __syncthreads();
+    unsigned above = incl - tot;
+    for (int w = 0; w < wave; ++w) above += S.wt[w];
+    if (shift == 52) {
+      kk = min(unsigned(k), S.wt[0] + S.wt[1] + S.wt[2] + S.wt[3]);
+      need = kk;
+    }
+    if (kk == 0u) break;
+    if (above < need && need <= above + tot) {      // exactly one thread
+#pragma unroll
+      for (int j = BPT - 1; j >= 0; --j) {           // c[BPT-1] is this thread's top bin
+        if (above < need && need <= above + c[j]) {
+          S.bin = unsigned(NBINS - BPT * (t + 1) + j);
+          S.need = need - above;
+          S.nb = c[j];
+        }
+        above += c[j];
       }
     }
+    __syncthreads();
+    prefix |= static_cast<unsigned long long>(S.bin) << shift;
+    pmask |= 0xfffull << shift;
+    need = S.need;
+    if (S.nb <= unsigned(SEL_RANK_MAX) || shift == 4) break;
   }
-  return kv;
+  if (kk > 0u) {
+    unsigned off[PER], pos = 0u;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const bool in = key[u] && (key[u] & pmask) >= prefix;
+      const unsigned long long bal = __ballot(in);
+      off[u] = pos + __builtin_amdgcn_mbcnt_hi(unsigned(bal >> 32), __builtin_amdgcn_mbcnt_lo(unsigned(bal), 0u));
+      pos += unsigned(__popcll(bal));
+    }
+    unsigned base = 0u;
+    if (pos && lane == 0) base = atomicAdd(&S.nc, pos);
+    base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+      if (key[u] && (key[u] & pmask) >= prefix) S.cand[base + off[u]] = key[u];
+    __syncthreads();
+    const unsigned nc = S.nc;
+    if (unsigned(t) < nc) {
+      const unsigned long long x = S.cand[t];
+      unsigned rank = 0u;
+#pragma unroll
+      for (int blk = 0; blk < SEL_CAND / 32; ++blk) {
+        if (unsigned(blk * 32) < nc) {
+#pragma unroll
+          for (int j = 0; j < 32; j += 2) {
+            const ulonglong2 v = *reinterpret_cast<const ulonglong2*>(&S.cand[blk * 32 + j]);
+            rank += (v.x > x ? 1u : 0u) + (v.y > x ? 1u : 0u);
+          }
+        }
+      }
+      if (rank < kk) S.out[rank] = x;
+    }
+  }
+  __syncthreads();
+  const unsigned long long r = (wave == 0 && unsigned(lane) < kk) ? S.out[lane] : 0ull;
+  if (t < SEL_CAND) S.cand[t] = 0ull;               // clear for the next call (its first barrier orders this)
+  if (t == 0) S.nc = 0u;
+  return r;
 }
 
 // Kept clusters of row blockIdx.x for top_k <= MASK_FAST_K (256 threads): the keys of the
@@ -150,14 +191,22 @@ __device__ unsigned long long block_top_keys(const unsigned long long (&key)[MAS
 __global__ __launch_bounds__(256) void k_select_topk(const float* __restrict__ cl, int C, int top_k,
                                                      int32_t* __restrict__ clusters) {
   constexpr int PER = MASK_MAX_CLUSTERS / 256;
+  __shared__ SelScratch sel;
   const int m = blockIdx.x, t = threadIdx.x;
+  float v[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int c = t + 256 * u;
+    v[u] = c < C ? cl[size_t(m) * C + c] : 0.0f;
+  }
+  sel_prepare(sel);
   unsigned long long key[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int c = t + 256 * u;
-    key[u] = c < C ? cluster_key(cl[size_t(m) * C + c], c) : 0ull;
+    key[u] = c < C ? cluster_key(v[u], c) : 0ull;
   }
-  const unsigned long long kv = block_top_keys(key, top_k);
+  const unsigned long long kv = block_top_keys(sel, key, top_k);
   if (t < top_k) clusters[size_t(m) * top_k + t] = int32_t(0xffffffffu - unsigned(kv));
 }
 

@@ -43,9 +43,11 @@ def parse():
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB five times (a plain copy kernel of known "
                          "size, used to scale the FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--workload", choices=("large-vocab", "full-model", "masked-head"), default="large-vocab",
-                    help="large-vocab (default, the headline metric), full-model (the 32-layer decoder verify) or "
-                         "masked-head (the drafter's centroid-masked LM head)")
+    ap.add_argument("--workload", choices=("large-vocab", "full-model", "masked-head", "filtered"),
+                    default="large-vocab",
+                    help="large-vocab (default, the headline metric), full-model (the 32-layer decoder verify), "
+                         "masked-head (the drafter's centroid-masked LM head) or filtered (the large-vocab step "
+                         "with top_k 64 / top_p 0.95 applied alike to the target)")
     ap.add_argument("--rows", type=int, default=1, help="masked-head: hidden states per call")
     ap.add_argument("--traffic-summary", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                                               "k_head_vocab262144_d1536_B1_traffic.md"))
@@ -66,6 +68,8 @@ def main():
         return full_model(args, torch, sv)
     if args.workload == "masked-head":
         return masked_head(args, torch, sv, workloads)
+    if args.workload == "filtered":
+        return filtered(args, torch, sv, workloads)
     root = os.path.dirname(os.path.abspath(__file__))
     sys.path.insert(0, root)
     dev = torch.device("cuda:0")
@@ -305,6 +309,71 @@ def masked_head(args, torch, sv, workloads):
                    "gbs": round(algo / (us * 1e-6) / 1e9, 1),
                    "frac_of_peak": round(algo / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                    "full_head_bytes": V * d * 2, "full_head_us_at_peak": round(V * d * 2 / (HBM_PEAK_GBS * 1e3), 2)},
+    }
+    print(json.dumps(out), flush=True)
+
+
+def filtered(args, torch, sv, workloads):
+    """The large-vocabulary step with the deployment's sampling filters (top_k 64,
+    top_p 0.95, T = 1) applied to the target as the drafter applied them: the LM-head
+    product (logits to the workspace), the top-k of every 4096-logit chunk, the per-row
+    top-k with the top-p cut, and the rule.  B = 1, gamma = 4, V = 262144, d = 1536.
+    q is the drafter's unfiltered distribution of the large-vocab workload (the rule
+    uses q as given; only its values at the drafts and the kept tokens are read), so
+    acceptance is lower than with a filtering drafter; the step's cost does not depend
+    on it.  The value is microseconds per step from HIP events around the timed loop."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, gamma, T, top_k, top_p, V, d = 1, 4, 1.0, 64, 0.95, 262144, 1536
+
+    def to_dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    cases, w = [], None
+    for s_ in range(N_SETS):
+        cs = workloads.lm_head_case(V, d, B, gamma, T, 1.0, 3, w=w, pos0=7 * s_, variant=s_)
+        w = cs.w
+        cases.append(cs)
+    model = sv.lm_head_model(to_dev_bf16(w))
+    sets = [(to_dev_bf16(cs.h), torch.from_numpy(cs.draft.astype(np.int32)).to(dev), to_dev_bf16(cs.q),
+             torch.from_numpy(cs.pos0).to(dev)) for cs in cases]
+    K, Wm = args.steps, args.warmup
+    n_out = torch.empty((K, B), dtype=torch.int32, device=dev)
+    t_out = torch.empty((K, B, gamma + 1), dtype=torch.int32, device=dev)
+    ws = sv.Workspace()
+
+    def step(i, out=None):
+        h, dr, q, p0 = sets[i % N_SETS]
+        return sv.spec_verify_sample_filtered(model, sv.SV_IN_HIDDEN, h, B, gamma, dr, q, T, top_k, top_p,
+                                              cases[0].seed, p0, out=out, ws=ws)
+
+    for i in range(Wm):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(K):
+        step(i, out=(n_out[i], t_out[i]))
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    us = ev0.elapsed_time(ev1) / K * 1e3
+    n_host = n_out.to(torch.int64).cpu()
+    require_valid(n_host, "filtered")
+    committed = int((n_host + 1).sum().item())
+    algo = V * d * 2 + B * (gamma + 1) * d * 2
+    out = {
+        "metric": "filtered verify-step latency (us/step), top_k 64 / top_p 0.95, gamma=4, V=262144",
+        "value": round(us, 2), "unit": "us/step", "n_gpus": 1, "steps": K, "warmup": Wm,
+        "ms_per_step": round(elapsed / K * 1e3, 4), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"large-vocab verify with aligned filters: bf16 LM head V={V} d={d}, B={B}, "
+                               f"gamma={gamma}, T={T}, top_k={top_k}, top_p={top_p}",
+                   "committed_tokens": committed, "verified_tokens_per_s": round(committed / elapsed, 1),
+                   "step_hbm_gbs": round(algo / (us * 1e-6) / 1e9, 1),
+                   "step_frac_of_peak": round(algo / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
     }
     print(json.dumps(out), flush=True)
 

@@ -139,3 +139,36 @@ def test_large_vocab_deployment_filters(large_w, B, T):
     n2, tok2 = run(model, c, B, 4)
     torch.cuda.synchronize()
     assert torch.equal(n, n2) and torch.equal(tok, tok2)
+
+
+@pytest.mark.parametrize("V,top_k", [(10000, 64), (10000, 7), (4096, 64)])
+def test_ties_at_the_top_k_cut(V, top_k):
+    """Integer-valued float32 logits (given as logits input, so both sides see the same
+    numbers) put many exact ties at the top-k cut, within and across chunks.  Drafts come
+    from the tied class at the cut, with q tiny at every token: a draft the lower-index
+    rule keeps is accepted surely, one it drops (p~ = 0) is rejected surely, so n is
+    decided by kept-set membership alone and must equal the oracle's exactly."""
+    B, gamma, T = 64, 4, 4.0
+    rng = np.random.default_rng(V + top_k)
+    l32 = np.floor(rng.standard_normal((B, gamma + 1, V)) * 3.0).astype(np.float32)
+    draft = np.empty((B, gamma), dtype=np.int32)
+    for b in range(B):
+        for i in range(gamma):
+            row = l32[b, i].astype(np.float64)
+            order = np.lexsort((np.arange(V), -row))
+            cut = row[order[top_k - 1]]
+            tied = np.nonzero(row == cut)[0]
+            draft[b, i] = tied[rng.integers(len(tied))]
+    q = np.full((B, gamma, V), 1e-7, dtype=np.float32)
+    pos0 = rng.integers(0, 1000, B).astype(np.int64)
+    n, tok = sv.spec_verify_sample_filtered(sv.logits_model(V), sv.SV_IN_LOGITS, dev(l32), B, gamma, dev(draft),
+                                            dev(q), T, top_k, 1.0, 99, dev(pos0))
+    torch.cuda.synchronize()
+    n, tok = n.cpu().numpy(), tok.cpu().numpy()
+    n0, t0, _ = rules.sample_rule_filtered(l32, draft, q.astype(np.float64), T, top_k, 1.0, 99, pos0)
+    assert n.tolist() == n0.tolist()
+    _, kept, _ = rules.filtered_probs(l32, T, top_k, 1.0)
+    for b in range(B):
+        assert tok[b, :n[b]].tolist() == draft[b, :n[b]].tolist()
+        assert kept[b, n[b], tok[b, n[b]]]
+    log(f"[filtered ties] V={V} top_k={top_k} accepted drafts {int(n.sum())} of {B * gamma}")

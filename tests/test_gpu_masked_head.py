@@ -102,3 +102,22 @@ def test_workspace_and_caller_cluster_scores_agree(full_case):
     b_sel, b_log = sv.draft_masked_logits(head, h, 32, cluster_logits=cl)
     torch.cuda.synchronize()
     assert torch.equal(a_sel, b_sel) and torch.equal(a_log, b_log)
+
+
+@pytest.mark.parametrize("distinct,top_k", [(3, 17), (3, 64), (1, 64), (40, 33)])
+def test_selection_with_ties_is_exact(distinct, top_k):
+    """Cluster tables with only ``distinct`` different rows give scores with many exact
+    ties: the kept clusters must be the top_k of the returned float32 scores, the lower id
+    first on equal scores, in that order (index work: bit-exact).  One distinct row makes
+    every score equal, which takes the selection's refinement down to the id bits."""
+    log(f"[masked] ties distinct={distinct} top_k={top_k}")
+    case = workloads.masked_head_case(V=8192, d=160, C=4096, M=2, top_k=top_k, k=5, variant=distinct)
+    cent = case.centroids[np.arange(4096) % distinct]
+    head = sv.masked_head(dev_bf16(case.w), dev_bf16(cent))
+    cl = torch.empty((2, 4096), dtype=torch.float32, device="cuda")
+    sel, _ = sv.draft_masked_logits(head, dev_bf16(case.h), top_k, cluster_logits=cl)
+    torch.cuda.synchronize()
+    sel, cl = sel.cpu().numpy(), cl.cpu().numpy()
+    for m in range(2):
+        order = np.lexsort((np.arange(4096), -cl[m].astype(np.float64)))
+        assert sel[m].tolist() == order[:top_k].tolist(), f"row {m}"

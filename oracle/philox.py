@@ -25,6 +25,9 @@ Stream layout used by the verify step (a reading; the pages fix no layout):
 * tag 1   -- the Gumbel noise of the correction/bonus sample at ``position``;
              vocab entry v uses block v >> 2, word v & 3:
              U = ((w >> 41) + 0.5) * 2**-23, in (0, 1).
+* tag 2   -- the drafter's Gumbel noise for the draft token at ``position``,
+             laid out as tag 1 (a stream of its own, so drafting and verifying
+             never share random numbers).
 
 Pinned by: bit-exact comparison with ``numpy.random.Philox`` (a library
 implementation of the same generator), see tests/test_oracle_philox.py.
@@ -39,6 +42,7 @@ _MASK64 = (1 << 64) - 1
 
 TAG_ACCEPT = 0
 TAG_GUMBEL = 1
+TAG_DRAFT = 2
 
 
 def philox4x64_10(ctr, key):
@@ -130,14 +134,16 @@ def gumbel_uniform(seed, seq, pos, v):
     return ((w >> np.uint64(41)).astype(np.float64) + 0.5) * 2.0 ** -23
 
 
-def gumbel_uniform_rows(seed, seq, pos, V):
+def gumbel_uniform_rows(seed, seq, pos, V, tag=TAG_GUMBEL):
     """The uniforms of :func:`gumbel_uniform` for entries 0..V-1 of one row per
     sequence: [B, V] float64 from ``seq``, ``pos`` of shape [B].  Each Philox
-    block is computed once and its four words laid out in vocab order."""
+    block is computed once and its four words laid out in vocab order.  ``tag``
+    selects the stream (TAG_GUMBEL for the verify's draw, TAG_DRAFT for the
+    drafter's)."""
     seq = np.asarray(seq, dtype=np.int64).astype(np.uint64)[:, None]
     pos = np.asarray(pos, dtype=np.int64).astype(np.uint64)[:, None]
     nb = (int(V) + 3) // 4
     blocks = np.arange(nb, dtype=np.uint64)[None, :]
-    words = philox4x64_10_np(blocks, pos, seq, TAG_GUMBEL, np.uint64(seed), 0)
+    words = philox4x64_10_np(blocks, pos, seq, np.uint64(tag), np.uint64(seed), 0)
     w = np.stack(words, axis=-1).reshape(seq.shape[0], nb * 4)[:, :int(V)]
     return ((w >> np.uint64(41)).astype(np.float64) + 0.5) * 2.0 ** -23

@@ -230,14 +230,14 @@ def residual_rows(p_rows32, q_rows):
     return r
 
 
-def gumbel_scores(r32, seed, seq, pos):
+def gumbel_scores(r32, seed, seq, pos, tag=philox.TAG_GUMBEL):
     """float32 scores log r_v + G_v (-inf where r_v = 0), one row per sequence.
 
     ``r32``: [B, V]; ``seq``, ``pos``: [B].  G_v = -log(-log U_v) with U_v the
-    Philox uniform of (seed, seq, pos, v).
+    Philox uniform of (seed, seq, pos, v) in stream ``tag``.
     """
     B, V = r32.shape
-    U = philox.gumbel_uniform_rows(seed, seq, pos, V).astype(np.float32)
+    U = philox.gumbel_uniform_rows(seed, seq, pos, V, tag).astype(np.float32)
     G = -np.log(-np.log(U))
     with np.errstate(divide="ignore"):
         s = np.where(r32 > 0, np.log(r32) + G, np.float32(-np.inf)).astype(np.float32)

@@ -392,3 +392,67 @@ def masked_head_case(V=262144, d=1536, C=2048, M=1, top_k=32, k=6, spread=0.01, 
     centroids = to_bf16_bits(cent.astype(np.float32))
     h = normal_bf16((M, d), 1.0, seed, (12, M, variant))
     return MaskedHeadCase(w=w, centroids=centroids, h=h, top_k=top_k)
+
+
+# ----------------------------------------------------------------------------
+# the MTP drafter's draft step
+
+@dataclass
+class DrafterCase:
+    d_model: int
+    hidden: int
+    n_heads: int
+    head_dim: int
+    d_ff: int
+    vocab: int
+    embed: np.ndarray            # bf16 bits [V, D] (cluster-ordered token table)
+    centroids: np.ndarray        # bf16 bits [C, D]
+    pre_proj: np.ndarray         # bf16 bits [H, 2D]
+    layers: list                 # per layer: dict attn_norm, wq, wo, ffn_norm, w_gate, w_up, w_down
+    final_norm: np.ndarray       # bf16 bits [H]
+    post_proj: np.ndarray        # bf16 bits [D, H]
+    kv_k: list                   # per drafter layer: bf16 bits [B, n_heads, max_len, head_dim]
+    kv_v: list
+    length: np.ndarray           # int32 [B]
+    last_token: np.ndarray       # int32 [B]
+    h_target: np.ndarray         # bf16 bits [B, D]
+    seed: int
+    top_k: int
+
+
+def drafter_case(V=262144, D=1536, H=256, n_layers=4, n_heads=4, head_dim=128, d_ff=2048, C=2048, top_k=32,
+                 B=1, length=2048, max_len=None, shared_layers=(0, 0, 0, 1), k=7, variant=0):
+    """A random-init drafter of the E2B shapes (V = 262144, D = 1536, H = 256, four
+    layers) with the masked head's synthetic clustered token table, and the target
+    state it drafts from: cache layers of N(0, 1) keys and values (drafter layer l
+    reads target layer shared_layers[l]), lengths ``length`` (an int or one per row),
+    the last emitted tokens and the target's last hidden states ~ N(0, 1).  Weight
+    scales keep every stage near unit size: pre_proj N(0, 1/(2D)), wq N(0, 1/H),
+    wo N(0, 1/(heads * head_dim)), gate/up N(0, 1/H), down N(0, 1/d_ff), post_proj
+    N(0, 0.2^2), norm gains 1."""
+    seed = input_seed(k)
+    mh = masked_head_case(V=V, d=D, C=C, M=1, top_k=top_k, k=k, variant=variant)
+    HD = n_heads * head_dim
+    one_h = to_bf16_bits(np.ones(H, dtype=np.float32))
+
+    def nb(shape, std, tag):
+        return normal_bf16(shape, std, seed, (20, variant) + tuple(tag))
+
+    layers = []
+    for l in range(n_layers):
+        layers.append(dict(attn_norm=one_h.copy(), wq=nb((HD, H), H ** -0.5, (l, 1)),
+                           wo=nb((H, HD), HD ** -0.5, (l, 2)), ffn_norm=one_h.copy(),
+                           w_gate=nb((d_ff, H), H ** -0.5, (l, 3)), w_up=nb((d_ff, H), H ** -0.5, (l, 4)),
+                           w_down=nb((H, d_ff), d_ff ** -0.5, (l, 5))))
+    max_len = max_len or int(np.max(length)) + 8
+    n_shared = max(shared_layers) + 1
+    ks = [nb((B, n_heads, max_len, head_dim), 1.0, (100 + j, B, max_len)) for j in range(n_shared)]
+    vs = [nb((B, n_heads, max_len, head_dim), 1.0, (200 + j, B, max_len)) for j in range(n_shared)]
+    lens = np.broadcast_to(np.asarray(length, dtype=np.int32), (B,)).copy()
+    rng = np.random.default_rng(seed + 31 * variant + B)
+    return DrafterCase(d_model=D, hidden=H, n_heads=n_heads, head_dim=head_dim, d_ff=d_ff, vocab=V,
+                       embed=mh.w, centroids=mh.centroids, pre_proj=nb((H, 2 * D), (2 * D) ** -0.5, (0, 0)),
+                       layers=layers, final_norm=one_h.copy(), post_proj=nb((D, H), 0.2, (0, 9)),
+                       kv_k=[ks[j] for j in shared_layers], kv_v=[vs[j] for j in shared_layers], length=lens,
+                       last_token=rng.integers(0, V, B).astype(np.int32),
+                       h_target=nb((B, D), 1.0, (300, B)), seed=philox_seed(k + variant), top_k=top_k)

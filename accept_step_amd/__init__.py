@@ -54,6 +54,21 @@ class _SvMaskedHead(ctypes.Structure):
                 ("wdtype", ctypes.c_int32), ("embed", ctypes.c_void_p), ("centroids", ctypes.c_void_p)]
 
 
+class _SvDrafter(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("d_model", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
+                ("embed", ctypes.c_void_p), ("pre_proj", ctypes.c_void_p),
+                ("layers", ctypes.POINTER(ctypes.c_void_p)), ("final_norm", ctypes.c_void_p),
+                ("post_proj", ctypes.c_void_p), ("centroids", ctypes.c_void_p), ("n_clusters", ctypes.c_int32),
+                ("top_k_clusters", ctypes.c_int32)]
+
+
+class _SvSharedKV(ctypes.Structure):
+    _fields_ = [("k", ctypes.POINTER(ctypes.c_void_p)), ("v", ctypes.POINTER(ctypes.c_void_p)),
+                ("max_len", ctypes.c_int32), ("len", ctypes.c_void_p)]
+
+
 class _SvKV(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("max_len", ctypes.c_int32),
                 ("len", ctypes.c_void_p)]
@@ -80,8 +95,10 @@ def library():
     lib.spec_verify_sample_filtered.argtypes = [M, i32, vp, i32, i32, vp, vp, i32, ctypes.c_float, i32,
                                                 ctypes.c_float, ctypes.c_uint64, vp, KV, vp, vp, vp, vp, sz, vp]
     lib.draft_masked_logits.argtypes = [ctypes.POINTER(_SvMaskedHead), vp, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.mtp_draft.argtypes = [ctypes.POINTER(_SvDrafter), ctypes.POINTER(_SvSharedKV), i32, i32, vp, vp,
+                              ctypes.c_float, ctypes.c_uint64, vp, vp, i32, vp, sz, vp]
     for f in (lib.verify_forward, lib.spec_verify_greedy, lib.spec_verify_sample, lib.sv_timing_enable,
-              lib.sv_timing_read, lib.draft_masked_logits, lib.spec_verify_sample_filtered):
+              lib.sv_timing_read, lib.draft_masked_logits, lib.spec_verify_sample_filtered, lib.mtp_draft):
         f.restype = i32
     lib.sv_version.restype = i32
     lib.sv_status_string.restype = ctypes.c_char_p
@@ -335,6 +352,93 @@ def spec_verify_sample_filtered(model, kind, inp, B, gamma, draft, q, temperatur
                    ctypes.byref(kvs) if kvs is not None else None, _ptr(n), _ptr(tok), _ptr(logits_out)),
                   inp.device, ws, stream)
     return n, tok
+
+
+DRAFTER_LAYER_KEYS = ("attn_norm", "wq", "wo", "ffn_norm", "w_gate", "w_up", "w_down")
+
+
+@dataclass
+class Drafter:
+    """The MTP drafter: the C struct plus the tensors and host arrays it points to."""
+    struct: _SvDrafter
+    keep: list = field(default_factory=list)
+
+
+def drafter(embed, pre_proj, layers, final_norm, post_proj, n_heads, head_dim, centroids=None, top_k_clusters=0,
+            rms_eps=1e-5, rope_theta=10000.0):
+    """Drafter from bf16 device tensors: token table [V, D] (shared with the target),
+    pre_proj [H, 2D], ``layers`` a list of dicts with DRAFTER_LAYER_KEYS, final_norm [H],
+    post_proj [D, H]; ``centroids`` [C, D] selects the centroid-masked head."""
+    ts = [embed, pre_proj, final_norm, post_proj] + ([centroids] if centroids is not None else [])
+    for t in ts:
+        _dev_tensor(t, "drafter weight", torch.bfloat16)
+    ptrs = []
+    for L in layers:
+        for k in DRAFTER_LAYER_KEYS:
+            _dev_tensor(L[k], k, torch.bfloat16)
+            ptrs.append(L[k].data_ptr())
+    arr = (ctypes.c_void_p * len(ptrs))(*ptrs)
+    s = _SvDrafter()
+    s.n_layers, s.d_model, s.hidden = len(layers), int(embed.shape[1]), int(pre_proj.shape[0])
+    s.n_heads, s.head_dim = int(n_heads), int(head_dim)
+    s.d_ff, s.vocab = int(layers[0]["w_gate"].shape[0]), int(embed.shape[0])
+    s.rms_eps, s.rope_theta = float(rms_eps), float(rope_theta)
+    s.embed, s.pre_proj, s.final_norm, s.post_proj = (embed.data_ptr(), pre_proj.data_ptr(), final_norm.data_ptr(),
+                                                      post_proj.data_ptr())
+    s.layers = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+    s.centroids = centroids.data_ptr() if centroids is not None else None
+    s.n_clusters = int(centroids.shape[0]) if centroids is not None else 0
+    s.top_k_clusters = int(top_k_clusters)
+    return Drafter(s, ts + [L[k] for L in layers for k in DRAFTER_LAYER_KEYS] + [arr])
+
+
+@dataclass
+class SharedKV:
+    """The drafter's view of the target cache: the C struct plus what it points to."""
+    struct: _SvSharedKV
+    keep: list = field(default_factory=list)
+
+
+def shared_kv(k_layers, v_layers, length):
+    """The target cache layers the drafter reads: bf16 device tensors [B, heads, max_len,
+    head_dim] per drafter layer (may repeat), ``length`` int32 device [B]."""
+    for t in list(k_layers) + list(v_layers):
+        _dev_tensor(t, "shared cache", torch.bfloat16)
+    _dev_tensor(length, "length", torch.int32)
+    ka = (ctypes.c_void_p * len(k_layers))(*[t.data_ptr() for t in k_layers])
+    va = (ctypes.c_void_p * len(v_layers))(*[t.data_ptr() for t in v_layers])
+    s = _SvSharedKV()
+    s.k = ctypes.cast(ka, ctypes.POINTER(ctypes.c_void_p))
+    s.v = ctypes.cast(va, ctypes.POINTER(ctypes.c_void_p))
+    s.max_len = int(k_layers[0].shape[2])
+    s.len = length.data_ptr()
+    return SharedKV(s, list(k_layers) + list(v_layers) + [length, ka, va])
+
+
+def mtp_draft(dr, kv, last_token, h_target, gamma, temperature, seed, q_dtype=None, draft=None, q=None, ws=None,
+              stream=None):
+    """gamma drafter steps (C: mtp_draft).  Returns (draft int32 [B, gamma], q [B, gamma,
+    V] or None at T = 0).  ``q_dtype`` torch.float32 (default) or torch.bfloat16."""
+    lib = library()
+    _dev_tensor(last_token, "last_token", torch.int32)
+    _dev_tensor(h_target, "h_target", torch.bfloat16)
+    B, dev = int(last_token.shape[0]), last_token.device
+    V = dr.struct.vocab
+    if draft is None:
+        draft = torch.empty((B, gamma), dtype=torch.int32, device=dev)
+    _dev_tensor(draft, "draft", torch.int32)
+    qd = SV_F32
+    if float(temperature) > 0.0:
+        dt = q_dtype or (q.dtype if q is not None else torch.float32)
+        if q is None:
+            q = torch.empty((B, gamma, V), dtype=dt, device=dev)
+        _dev_tensor(q, "q", dt)
+        qd = SV_BF16 if dt == torch.bfloat16 else SV_F32
+    _call_with_ws(lib.mtp_draft,
+                  (ctypes.byref(dr.struct), ctypes.byref(kv.struct), B, int(gamma), _ptr(last_token), _ptr(h_target),
+                   float(temperature), ctypes.c_uint64(int(seed)), _ptr(draft), _ptr(q), qd),
+                  dev, ws, stream)
+    return draft, q
 
 
 def timing_enable(mask=0b111):

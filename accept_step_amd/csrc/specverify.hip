@@ -26,6 +26,7 @@
 #include "sv_head.hpp"
 #include "sv_masked.hpp"
 #include "sv_filter.hpp"
+#include "sv_drafter.hpp"
 
 using namespace sv;
 
@@ -1059,6 +1060,189 @@ sv_status spec_verify_sample_filtered(const sv_model* m, sv_input_kind kind, con
   fa.seed = seed; fa.n_accepted = n_accepted; fa.tokens_out = tokens_out;
   TimeScope ts(s, 2);
   hipLaunchKernelGGL(k_filter_tail, dim3(nch, sh.M), dim3(256), 0, s, fa);
+  SV_HIP(hipGetLastError());
+  return SV_OK;
+}
+
+// The MTP drafter's gamma steps.  [X-thread] "Gemma 4's MTP", [MTP-deep-dive] 3.1-3.4.
+sv_status mtp_draft(const sv_drafter* dr, const sv_shared_kv* kv, int32_t B, int32_t gamma,
+                    const int32_t* last_token, const void* h_target, float temperature, uint64_t seed,
+                    int32_t* draft, void* q, sv_dtype q_dtype, void* ws, size_t* ws_bytes, void* stream) {
+  g_err.clear();
+  if (!dr || !kv || !last_token || !h_target || !draft) return fail(SV_ERR_ARG, "NULL argument");
+  if (!dr->embed || !dr->pre_proj || !dr->layers || !dr->final_norm || !dr->post_proj)
+    return fail(SV_ERR_ARG, "drafter weight pointer is NULL");
+  if (!kv->k || !kv->v || !kv->len) return fail(SV_ERR_ARG, "shared cache pointer is NULL");
+  const int nl = dr->n_layers, D = dr->d_model, H = dr->hidden, nh = dr->n_heads, hd = dr->head_dim;
+  const int ff = dr->d_ff, V = dr->vocab, HQ = nh * hd;
+  if (nl < 1 || nl > 64) return fail(SV_ERR_ARG, "n_layers must be in [1, 64]");
+  if (D < 32 || D % 32 || D > 16384) return fail(SV_ERR_SHAPE, "d_model must be a multiple of 32 in [32, 16384]");
+  if (H < 32 || H % 32 || H > 256 * 4 * RMS_VEC) return fail(SV_ERR_SHAPE, "hidden must be a multiple of 32, <= 8192");
+  if (hd != 64 && hd != 128) return fail(SV_ERR_SHAPE, "head_dim must be 64 or 128");
+  if (nh < 1 || HQ > 16384) return fail(SV_ERR_SHAPE, "n_heads * head_dim must be in [64, 16384]");
+  if (ff < 32 || ff % 32) return fail(SV_ERR_SHAPE, "d_ff must be a positive multiple of 32");
+  if (V < 2) return fail(SV_ERR_ARG, "vocab must be >= 2");
+  if (gamma < 1 || gamma > 15) return fail(SV_ERR_ARG, "gamma must be in [1, 15]");
+  if (kv->max_len < 1) return fail(SV_ERR_ARG, "max_len must be >= 1");
+  if (!std::isfinite(temperature) || temperature < 0.0f) return fail(SV_ERR_ARG, "temperature must be finite and >= 0");
+  const bool greedy = temperature == 0.0f;
+  if (!greedy && !q) return fail(SV_ERR_ARG, "q is NULL");
+  if (!greedy && q_dtype != SV_F32 && q_dtype != SV_BF16) return fail(SV_ERR_DTYPE, "q_dtype must be SV_F32 or SV_BF16");
+  if (!greedy && !is_aligned(q, 16)) return fail(SV_ERR_ARG, "q must be 16-byte aligned");
+  const bool masked = dr->centroids != nullptr;
+  const int C = dr->n_clusters, tk = dr->top_k_clusters;
+  int cs = 1, n_scored = V;
+  if (masked) {
+    if (C < 1 || V % C) return fail(SV_ERR_SHAPE, "vocab must be a positive multiple of n_clusters");
+    if (C > MASK_MAX_CLUSTERS) return fail(SV_ERR_UNSUPPORTED, "at most %d clusters", MASK_MAX_CLUSTERS);
+    if (tk < 1 || tk > MASK_FAST_K || tk > C) return fail(SV_ERR_ARG, "top_k_clusters must be in [1, min(64, n_clusters)]");
+    cs = V / C;
+    n_scored = tk * cs;
+  }
+  if (B < 1 || B > (masked ? HEAD_MAX_ROWS : 64)) return fail(SV_ERR_ARG, "B must be in [1, %d]", masked ? HEAD_MAX_ROWS : 64);
+  if (!is_aligned(h_target, 16) || !is_aligned(dr->embed, 16) || (masked && !is_aligned(dr->centroids, 16)))
+    return fail(SV_ERR_ARG, "h_target, embed and centroids must be 16-byte aligned");
+  for (int l = 0; l < nl; ++l) {
+    for (int i = 0; i < 7; ++i)
+      if (!dr->layers[size_t(l) * 7 + i]) return fail(SV_ERR_ARG, "layer %d weight %d is NULL", l, i);
+    if (!kv->k[l] || !kv->v[l]) return fail(SV_ERR_ARG, "shared cache of layer %d is NULL", l);
+  }
+  const int S = std::max(1, std::min((kv->max_len + 255) / 256, ATT_SPLITS_MAX));
+  Bump b;
+  const size_t o_lenq = b.take(size_t(B) * 4), o_inv = b.take(size_t(B) * 4), o_tok = b.take(size_t(B) * 4);
+  const size_t o_cnt = b.take(size_t(B) * nh * 4);
+  const size_t o_attp = b.take(size_t(B) * nh * S * (hd + 2) * 4);
+  const size_t o_z = b.take(size_t(B) * 2 * D * 2);
+  const size_t o_x = b.take(size_t(B) * H * 4), o_delta = b.take(size_t(B) * H * 4);
+  const size_t o_h = b.take(size_t(B) * H * 2), o_f = b.take(size_t(B) * ff * 2);
+  const size_t o_q = b.take(size_t(B) * HQ * 4), o_att = b.take(size_t(B) * HQ * 2);
+  const size_t o_gate = b.take(size_t(B) * ff * 4), o_up = b.take(size_t(B) * ff * 4);
+  const size_t o_gp = b.take(size_t(B) * D * 4), o_g = b.take(size_t(B) * D * 2);
+  const size_t o_log = b.take(size_t(B) * n_scored * 4);
+  const size_t o_cl = masked ? b.take(size_t(B) * C * 4) : 0, o_sel = masked ? b.take(size_t(B) * tk * 4) : 0;
+  Layout L;
+  L.total = b.off;
+  bool query = false;
+  sv_status st = check_ws(ws, ws_bytes, L, &query);
+  if (st || query) return st;
+  DevInfo di;
+  if ((st = dev_info(&di))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int* lenq = at<int>(ws, o_lenq);
+  int* invalid = at<int>(ws, o_inv);
+  int* tok = at<int>(ws, o_tok);
+  unsigned* cnt = at<unsigned>(ws, o_cnt);
+  float* attp = at<float>(ws, o_attp);
+  bf16_t* z = at<bf16_t>(ws, o_z);
+  float* x = at<float>(ws, o_x);
+  float* delta = at<float>(ws, o_delta);
+  bf16_t* h = at<bf16_t>(ws, o_h);
+  bf16_t* f = at<bf16_t>(ws, o_f);
+  float* qb = at<float>(ws, o_q);
+  bf16_t* att = at<bf16_t>(ws, o_att);
+  float* gate = at<float>(ws, o_gate);
+  float* up = at<float>(ws, o_up);
+  float* gp = at<float>(ws, o_gp);
+  bf16_t* g = at<bf16_t>(ws, o_g);
+  float* logits = at<float>(ws, o_log);
+  const int ncnt = B * nh;
+  hipLaunchKernelGGL(k_mtp_prep, dim3((std::max(B, ncnt) + 255) / 256), dim3(256), 0, s, kv->len, last_token, lenq,
+                     invalid, tok, cnt, ncnt, B, kv->max_len, V);
+  if (!greedy && masked) {   // q is written at the scored tokens only
+    const size_t bytes = size_t(B) * gamma * V * (q_dtype == SV_BF16 ? 2 : 4);
+    hipLaunchKernelGGL(k_zero_bytes, dim3(unsigned(std::min<size_t>((bytes / 16 + 255) / 256 + 1, 4096))), dim3(256),
+                       0, s, static_cast<unsigned char*>(q), bytes);
+  }
+  DecArgs da;
+  da.B = B; da.G1 = 1; da.d = H; da.H = nh; da.hd = hd; da.ff = ff; da.V = V; da.max_len = kv->max_len;
+  da.n_layers = nl; da.eps = dr->rms_eps;
+  const float qscale = 1.0f / sqrtf(float(hd)) * 1.4426950408889634f;
+  const bf16_t* hcur = static_cast<const bf16_t*>(h_target);
+  for (int k = 0; k < gamma; ++k) {
+    hipLaunchKernelGGL(k_mtp_join, dim3(B), dim3(256), 0, s, tok, static_cast<const bf16_t*>(dr->embed), hcur, z, D);
+    {
+      const void* w1[1] = {dr->pre_proj};
+      float* o1[1] = {x};
+      const int n1[1] = {H};
+      if ((st = run_product(z, B, 2 * D, 1, w1, o1, n1, di, s))) return st;
+    }
+    const float* pending = nullptr;
+    for (int l = 0; l < nl; ++l) {
+      const void* const* w = dr->layers + size_t(l) * 7;
+      hipLaunchKernelGGL(k_add_rmsnorm, dim3(B), dim3(256), 0, s, x, pending, static_cast<const bf16_t*>(w[0]), h, H,
+                         dr->rms_eps);
+      {
+        const void* w1[1] = {w[1]};
+        float* o1[1] = {qb};
+        const int n1[1] = {HQ};
+        if ((st = run_product(h, B, H, 1, w1, o1, n1, di, s))) return st;
+      }
+      hipLaunchKernelGGL(k_mtp_rope_q, dim3(B, nh), dim3(hd / 2), 0, s, qb, kv->len, k, nh, hd, dr->rope_theta);
+      const bf16_t* kc = static_cast<const bf16_t*>(kv->k[l]);
+      const bf16_t* vc = static_cast<const bf16_t*>(kv->v[l]);
+      if (hd == 128)
+        hipLaunchKernelGGL((k_attn<128, 2>), dim3(S, nh, B), dim3(256), 0, s, qb, kc, vc, lenq, invalid, attp, att,
+                           cnt, da, 0, S, 1, qscale);
+      else
+        hipLaunchKernelGGL((k_attn<64, 2>), dim3(S, nh, B), dim3(256), 0, s, qb, kc, vc, lenq, invalid, attp, att,
+                           cnt, da, 0, S, 1, qscale);
+      {
+        const void* w1[1] = {w[2]};
+        float* o1[1] = {delta};
+        const int n1[1] = {H};
+        if ((st = run_product(att, B, HQ, 1, w1, o1, n1, di, s))) return st;
+      }
+      hipLaunchKernelGGL(k_add_rmsnorm, dim3(B), dim3(256), 0, s, x, delta, static_cast<const bf16_t*>(w[3]), h, H,
+                         dr->rms_eps);
+      {
+        const void* w2[2] = {w[4], w[5]};
+        float* o2[2] = {gate, up};
+        const int n2[2] = {ff, ff};
+        if ((st = run_product(h, B, H, 2, w2, o2, n2, di, s))) return st;
+      }
+      hipLaunchKernelGGL(k_silu_mul, dim3((B * ff + 255) / 256), dim3(256), 0, s, gate, up, f, B * ff);
+      {
+        const void* w1[1] = {w[6]};
+        float* o1[1] = {delta};
+        const int n1[1] = {H};
+        if ((st = run_product(f, B, ff, 1, w1, o1, n1, di, s))) return st;
+      }
+      pending = delta;
+    }
+    hipLaunchKernelGGL(k_add_rmsnorm, dim3(B), dim3(256), 0, s, x, pending, static_cast<const bf16_t*>(dr->final_norm),
+                       h, H, dr->rms_eps);
+    {
+      const void* w1[1] = {dr->post_proj};
+      float* o1[1] = {gp};
+      const int n1[1] = {D};
+      if ((st = run_product(h, B, H, 1, w1, o1, n1, di, s))) return st;
+    }
+    hipLaunchKernelGGL(k_f32_to_bf16, dim3((B * D + 255) / 256), dim3(256), 0, s, gp, g, B * D);
+    hcur = g;
+    int32_t* sel = nullptr;
+    if (masked) {
+      float* cl = at<float>(ws, o_cl);
+      sel = at<int32_t>(ws, o_sel);
+      const void* w1[1] = {dr->centroids};
+      float* o1[1] = {cl};
+      const int n1[1] = {C};
+      if ((st = run_product(g, B, D, 1, w1, o1, n1, di, s))) return st;
+      hipLaunchKernelGGL(k_select_topk, dim3(B), dim3(256), 0, s, cl, C, tk, sel);
+      hipLaunchKernelGGL(k_gather_logits, dim3(tk, (cs + MASK_ROWS_PER_WG - 1) / MASK_ROWS_PER_WG, B), dim3(256),
+                         size_t(D) * 4, s, static_cast<const bf16_t*>(dr->embed), g, sel, D, cs, tk, logits);
+    } else {
+      const void* w1[1] = {dr->embed};
+      float* o1[1] = {logits};
+      const int n1[1] = {V};
+      if ((st = run_product(g, B, D, 1, w1, o1, n1, di, s))) return st;
+    }
+    DraftSampleArgs sa;
+    sa.logits = logits; sa.clusters = sel; sa.n = n_scored; sa.cs = cs; sa.top_k = tk; sa.V = V; sa.gamma = gamma;
+    sa.k = k; sa.inv_t = greedy ? 0.0f : 1.0f / temperature; sa.greedy = greedy ? 1 : 0; sa.seed = seed;
+    sa.len = kv->len; sa.invalid = invalid; sa.draft = draft; sa.tok = tok; sa.q = q;
+    sa.q_bf16 = q_dtype == SV_BF16 ? 1 : 0;
+    hipLaunchKernelGGL(k_mtp_sample, dim3(B), dim3(256), 0, s, sa);
+  }
   SV_HIP(hipGetLastError());
   return SV_OK;
 }

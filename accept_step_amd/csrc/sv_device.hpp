@@ -208,6 +208,7 @@ __device__ __forceinline__ Philox4 philox4x64_10(uint64_t c0, uint64_t c1, uint6
 
 constexpr uint64_t TAG_ACCEPT = 0;
 constexpr uint64_t TAG_GUMBEL = 1;
+constexpr uint64_t TAG_DRAFT = 2;    // the drafter's Gumbel noise (laid out as tag 1)
 
 // Acceptance uniform of the token at absolute position ``pos`` of sequence ``seq``:
 // 24 random bits, exact in float32.

@@ -43,11 +43,12 @@ def parse():
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB five times (a plain copy kernel of known "
                          "size, used to scale the FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--workload", choices=("large-vocab", "full-model", "masked-head", "filtered"),
+    ap.add_argument("--workload", choices=("large-vocab", "full-model", "masked-head", "filtered", "drafter"),
                     default="large-vocab",
                     help="large-vocab (default, the headline metric), full-model (the 32-layer decoder verify), "
-                         "masked-head (the drafter's centroid-masked LM head) or filtered (the large-vocab step "
-                         "with top_k 64 / top_p 0.95 applied alike to the target)")
+                         "masked-head (the drafter's centroid-masked LM head), filtered (the large-vocab step "
+                         "with top_k 64 / top_p 0.95 applied alike to the target) or drafter (the MTP drafter's "
+                         "gamma = 4 draft steps)")
     ap.add_argument("--rows", type=int, default=1, help="masked-head: hidden states per call")
     ap.add_argument("--traffic-summary", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                                               "k_head_vocab262144_d1536_B1_traffic.md"))
@@ -70,6 +71,8 @@ def main():
         return masked_head(args, torch, sv, workloads)
     if args.workload == "filtered":
         return filtered(args, torch, sv, workloads)
+    if args.workload == "drafter":
+        return drafter(args, torch, sv, workloads)
     root = os.path.dirname(os.path.abspath(__file__))
     sys.path.insert(0, root)
     dev = torch.device("cuda:0")
@@ -374,6 +377,72 @@ def filtered(args, torch, sv, workloads):
                    "committed_tokens": committed, "verified_tokens_per_s": round(committed / elapsed, 1),
                    "step_hbm_gbs": round(algo / (us * 1e-6) / 1e9, 1),
                    "step_frac_of_peak": round(algo / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+    print(json.dumps(out), flush=True)
+
+
+def drafter(args, torch, sv, workloads):
+    """The MTP drafter's draft round: gamma = 4 steps for B = ``--rows`` sequences of a
+    random-init drafter of the E2B shapes (V = 262144 shared token table, D = 1536,
+    H = 256, four layers of 4 x 128 query heads reading 2048 cached positions, d_ff 2048,
+    2048 clusters with 32 kept), T = 1, q in bf16.  The value is microseconds per round
+    from HIP events around the timed loop.  Algorithmic bytes per step: the drafter's
+    weights, the cluster table, the kept clusters' token rows and the cached keys and
+    values each layer reads, once."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, gamma, T = args.rows, 4, 1.0
+    c = workloads.drafter_case(B=B, length=2048, max_len=2048)
+
+    def to_dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    layers = [{k: to_dev_bf16(L[k]) for k in sv.DRAFTER_LAYER_KEYS} for L in c.layers]
+    dr = sv.drafter(to_dev_bf16(c.embed), to_dev_bf16(c.pre_proj), layers, to_dev_bf16(c.final_norm),
+                    to_dev_bf16(c.post_proj), c.n_heads, c.head_dim, centroids=to_dev_bf16(c.centroids),
+                    top_k_clusters=c.top_k)
+    cache = {}
+    ks = [cache.setdefault(id(a), to_dev_bf16(a)) for a in c.kv_k]
+    vs = [cache.setdefault(id(a), to_dev_bf16(a)) for a in c.kv_v]
+    kv = sv.shared_kv(ks, vs, torch.from_numpy(c.length.astype(np.int32)).to(dev))
+    tok = torch.from_numpy(c.last_token.astype(np.int32)).to(dev)
+    hid = to_dev_bf16(c.h_target)
+    draft = torch.empty((B, gamma), dtype=torch.int32, device=dev)
+    q = torch.empty((B, gamma, c.vocab), dtype=torch.bfloat16, device=dev)
+    ws = sv.Workspace()
+    K, Wm = args.steps, args.warmup
+    for i in range(Wm):
+        sv.mtp_draft(dr, kv, tok, hid, gamma, T, 1234 + i, draft=draft, q=q, ws=ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(K):
+        sv.mtp_draft(dr, kv, tok, hid, gamma, T, 99 + i, draft=draft, q=q, ws=ws)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    us = ev0.elapsed_time(ev1) / K * 1e3
+    if int((draft < 0).sum().item()):
+        print("bench.py: the drafter returned invalid drafts; no result reported", file=sys.stderr)
+        sys.exit(3)
+    H, D, ff, HQ, L, C, cs = c.hidden, c.d_model, c.d_ff, c.n_heads * c.head_dim, len(c.layers), 2048, c.vocab // 2048
+    weights = 2 * (H * 2 * D + L * (2 * H * HQ + 3 * H * ff) + D * H)
+    head = 2 * (C * D + B * c.top_k * cs * D)
+    kvb = 2 * 2 * L * B * 2048 * HQ
+    algo = weights + head + kvb
+    out = {
+        "metric": "MTP draft round latency (us per gamma=4 steps) and HBM GB/s",
+        "value": round(us, 2), "unit": "us/round", "n_gpus": 1, "steps": K, "warmup": Wm,
+        "ms_per_step": round(elapsed / K * 1e3, 4), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"MTP drafter draft round: V={c.vocab} shared table, D={D}, H={H}, {L} Q-only layers "
+                               f"of {c.n_heads}x{c.head_dim} over 2048 cached positions, d_ff={ff}, masked head "
+                               f"{C} clusters top {c.top_k}, B={B}, gamma={gamma}, T={T}, q bf16",
+                   "us_per_draft_step": round(us / gamma, 2), "algorithmic_bytes_per_step": algo,
+                   "step_gbs": round(algo / (us / gamma * 1e-6) / 1e9, 1),
+                   "step_frac_of_peak": round(algo / (us / gamma * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
     }
     print(json.dumps(out), flush=True)
 

@@ -237,6 +237,70 @@ sv_status draft_masked_logits(const sv_masked_head* head, const void* hidden, in
                               int32_t* clusters, float* logits, float* cluster_logits,
                               void* ws, size_t* ws_bytes, void* stream);
 
+/* The MTP drafter: a small decoder attached to the target ([X-thread] "Gemma 4's MTP":
+ * target activations, KV cache sharing, efficient embedder; [MTP-deep-dive] 3.1-3.4).
+ * Each step joins the embedding of the current token (the target's table, d_model wide)
+ * with a d_model-wide hidden state, [embedding, hidden], projects the pair down to
+ * `hidden` (pre_proj), runs n_layers pre-norm decoder layers whose attention has query
+ * projections only and reads keys and values from the target's cache, applies a final
+ * RMSNorm and projects back up to d_model (post_proj).  The result, rounded to bf16, is
+ * the next step's hidden state and the input of the LM head tied to the token table:
+ * every token is scored, or with centroids given, the centroid-masked head (see
+ * draft_masked_logits) scores the members of the top_k_clusters clusters only.
+ * All weights bf16, row-major [out, in]. */
+typedef struct sv_drafter {
+  int32_t n_layers;            /* 1 .. 64 */
+  int32_t d_model;             /* D: the target's hidden size; multiple of 32 */
+  int32_t hidden;              /* H: the drafter's width; multiple of 32, <= 8192 */
+  int32_t n_heads, head_dim;   /* query heads; head_dim 64 or 128 (that of the shared cache) */
+  int32_t d_ff;                /* multiple of 32 */
+  int32_t vocab;               /* V */
+  float rms_eps, rope_theta;
+  const void* embed;           /* [V, D] token table shared with the target; the tied LM head */
+  const void* pre_proj;        /* [H, 2D] */
+  const void* const* layers;   /* host array, 7 device pointers per layer: attn_norm [H],
+                                  wq [n_heads*head_dim, H], wo [H, n_heads*head_dim],
+                                  ffn_norm [H], w_gate [d_ff, H], w_up [d_ff, H], w_down [H, d_ff] */
+  const void* final_norm;      /* [H] */
+  const void* post_proj;       /* [D, H] */
+  const void* centroids;       /* [n_clusters, D] or NULL (tied head over every token) */
+  int32_t n_clusters;          /* V a multiple of it, <= 4096 (masked head) */
+  int32_t top_k_clusters;      /* 1 .. 64 (masked head) */
+} sv_drafter;
+
+/* The target cache layers the drafter reads: k[l], v[l] (host arrays of n_layers device
+ * pointers; layers may share one) each [B, n_heads, max_len, head_dim] bf16 with one
+ * key/value head per query head; len: device int32 [B], the cached positions [0, len). */
+typedef struct sv_shared_kv {
+  const void* const* k;
+  const void* const* v;
+  int32_t max_len;
+  const int32_t* len;
+} sv_shared_kv;
+
+/* gamma autoregressive drafter steps for B sequences, all on the device.
+ *   last_token: device int32 [B], the last emitted token (position len[b]).
+ *   h_target:   device bf16 [B, D], the target's last hidden state (the one that
+ *               produced last_token's distribution).
+ *   Step k (0-based) processes its token at position len + k (RoPE on the queries;
+ *   every cached position [0, len) is visible, the cache is not written) and drafts
+ *   the token of position len + k + 1.
+ *   temperature > 0: q_k = softmax(logits / T) over the scored tokens (0 elsewhere),
+ *     written to q (device [B, gamma, V], q_dtype SV_F32 or SV_BF16); the draft is
+ *     argmax over scored v of log q_v + G_v with G_v = -log(-log U_v), U_v from
+ *     Philox4x64-10 key (seed, 0), counter (v >> 2, position, b, 2), word v & 3,
+ *     U = ((w >> 41) + 0.5) 2^-23 (the verify's sampling stream layout under its own
+ *     tag), lower id first on ties.  These q feed spec_verify_sample with pos0 = len.
+ *   temperature == 0: the draft is the argmax of the logits (lower id first); q is
+ *     not written and may be NULL.
+ *   draft: out device int32 [B, gamma].  A sequence whose len is outside [1, max_len]
+ *     or whose last_token is no token gets drafts -1 and q rows of zeros.
+ * B: 1 .. 24 with the masked head, 1 .. 64 with the tied head.  Workspace, streams and
+ * errors as above. */
+sv_status mtp_draft(const sv_drafter* dr, const sv_shared_kv* kv, int32_t B, int32_t gamma,
+                    const int32_t* last_token, const void* h_target, float temperature, uint64_t seed,
+                    int32_t* draft, void* q, sv_dtype q_dtype, void* ws, size_t* ws_bytes, void* stream);
+
 /* Library version (major * 10000 + minor * 100 + patch). */
 int32_t sv_version(void);
 

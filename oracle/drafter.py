@@ -135,10 +135,12 @@ def step_hidden(wts: DrafterWeights, kv: SharedKV, tokens, g_bits, k):
     return g
 
 
-def scored_logits(wts: DrafterWeights, g_bits, chunk=16384):
+def scored_logits(wts: DrafterWeights, g_bits, chunk=16384, margin=FLAG):
     """The head over the new hidden states: (vocabulary ids [B, n], float64 logits
     [B, n], selection flags [B]).  Tied head: every token, logits g . embed^T.  Masked
-    head: the members of the top_k_clusters clusters (oracle.masked_head)."""
+    head: the members of the top_k_clusters clusters (oracle.masked_head); a row is
+    flagged when its k-th and (k+1)-th float32 cluster scores are closer than
+    ``margin``."""
     g = _w(g_bits)
     B = g.shape[0]
     V = wts.vocab
@@ -149,8 +151,13 @@ def scored_logits(wts: DrafterWeights, g_bits, chunk=16384):
         return np.broadcast_to(np.arange(V), (B, V)).copy(), out, np.zeros(B, dtype=bool)
     C = wts.centroids.shape[0]
     cs = mh.cluster_size(V, C)
-    sel, flags = mh.select_clusters(mh.cluster_logits(g, _w(wts.centroids)), wts.top_k_clusters)
+    cl = mh.cluster_logits(g, _w(wts.centroids))
+    sel, _ = mh.select_clusters(cl, wts.top_k_clusters)
     k = wts.top_k_clusters
+    flags = np.zeros(B, dtype=bool)
+    if k < C:
+        c32 = np.sort(cl.astype(np.float32).astype(np.float64), axis=1)
+        flags = c32[:, C - k] - c32[:, C - k - 1] < margin
     ids = (sel[:, :, None] * cs + np.arange(cs)[None, None, :]).reshape(B, k * cs)
     out = np.empty((B, k * cs))
     for b in range(B):
@@ -158,10 +165,11 @@ def scored_logits(wts: DrafterWeights, g_bits, chunk=16384):
     return ids, out, flags
 
 
-def sample_step(ids, l64, V, temperature, seed, pos, ok):
+def sample_step(ids, l64, V, temperature, seed, pos, ok, margin=FLAG):
     """Drafts and dense q for one step.  ``ids`` [B, n] scored vocabulary ids,
     ``l64`` their logits, ``pos`` [B] the drafted tokens' absolute positions.
-    Returns (draft int64 [B], q float32 [B, V] or None, flags [B])."""
+    Returns (draft int64 [B], q float32 [B, V] or None, flags [B]): a row is flagged
+    when its two best logits (T = 0) or scores (T > 0) are closer than ``margin``."""
     B = ids.shape[0]
     l32 = np.asarray(l64, dtype=np.float64).astype(np.float32)
     draft = np.full(B, -1, dtype=np.int64)
@@ -174,7 +182,7 @@ def sample_step(ids, l64, V, temperature, seed, pos, ok):
             dense[ids[b]] = l32[b]
             draft[b] = int(np.argmax(dense))
             _, gap = rules.top2(l32[b])
-            flags[b] = l32.shape[1] > 1 and gap < FLAG
+            flags[b] = l32.shape[1] > 1 and gap < margin
         return draft, None, flags
     q = np.zeros((B, V), dtype=np.float32)
     for b in range(B):
@@ -187,16 +195,17 @@ def sample_step(ids, l64, V, temperature, seed, pos, ok):
             continue
         draft[b] = int(np.argmax(sc[b]))
         fin = np.sort(sc[b][np.isfinite(sc[b])].astype(np.float64))
-        flags[b] = fin.size > 1 and fin[-1] - fin[-2] < FLAG
+        flags[b] = fin.size > 1 and fin[-1] - fin[-2] < margin
     return draft, q, flags
 
 
-def draft(wts: DrafterWeights, kv: SharedKV, last_token, h_target_bits, gamma, temperature, seed):
+def draft(wts: DrafterWeights, kv: SharedKV, last_token, h_target_bits, gamma, temperature, seed, margin=FLAG):
     """gamma autoregressive drafter steps.  Returns a dict with ``draft`` int64 [B, gamma]
     (-1 for rows that are not valid), ``q`` float32 [B, gamma, V] (None at T = 0),
     ``g`` the hidden states after every step (bf16 bits [gamma, B, D]), ``logits`` the
     scored (ids, float64 logits) of every step, and ``flags`` [B, gamma] (a decision or
-    a cluster cut within 1e-3 at that step; later steps of that row depend on it)."""
+    a cluster cut within ``margin`` at that step; later steps of that row depend on
+    it).  ``margin`` is one value or one per step."""
     tokens = np.asarray(last_token, dtype=np.int64).copy()
     B = tokens.shape[0]
     ok = valid_rows(kv, tokens, wts.vocab)
@@ -208,8 +217,9 @@ def draft(wts: DrafterWeights, kv: SharedKV, last_token, h_target_bits, gamma, t
     gs, ls = [], []
     for k in range(gamma):
         g = step_hidden(wts, kv, np.where(ok, tokens, 0), g, k)
-        ids, l64, sflag = scored_logits(wts, g)
-        x, q, dflag = sample_step(ids, l64, wts.vocab, temperature, seed, lens + k + 1, ok)
+        mk = float(np.broadcast_to(np.asarray(margin, dtype=np.float64), (gamma,))[k])
+        ids, l64, sflag = scored_logits(wts, g, margin=mk)
+        x, q, dflag = sample_step(ids, l64, wts.vocab, temperature, seed, lens + k + 1, ok, mk)
         drafts[:, k] = np.where(ok, x, -1)
         if qs is not None:
             qs[:, k] = q

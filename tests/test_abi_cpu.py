@@ -159,3 +159,39 @@ def test_filtered_sampling_argument_errors_and_query(lib):
     assert call(V=262144 + 4096, k=32)[0] == 0
     assert call(T=0.0, q=None, pos0=None)[0] == 0             # T == 0 is the greedy rule
     assert call(ws=FAKE, nbytes=need - 1)[0] == 4
+
+
+def test_drafter_argument_errors_and_query(lib):
+    ptrs = (ctypes.c_void_p * 28)(*([0x40000] * 28))
+    kvp = (ctypes.c_void_p * 4)(*([0x50000] * 4))
+
+    def call(nl=4, D=1536, H=256, nh=4, hd=128, ff=2048, V=262144, C=2048, tk=32, cent=True, B=1, gamma=4, T=1.0,
+             q=FAKE, qd=sv.SV_F32, max_len=2048, ws=None, nbytes=0):
+        d = sv._SvDrafter()
+        d.n_layers, d.d_model, d.hidden, d.n_heads, d.head_dim, d.d_ff, d.vocab = nl, D, H, nh, hd, ff, V
+        d.rms_eps, d.rope_theta = 1e-5, 10000.0
+        d.embed = d.pre_proj = d.final_norm = d.post_proj = 0x10000
+        d.layers = ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p))
+        d.centroids = 0x30000 if cent else None
+        d.n_clusters, d.top_k_clusters = C, tk
+        k = sv._SvSharedKV()
+        k.k = k.v = ctypes.cast(kvp, ctypes.POINTER(ctypes.c_void_p))
+        k.max_len, k.len = max_len, 0x60000
+        n = ctypes.c_size_t(nbytes)
+        st = lib.mtp_draft(ctypes.byref(d), ctypes.byref(k), B, gamma, FAKE, FAKE, T, 5, FAKE, q, qd, ws,
+                           ctypes.byref(n), None)
+        return st, n.value
+
+    st, need = call()
+    assert st == 0 and need >= 32 * 128 * 4               # the scored logits live in the workspace
+    st, need_tied = call(cent=False)
+    assert st == 0 and need_tied >= 262144 * 4           # every token scored
+    assert call(T=0.0, q=None)[0] == 0                   # greedy drafting needs no q
+    assert call(q=None)[0] == 1 and call(T=-1.0)[0] == 1 and call(qd=7)[0] == 2
+    assert call(nl=0)[0] == 1 and call(gamma=0)[0] == 1 and call(gamma=16)[0] == 1
+    assert call(D=48)[0] == 3 and call(H=40)[0] == 3 and call(hd=96)[0] == 3 and call(ff=50)[0] == 3
+    assert call(V=262145)[0] == 3                        # not a multiple of the cluster count
+    assert call(C=8192, V=8192 * 32)[0] == 6 and call(tk=65)[0] == 1
+    assert call(B=25)[0] == 1 and call(B=25, cent=False)[0] == 0
+    assert call(max_len=0)[0] == 1
+    assert call(ws=FAKE, nbytes=need - 1)[0] == 4

@@ -97,8 +97,12 @@ def library():
     lib.draft_masked_logits.argtypes = [ctypes.POINTER(_SvMaskedHead), vp, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.mtp_draft.argtypes = [ctypes.POINTER(_SvDrafter), ctypes.POINTER(_SvSharedKV), i32, i32, vp, vp,
                               ctypes.c_float, ctypes.c_uint64, vp, vp, i32, vp, sz, vp]
+    lib.round_pad_drafts.argtypes = [i32, i32, i32, vp, vp, vp, i32, ctypes.c_float, vp, sz, vp]
+    lib.round_update_gamma.argtypes = [i32, vp, vp, i32, i32, vp]
+    lib.round_select_candidates.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp]
     for f in (lib.verify_forward, lib.spec_verify_greedy, lib.spec_verify_sample, lib.sv_timing_enable,
-              lib.sv_timing_read, lib.draft_masked_logits, lib.spec_verify_sample_filtered, lib.mtp_draft):
+              lib.sv_timing_read, lib.draft_masked_logits, lib.spec_verify_sample_filtered, lib.mtp_draft,
+              lib.round_pad_drafts, lib.round_update_gamma, lib.round_select_candidates):
         f.restype = i32
     lib.sv_version.restype = i32
     lib.sv_status_string.restype = ctypes.c_char_p
@@ -439,6 +443,45 @@ def mtp_draft(dr, kv, last_token, h_target, gamma, temperature, seed, q_dtype=No
                    float(temperature), ctypes.c_uint64(int(seed)), _ptr(draft), _ptr(q), qd),
                   dev, ws, stream)
     return draft, q
+
+
+def round_pad_drafts(gamma_b, draft, q=None, tau=0.0, ws=None, stream=None):
+    """Per-sequence draft length by padding (C: round_pad_drafts): ``gamma_b`` int32 [B]
+    (updated in place: clamped, and cut by the confidence rule when tau > 0), ``draft``
+    int32 [B, G] and ``q`` [B, G, V] (float32 or bfloat16, or None) padded in place."""
+    lib = library()
+    _dev_tensor(gamma_b, "gamma_b", torch.int32)
+    _dev_tensor(draft, "draft", torch.int32)
+    _dev_tensor(q, "q")
+    B, G = int(draft.shape[0]), int(draft.shape[1])
+    V = int(q.shape[2]) if q is not None else 1
+    qd = SV_BF16 if (q is not None and q.dtype == torch.bfloat16) else SV_F32
+    _call_with_ws(lib.round_pad_drafts, (B, G, V, _ptr(gamma_b), _ptr(draft), _ptr(q), qd, float(tau)),
+                  draft.device, ws, stream)
+
+
+def round_update_gamma(n_accepted, gamma_b, gamma_min=1, gamma_max=15, stream=None):
+    """Heuristic schedule in place on ``gamma_b`` (C: round_update_gamma)."""
+    _dev_tensor(n_accepted, "n_accepted", torch.int32)
+    _dev_tensor(gamma_b, "gamma_b", torch.int32)
+    _check(library().round_update_gamma(int(gamma_b.shape[0]), _ptr(n_accepted), _ptr(gamma_b), int(gamma_min),
+                                        int(gamma_max), _stream(stream)))
+
+
+def round_select_candidates(n_accepted, tokens, stream=None):
+    """The longest accepted of C candidates per sequence (C: round_select_candidates):
+    ``n_accepted`` int32 [B, C], ``tokens`` int32 [B, C, G1].  Returns (best [B],
+    n [B], tokens [B, G1])."""
+    _dev_tensor(n_accepted, "n_accepted", torch.int32)
+    _dev_tensor(tokens, "tokens", torch.int32)
+    B, C, G1 = (int(x) for x in tokens.shape)
+    dev = tokens.device
+    best = torch.empty(B, dtype=torch.int32, device=dev)
+    n = torch.empty(B, dtype=torch.int32, device=dev)
+    tok = torch.empty((B, G1), dtype=torch.int32, device=dev)
+    _check(library().round_select_candidates(B, C, G1, _ptr(n_accepted), _ptr(tokens), _ptr(best), _ptr(n),
+                                             _ptr(tok), _stream(stream)))
+    return best, n, tok
 
 
 def timing_enable(mask=0b111):

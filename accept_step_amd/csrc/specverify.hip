@@ -27,6 +27,7 @@
 #include "sv_masked.hpp"
 #include "sv_filter.hpp"
 #include "sv_drafter.hpp"
+#include "sv_rounds.hpp"
 
 using namespace sv;
 
@@ -1119,6 +1120,7 @@ sv_status mtp_draft(const sv_drafter* dr, const sv_shared_kv* kv, int32_t B, int
   const size_t o_gate = b.take(size_t(B) * ff * 4), o_up = b.take(size_t(B) * ff * 4);
   const size_t o_gp = b.take(size_t(B) * D * 4), o_g = b.take(size_t(B) * D * 2);
   const size_t o_log = b.take(size_t(B) * n_scored * 4);
+  const size_t o_ss = b.take(size_t(GEMM_MAX_WG) * B * 4);
   const size_t o_cl = masked ? b.take(size_t(B) * C * 4) : 0, o_sel = masked ? b.take(size_t(B) * tk * 4) : 0;
   Layout L;
   L.total = b.off;
@@ -1158,8 +1160,117 @@ sv_status mtp_draft(const sv_drafter* dr, const sv_shared_kv* kv, int32_t B, int
   da.n_layers = nl; da.eps = dr->rms_eps;
   const float qscale = 1.0f / sqrtf(float(hd)) * 1.4426950408889634f;
   const bf16_t* hcur = static_cast<const bf16_t*>(h_target);
-  for (int k = 0; k < gamma; ++k) {
-    hipLaunchKernelGGL(k_mtp_join, dim3(B), dim3(256), 0, s, tok, static_cast<const bf16_t*>(dr->embed), hcur, z, D);
+  // The head over the new hidden state g and the draw of step k.
+  auto draft_head_and_sample = [&](int k) -> sv_status {
+    int32_t* sel = nullptr;
+    if (masked) {
+      float* cl = at<float>(ws, o_cl);
+      sel = at<int32_t>(ws, o_sel);
+      const void* w1[1] = {dr->centroids};
+      float* o1[1] = {cl};
+      const int n1[1] = {C};
+      sv_status r = run_product(g, B, D, 1, w1, o1, n1, di, s);
+      if (r) return r;
+      hipLaunchKernelGGL(k_select_topk, dim3(B), dim3(256), 0, s, cl, C, tk, sel);
+      hipLaunchKernelGGL(k_gather_logits, dim3(tk, (cs + MASK_ROWS_PER_WG - 1) / MASK_ROWS_PER_WG, B), dim3(256),
+                         size_t(D) * 4, s, static_cast<const bf16_t*>(dr->embed), g, sel, D, cs, tk, logits);
+    } else {
+      const void* w1[1] = {dr->embed};
+      float* o1[1] = {logits};
+      const int n1[1] = {V};
+      sv_status r = run_product(g, B, D, 1, w1, o1, n1, di, s);
+      if (r) return r;
+    }
+    DraftSampleArgs sa;
+    sa.logits = logits; sa.clusters = sel; sa.n = n_scored; sa.cs = cs; sa.top_k = tk; sa.V = V; sa.gamma = gamma;
+    sa.k = k; sa.inv_t = greedy ? 0.0f : 1.0f / temperature; sa.greedy = greedy ? 1 : 0; sa.seed = seed;
+    sa.len = kv->len; sa.invalid = invalid; sa.draft = draft; sa.tok = tok; sa.q = q;
+    sa.q_bf16 = q_dtype == SV_BF16 ? 1 : 0;
+    hipLaunchKernelGGL(k_mtp_sample, dim3(B), dim3(256), 0, s, sa);
+    return SV_OK;
+  };
+  // Every product on the k-split kernel: the RMSNorms happen while the next product
+  // stages its rows from the float32 residual stream (sums of squares left by the
+  // products that add into it), as in the target decoder.
+  bool fused = B <= ACC_MAX_ROWS;
+  {
+    const int nH[1] = {H}, nQ[1] = {HQ}, nF[2] = {ff, ff}, nD[1] = {D};
+    fused = fused && plan_head(B, 2 * D, nH, 1, di).ok && plan_head(B, H, nQ, 1, di).ok &&
+            plan_head(B, HQ, nH, 1, di).ok && plan_head(B, H, nF, 2, di).ok && plan_head(B, ff, nH, 1, di).ok &&
+            plan_head(B, H, nD, 1, di).ok;
+  }
+  float* ss = at<float>(ws, o_ss);
+  for (int k = 0; k < gamma && fused; ++k) {
+    hipLaunchKernelGGL(k_mtp_join, dim3(B), dim3(256), 0, s, tok, static_cast<const bf16_t*>(dr->embed), hcur, z, D,
+                       x, H);
+    ProductFuse fr;
+    fr.residual = true;
+    fr.ss_out = ss;
+    int parts = 1;
+    {
+      const void* w1[1] = {dr->pre_proj};
+      float* o1[1] = {x};
+      const int n1[1] = {H};
+      if ((st = run_product_fused(z, B, 2 * D, 1, w1, o1, n1, fr, &parts, di, s))) return st;
+    }
+    for (int l = 0; l < nl; ++l) {
+      const void* const* w = dr->layers + size_t(l) * 7;
+      ProductFuse fn;
+      fn.Xf = x; fn.ss_in = ss; fn.ss_parts = parts; fn.eps = dr->rms_eps;
+      fn.norm_w = static_cast<const bf16_t*>(w[0]);
+      {
+        const void* w1[1] = {w[1]};
+        float* o1[1] = {qb};
+        const int n1[1] = {HQ};
+        if ((st = run_product_fused(nullptr, B, H, 1, w1, o1, n1, fn, nullptr, di, s))) return st;
+      }
+      hipLaunchKernelGGL(k_mtp_rope_q, dim3(B, nh), dim3(hd / 2), 0, s, qb, kv->len, k, nh, hd, dr->rope_theta);
+      const bf16_t* kc = static_cast<const bf16_t*>(kv->k[l]);
+      const bf16_t* vc = static_cast<const bf16_t*>(kv->v[l]);
+      if (hd == 128)
+        hipLaunchKernelGGL((k_attn<128, 2>), dim3(S, nh, B), dim3(256), 0, s, qb, kc, vc, lenq, invalid, attp, att,
+                           cnt, da, 0, S, 1, qscale);
+      else
+        hipLaunchKernelGGL((k_attn<64, 2>), dim3(S, nh, B), dim3(256), 0, s, qb, kc, vc, lenq, invalid, attp, att,
+                           cnt, da, 0, S, 1, qscale);
+      {
+        const void* w1[1] = {w[2]};
+        float* o1[1] = {x};
+        const int n1[1] = {H};
+        if ((st = run_product_fused(att, B, HQ, 1, w1, o1, n1, fr, &parts, di, s))) return st;
+      }
+      fn.ss_parts = parts;
+      fn.norm_w = static_cast<const bf16_t*>(w[3]);
+      {
+        const void* w2[2] = {w[4], w[5]};
+        float* o2[2] = {gate, up};
+        const int n2[2] = {ff, ff};
+        if ((st = run_product_fused(nullptr, B, H, 2, w2, o2, n2, fn, nullptr, di, s))) return st;
+      }
+      hipLaunchKernelGGL(k_silu_mul, dim3((B * ff + 255) / 256), dim3(256), 0, s, gate, up, f, B * ff);
+      {
+        const void* w1[1] = {w[6]};
+        float* o1[1] = {x};
+        const int n1[1] = {H};
+        if ((st = run_product_fused(f, B, ff, 1, w1, o1, n1, fr, &parts, di, s))) return st;
+      }
+    }
+    {
+      ProductFuse fn;
+      fn.Xf = x; fn.ss_in = ss; fn.ss_parts = parts; fn.eps = dr->rms_eps;
+      fn.norm_w = static_cast<const bf16_t*>(dr->final_norm);
+      const void* w1[1] = {dr->post_proj};
+      float* o1[1] = {gp};
+      const int n1[1] = {D};
+      if ((st = run_product_fused(nullptr, B, H, 1, w1, o1, n1, fn, nullptr, di, s))) return st;
+    }
+    hipLaunchKernelGGL(k_f32_to_bf16, dim3((B * D + 255) / 256), dim3(256), 0, s, gp, g, B * D);
+    hcur = g;
+    if ((st = draft_head_and_sample(k))) return st;
+  }
+  for (int k = 0; k < gamma && !fused; ++k) {
+    hipLaunchKernelGGL(k_mtp_join, dim3(B), dim3(256), 0, s, tok, static_cast<const bf16_t*>(dr->embed), hcur, z, D,
+                       nullptr, H);
     {
       const void* w1[1] = {dr->pre_proj};
       float* o1[1] = {x};
@@ -1219,30 +1330,60 @@ sv_status mtp_draft(const sv_drafter* dr, const sv_shared_kv* kv, int32_t B, int
     }
     hipLaunchKernelGGL(k_f32_to_bf16, dim3((B * D + 255) / 256), dim3(256), 0, s, gp, g, B * D);
     hcur = g;
-    int32_t* sel = nullptr;
-    if (masked) {
-      float* cl = at<float>(ws, o_cl);
-      sel = at<int32_t>(ws, o_sel);
-      const void* w1[1] = {dr->centroids};
-      float* o1[1] = {cl};
-      const int n1[1] = {C};
-      if ((st = run_product(g, B, D, 1, w1, o1, n1, di, s))) return st;
-      hipLaunchKernelGGL(k_select_topk, dim3(B), dim3(256), 0, s, cl, C, tk, sel);
-      hipLaunchKernelGGL(k_gather_logits, dim3(tk, (cs + MASK_ROWS_PER_WG - 1) / MASK_ROWS_PER_WG, B), dim3(256),
-                         size_t(D) * 4, s, static_cast<const bf16_t*>(dr->embed), g, sel, D, cs, tk, logits);
-    } else {
-      const void* w1[1] = {dr->embed};
-      float* o1[1] = {logits};
-      const int n1[1] = {V};
-      if ((st = run_product(g, B, D, 1, w1, o1, n1, di, s))) return st;
-    }
-    DraftSampleArgs sa;
-    sa.logits = logits; sa.clusters = sel; sa.n = n_scored; sa.cs = cs; sa.top_k = tk; sa.V = V; sa.gamma = gamma;
-    sa.k = k; sa.inv_t = greedy ? 0.0f : 1.0f / temperature; sa.greedy = greedy ? 1 : 0; sa.seed = seed;
-    sa.len = kv->len; sa.invalid = invalid; sa.draft = draft; sa.tok = tok; sa.q = q;
-    sa.q_bf16 = q_dtype == SV_BF16 ? 1 : 0;
-    hipLaunchKernelGGL(k_mtp_sample, dim3(B), dim3(256), 0, s, sa);
+    if ((st = draft_head_and_sample(k))) return st;
   }
+  SV_HIP(hipGetLastError());
+  return SV_OK;
+}
+// Round policies.  [MTP-drafters] 6, [MTP-deep-dive] 5.1, [Self-spec] 3.3.
+sv_status round_pad_drafts(int32_t B, int32_t G, int32_t V, int32_t* gamma_b, int32_t* draft, void* q,
+                           sv_dtype q_dtype, float tau, void* ws, size_t* ws_bytes, void* stream) {
+  g_err.clear();
+  if (B < 1 || G < 1 || G > 15 || V < 1) return fail(SV_ERR_ARG, "need B >= 1, 1 <= G <= 15, V >= 1");
+  if (!gamma_b || !draft) return fail(SV_ERR_ARG, "gamma_b and draft must not be NULL");
+  if (!std::isfinite(tau) || tau < 0.0f) return fail(SV_ERR_ARG, "tau must be finite and >= 0");
+  if (tau > 0.0f && !q) return fail(SV_ERR_ARG, "the confidence cut needs q");
+  if (q && q_dtype != SV_F32 && q_dtype != SV_BF16) return fail(SV_ERR_DTYPE, "q_dtype must be SV_F32 or SV_BF16");
+  Bump b;
+  const size_t o_conf = tau > 0.0f ? b.take(size_t(B) * G * 4) : 0;
+  Layout L;
+  L.total = tau > 0.0f ? b.off : 0;
+  bool query = false;
+  sv_status st = check_ws(ws, ws_bytes, L, &query);
+  if (st || query) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int qb = q_dtype == SV_BF16 ? 1 : 0;
+  float* conf = nullptr;
+  if (tau > 0.0f) {
+    conf = at<float>(ws, o_conf);
+    hipLaunchKernelGGL(k_round_conf, dim3(G, B), dim3(256), 0, s, q, qb, G, V, conf);
+  }
+  hipLaunchKernelGGL(k_round_cut, dim3((B + 255) / 256), dim3(256), 0, s, gamma_b, conf, tau, B, G);
+  hipLaunchKernelGGL(k_round_pad, dim3(G, B, q ? (V + 4095) / 4096 : 1), dim3(256), 0, s, gamma_b, draft, q, qb, G, V);
+  SV_HIP(hipGetLastError());
+  return SV_OK;
+}
+
+sv_status round_update_gamma(int32_t B, const int32_t* n_accepted, int32_t* gamma_b, int32_t gamma_min,
+                             int32_t gamma_max, void* stream) {
+  g_err.clear();
+  if (B < 1 || !n_accepted || !gamma_b) return fail(SV_ERR_ARG, "need B >= 1 and non-NULL arrays");
+  if (gamma_min < 1 || gamma_min > gamma_max || gamma_max > 15)
+    return fail(SV_ERR_ARG, "need 1 <= gamma_min <= gamma_max <= 15");
+  hipLaunchKernelGGL(k_round_schedule, dim3((B + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     n_accepted, gamma_b, B, gamma_min, gamma_max);
+  SV_HIP(hipGetLastError());
+  return SV_OK;
+}
+
+sv_status round_select_candidates(int32_t B, int32_t C, int32_t G1, const int32_t* n_accepted,
+                                  const int32_t* tokens, int32_t* best, int32_t* n_out, int32_t* tokens_out,
+                                  void* stream) {
+  g_err.clear();
+  if (B < 1 || C < 1 || G1 < 2 || G1 > 16) return fail(SV_ERR_ARG, "need B >= 1, C >= 1, 2 <= G1 <= 16");
+  if (!n_accepted || !tokens || !n_out || !tokens_out) return fail(SV_ERR_ARG, "NULL array");
+  hipLaunchKernelGGL(k_round_select, dim3((B + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     n_accepted, tokens, B, C, G1, best, n_out, tokens_out);
   SV_HIP(hipGetLastError());
   return SV_OK;
 }

@@ -35,10 +35,14 @@ __global__ __launch_bounds__(256) void k_mtp_prep(const int* __restrict__ len, c
 }
 
 // z[b] = [embed[tok[b]], g[b]] in bf16, [B, 2D].  One workgroup per row, 16 bytes
-// per thread and step.
+// per thread and step.  Also clears the row's residual stream x[b, 0..H) when x is given
+// (the down-projection of the joined input then adds into it).
 __global__ __launch_bounds__(256) void k_mtp_join(const int* __restrict__ tok, const bf16_t* __restrict__ embed,
-                                                  const bf16_t* __restrict__ g, bf16_t* __restrict__ z, int D) {
+                                                  const bf16_t* __restrict__ g, bf16_t* __restrict__ z, int D,
+                                                  float* __restrict__ x, int H) {
   const int b = blockIdx.x;
+  if (x)
+    for (int i = threadIdx.x; i < H; i += blockDim.x) x[size_t(b) * H + i] = 0.0f;
   const int n8 = D / 8;
   const u32x4* e = reinterpret_cast<const u32x4*>(embed + size_t(tok[b]) * D);
   const u32x4* h = reinterpret_cast<const u32x4*>(g + size_t(b) * D);
@@ -108,49 +112,111 @@ __device__ __forceinline__ int draft_token_id(const DraftSampleArgs& a, int b, i
   return a.clusters[size_t(b) * a.top_k + c] * a.cs + (j - c * a.cs);
 }
 
-// One workgroup (256 threads) per sequence over its n scored tokens.  T > 0:
-// m = max l, Z = sum exp((l - m) / T), q_j = exp((l_j - m) / T) / Z stored at its token
-// id; the draft is the largest (log q_j + G, lower id) with G the Gumbel noise of Philox
-// stream tag 2 at position len + k + 1.  T = 0: the largest (l, lower id).
+// Online (max, sum of exp((l - max) / T)) merge.
+__device__ __forceinline__ void softmax_merge(float& m, float& s, float m2, float s2, float inv_t) {
+  const float mm = fmaxf(m, m2);
+  if (mm == -INFINITY) return;
+  s = (m == -INFINITY ? 0.0f : s * expf((m - mm) * inv_t)) + (m2 == -INFINITY ? 0.0f : s2 * expf((m2 - mm) * inv_t));
+  m = mm;
+}
+
+// One workgroup (256 threads) per sequence over its n scored tokens, four consecutive
+// entries per thread and step (one Philox block per four vocabulary ids when they are
+// consecutive and aligned, as the members of a cluster are).  T > 0: one pass for
+// m = max l and Z = sum exp((l - m) / T) (online per thread, merged over the block),
+// one for q_j = exp((l_j - m) / T) / Z, stored at its token id, and the draft = the
+// largest (log q_j + G, lower id) with G the Gumbel noise of Philox stream tag 2 at
+// position len + k + 1.  T = 0: the largest (l, lower id).
 __global__ __launch_bounds__(256) void k_mtp_sample(DraftSampleArgs a) {
   const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  __shared__ float s_red[4];
+  __shared__ float s_m[4], s_s[4];
   __shared__ unsigned long long s_key[4];
   const float* l = a.logits + size_t(b) * a.n;
   const bool bad = a.invalid[b] != 0;
   const size_t qrow = (size_t(b) * a.gamma + a.k) * a.V;
+  const int ng = (a.n + 3) / 4;
+  auto load4 = [&](int g, float (&v)[4]) {
+    const int j0 = 4 * g;
+    if (j0 + 4 <= a.n && (a.n & 3) == 0) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(l + j0);
+      v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = j0 + e < a.n ? l[j0 + e] : -INFINITY;
+    }
+  };
   unsigned long long key = 0ull;
   if (a.greedy) {
-    for (int j = t; j < a.n; j += 256) key = max_u64(key, win_key(false, l[j], draft_token_id(a, b, j)));
+    for (int g = t; g < ng; g += 256) {
+      float v[4];
+      load4(g, v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * g + e < a.n) key = max_u64(key, win_key(false, v[e], draft_token_id(a, b, 4 * g + e)));
+    }
   } else {
-    float m = -INFINITY;
-    for (int j = t; j < a.n; j += 256) m = fmaxf(m, l[j]);
-    m = wave_max_rl(m);
-    if (lane == 0) s_red[wave] = m;
+    float m = -INFINITY, sum = 0.0f;
+    for (int g = t; g < ng; g += 256) {
+      float v[4];
+      load4(g, v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) softmax_merge(m, sum, v[e], 1.0f, a.inv_t);
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(sum, o);
+      softmax_merge(m, sum, m2, s2, a.inv_t);
+    }
+    if (lane == 0) { s_m[wave] = m; s_s[wave] = sum; }
     __syncthreads();
-    m = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-    __syncthreads();
-    float z = 0.0f;
-    for (int j = t; j < a.n; j += 256) z += expf((l[j] - m) * a.inv_t);
-    z = wave_sum_rl(z);
-    if (lane == 0) s_red[wave] = z;
-    __syncthreads();
-    z = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
-    const float inv_z = 1.0f / z;
+    m = s_m[0];
+    sum = s_s[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) softmax_merge(m, sum, s_m[w], s_s[w], a.inv_t);
+    const float inv_z = 1.0f / sum;
     const uint64_t pos = uint64_t(int64_t(a.len[b]) + a.k + 1);
-    for (int j = t; j < a.n; j += 256) {
-      const int id = draft_token_id(a, b, j);
-      const float qv = bad ? 0.0f : expf((l[j] - m) * a.inv_t) * inv_z;
-      if (a.q_bf16) reinterpret_cast<bf16_t*>(a.q)[qrow + id] = f32_to_bf16(qv);
-      else reinterpret_cast<float*>(a.q)[qrow + id] = qv;
-      if (qv > 0.0f) {
-        float G[4];
-        draft_gumbel4(a.seed, b, pos, id & ~3, G);
+    for (int g = t; g < ng; g += 256) {
+      float v[4];
+      load4(g, v);
+      int id[4];
+      float qv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        id[e] = 4 * g + e < a.n ? draft_token_id(a, b, 4 * g + e) : -1;
+        qv[e] = (bad || id[e] < 0) ? 0.0f : expf((v[e] - m) * a.inv_t) * inv_z;
+      }
+      const bool run = id[3] == id[0] + 3 && ((qrow + size_t(id[0])) & 3) == 0;   // four ids, aligned store
+      if (run) {
+        if (a.q_bf16) {
+          uint2 w;
+          w.x = uint32_t(f32_to_bf16(qv[0])) | (uint32_t(f32_to_bf16(qv[1])) << 16);
+          w.y = uint32_t(f32_to_bf16(qv[2])) | (uint32_t(f32_to_bf16(qv[3])) << 16);
+          *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(a.q) + qrow + id[0]) = w;
+        } else {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.q) + qrow + id[0]) = f32x4{qv[0], qv[1], qv[2], qv[3]};
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (id[e] < 0) continue;
+          if (a.q_bf16) reinterpret_cast<bf16_t*>(a.q)[qrow + id[e]] = f32_to_bf16(qv[e]);
+          else reinterpret_cast<float*>(a.q)[qrow + id[e]] = qv[e];
+        }
+      }
+      float G[4];
+      int blk = -1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (!(qv[e] > 0.0f)) continue;
+        if ((id[e] >> 2) != blk) {
+          blk = id[e] >> 2;
+          draft_gumbel4(a.seed, b, pos, id[e] & ~3, G);
+        }
         float gv = G[0];
 #pragma unroll
-        for (int e = 1; e < 4; ++e)
-          if ((id & 3) == e) gv = G[e];
-        key = max_u64(key, win_key(false, logf(qv) + gv, id));
+        for (int u = 1; u < 4; ++u)
+          if ((id[e] & 3) == u) gv = G[u];
+        key = max_u64(key, win_key(false, logf(qv[e]) + gv, id[e]));
       }
     }
   }

@@ -43,12 +43,14 @@ def parse():
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB five times (a plain copy kernel of known "
                          "size, used to scale the FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--workload", choices=("large-vocab", "full-model", "masked-head", "filtered", "drafter"),
+    ap.add_argument("--workload", choices=("large-vocab", "full-model", "masked-head", "filtered", "drafter",
+                                           "rounds"),
                     default="large-vocab",
                     help="large-vocab (default, the headline metric), full-model (the 32-layer decoder verify), "
                          "masked-head (the drafter's centroid-masked LM head), filtered (the large-vocab step "
-                         "with top_k 64 / top_p 0.95 applied alike to the target) or drafter (the MTP drafter's "
-                         "gamma = 4 draft steps)")
+                         "with top_k 64 / top_p 0.95 applied alike to the target), drafter (the MTP drafter's "
+                         "gamma = 4 draft steps) or rounds (draft, per-sequence padding, verify and the heuristic "
+                         "schedule, on the device)")
     ap.add_argument("--rows", type=int, default=1, help="masked-head: hidden states per call")
     ap.add_argument("--traffic-summary", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                                               "k_head_vocab262144_d1536_B1_traffic.md"))
@@ -73,6 +75,8 @@ def main():
         return filtered(args, torch, sv, workloads)
     if args.workload == "drafter":
         return drafter(args, torch, sv, workloads)
+    if args.workload == "rounds":
+        return rounds_bench(args, torch, sv, workloads)
     root = os.path.dirname(os.path.abspath(__file__))
     sys.path.insert(0, root)
     dev = torch.device("cuda:0")
@@ -443,6 +447,82 @@ def drafter(args, torch, sv, workloads):
                    "us_per_draft_step": round(us / gamma, 2), "algorithmic_bytes_per_step": algo,
                    "step_gbs": round(algo / (us / gamma * 1e-6) / 1e9, 1),
                    "step_frac_of_peak": round(algo / (us / gamma * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+    print(json.dumps(out), flush=True)
+
+
+def rounds_bench(args, torch, sv, workloads):
+    """Device-resident speculative rounds at gamma_max = 6 for B = ``--rows`` sequences:
+    the MTP drafter of the drafter workload drafts 6 tokens, round_pad_drafts pads each
+    sequence to its current draft length, the large-vocab verify (V = 262144, d = 1536,
+    T = 1) checks the padded batch, and round_update_gamma applies the heuristic
+    schedule; nothing returns to the host between rounds.  The target's hidden states
+    are synthetic (no trained target), so acceptance is low and the schedule mostly
+    shortens the drafts; the timing of the round's kernels is what this measures."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, G, T = args.rows, 6, 1.0
+    c = workloads.drafter_case(B=B, length=2048, max_len=2048)
+
+    def to_dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    emb = to_dev_bf16(c.embed)
+    layers = [{k: to_dev_bf16(L[k]) for k in sv.DRAFTER_LAYER_KEYS} for L in c.layers]
+    dr = sv.drafter(emb, to_dev_bf16(c.pre_proj), layers, to_dev_bf16(c.final_norm), to_dev_bf16(c.post_proj),
+                    c.n_heads, c.head_dim, centroids=to_dev_bf16(c.centroids), top_k_clusters=c.top_k)
+    cache = {}
+    ks = [cache.setdefault(id(a), to_dev_bf16(a)) for a in c.kv_k]
+    vs = [cache.setdefault(id(a), to_dev_bf16(a)) for a in c.kv_v]
+    kv = sv.shared_kv(ks, vs, torch.from_numpy(c.length.astype(np.int32)).to(dev))
+    model = sv.lm_head_model(emb)                  # the target's head: the shared token table
+    tok = torch.from_numpy(c.last_token.astype(np.int32)).to(dev)
+    hid = to_dev_bf16(c.h_target)
+    hs = [to_dev_bf16(workloads.normal_bf16((B, G + 1, c.d_model), 1.0, 55, (i, B))) for i in range(4)]
+    pos0 = torch.from_numpy(c.length.astype(np.int64)).to(dev)
+    gamma_b = torch.full((B,), 4, dtype=torch.int32, device=dev)
+    draft = torch.empty((B, G), dtype=torch.int32, device=dev)
+    q = torch.empty((B, G, c.vocab), dtype=torch.bfloat16, device=dev)
+    K, Wm = args.steps, args.warmup
+    n_all = torch.empty((K, B), dtype=torch.int32, device=dev)
+    g_all = torch.empty((K, B), dtype=torch.int32, device=dev)
+    t_out = torch.empty((B, G + 1), dtype=torch.int32, device=dev)
+    wsd, wsp, wsv = sv.Workspace(), sv.Workspace(), sv.Workspace()
+
+    def one(i, n_out):
+        sv.mtp_draft(dr, kv, tok, hid, G, T, 7 + i, draft=draft, q=q, ws=wsd)
+        sv.round_pad_drafts(gamma_b, draft, q, ws=wsp)
+        sv.spec_verify_sample(model, sv.SV_IN_HIDDEN, hs[i % 4], B, G, draft, q, T, 99, pos0, out=(n_out, t_out),
+                              ws=wsv)
+        sv.round_update_gamma(n_out, gamma_b, 1, G)
+
+    for i in range(Wm):
+        one(i, n_all[0])
+    torch.cuda.synchronize()
+    gamma_b.fill_(4)
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(K):
+        g_all[i].copy_(gamma_b)
+        one(i, n_all[i])
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    us = ev0.elapsed_time(ev1) / K * 1e3
+    n_host = n_all.to(torch.int64).cpu()
+    require_valid(n_host, "rounds")
+    committed = int((n_host + 1).sum().item())
+    out = {
+        "metric": "device-resident speculative round latency (us per round: draft, pad, verify, schedule)",
+        "value": round(us, 2), "unit": "us/round", "n_gpus": 1, "steps": K, "warmup": Wm,
+        "ms_per_step": round(elapsed / K * 1e3, 4), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"rounds: MTP drafter (masked head) drafting {G}, per-sequence padding, large-vocab "
+                               f"verify V={c.vocab} d={c.d_model} T={T}, heuristic schedule in [1, {G}], B={B}",
+                   "committed_tokens": committed, "mean_gamma": round(float(g_all.float().mean().item()), 3),
+                   "note": "synthetic target hidden states: acceptance is not meaningful"},
     }
     print(json.dumps(out), flush=True)
 

@@ -301,6 +301,40 @@ sv_status mtp_draft(const sv_drafter* dr, const sv_shared_kv* kv, int32_t B, int
                     const int32_t* last_token, const void* h_target, float temperature, uint64_t seed,
                     int32_t* draft, void* q, sv_dtype q_dtype, void* ws, size_t* ws_bytes, void* stream);
 
+/* Round policies around the verify step ([MTP-drafters] 6: adaptive draft length and
+ * several draft candidates; [MTP-deep-dive] 5.1: the heuristic schedule; [Self-spec] 3.3:
+ * each sequence keeps what it accepted).  All arrays are device arrays; each call
+ * enqueues small kernels on the stream.
+ *
+ * round_pad_drafts: per-sequence draft length within a batch of G = gamma_max slots.
+ *   gamma_b (int32 [B], in/out) is clamped to [1, G]; with tau > 0 it is cut further to
+ *   the leading steps whose largest q is >= tau (at least 1; needs q).  Then the slots
+ *   i >= gamma_b[b] are padded: draft[b, i] = -1, q[b, i, :] = 0 (q may be NULL for the
+ *   greedy rule).  Verifying the padded batch gives each sequence exactly what verifying
+ *   it alone with gamma_b drafts gives: the rule rejects at slot gamma_b at the latest
+ *   (no id matches -1) and the residual there is max(0, p - 0) = p, the bonus
+ *   distribution, drawn at the bonus's position.  ws as elsewhere (B * G floats when
+ *   tau > 0, else none). */
+sv_status round_pad_drafts(int32_t B, int32_t G, int32_t V, int32_t* gamma_b, int32_t* draft, void* q,
+                           sv_dtype q_dtype, float tau, void* ws, size_t* ws_bytes, void* stream);
+
+/* round_update_gamma: the heuristic schedule.  gamma_b[b] (in/out) becomes gamma_b + 2
+ * when every draft was accepted (n_accepted[b] >= gamma_b[b]), else gamma_b - 1, kept
+ * within [gamma_min, gamma_max]; a sequence with n_accepted < 0 (invalid) keeps it.
+ * 1 <= gamma_min <= gamma_max <= 15. */
+sv_status round_update_gamma(int32_t B, const int32_t* n_accepted, int32_t* gamma_b, int32_t gamma_min,
+                             int32_t gamma_max, void* stream);
+
+/* round_select_candidates: C draft candidates per sequence verified as rows b * C + c
+ * of one batch (greedy rule); keeps the one with the most accepted drafts, the lower
+ * index on ties: best[b] (may be NULL), n_out[b], tokens_out[b, 0..G1).  Under the
+ * greedy rule every candidate's accepted prefix is the target's own argmax chain, so
+ * the choice is lossless; under the sampling rule it is not (the best of several
+ * independent verifications is biased), and this call is not meant for it. */
+sv_status round_select_candidates(int32_t B, int32_t C, int32_t G1, const int32_t* n_accepted,
+                                  const int32_t* tokens, int32_t* best, int32_t* n_out, int32_t* tokens_out,
+                                  void* stream);
+
 /* Library version (major * 10000 + minor * 100 + patch). */
 int32_t sv_version(void);
 

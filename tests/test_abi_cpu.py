@@ -195,3 +195,20 @@ def test_drafter_argument_errors_and_query(lib):
     assert call(B=25)[0] == 1 and call(B=25, cent=False)[0] == 0
     assert call(max_len=0)[0] == 1
     assert call(ws=FAKE, nbytes=need - 1)[0] == 4
+
+
+def test_round_policy_argument_errors(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.round_pad_drafts(0, 4, 10, FAKE, FAKE, None, sv.SV_F32, 0.0, None, ctypes.byref(n), None) == 1
+    assert lib.round_pad_drafts(2, 16, 10, FAKE, FAKE, None, sv.SV_F32, 0.0, None, ctypes.byref(n), None) == 1
+    assert lib.round_pad_drafts(2, 4, 10, None, FAKE, None, sv.SV_F32, 0.0, None, ctypes.byref(n), None) == 1
+    assert lib.round_pad_drafts(2, 4, 10, FAKE, FAKE, None, sv.SV_F32, 0.5, None, ctypes.byref(n), None) == 1
+    assert lib.round_pad_drafts(2, 4, 10, FAKE, FAKE, FAKE, 9, 0.0, None, ctypes.byref(n), None) == 2
+    assert lib.round_pad_drafts(2, 4, 10, FAKE, FAKE, FAKE, sv.SV_F32, 0.5, None, ctypes.byref(n), None) == 0
+    assert n.value >= 2 * 4 * 4                          # the per-step confidences
+    assert lib.round_update_gamma(2, FAKE, FAKE, 0, 4, None) == 1
+    assert lib.round_update_gamma(2, FAKE, FAKE, 5, 4, None) == 1
+    assert lib.round_update_gamma(2, None, FAKE, 1, 4, None) == 1
+    assert lib.round_select_candidates(2, 3, 1, FAKE, FAKE, None, FAKE, FAKE, None) == 1
+    assert lib.round_select_candidates(2, 0, 5, FAKE, FAKE, None, FAKE, FAKE, None) == 1
+    assert lib.round_select_candidates(2, 3, 5, FAKE, None, None, FAKE, FAKE, None) == 1

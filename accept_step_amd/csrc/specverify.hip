@@ -969,9 +969,10 @@ sv_status draft_masked_logits(const sv_masked_head* head, const void* hidden, in
   if (!is_aligned(hidden, 16) || !is_aligned(head->embed, 16) || !is_aligned(head->centroids, 16))
     return fail(SV_ERR_ARG, "hidden, embed and centroids must be 16-byte aligned");
   Bump b;
+  b.take(CNT_BYTES);                 // the counter block other calls keep state in: never scratch
   const size_t cl_off = cluster_logits ? 0 : b.take(size_t(M) * C * 4);
   Layout L;
-  L.total = b.off;
+  L.total = cluster_logits ? 0 : b.off;
   bool query = false;
   sv_status st = check_ws(ws, ws_bytes, L, &query);
   if (st || query) return st;
@@ -1110,6 +1111,7 @@ sv_status mtp_draft(const sv_drafter* dr, const sv_shared_kv* kv, int32_t B, int
   }
   const int S = std::max(1, std::min((kv->max_len + 255) / 256, ATT_SPLITS_MAX));
   Bump b;
+  b.take(CNT_BYTES);                 // the counter block other calls keep state in: never scratch
   const size_t o_lenq = b.take(size_t(B) * 4), o_inv = b.take(size_t(B) * 4), o_tok = b.take(size_t(B) * 4);
   const size_t o_cnt = b.take(size_t(B) * nh * 4);
   const size_t o_attp = b.take(size_t(B) * nh * S * (hd + 2) * 4);
@@ -1345,6 +1347,7 @@ sv_status round_pad_drafts(int32_t B, int32_t G, int32_t V, int32_t* gamma_b, in
   if (tau > 0.0f && !q) return fail(SV_ERR_ARG, "the confidence cut needs q");
   if (q && q_dtype != SV_F32 && q_dtype != SV_BF16) return fail(SV_ERR_DTYPE, "q_dtype must be SV_F32 or SV_BF16");
   Bump b;
+  b.take(CNT_BYTES);                 // the counter block other calls keep state in: never scratch
   const size_t o_conf = tau > 0.0f ? b.take(size_t(B) * G * 4) : 0;
   Layout L;
   L.total = tau > 0.0f ? b.off : 0;

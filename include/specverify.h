@@ -31,7 +31,9 @@
  *             (all of it) once before its first use; the library keeps state in
  *             it between calls (counters through which the workgroups of one
  *             launch hand work to each other, and a launch epoch), so keep using
- *             the same workspace or zero-fill a new one.  The sampling step with a
+ *             the same workspace or zero-fill a new one.  Every entry point keeps its
+ *             scratch out of the first 4096 bytes (that state), so one workspace
+ *             serves all of them.  The sampling step with a
  *             small batch runs as one kernel whose workgroups wait for each other
  *             (bounded): if the device cannot run them all at once for about a
  *             second (e.g. it is shared), the step reports every sequence invalid

@@ -127,3 +127,38 @@ def test_padded_verify_equals_per_sequence_verify(T):
         assert n[b] == n1[0] and tok[b, :g + 1].tolist() == t1[0].tolist() and np.all(tok[b, g + 1:] == -1), b
         compare_decisions(n[b:b + 1], tok[b:b + 1, :g + 1], r[0], r[1], r[2], f"seq {b}")
     log(f"[rounds] n={n.tolist()} gamma_b={gamma_b.tolist()}")
+
+
+def test_one_workspace_serves_every_entry_point():
+    """Calls that only need scratch (masked head, drafter, padding) share the default
+    workspace with the verify calls that keep counters and a launch epoch in it: the
+    filtered verify (one-shot tickets) and the fused sampling verify (epoch) still give
+    the results of a fresh workspace afterwards."""
+    rng = np.random.default_rng(13)
+    V, d, B, G = 4096, 256, 2, 4
+    w = workloads.to_bf16_bits((rng.standard_normal((V, d)) * 0.3).astype(np.float32))
+    h = workloads.to_bf16_bits(rng.standard_normal((B, G + 1, d)).astype(np.float32))
+    from tests.gpu_util import dev_bf16
+    model = sv.lm_head_model(dev_bf16(w))
+    draft = dev(rng.integers(0, V, (B, G)).astype(np.int32))
+    qn = rng.random((B, G, V)).astype(np.float32)
+    q = dev(qn / qn.sum(-1, keepdims=True))
+    pos0 = dev(np.array([5, 9], np.int64))
+
+    def verify_pair(ws):
+        a = sv.spec_verify_sample_filtered(model, sv.SV_IN_HIDDEN, dev_bf16(h), B, G, draft, q, 1.0, 64, 0.95, 3,
+                                           pos0, ws=ws)
+        b = sv.spec_verify_sample(model, sv.SV_IN_HIDDEN, dev_bf16(h), B, G, draft, q, 1.0, 3, pos0, ws=ws)
+        torch.cuda.synchronize()
+        return [t.cpu().numpy() for t in a + b]
+
+    fresh = verify_pair(sv.Workspace())
+    # scratch-only calls on the default workspace, then the verifies on it
+    head = sv.masked_head(dev_bf16(w), dev_bf16(w[::64].copy()))
+    sv.draft_masked_logits(head, dev_bf16(h[:, 0].copy()), 8)
+    gb = dev(np.array([4, 2], np.int32))
+    sv.round_pad_drafts(gb, dev(np.zeros((B, G), np.int32)), q.clone(), tau=1e-9)
+    shared = verify_pair(None)
+    for x, y in zip(fresh, shared):
+        assert np.array_equal(x, y)
+    assert np.all((shared[0] >= 0) & (shared[0] <= G))

@@ -388,29 +388,53 @@ __global__ __launch_bounds__(256) void k_attn(const float* __restrict__ q, const
     store_coherent(po + 2 + d, ov);
   }
   if (!last_workgroup(cnt + (size_t(b) * a.H + h) * NQ + qg, unsigned(S))) return;
-  // last workgroup of the head: combine the S partials of every query (all loads of an
-  // output issued together)
+  // last workgroup of the head: combine the S partials of every query.  The split
+  // weights f_u = 2^(m_u - M) and the total l of a query are the same for all of its
+  // dimensions: one thread per query computes them into LDS.  Every thread issues the
+  // value loads of all its outputs first (they do not depend on the weights), so the
+  // merge waits for one round of loads, then sums in split order.
   const float* pb = part + ((size_t(b) * a.H + h) * S * G1 + q0) * psz;
-  for (int t = threadIdx.x; t < nq * HD; t += blockDim.x) {
+  __shared__ float s_f[ATT_SPLITS_CAP][ATT_QMAX], s_l[ATT_QMAX];
+  constexpr int EPT = (ATT_QMAX * HD + 255) / 256;   // outputs per thread at most (256 threads)
+  float pv[EPT][ATT_SPLITS_CAP];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int t = min(int(threadIdx.x) + e * int(blockDim.x), nq * HD - 1);
     const int i = t / HD, d = t - i * HD;
-    float pm[ATT_SPLITS_CAP], pl[ATT_SPLITS_CAP], pv[ATT_SPLITS_CAP];
+#pragma unroll
+    for (int u = 0; u < ATT_SPLITS_CAP; ++u) pv[e][u] = pb[(size_t(min(u, S - 1)) * G1 + i) * psz + 2 + d];
+  }
+  if (threadIdx.x < nq) {
+    const int i = threadIdx.x;
+    float pm[ATT_SPLITS_CAP], pl[ATT_SPLITS_CAP];
 #pragma unroll
     for (int u = 0; u < ATT_SPLITS_CAP; ++u) {
       const float* pp = pb + (size_t(min(u, S - 1)) * G1 + i) * psz;
       pm[u] = pp[0];
       pl[u] = pp[1];
-      pv[u] = pp[2 + d];
     }
     float M = -INFINITY;
 #pragma unroll
     for (int u = 0; u < ATT_SPLITS_CAP; ++u) M = fmaxf(M, pm[u]);
-    float l = 0.0f, ov = 0.0f;
+    float l = 0.0f;
 #pragma unroll
     for (int u = 0; u < ATT_SPLITS_CAP; ++u) {
       const float f = (u >= S || M == -INFINITY || pm[u] == -INFINITY) ? 0.0f : exp2f(pm[u] - M);
       l += pl[u] * f;
-      ov += pv[u] * f;
+      s_f[u][i] = f;
     }
+    s_l[i] = l;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int t = int(threadIdx.x) + e * int(blockDim.x);
+    if (t >= nq * HD) continue;
+    const int i = t / HD, d = t - i * HD;
+    float ov = 0.0f;
+#pragma unroll
+    for (int u = 0; u < ATT_SPLITS_CAP; ++u) ov += pv[e][u] * s_f[u][i];
+    const float l = s_l[i];
     outp[size_t(i) * a.H * HD + d] = f32_to_bf16(l > 0.0f ? ov / l : 0.0f);
   }
 }

@@ -1123,6 +1123,7 @@ sv_status mtp_draft(const sv_drafter* dr, const sv_shared_kv* kv, int32_t B, int
   const size_t o_gp = b.take(size_t(B) * D * 4), o_g = b.take(size_t(B) * D * 2);
   const size_t o_log = b.take(size_t(B) * n_scored * 4);
   const size_t o_ss = b.take(size_t(GEMM_MAX_WG) * B * 4);
+  const size_t o_rope = b.take(size_t(gamma) * B * (hd / 2) * sizeof(float2));
   const size_t o_cl = masked ? b.take(size_t(B) * C * 4) : 0, o_sel = masked ? b.take(size_t(B) * tk * 4) : 0;
   Layout L;
   L.total = b.off;
@@ -1163,7 +1164,7 @@ sv_status mtp_draft(const sv_drafter* dr, const sv_shared_kv* kv, int32_t B, int
   const float qscale = 1.0f / sqrtf(float(hd)) * 1.4426950408889634f;
   const bf16_t* hcur = static_cast<const bf16_t*>(h_target);
   // The head over the new hidden state g and the draw of step k.
-  auto draft_head_and_sample = [&](int k) -> sv_status {
+  auto draft_head_and_sample = [&](int k, bool feed) -> sv_status {
     int32_t* sel = nullptr;
     if (masked) {
       float* cl = at<float>(ws, o_cl);
@@ -1188,6 +1189,11 @@ sv_status mtp_draft(const sv_drafter* dr, const sv_shared_kv* kv, int32_t B, int
     sa.k = k; sa.inv_t = greedy ? 0.0f : 1.0f / temperature; sa.greedy = greedy ? 1 : 0; sa.seed = seed;
     sa.len = kv->len; sa.invalid = invalid; sa.draft = draft; sa.tok = tok; sa.q = q;
     sa.q_bf16 = q_dtype == SV_BF16 ? 1 : 0;
+    sa.z = feed ? z : nullptr;
+    sa.embed = static_cast<const bf16_t*>(dr->embed);
+    sa.x_res = x;
+    sa.D = D;
+    sa.H = H;
     hipLaunchKernelGGL(k_mtp_sample, dim3(B), dim3(256), 0, s, sa);
     return SV_OK;
   };
@@ -1202,9 +1208,18 @@ sv_status mtp_draft(const sv_drafter* dr, const sv_shared_kv* kv, int32_t B, int
             plan_head(B, H, nD, 1, di).ok;
   }
   float* ss = at<float>(ws, o_ss);
+  float2* rope = at<float2>(ws, o_rope);
+  if (fused) {
+    const int nrope = gamma * B * (hd / 2);
+    hipLaunchKernelGGL(k_mtp_rope_table, dim3(std::min((nrope + 255) / 256, 1024)), dim3(256), 0, s, kv->len, rope, B,
+                       gamma, hd, dr->rope_theta);
+  }
   for (int k = 0; k < gamma && fused; ++k) {
-    hipLaunchKernelGGL(k_mtp_join, dim3(B), dim3(256), 0, s, tok, static_cast<const bf16_t*>(dr->embed), hcur, z, D,
-                       x, H);
+    // step 0 joins [embedding, target hidden state]; later steps' inputs were written by
+    // the previous step's conversion (hidden half) and draw (embedding half, cleared x)
+    if (k == 0)
+      hipLaunchKernelGGL(k_mtp_join, dim3(B), dim3(256), 0, s, tok, static_cast<const bf16_t*>(dr->embed), hcur, z, D,
+                         x, H);
     ProductFuse fr;
     fr.residual = true;
     fr.ss_out = ss;
@@ -1226,15 +1241,15 @@ sv_status mtp_draft(const sv_drafter* dr, const sv_shared_kv* kv, int32_t B, int
         const int n1[1] = {HQ};
         if ((st = run_product_fused(nullptr, B, H, 1, w1, o1, n1, fn, nullptr, di, s))) return st;
       }
-      hipLaunchKernelGGL(k_mtp_rope_q, dim3(B, nh), dim3(hd / 2), 0, s, qb, kv->len, k, nh, hd, dr->rope_theta);
       const bf16_t* kc = static_cast<const bf16_t*>(kv->k[l]);
       const bf16_t* vc = static_cast<const bf16_t*>(kv->v[l]);
+      const float2* rk = rope + size_t(k) * B * (hd / 2);   // RoPE applied while the queries are staged
       if (hd == 128)
         hipLaunchKernelGGL((k_attn<128, 2>), dim3(S, nh, B), dim3(256), 0, s, qb, kc, vc, lenq, invalid, attp, att,
-                           cnt, da, 0, S, 1, qscale);
+                           cnt, da, 0, S, 1, qscale, rk);
       else
         hipLaunchKernelGGL((k_attn<64, 2>), dim3(S, nh, B), dim3(256), 0, s, qb, kc, vc, lenq, invalid, attp, att,
-                           cnt, da, 0, S, 1, qscale);
+                           cnt, da, 0, S, 1, qscale, rk);
       {
         const void* w1[1] = {w[2]};
         float* o1[1] = {x};
@@ -1266,9 +1281,10 @@ sv_status mtp_draft(const sv_drafter* dr, const sv_shared_kv* kv, int32_t B, int
       const int n1[1] = {D};
       if ((st = run_product_fused(nullptr, B, H, 1, w1, o1, n1, fn, nullptr, di, s))) return st;
     }
-    hipLaunchKernelGGL(k_f32_to_bf16, dim3((B * D + 255) / 256), dim3(256), 0, s, gp, g, B * D);
+    hipLaunchKernelGGL(k_f32_to_bf16, dim3((B * D + 255) / 256), dim3(256), 0, s, gp, g, B * D,
+                       k + 1 < gamma ? z : nullptr, D);
     hcur = g;
-    if ((st = draft_head_and_sample(k))) return st;
+    if ((st = draft_head_and_sample(k, k + 1 < gamma))) return st;
   }
   for (int k = 0; k < gamma && !fused; ++k) {
     hipLaunchKernelGGL(k_mtp_join, dim3(B), dim3(256), 0, s, tok, static_cast<const bf16_t*>(dr->embed), hcur, z, D,
@@ -1330,9 +1346,9 @@ sv_status mtp_draft(const sv_drafter* dr, const sv_shared_kv* kv, int32_t B, int
       const int n1[1] = {D};
       if ((st = run_product(h, B, H, 1, w1, o1, n1, di, s))) return st;
     }
-    hipLaunchKernelGGL(k_f32_to_bf16, dim3((B * D + 255) / 256), dim3(256), 0, s, gp, g, B * D);
+    hipLaunchKernelGGL(k_f32_to_bf16, dim3((B * D + 255) / 256), dim3(256), 0, s, gp, g, B * D, nullptr, D);
     hcur = g;
-    if ((st = draft_head_and_sample(k))) return st;
+    if ((st = draft_head_and_sample(k, false))) return st;
   }
   SV_HIP(hipGetLastError());
   return SV_OK;

@@ -183,7 +183,9 @@ __device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) 
 //   * P V on the vector ALU: the value rows are read fully coalesced (a lane holds 8
 //     dimensions of one key per load) and each lane accumulates its 8 dimensions over
 //     its keys for every query; the weights and rescale factors go through LDS.
-// All loads of a block are issued before the first product.  The four wavefronts are
+// With ``rope`` given ([row][HD/2] cos/sin of each query row's position), the queries
+// are rotated as they are staged.  All loads of a block are issued before the first
+// product.  The four wavefronts are
 // merged in LDS and the workgroup's partial (max, sum, unnormalised output) per query
 // is stored for the other workgroups of the head; the last of the S workgroups to
 // finish combines them and writes the bf16 attention output.  cnt[(b*H + h)*NQ + g]
@@ -193,7 +195,8 @@ __global__ __launch_bounds__(256) void k_attn(const float* __restrict__ q, const
                                               const bf16_t* __restrict__ vc, const int* __restrict__ len,
                                               const int* __restrict__ invalid, float* __restrict__ part,
                                               bf16_t* __restrict__ out, unsigned* __restrict__ cnt, DecArgs a,
-                                              int layer, int S, int NQ, float qscale) {
+                                              int layer, int S, int NQ, float qscale,
+                                              const float2* __restrict__ rope = nullptr) {
   static_assert(HD == 64 || HD == 128, "head_dim 64 or 128");
   static_assert(QG >= 1 && QG <= ATT_QMAX, "query slots per workgroup");
   constexpr int KC = HD / 32;          // 32-dimension chunks of a score product
@@ -241,9 +244,26 @@ __global__ __launch_bounds__(256) void k_attn(const float* __restrict__ q, const
   const int qd0 = 32 * qkc + 8 * (ql >> 4);
   f32x4 x0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f}, x1 = x0;
   if (tq < KC * 64) {
-    const float* qr = q + (size_t(b) * G1 + q0 + min(qm, nq - 1)) * a.H * HD + size_t(h) * HD + qd0;
+    const int qrow = int(b) * G1 + q0 + min(qm, nq - 1);
+    const float* qr = q + size_t(qrow) * a.H * HD + size_t(h) * HD + qd0;
     x0 = *reinterpret_cast<const f32x4*>(qr);
     x1 = *reinterpret_cast<const f32x4*>(qr + 4);
+    if (rope) {
+      // RoPE on the query (rotate-half: dimension j pairs with j + HD/2), from the
+      // cos/sin table of the row's position: the lane's 8 dimensions and their partners.
+      constexpr int HALF = HD / 2;
+      const bool lo_half = qd0 < HALF;
+      const float* pr = qr + (lo_half ? HALF : -HALF);
+      const f32x4 p0 = *reinterpret_cast<const f32x4*>(pr), p1 = *reinterpret_cast<const f32x4*>(pr + 4);
+      const float2* cs = rope + size_t(qrow) * HALF + (lo_half ? qd0 : qd0 - HALF);
+      const float sg = lo_half ? -1.0f : 1.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float2 c0 = cs[e], c1 = cs[4 + e];
+        x0[e] = x0[e] * c0.x + sg * (p0[e] * c0.y);
+        x1[e] = x1[e] * c1.x + sg * (p1[e] * c1.y);
+      }
+    }
   }
   int k0 = s * ATT_KEYS + wave * 64;
   load_block(k0);

@@ -68,9 +68,27 @@ __global__ void k_mtp_rope_q(float* __restrict__ q, const int* __restrict__ len,
   r[j + half] = x2 * c + x1 * s;
 }
 
-__global__ __launch_bounds__(256) void k_f32_to_bf16(const float* __restrict__ x, bf16_t* __restrict__ y, int n) {
+// cos/sin of the queries of every step, once per call: tab[(k * B + b) * hd/2 + j] for
+// position len[b] + k (angle in float64, as k_mtp_rope_q).  Grid-stride.
+__global__ __launch_bounds__(256) void k_mtp_rope_table(const int* __restrict__ len, float2* __restrict__ tab, int B,
+                                                        int gamma, int hd, float theta) {
+  const int half = hd / 2, n = gamma * B * half;
+  for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < n; t += gridDim.x * blockDim.x) {
+    const int j = t % half, kb = t / half, b = kb % B, k = kb / B;
+    const double ang = (double(len[b]) + double(k)) * exp(-(2.0 * j / double(hd)) * log(double(theta)));
+    tab[t] = make_float2(float(cos(ang)), float(sin(ang)));
+  }
+}
+
+// y = bf16(x) for the new hidden state [B, D]; with z given, also into the hidden half of
+// the next step's joined input z[b, D..2D).
+__global__ __launch_bounds__(256) void k_f32_to_bf16(const float* __restrict__ x, bf16_t* __restrict__ y, int n,
+                                                     bf16_t* __restrict__ z = nullptr, int D = 0) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t < n) y[t] = f32_to_bf16(x[t]);
+  if (t >= n) return;
+  const bf16_t v = f32_to_bf16(x[t]);
+  y[t] = v;
+  if (z) z[size_t(t / D) * 2 * D + D + t % D] = v;
 }
 
 // Zero fill of n bytes at p (16-byte aligned): 16 bytes per thread and step, then the
@@ -104,6 +122,12 @@ struct DraftSampleArgs {
   int* tok;                   // [B] the next step's token
   void* q;                    // [B, gamma, V] or null (greedy)
   int q_bf16;
+  // with z given: the next step's joined input gets the drafted token's embedding
+  // (z[b, 0..D) = embed[x]) and the residual stream x_res[b, 0..H) is cleared
+  bf16_t* z;
+  const bf16_t* embed;
+  float* x_res;
+  int D, H;
 };
 
 __device__ __forceinline__ int draft_token_id(const DraftSampleArgs& a, int b, int j) {
@@ -223,12 +247,20 @@ __global__ __launch_bounds__(256) void k_mtp_sample(DraftSampleArgs a) {
   key = wave_allmax_u64(key);
   if (lane == 0) s_key[wave] = key;
   __syncthreads();
+  __shared__ int s_x;
   if (t == 0) {
     const unsigned long long kb = max_u64(max_u64(s_key[0], s_key[1]), max_u64(s_key[2], s_key[3]));
     const int x = (bad || !kb) ? -1 : win_index(kb);
     a.draft[size_t(b) * a.gamma + a.k] = x;
     a.tok[b] = x < 0 ? 0 : x;
+    s_x = x < 0 ? 0 : x;
   }
+  if (!a.z) return;
+  __syncthreads();
+  const u32x4* e = reinterpret_cast<const u32x4*>(a.embed + size_t(s_x) * a.D);
+  u32x4* o = reinterpret_cast<u32x4*>(a.z + size_t(b) * 2 * a.D);
+  for (int i = t; i < a.D / 8; i += 256) o[i] = e[i];
+  for (int i = t; i < a.H; i += 256) a.x_res[size_t(b) * a.H + i] = 0.0f;
 }
 
 }  // namespace sv

@@ -189,6 +189,17 @@ struct Philox4 {
   uint64_t w[4];
 };
 
+// 128-bit product a * b from four 32 x 32 -> 64-bit partial products (schoolbook; each
+// step is one v_mad_u64_u32, and no intermediate sum overflows 64 bits).
+__device__ __forceinline__ void mul_wide64(uint64_t a, uint64_t b, uint64_t& hi, uint64_t& lo) {
+  const uint32_t al = uint32_t(a), ah = uint32_t(a >> 32), bl = uint32_t(b), bh = uint32_t(b >> 32);
+  const uint64_t p0 = uint64_t(al) * bl;
+  const uint64_t t = uint64_t(al) * bh + (p0 >> 32);
+  const uint64_t u = uint64_t(ah) * bl + uint32_t(t);
+  lo = (u << 32) | uint32_t(p0);
+  hi = uint64_t(ah) * bh + ((t >> 32) + (u >> 32));
+}
+
 __device__ __forceinline__ Philox4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3,
                                                  uint64_t k0, uint64_t k1) {
   const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
@@ -196,8 +207,9 @@ __device__ __forceinline__ Philox4 philox4x64_10(uint64_t c0, uint64_t c1, uint6
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     if (r) { k0 += W0; k1 += W1; }
-    uint64_t hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
-    uint64_t hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
+    uint64_t hi0, lo0, hi1, lo1;
+    mul_wide64(M0, c0, hi0, lo0);
+    mul_wide64(M1, c2, hi1, lo1);
     uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
     c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
   }

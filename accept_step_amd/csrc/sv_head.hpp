@@ -351,12 +351,17 @@ __device__ __forceinline__ void head_prefetch_q(const AcceptArgs& ac, unsigned (
 }
 
 // Gumbel noise G = -log(-log U) of the four vocab entries vb .. vb+3 at absolute
-// position pos of sequence b (Philox block vb / 4, tag 1).  U lies in [2^-24, 1), so
-// both logarithms take normal arguments and the hardware logarithm serves.
+// position pos of sequence b (Philox block vb / 4, tag 1).  U lies in [2^-24, 1 - 2^-24],
+// so -ln U lies in [6e-8, 16.7]: both logarithms take normal arguments and the bare
+// hardware base-2 logarithm serves (no rescaling of denormal inputs).  The block index
+// and the sequence are below 2^32, which saves the first round two partial products.
 __device__ __forceinline__ void gumbel4(uint64_t seed, int b, uint64_t pos, int vb, float (&G)[4]) {
-  const Philox4 w = philox4x64_10(uint64_t(vb) >> 2, pos, uint64_t(b), TAG_GUMBEL, seed, 0);
+  const Philox4 w = philox4x64_10(uint64_t(unsigned(vb) >> 2), pos, uint64_t(unsigned(b)), TAG_GUMBEL, seed, 0);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) G[e] = -__logf(-__logf(gumbel_uniform_from_word(w.w[e])));
+  for (int e = 0; e < 4; ++e) {
+    const float nl = -LN2 * __builtin_amdgcn_logf(gumbel_uniform_from_word(w.w[e]));   // -ln U
+    G[e] = -LN2 * __builtin_amdgcn_logf(nl);
+  }
 }
 
 // Loads of one staging round of head_stage_norm: HEAD_STAGE_F pieces of 8 values per

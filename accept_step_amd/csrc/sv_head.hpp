@@ -173,6 +173,23 @@ __device__ __forceinline__ void head_load(const HeadItem& it, unsigned voff, u32
 
 // One work item: GRP steps of NB MFMAs.  The X operands of the item are read from
 // LDS in one batch (lanes of padding rows read the zero row, so no read is conditional).
+// A wavefront's first two work items, requested by the staging code once its own first
+// loads are out.  Both are always requested (from the last tile, or item 0 again, when
+// the wavefront has fewer; those registers are never used), so no branch hides them from
+// the compiler's count of outstanding loads.
+struct HeadFirst {
+  int items, first, tstride, item_k, ntiles;
+  unsigned voff;
+};
+
+template <int S, int NB, int GRP>
+__device__ __forceinline__ void head_first_loads(const HeadArgs& a, const HeadFirst& hf, u32x4 (&bufA)[GRP],
+                                                 u32x4 (&bufB)[GRP]) {
+  const int f = min(hf.first, hf.ntiles - 1), k1 = hf.items > 1 ? 1 : 0;
+  head_load<S, NB, GRP>(head_item<S>(a, 0, f, hf.tstride, hf.item_k), hf.voff, bufA);
+  head_load<S, NB, GRP>(head_item<S>(a, k1, f, hf.tstride, hf.item_k), hf.voff, bufB);
+}
+
 template <int S, int NB, int GRP>
 __device__ __forceinline__ void head_mfma(const u32x4 (&buf)[GRP], const bf16_t* const (&xp)[NB], int kofs,
                                           f32x4 (&acc)[NB]) {
@@ -365,20 +382,76 @@ __device__ __forceinline__ void gumbel4(uint64_t seed, int b, uint64_t pos, int 
 }
 
 // Loads of one staging round of head_stage_norm: HEAD_STAGE_F pieces of 8 values per
-// thread (the rows of Xf and the gain), zeros outside the rows and past K.
+// thread (the rows of Xf and the gain).  A wavefront skips a piece slot only when none of
+// its lanes has a piece there (a uniform test); otherwise every lane loads, from a
+// clamped in-bounds address, straight into the zeroed registers, and the conversion
+// zeroes what lies outside the rows and past K.  Loads behind per-lane branches, or
+// whose values are selected right away, make the compiler wait for every older load
+// there (here: the stream's first weights).
 __device__ __forceinline__ void head_norm_issue(const HeadArgs& a, int t0, int pieces, int kpieces, int total,
                                                 f32x4 (&x0)[HEAD_STAGE_F], f32x4 (&x1)[HEAD_STAGE_F],
                                                 u32x4 (&gw)[HEAD_STAGE_F]) {
+  const int wbase = __builtin_amdgcn_readfirstlane(t0 - (int(threadIdx.x) & 63));   // the wavefront's lane 0
 #pragma unroll
   for (int u = 0; u < HEAD_STAGE_F; ++u) {
     const int t = t0 + u * int(blockDim.x), row = t / pieces, c = t - row * pieces;
     x0[u] = x1[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     gw[u] = u32x4{0u, 0u, 0u, 0u};
-    if (t < total && row < a.M && c < kpieces) {
-      const float* xr = a.Xf + size_t(row) * a.K + c * 8;
+    if (wbase + u * int(blockDim.x) < total) {
+      const float* xr = a.Xf + size_t(min(row, a.M - 1)) * a.K + min(c, kpieces - 1) * 8;
       x0[u] = *reinterpret_cast<const f32x4*>(xr);
       x1[u] = *reinterpret_cast<const f32x4*>(xr + 4);
-      gw[u] = load16(a.norm_w + c * 8);
+      gw[u] = load16(a.norm_w + min(c, kpieces - 1) * 8);
+    }
+  }
+}
+
+// One staging round of bf16 rows taken as they are (HEAD_STAGE pieces per thread):
+// loads as in head_norm_issue, then the stores (zeros outside the rows and past K).
+__device__ __forceinline__ void head_plain_issue(const HeadArgs& a, int t0, int pieces, int kpieces, int total,
+                                                 u32x4 (&v)[HEAD_STAGE]) {
+  const int wbase = __builtin_amdgcn_readfirstlane(t0 - (int(threadIdx.x) & 63));   // the wavefront's lane 0
+#pragma unroll
+  for (int u = 0; u < HEAD_STAGE; ++u) {
+    const int t = t0 + u * int(blockDim.x), row = t / pieces, c = t - row * pieces;
+    v[u] = u32x4{0u, 0u, 0u, 0u};
+    if (wbase + u * int(blockDim.x) < total)
+      v[u] = load16(a.X + size_t(min(row, a.M - 1)) * a.K + min(c, kpieces - 1) * 8);
+  }
+}
+
+__device__ __forceinline__ void head_plain_store(const HeadArgs& a, int t0, int pieces, int kpieces, int total,
+                                                 const u32x4 (&v)[HEAD_STAGE], bf16_t* sX, int ld) {
+#pragma unroll
+  for (int u = 0; u < HEAD_STAGE; ++u) {
+    const int t = t0 + u * int(blockDim.x), row = t / pieces, c = t - row * pieces;
+    if (t < total)
+      *reinterpret_cast<u32x4*>(sX + row * ld + c * 8) = (row < a.M && c < kpieces) ? v[u] : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// One staging round's conversion: normalise, scale by the gain, round to bf16 and store
+// to LDS (zeros outside the rows and past K).
+__device__ __forceinline__ void head_norm_convert(const HeadArgs& a, int t0, int pieces, int kpieces, int total,
+                                                  const float* s_scale, const f32x4 (&x0)[HEAD_STAGE_F],
+                                                  const f32x4 (&x1)[HEAD_STAGE_F], const u32x4 (&gw)[HEAD_STAGE_F],
+                                                  bf16_t* sX, int ld) {
+  const int M = a.M;
+#pragma unroll
+  for (int u = 0; u < HEAD_STAGE_F; ++u) {
+    const int t = t0 + u * int(blockDim.x), row = t / pieces, c = t - row * pieces;
+    if (t < total) {
+      const bool in = row < M && c < kpieces;
+      const float sc = row < M ? s_scale[row] : 0.0f;
+      u32x4 o;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float xa = w < 2 ? x0[u][2 * w] : x1[u][2 * w - 4];
+        const float xb = w < 2 ? x0[u][2 * w + 1] : x1[u][2 * w - 3];
+        const float ga = __uint_as_float(gw[u][w] << 16), gb = __uint_as_float(gw[u][w] & 0xffff0000u);
+        o[w] = in ? uint32_t(f32_to_bf16(xa * sc * ga)) | (uint32_t(f32_to_bf16(xb * sc * gb)) << 16) : 0u;
+      }
+      *reinterpret_cast<u32x4*>(sX + row * ld + c * 8) = o;
     }
   }
 }
@@ -389,8 +462,13 @@ __device__ __forceinline__ void head_norm_issue(const HeadArgs& a, int t0, int p
 // sums in order); every piece is normalised, scaled by the gain and rounded to bf16 as it
 // is written to LDS (zeros past K and in the extra row).  The arithmetic matches a
 // separate RMSNorm pass: bf16((x * scale) * g).  The first round of X loads goes out
-// before the partial sums are read, so the two round trips overlap.
-__device__ __forceinline__ void head_stage_norm(const HeadArgs& a, bf16_t* sX, int ld, int Kp) {
+// before the partial sums are read, so the two round trips overlap, and both go out
+// before the stream's first work items (HeadFirst): vector loads complete in issue
+// order, so staging loads requested after the weights would wait for them, HBM reads
+// queued behind the whole chip's stream.
+template <int S, int NB, int GRP>
+__device__ __forceinline__ void head_stage_norm(const HeadArgs& a, bf16_t* sX, int ld, int Kp, const HeadFirst& hf,
+                                                u32x4 (&bufA)[GRP], u32x4 (&bufB)[GRP]) {
   __shared__ float s_scale[HEAD_MAX_ROWS];
   __shared__ float s_red[HEAD_WAVES][HEAD_MAX_ROWS];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -399,20 +477,36 @@ __device__ __forceinline__ void head_stage_norm(const HeadArgs& a, bf16_t* sX, i
   f32x4 x0[HEAD_STAGE_F], x1[HEAD_STAGE_F];
   u32x4 gw[HEAD_STAGE_F];
   head_norm_issue(a, threadIdx.x, pieces, kpieces, total, x0, x1, gw);
-  float part[HEAD_MAX_ROWS];
+  // rows are reduced up to MR, the rows the launch's column blocks cover (M <= MR), all
+  // of them unconditionally: a load whose only use sits behind the uniform test m < M is
+  // moved into that branch, and each such load then waits for every older load in turn
+  constexpr int MR = (16 / S) * NB < HEAD_MAX_ROWS ? (16 / S) * NB : HEAD_MAX_ROWS;
+  // (rows past M and threads past ss_parts load a clamped partial, replaced by zero in
+  // the reduction, where the loaded values are first used)
+  float part[MR];
+  {
+    const int pc = min(int(threadIdx.x), a.ss_parts - 1);      // ss_parts >= 1 with a norm
 #pragma unroll
-  for (int m = 0; m < HEAD_MAX_ROWS; ++m) part[m] = 0.0f;
-  for (int p0 = 0; p0 < a.ss_parts; p0 += int(blockDim.x)) {
+    for (int m = 0; m < MR; ++m) part[m] = a.ss_in[size_t(pc) * M + min(m, M - 1)];
+  }
+  head_first_loads<S, NB, GRP>(a, hf, bufA, bufB);
+  for (int p0 = int(blockDim.x); p0 < a.ss_parts; p0 += int(blockDim.x)) {
     const int p = p0 + int(threadIdx.x);
 #pragma unroll
-    for (int m = 0; m < HEAD_MAX_ROWS; ++m)
+    for (int m = 0; m < MR; ++m)
       if (m < M && p < a.ss_parts) part[m] += a.ss_in[size_t(p) * M + m];
   }
+  // rows below TR * (NB - 1) + 1 exist in every launch of this instantiation; the rest
+  // only when M reaches them (their loads then wait for the weights: B * (gamma + 1)
+  // just past a multiple of TR)
+  constexpr int MSURE = (16 / S) * (NB - 1) + 1 < MR ? (16 / S) * (NB - 1) + 1 : MR;
+  const bool own = int(threadIdx.x) < a.ss_parts;
 #pragma unroll
-  for (int m = 0; m < HEAD_MAX_ROWS; ++m) {
-    if (m >= M) break;
-    const float v = wave_allsum(part[m]);
-    if (lane == 0) s_red[wave][m] = v;
+  for (int m = 0; m < MR; ++m) {
+    if (m < MSURE || m < M) {
+      const float v = wave_allsum((own && m < M) ? part[m] : 0.0f);
+      if (lane == 0) s_red[wave][m] = v;
+    }
   }
   __syncthreads();
   if (int(threadIdx.x) < M) {
@@ -421,26 +515,12 @@ __device__ __forceinline__ void head_stage_norm(const HeadArgs& a, bf16_t* sX, i
     s_scale[m] = 1.0f / sqrtf(ss / float(a.K) + a.eps);
   }
   __syncthreads();
-  for (int t0 = threadIdx.x;;) {
-#pragma unroll
-    for (int u = 0; u < HEAD_STAGE_F; ++u) {
-      const int t = t0 + u * int(blockDim.x), row = t / pieces, c = t - row * pieces;
-      if (t < total) {
-        const float sc = row < M ? s_scale[row] : 0.0f;
-        u32x4 o;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float xa = w < 2 ? x0[u][2 * w] : x1[u][2 * w - 4];
-          const float xb = w < 2 ? x0[u][2 * w + 1] : x1[u][2 * w - 3];
-          const float ga = __uint_as_float(gw[u][w] << 16), gb = __uint_as_float(gw[u][w] & 0xffff0000u);
-          o[w] = uint32_t(f32_to_bf16(xa * sc * ga)) | (uint32_t(f32_to_bf16(xb * sc * gb)) << 16);
-        }
-        *reinterpret_cast<u32x4*>(sX + row * ld + c * 8) = o;
-      }
-    }
-    t0 += HEAD_STAGE_F * int(blockDim.x);
-    if (t0 >= total) break;
-    head_norm_issue(a, t0, pieces, kpieces, total, x0, x1, gw);
+  // the first round outside the loop: inside it, the wait for the rows would also cover
+  // the later rounds' loads, which go out after the weights
+  head_norm_convert(a, threadIdx.x, pieces, kpieces, total, s_scale, x0, x1, gw, sX, ld);
+  for (int base = HEAD_STAGE_F * int(blockDim.x); base < total; base += HEAD_STAGE_F * int(blockDim.x)) {
+    head_norm_issue(a, base + int(threadIdx.x), pieces, kpieces, total, x0, x1, gw);
+    head_norm_convert(a, base + int(threadIdx.x), pieces, kpieces, total, s_scale, x0, x1, gw, sX, ld);
   }
 }
 
@@ -574,52 +654,49 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   __shared__ long long s_pos0[HEAD_MAX_ROWS];
   __shared__ unsigned s_ep;                       // HEAD_SAMPLE: this launch's epoch
 
-  // The wavefront's first two work items are requested before X is staged: the
-  // latencies overlap instead of adding up, and the stream starts two items deep.
+  // What the prologue waits for is requested before the wavefront's first two work
+  // items: the rule's per-row inputs and the launch epoch here, the first round of X
+  // (and the norm's partial sums) by the staging code, which then requests the two items.
+  // Vector loads complete in issue order, so loads requested after the weights would wait
+  // for them; this way the stream starts two items deep while X is converted and stored.
   const int first = blockIdx.x * HEAD_WAVES + wave, tstride = gridDim.x * HEAD_WAVES;
   const int n_my = first < ntiles ? (ntiles - 1 - first) / tstride + 1 : 0;
   const int items = n_my * a.gpt;
   const int item_k = 32 * S * GRP;                // elements of a row per work item
   const int lane_ofs = 8 * (S * g + r % S);       // element offset of the lane's piece in step 0
+  int my_draft = -1, my_bad = 0;
+  long long my_pos0 = 0, my_pos0_row = 0;        // pos0 of sequence threadIdx.x, of row threadIdx.x's sequence
+  unsigned my_ep = 0u;
+  if (rule && threadIdx.x < M) {
+    const int b = threadIdx.x / G1, i = threadIdx.x - b * G1;
+    if (i < ac.gamma) my_draft = ac.draft[size_t(b) * ac.draft_stride + ac.draft_offset + i];
+    if (sample) my_pos0_row = ac.pos0[b];
+  }
+  if (sample && threadIdx.x < ac.B) {
+    my_pos0 = ac.pos0[threadIdx.x];
+    my_bad = ac.invalid ? ac.invalid[threadIdx.x] : 0;
+  }
+  if (sample && threadIdx.x == 0) my_ep = load_coherent(a.counter + CNT_EPOCH);
+  const HeadFirst hf{items, first, tstride, item_k, ntiles,
+                     (unsigned(r / S) * unsigned(a.K) + unsigned(lane_ofs)) * 2u};   // the lane's W bytes
+  const unsigned voff = hf.voff;
   u32x4 bufA[GRP], bufB[GRP];
-  const unsigned voff = (unsigned(r / S) * unsigned(a.K) + unsigned(lane_ofs)) * 2u;   // the lane's W bytes
-  if (items > 0) head_load<S, NB, GRP>(head_item<S>(a, 0, first, tstride, item_k), voff, bufA);
-  if (items > 1) head_load<S, NB, GRP>(head_item<S>(a, 1, first, tstride, item_k), voff, bufB);
 
   // stage all of X (zeros from K to Kp) and the zero row, HEAD_STAGE pieces per thread
-  // in flight at a time (one load and store at a time would chain the L2 round trips);
-  // fetch the drafts
+  // in flight at a time (one load and store at a time would chain the L2 round trips)
   if (a.Xf) {
-    head_stage_norm(a, sX, ld, Kp);
+    head_stage_norm<S, NB, GRP>(a, sX, ld, Kp, hf, bufA, bufB);
   } else {
     const int pieces = Kp / 8, kpieces = a.K / 8, total = (M + 1) * pieces;
-    for (int t0 = threadIdx.x; t0 < total; t0 += HEAD_STAGE * int(blockDim.x)) {
-      u32x4 v[HEAD_STAGE];
-#pragma unroll
-      for (int u = 0; u < HEAD_STAGE; ++u) {
-        const int t = t0 + u * int(blockDim.x), row = t / pieces, c = t - row * pieces;
-        v[u] = u32x4{0u, 0u, 0u, 0u};
-        if (t < total && row < M && c < kpieces) v[u] = load16(a.X + size_t(row) * a.K + c * 8);
-      }
-#pragma unroll
-      for (int u = 0; u < HEAD_STAGE; ++u) {
-        const int t = t0 + u * int(blockDim.x), row = t / pieces, c = t - row * pieces;
-        if (t < total) *reinterpret_cast<u32x4*>(sX + row * ld + c * 8) = v[u];
-      }
-    }
-  }
-  {
-    if (rule && threadIdx.x < M) {
-      const int b = threadIdx.x / G1, i = threadIdx.x - b * G1;
-      s_draft[threadIdx.x] = i < ac.gamma ? ac.draft[size_t(b) * ac.draft_stride + ac.draft_offset + i] : -1;
-    }
-    if (sample && threadIdx.x < ac.B) {
-      s_pos0[threadIdx.x] = ac.pos0[threadIdx.x];
-      s_bad[threadIdx.x] = ac.invalid ? ac.invalid[threadIdx.x] : 0;
-    }
-    if (sample && threadIdx.x == 0) {
-      const unsigned e = load_coherent(a.counter + CNT_EPOCH);
-      s_ep = e == EPOCH_POISON ? e : (e + 1u >= EPOCH_POISON ? 1u : e + 1u);   // 0 never tags a record
+    // the first round's loads, then the stream's first work items, then its stores; the
+    // later rounds (long or many rows) after
+    u32x4 v[HEAD_STAGE];
+    head_plain_issue(a, threadIdx.x, pieces, kpieces, total, v);
+    head_first_loads<S, NB, GRP>(a, hf, bufA, bufB);
+    head_plain_store(a, threadIdx.x, pieces, kpieces, total, v, sX, ld);
+    for (int base = HEAD_STAGE * int(blockDim.x); base < total; base += HEAD_STAGE * int(blockDim.x)) {
+      head_plain_issue(a, base + int(threadIdx.x), pieces, kpieces, total, v);
+      head_plain_store(a, base + int(threadIdx.x), pieces, kpieces, total, v, sX, ld);
     }
   }
   __syncthreads();
@@ -632,13 +709,13 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   float my_qx = 0.0f;
   if (sample && threadIdx.x < M) {
     const int t = threadIdx.x, b = t / G1, i = t - b * G1;
-    const int x = s_draft[t];
+    const int x = my_draft;
     if (x >= 0 && x < ac.V) {
       const size_t qi = (size_t(b) * ac.gamma + i) * ac.V + x;
       my_qx = ac.q_bf16 ? bf16_to_f32(reinterpret_cast<const bf16_t*>(ac.q)[qi])
                         : reinterpret_cast<const float*>(ac.q)[qi];
     }
-    s_u[t] = i < ac.gamma ? accept_uniform(ac.seed, uint64_t(b), uint64_t(s_pos0[b] + i + 1)) : 1.0f;
+    s_u[t] = i < ac.gamma ? accept_uniform(ac.seed, uint64_t(b), uint64_t(my_pos0_row + i + 1)) : 1.0f;
   }
 
   const int kg = (nloc / 4 + int(blockDim.x) - 1) / int(blockDim.x);   // groups of four per thread
@@ -693,6 +770,14 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
 #undef SV_HEAD_ITEM
   }
   if (sample && threadIdx.x < M) s_qx[threadIdx.x] = my_qx;
+  // the rule's per-row inputs, requested before the stream; the barrier below publishes them
+  if (rule && threadIdx.x < M) s_draft[threadIdx.x] = my_draft;
+  if (sample && threadIdx.x < ac.B) {
+    s_pos0[threadIdx.x] = my_pos0;
+    s_bad[threadIdx.x] = my_bad;
+  }
+  if (sample && threadIdx.x == 0)
+    s_ep = my_ep == EPOCH_POISON ? my_ep : (my_ep + 1u >= EPOCH_POISON ? 1u : my_ep + 1u);   // 0 never tags a record
 
   // ---- statistics partials: lanes of a row differ in g (xor 16, 32), then the waves
   __shared__ float s_m[HEAD_WAVES][HEAD_MAX_ROWS], s_s[HEAD_WAVES][HEAD_MAX_ROWS];

@@ -1194,7 +1194,7 @@ sv_status mtp_draft(const sv_drafter* dr, const sv_shared_kv* kv, int32_t B, int
     sa.x_res = x;
     sa.D = D;
     sa.H = H;
-    hipLaunchKernelGGL(k_mtp_sample, dim3(B), dim3(256), 0, s, sa);
+    hipLaunchKernelGGL(k_mtp_sample, dim3(B), dim3(MTP_SAMPLE_THREADS), 0, s, sa);
     return SV_OK;
   };
   // Every product on the k-split kernel: the RMSNorms happen while the next product

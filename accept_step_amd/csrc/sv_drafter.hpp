@@ -144,17 +144,22 @@ __device__ __forceinline__ void softmax_merge(float& m, float& s, float m2, floa
   m = mm;
 }
 
-// One workgroup (256 threads) per sequence over its n scored tokens, four consecutive
+// Threads of the draw: one group of four scored ids (one Philox block) per thread at
+// the masked head's 4096 scored tokens.
+constexpr int MTP_SAMPLE_THREADS = 1024;
+
+// One workgroup (MTP_SAMPLE_THREADS threads) per sequence over its n scored tokens, four consecutive
 // entries per thread and step (one Philox block per four vocabulary ids when they are
 // consecutive and aligned, as the members of a cluster are).  T > 0: one pass for
 // m = max l and Z = sum exp((l - m) / T) (online per thread, merged over the block),
 // one for q_j = exp((l_j - m) / T) / Z, stored at its token id, and the draft = the
 // largest (log q_j + G, lower id) with G the Gumbel noise of Philox stream tag 2 at
 // position len + k + 1.  T = 0: the largest (l, lower id).
-__global__ __launch_bounds__(256) void k_mtp_sample(DraftSampleArgs a) {
+__global__ __launch_bounds__(MTP_SAMPLE_THREADS) void k_mtp_sample(DraftSampleArgs a) {
+  constexpr int NT = MTP_SAMPLE_THREADS, NW = NT / 64;
   const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  __shared__ float s_m[4], s_s[4];
-  __shared__ unsigned long long s_key[4];
+  __shared__ float s_m[NW], s_s[NW];
+  __shared__ unsigned long long s_key[NW];
   const float* l = a.logits + size_t(b) * a.n;
   const bool bad = a.invalid[b] != 0;
   const size_t qrow = (size_t(b) * a.gamma + a.k) * a.V;
@@ -171,7 +176,7 @@ __global__ __launch_bounds__(256) void k_mtp_sample(DraftSampleArgs a) {
   };
   unsigned long long key = 0ull;
   if (a.greedy) {
-    for (int g = t; g < ng; g += 256) {
+    for (int g = t; g < ng; g += NT) {
       float v[4];
       load4(g, v);
 #pragma unroll
@@ -180,7 +185,7 @@ __global__ __launch_bounds__(256) void k_mtp_sample(DraftSampleArgs a) {
     }
   } else {
     float m = -INFINITY, sum = 0.0f;
-    for (int g = t; g < ng; g += 256) {
+    for (int g = t; g < ng; g += NT) {
       float v[4];
       load4(g, v);
 #pragma unroll
@@ -196,10 +201,10 @@ __global__ __launch_bounds__(256) void k_mtp_sample(DraftSampleArgs a) {
     m = s_m[0];
     sum = s_s[0];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) softmax_merge(m, sum, s_m[w], s_s[w], a.inv_t);
+    for (int w = 1; w < NW; ++w) softmax_merge(m, sum, s_m[w], s_s[w], a.inv_t);
     const float inv_z = 1.0f / sum;
     const uint64_t pos = uint64_t(int64_t(a.len[b]) + a.k + 1);
-    for (int g = t; g < ng; g += 256) {
+    for (int g = t; g < ng; g += NT) {
       float v[4];
       load4(g, v);
       int id[4];
@@ -249,7 +254,8 @@ __global__ __launch_bounds__(256) void k_mtp_sample(DraftSampleArgs a) {
   __syncthreads();
   __shared__ int s_x;
   if (t == 0) {
-    const unsigned long long kb = max_u64(max_u64(s_key[0], s_key[1]), max_u64(s_key[2], s_key[3]));
+    unsigned long long kb = s_key[0];
+    for (int w = 1; w < NW; ++w) kb = max_u64(kb, s_key[w]);
     const int x = (bad || !kb) ? -1 : win_index(kb);
     a.draft[size_t(b) * a.gamma + a.k] = x;
     a.tok[b] = x < 0 ? 0 : x;
@@ -259,8 +265,8 @@ __global__ __launch_bounds__(256) void k_mtp_sample(DraftSampleArgs a) {
   __syncthreads();
   const u32x4* e = reinterpret_cast<const u32x4*>(a.embed + size_t(s_x) * a.D);
   u32x4* o = reinterpret_cast<u32x4*>(a.z + size_t(b) * 2 * a.D);
-  for (int i = t; i < a.D / 8; i += 256) o[i] = e[i];
-  for (int i = t; i < a.H; i += 256) a.x_res[size_t(b) * a.H + i] = 0.0f;
+  for (int i = t; i < a.D / 8; i += NT) o[i] = e[i];
+  for (int i = t; i < a.H; i += NT) a.x_res[size_t(b) * a.H + i] = 0.0f;
 }
 
 }  // namespace sv

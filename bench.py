@@ -63,7 +63,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); "
+        print(f"bench.py: measures one GPU only (got --gpus {args.gpus}); "
               "multi-GPU sharding of the verify step is a design note, not a measured path", file=sys.stderr)
         sys.exit(2)
     import torch

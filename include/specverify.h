@@ -72,7 +72,7 @@ typedef enum sv_status {
   SV_ERR_SHAPE = 3,        /* sizes the kernels do not support (e.g. d % 32 != 0) */
   SV_ERR_WORKSPACE = 4,    /* *ws_bytes smaller than required, or misaligned ws */
   SV_ERR_HIP = 5,          /* a HIP runtime call failed (no device, launch error) */
-  SV_ERR_UNSUPPORTED = 6   /* valid request this build does not implement */
+  SV_ERR_UNSUPPORTED = 6   /* valid request this library does not implement */
 } sv_status;
 
 typedef enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;

@@ -199,13 +199,86 @@ def sample_step(ids, l64, V, temperature, seed, pos, ok, margin=FLAG):
     return draft, q, flags
 
 
-def draft(wts: DrafterWeights, kv: SharedKV, last_token, h_target_bits, gamma, temperature, seed, margin=FLAG):
+def cut_band(wts: DrafterWeights, g_bits, margin):
+    """The masked head's clusters near its cut, per row: (kept, excluded) lists of
+    cluster ids -- the kept clusters whose float32 score is within ``margin`` of the
+    best excluded one, and the excluded clusters within ``margin`` of the worst kept
+    one.  A perturbation of the scores smaller than ``margin / 2`` can only move
+    clusters of the band across the cut."""
+    g = _w(g_bits)
+    cl = mh.cluster_logits(g, _w(wts.centroids))
+    c32 = cl.astype(np.float32).astype(np.float64)
+    sel, _ = mh.select_clusters(cl, wts.top_k_clusters)
+    out = []
+    for b in range(g.shape[0]):
+        kept = np.zeros(c32.shape[1], dtype=bool)
+        kept[sel[b]] = True
+        if kept.all():
+            out.append(([], []))
+            continue
+        vk, vk1 = c32[b][kept].min(), c32[b][~kept].max()
+        out.append((np.nonzero(kept & (c32[b] < vk1 + margin))[0].tolist(),
+                    np.nonzero(~kept & (c32[b] > vk - margin))[0].tolist()))
+    return out
+
+
+def cut_flags(wts: DrafterWeights, g_bits, ids, l64, drafts, temperature, seed, pos, ok, margin):
+    """Rows whose draft could change if the clusters of :func:`cut_band` moved across the
+    cut: the draft's own cluster is a kept one of the band (it could be dropped), or an
+    excluded cluster of the band holds a token whose score comes within ``margin`` of the
+    draft's (it could be added and win).  Scores as the draw takes them: the float32
+    logit at T = 0; log q + G with q normalised over the kept tokens otherwise.  Returns
+    (flags [B], band per row)."""
+    B = ids.shape[0]
+    flags = np.zeros(B, dtype=bool)
+    band = cut_band(wts, g_bits, margin)
+    cs = mh.cluster_size(wts.vocab, wts.centroids.shape[0])
+    g = _w(g_bits)
+    t = float(temperature)
+    for b in range(B):
+        near_in, near_out = band[b]
+        if not ok[b] or (not near_in and not near_out):
+            continue
+        x = int(drafts[b])
+        if x // cs in near_in:
+            flags[b] = True
+            continue
+        if not near_out:
+            continue
+        extra = (np.asarray(near_out)[:, None] * cs + np.arange(cs)[None, :]).reshape(-1)
+        l_extra = (g[b] @ _w(wts.embed[extra]).T).astype(np.float32).astype(np.float64)
+        l_kept = np.asarray(l64[b], dtype=np.float64).astype(np.float32).astype(np.float64)
+        j = int(np.nonzero(ids[b] == x)[0][0])
+        if t == 0.0:
+            s_win, s_extra = l_kept[j], l_extra
+        else:
+            mx = l_kept.max()
+            lz = np.log(np.exp((l_kept - mx) / t).sum())
+            U = philox.gumbel_uniform_rows(seed, [b], [int(pos[b])], wts.vocab, tag=philox.TAG_DRAFT)[0]
+            G = -np.log(-np.log(U))
+            s_win = (l_kept[j] - mx) / t - lz + G[x]
+            s_extra = (l_extra - mx) / t - lz + G[extra]
+        flags[b] = bool(s_extra.max() > s_win - margin)
+    return flags, band
+
+
+def draft(wts: DrafterWeights, kv: SharedKV, last_token, h_target_bits, gamma, temperature, seed, margin=FLAG,
+          force=None):
     """gamma autoregressive drafter steps.  Returns a dict with ``draft`` int64 [B, gamma]
     (-1 for rows that are not valid), ``q`` float32 [B, gamma, V] (None at T = 0),
     ``g`` the hidden states after every step (bf16 bits [gamma, B, D]), ``logits`` the
-    scored (ids, float64 logits) of every step, and ``flags`` [B, gamma] (a decision or
-    a cluster cut within ``margin`` at that step; later steps of that row depend on
-    it).  ``margin`` is one value or one per step."""
+    scored (ids, float64 logits) of every step, and ``flags`` [B, gamma]: the step's
+    draft could change under perturbations of ``margin`` -- its two best scores are
+    closer than ``margin`` (``flags_draw``), or, with the masked head, clusters near the
+    cut could move across it and change the draft (``flags_cut``; :func:`cut_flags`;
+    ``band`` lists those clusters per step and row).  Later steps of a flagged row depend
+    on it.  ``margin`` is one value or one per step.
+
+    ``force`` (int [B, gamma], optional): the tokens fed back after each step in place
+    of the drafts drawn here (entries < 0 keep the drawn draft).  Every step still
+    draws and flags its own draft; forcing only chooses the token the next step
+    processes, so another implementation's path can be followed past a flagged step.
+    Forcing the drafts this function draws reproduces the unforced result."""
     tokens = np.asarray(last_token, dtype=np.int64).copy()
     B = tokens.shape[0]
     ok = valid_rows(kv, tokens, wts.vocab)
@@ -213,18 +286,28 @@ def draft(wts: DrafterWeights, kv: SharedKV, last_token, h_target_bits, gamma, t
     lens = np.asarray(kv.length, dtype=np.int64)
     drafts = np.full((B, gamma), -1, dtype=np.int64)
     qs = None if float(temperature) == 0.0 else np.zeros((B, gamma, wts.vocab), dtype=np.float32)
-    flags = np.zeros((B, gamma), dtype=bool)
+    flags_draw = np.zeros((B, gamma), dtype=bool)
+    flags_cut = np.zeros((B, gamma), dtype=bool)
+    bands = []
     gs, ls = [], []
     for k in range(gamma):
         g = step_hidden(wts, kv, np.where(ok, tokens, 0), g, k)
         mk = float(np.broadcast_to(np.asarray(margin, dtype=np.float64), (gamma,))[k])
-        ids, l64, sflag = scored_logits(wts, g, margin=mk)
+        ids, l64, _ = scored_logits(wts, g, margin=mk)
         x, q, dflag = sample_step(ids, l64, wts.vocab, temperature, seed, lens + k + 1, ok, mk)
         drafts[:, k] = np.where(ok, x, -1)
         if qs is not None:
             qs[:, k] = q
-        flags[:, k] = ok & (sflag | dflag)
-        tokens = np.where(ok, x, 0)
+        flags_draw[:, k] = ok & dflag
+        if wts.centroids is not None:
+            cf, band = cut_flags(wts, g, ids, l64, x, temperature, seed, lens + k + 1, ok, mk)
+            flags_cut[:, k] = ok & cf
+            bands.append(band)
+        else:
+            bands.append([([], [])] * B)
+        fed = x if force is None else np.where(np.asarray(force)[:, k] >= 0, np.asarray(force)[:, k], x)
+        tokens = np.where(ok, fed, 0)
         gs.append(g.copy())
         ls.append((ids, l64))
-    return dict(draft=drafts, q=qs, g=np.stack(gs), logits=ls, flags=flags)
+    return dict(draft=drafts, q=qs, g=np.stack(gs), logits=ls, flags=flags_draw | flags_cut, flags_draw=flags_draw,
+                flags_cut=flags_cut, band=bands)

@@ -1,8 +1,14 @@
 """GPU parity of mtp_draft (the MTP drafter's gamma steps) against the oracle's
-drafter.draft: drafts bit-exact step by step until the first step the oracle flags
-(a draw or a cluster cut within its rounding margin; every later step of that sequence
-depends on it), q within a tolerance derived from the bf16 rounding of the hidden state,
-exact zeros outside the scored tokens, -1 drafts for invalid rows."""
+drafter.draft: drafts bit-exact at every step of every sequence except where the oracle
+flags the step (a draw or a cluster cut within the derived margin), q within the derived
+tolerance, exact zeros outside the scored tokens, -1 drafts for invalid rows.  The oracle
+follows the GPU's drafted tokens (teacher forcing), so a flagged divergence does not end
+the comparison: every one of the B * gamma steps is compared.
+
+The margin and the q tolerance come from tests/drafter_bounds.py: a float32 evaluation of
+the same recipe on the CPU drifts from the float64 oracle by a measured amount per step
+(tests/test_drafter_drift_cpu.py recomputes it at the full shapes and checks that these
+bounds cover it); they are not fitted to the GPU."""
 import numpy as np
 import pytest
 import torch
@@ -10,25 +16,10 @@ import torch
 import accept_step_amd as sv
 import workloads
 from oracle import drafter as od
+from tests import drafter_bounds as dbnd
 from tests.gpu_util import dev, dev_bf16, log
 
 pytestmark = pytest.mark.gpu
-
-# The drafter's hidden state passes through the target decoder's bf16 rounding points
-# and is fed back at every step, so its drift from the float64 oracle compounds with the
-# depth traversed.  A float32 evaluation of the same recipe on the CPU at the full shapes
-# (D = 1536, H = 256, four layers, 700-2048 cached positions, masked head; 12 rows)
-# drifts in the logits by up to 3.4e-2, 5.2e-2, 7.0e-2 at steps 0, 1, 2 (about 1 % of
-# the row maximum; by step 2 about 1100 of the 1536 hidden entries round to another
-# bf16 value) and in q by up to 1.6e-2, 3.7e-2, 3.4e-2.  Decisions closer than MARGIN
-# (a score difference moves by up to two logit errors) are flagged, and q is held to
-# Q_TOL, both times the square root of the depth, (k + 1) * layers / 4.
-MARGIN = 8e-2
-Q_TOL = 4e-2      # max |q_gpu - q_oracle| / max q_oracle per row, at four layers deep
-
-
-def depth_scale(k, n_layers):
-    return max(1.0, np.sqrt((k + 1) * n_layers / 4.0))
 
 
 def oracle_weights(c, masked):
@@ -50,32 +41,38 @@ def device_drafter(c, masked, embed_dev=None):
 
 
 def compare(c, out, gd, gq, label):
-    """Step by step per sequence: the draft must match the oracle's, and (T > 0) the
-    support of q (the kept clusters) too, with q within the depth-scaled Q_TOL.  A
-    mismatch is allowed only at a step the oracle flags: another draft ends the
-    comparison of that sequence (its later steps start from another token), another
-    kept cluster set skips that step's q.  Returns (steps compared, sequences that
-    diverged at a flagged step)."""
+    """Every step of every sequence: the draft must be the oracle's unless the oracle
+    flags the step (two scores within the margin, or clusters near the cut whose move
+    could change the draft).  With T > 0, q must keep the oracle's clusters except for
+    clusters of the oracle's band around the cut, and where the kept clusters agree q
+    lies within the step's tolerance.  Returns a dict of counts."""
     B, gamma = out["draft"].shape
-    steps, diverged = 0, 0
+    nl = len(c.layers)
+    cs = c.vocab // c.centroids.shape[0] if out["band"] and c.centroids is not None else 1
+    n = dict(steps=0, draft_differs=0, cut_differs=0, flagged=int(out["flags"].sum()),
+             flagged_draw=int(out["flags_draw"].sum()), flagged_cut=int(out["flags_cut"].sum()))
     for b in range(B):
         for k in range(gamma):
+            n["steps"] += 1
             if gd[b, k] != out["draft"][b, k]:
                 assert out["flags"][b, k], (f"{label}: b={b} step {k}: gpu draft {gd[b, k]} oracle "
                                             f"{out['draft'][b, k]} (unflagged)")
-                diverged += 1
-                break
-            steps += 1
+                n["draft_differs"] += 1
             if out["q"] is None:
                 continue
             qo, qg = out["q"][b, k].astype(np.float64), gq[b, k].astype(np.float64)
-            if not np.array_equal(qo > 0, qg > 0):       # another kept cluster set: the cut must be flagged
-                assert out["flags"][b, k], f"{label}: b={b} step {k}: kept clusters differ (unflagged)"
+            if not np.array_equal(qo > 0, qg > 0):       # another kept cluster set: only band clusters may move
+                co = set((np.nonzero(qo > 0)[0] // cs).tolist())
+                cg = set((np.nonzero(qg > 0)[0] // cs).tolist())
+                near_in, near_out = out["band"][k][b]
+                assert (co ^ cg) <= set(near_in) | set(near_out), (
+                    f"{label}: b={b} step {k}: kept clusters differ outside the band: {sorted(co ^ cg)}")
+                n["cut_differs"] += 1
                 continue
             if qo.max() > 0:
                 err = np.abs(qg - qo).max() / qo.max()
-                assert err <= Q_TOL * depth_scale(k, len(c.layers)), f"{label}: b={b} step {k} q err {err:.2e}"
-    return steps, diverged
+                assert err <= dbnd.q_tol(k, nl), f"{label}: b={b} step {k} q err {err:.2e}"
+    return n
 
 
 def run(c, masked, gamma, T, q_dtype=torch.float32, seed=None):
@@ -86,8 +83,9 @@ def run(c, masked, gamma, T, q_dtype=torch.float32, seed=None):
     torch.cuda.synchronize()
     gd = gd.cpu().numpy()
     gq = None if gq is None else gq.float().cpu().numpy()
+    nl = len(c.layers)
     out = od.draft(oracle_weights(c, masked), od.SharedKV(k=c.kv_k, v=c.kv_v, length=c.length), c.last_token,
-                   c.h_target, gamma, T, seed, margin=[MARGIN * depth_scale(k, len(c.layers)) for k in range(gamma)])
+                   c.h_target, gamma, T, seed, margin=[dbnd.margin(k, nl, T) for k in range(gamma)], force=gd)
     if q_dtype == torch.bfloat16 and out["q"] is not None:
         out["q"] = workloads.bf16_bits_to_f32(workloads.to_bf16_bits(out["q"]))
     return gd, gq, out
@@ -111,11 +109,12 @@ def test_small_and_ragged(V, D, H, nl, nh, hd, ff, C, tk, B, lens, gamma, T, mas
     c = workloads.drafter_case(V=V, D=D, H=H, n_layers=nl, n_heads=nh, head_dim=hd, d_ff=ff, C=C, top_k=tk, B=B,
                                length=lens, shared_layers=tuple(min(l, 1) for l in range(nl)), variant=V + B)
     gd, gq, out = run(c, masked, gamma, T)
-    steps, div = compare(c, out, gd, gq, f"V={V} B={B}")
+    n = compare(c, out, gd, gq, f"V={V} B={B}")
+    assert n["steps"] == B * gamma
     assert np.all((gd >= 0) & (gd < V))
     if gq is not None:
         np.testing.assert_allclose(gq.sum(-1), 1.0, atol=1e-4)
-    log(f"[drafter] drafts {gd.tolist()}: {steps} of {B * gamma} steps compared, {div} diverged at a flagged step")
+    log(f"[drafter] drafts {gd.tolist()}: {n}")
 
 
 def test_invalid_rows_and_bf16_q():
@@ -145,6 +144,6 @@ def test_full_size(full_case, B, T, qdt):
                                      "kv_v": [a[:B] for a in c.kv_v]})
     log(f"[drafter full] B={B} T={T}")
     gd, gq, out = run(c, True, 4, T, q_dtype=qdt or torch.float32)
-    steps, div = compare(c, out, gd, gq, f"full B={B} T={T}")
-    log(f"[drafter full] B={B} T={T} drafts {gd.tolist()}: {steps} of {B * 4} steps compared, {div} diverged")
-    assert steps >= B * 2
+    n = compare(c, out, gd, gq, f"full B={B} T={T}")
+    log(f"[drafter full] B={B} T={T} drafts {gd.tolist()}: {n}")
+    assert n["steps"] == B * 4

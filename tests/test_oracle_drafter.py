@@ -147,3 +147,78 @@ def test_invalid_rows_draft_nothing():
     t[2] = c.vocab + 5
     out = od.draft(weights(c), shared(c), t, c.h_target, 2, 1.0, 3)
     assert np.all(out["draft"][2] == -1) and np.all(out["draft"][:2] >= 0)
+
+
+@pytest.mark.parametrize("T", [0.0, 1.0])
+def test_forcing_own_drafts_changes_nothing_and_other_tokens_are_fed(T):
+    """force = the drafts the oracle draws reproduces the unforced result exactly; forcing
+    another token at step 0 changes what step 1 processes (the hidden state and the draw
+    of step 1 follow the forced token) while step 0 itself is unchanged."""
+    c = small()
+    w, kv = weights(c), shared(c)
+    free = od.draft(w, kv, c.last_token, c.h_target, 3, T, c.seed)
+    same = od.draft(w, kv, c.last_token, c.h_target, 3, T, c.seed, force=free["draft"])
+    for key in ("draft", "flags", "g"):
+        assert np.array_equal(free[key], same[key])
+    other = free["draft"].copy()
+    other[:, 0] = (other[:, 0] + 17) % c.vocab
+    other[:, 1:] = -1                               # later steps keep their own drafts
+    forced = od.draft(w, kv, c.last_token, c.h_target, 3, T, c.seed, force=other)
+    assert np.array_equal(forced["draft"][:, 0], free["draft"][:, 0])
+    assert np.array_equal(forced["g"][0], free["g"][0])
+    assert not np.array_equal(forced["g"][1], free["g"][1])
+    # and step 1 of the forced run is the unforced step taken from the forced token
+    tok = other[:, 0].astype(np.int64)
+    g1 = od.step_hidden(w, kv, tok, free["g"][0], 1)
+    assert np.array_equal(g1, forced["g"][1])
+
+
+def _draw_over(w, g_bits, clusters, T, seed, pos, b):
+    """The draft of row b drawn over the member tokens of ``clusters`` (brute force)."""
+    from oracle import philox
+    from oracle.bf16 import bf16_to_f64
+    cs = c_size(w)
+    toks = (np.sort(np.asarray(clusters))[:, None] * cs + np.arange(cs)[None, :]).reshape(-1)
+    l32 = (bf16_to_f64(g_bits[b]) @ bf16_to_f64(w.embed[toks]).T).astype(np.float32)
+    if T == 0.0:
+        return int(toks[np.argmax(l32)])
+    q = rules.target_probs(l32, T).astype(np.float32)
+    U = philox.gumbel_uniform_rows(seed, [b], [pos], w.vocab, tag=philox.TAG_DRAFT)[0][toks].astype(np.float32)
+    sc = np.where(q > 0, np.log(q) + (-np.log(-np.log(U))), -np.inf)
+    return int(toks[np.argmax(sc)])
+
+
+def c_size(w):
+    return w.vocab // w.centroids.shape[0]
+
+
+@pytest.mark.parametrize("T", [0.0, 1.0])
+def test_cut_flags_by_moving_each_band_cluster(T):
+    """A step is cut-flagged only if moving a cluster of the band across the cut can change
+    its draft: for every unflagged row, dropping any kept band cluster or adding any
+    excluded one (one at a time) leaves the draft unchanged (brute force), and a margin
+    of 0 gives an empty band."""
+    c = small(B=3, top_k=8)
+    w, kv = weights(c), shared(c)
+    lens = c.length.astype(np.int64)
+    g = od.step_hidden(w, kv, c.last_token.astype(np.int64), c.h_target, 0)
+    ids, l64, _ = od.scored_logits(w, g)
+    ok = np.ones(3, bool)
+    x, _, _ = od.sample_step(ids, l64, c.vocab, T, c.seed, lens + 1, ok)
+    assert all(not a and not e for a, e in od.cut_band(w, g, 0.0))
+    checked = 0
+    for mg in (0.05, 0.2, 0.5):
+        flags, band = od.cut_flags(w, g, ids, l64, x, T, c.seed, lens + 1, ok, mg)
+        sel = (ids[:, ::c_size(w)] // c_size(w))
+        for b in range(3):
+            if flags[b]:
+                continue
+            kept = set(sel[b].tolist())
+            near_in, near_out = band[b]
+            for cl in near_in:
+                assert _draw_over(w, g, sorted(kept - {cl}), T, c.seed, int(lens[b] + 1), b) == x[b]
+                checked += 1
+            for cl in near_out:
+                assert _draw_over(w, g, sorted(kept | {cl}), T, c.seed, int(lens[b] + 1), b) == x[b]
+                checked += 1
+    assert checked > 0

@@ -20,7 +20,7 @@ import torch
 __all__ = ["SV_F32", "SV_BF16", "SV_IN_LOGITS", "SV_IN_HIDDEN", "SV_IN_TOKENS", "VerifyError",
            "Model", "KVCache", "Workspace", "lm_head_model", "logits_model", "decoder_model",
            "verify_forward", "spec_verify_greedy", "spec_verify_sample", "library", "library_path",
-           "timing_enable", "timing_read", "LAYER_KEYS", "MaskedHead", "masked_head", "draft_masked_logits"]
+           "timing_enable", "timing_read", "set_option", "SV_OPT_WAIT_LIMIT", "LAYER_KEYS", "MaskedHead", "masked_head", "draft_masked_logits"]
 
 SV_F32, SV_BF16 = 0, 1
 SV_IN_LOGITS, SV_IN_HIDDEN, SV_IN_TOKENS = 0, 1, 2
@@ -104,6 +104,8 @@ def library():
               lib.sv_timing_read, lib.draft_masked_logits, lib.spec_verify_sample_filtered, lib.mtp_draft,
               lib.round_pad_drafts, lib.round_update_gamma, lib.round_select_candidates):
         f.restype = i32
+    lib.sv_set_option.argtypes = [i32, ctypes.c_int64]
+    lib.sv_set_option.restype = i32
     lib.sv_version.restype = i32
     lib.sv_status_string.restype = ctypes.c_char_p
     lib.sv_status_string.argtypes = [i32]
@@ -218,11 +220,20 @@ class KVCache:
         return s
 
 
+SV_OPT_WAIT_LIMIT = 0
+
+
+def set_option(option, value):
+    """Process-wide library option (C: sv_set_option); value < 0 restores the default."""
+    _check(library().sv_set_option(int(option), int(value)))
+
+
 class Workspace:
     """Caller-owned scratch for the library, grown on demand (one per device).
     Allocated zero-filled, as the library requires of a new workspace (it keeps
     counters and a launch epoch in it between calls).  ``reset()`` zero-fills it
-    again, e.g. after a step that timed out."""
+    again (needed only after a sampling step that found part of its grid not
+    started; see the header)."""
 
     def __init__(self):
         self.buf = None

@@ -15,6 +15,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -89,10 +90,8 @@ sv_status dev_info(DevInfo* out) {
   return SV_OK;
 }
 
-int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  return v && *v ? atoi(v) : dflt;
-}
+// Process-wide options (sv_set_option).
+std::atomic<unsigned> g_wait_limit{HEAD_SPIN_LIMIT};
 
 // ---------------------------------------------------------------------------
 // timing with events on the caller's stream
@@ -227,11 +226,7 @@ GemmPlan plan_gemm(int M, int N_total_tiles, int K, size_t lds_limit = 0) {
   return p;
 }
 
-int gemm_grid_x(const GemmPlan& p, const DevInfo& di) {
-  const int per_cu = env_int("SV_GEMM_WG_PER_CU", 1);
-  int g = di.cus * (per_cu > 0 ? per_cu : 1);
-  return std::max(1, std::min(g, p.grid_x_max));
-}
+int gemm_grid_x(const GemmPlan& p, const DevInfo& di) { return std::max(1, std::min(di.cus, p.grid_x_max)); }
 
 template <int MB>
 sv_status launch_gemm_mb(const GemmPlan& p, const GemmArgs& a, dim3 grid, hipStream_t s) {
@@ -300,32 +295,30 @@ int head_nb_max(int S) { return S == 4 ? 5 : 3; }
 // tried in the order 4, 8, 6 for products (decoder linears, verify_forward) and 6, 4, 8
 // for the LM-head launch that applies the rule (rule = true; 805 MB head, K = 1536:
 // 130.6 us against 137.1 us with items of 4).  only_s != 0 admits that split factor
-// alone.  SV_HEAD_S, SV_HEAD_GRP and SV_HEAD_WG_PER_CU override the choices.
+// alone.  The plan depends on the shapes and the device only, so the summation order
+// (and so every logit bit) is the same from call to call.
 HeadPlan plan_head(int M, int K, const int* N, int nseg, const DevInfo& di, bool rule = false, int only_s = 0) {
   HeadPlan p;
   if (M < 1 || M > HEAD_MAX_ROWS || K % 8) return p;
   for (int i = 0; i < nseg; ++i)    // weights are addressed with 32-bit byte offsets
     if (int64_t(N[i]) * K * 2 > int64_t(0xffffffffLL) - 4096) return p;
-  const int want_s = env_int("SV_HEAD_S", 0), want_grp = env_int("SV_HEAD_GRP", 0);
-  const int per_cu = std::max(1, env_int("SV_HEAD_WG_PER_CU", 1));
   const int order_product[3] = {4, 8, 6}, order_rule[3] = {6, 4, 8};
   const int* order = rule ? order_rule : order_product;
   for (int S : {4, 2}) {
-    if ((want_s && S != want_s) || (only_s && S != only_s)) continue;
+    if (only_s && S != only_s) continue;
     const int TR = 16 / S, NB = (M + TR - 1) / TR;
     if (NB > head_nb_max(S) || K % (32 * S)) continue;
     const int steps = K / (32 * S);
     int GRP = 0;
     for (int i = 0; i < 3; ++i) {
       const int gc = order[i];
-      if (want_grp && gc != want_grp) continue;
       if (steps % gc == 0) { GRP = gc; break; }
     }
-    if (!GRP) GRP = want_grp ? want_grp : 4;   // the last item of a tile runs past K over zeros in X
+    if (!GRP) GRP = 4;   // the last item of a tile runs past K over zeros in X
     const int gpt = (steps + GRP - 1) / GRP, Kp = gpt * GRP * 32 * S;
     int ntiles = 0;
     for (int i = 0; i < nseg; ++i) ntiles += (N[i] + TR - 1) / TR;
-    int grid = std::min(di.cus * per_cu, GEMM_MAX_WG);
+    int grid = std::min(di.cus, GEMM_MAX_WG);
     grid = std::max(1, std::min(grid, (ntiles + HEAD_WAVES - 1) / HEAD_WAVES));
     const int tpw = (ntiles + grid * HEAD_WAVES - 1) / (grid * HEAD_WAVES) * HEAD_WAVES;
     const size_t lds = head_lds(M, Kp, S, tpw * TR);
@@ -402,18 +395,23 @@ sv_status head_set_lds(const void* fn, size_t lds) {
   return SV_OK;
 }
 
-// Whether every workgroup of the plan can be resident at once (the fused sampler's
-// grid barrier needs it).
+// Whether the fused sampler can run: its workgroups wait for each other, so they must
+// all be resident at once.  The step runs only at one workgroup per CU with the whole
+// grid within the CUs and within what the occupancy query admits; otherwise the
+// two-launch path runs.  A plain launch does not promise co-residency (with two
+// workgroups per CU the query admitted the grid, yet in back-to-back launches some
+// workgroups started only after others had given up waiting), and a cooperative launch,
+// which would, cost 16-18 us more per step on this device than the whole tail; the
+// bounded waits and the epoch check handle the case (see k_head).  The group merge
+// takes a lane per member.
 sv_status head_all_resident(const HeadPlan& p, const DevInfo& di, bool* yes) {
+  *yes = false;
   const void* fn = head_fn(p);
   sv_status st = head_set_lds(fn, p.lds);
   if (st) return st;
   int per_cu = 0;
   SV_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, HEAD_WAVES * 64, p.lds));
-  // One workgroup per CU at most: with two per CU the occupancy query allowed the grid,
-  // yet back-to-back launches did not always have every workgroup resident and the
-  // bounded waits timed out.  The group merge takes a lane per member.
-  *yes = per_cu >= 1 && p.grid <= di.cus && p.grid <= 64 * CNT_GROUPS;
+  *yes = per_cu >= 1 && p.grid <= per_cu * di.cus && p.grid <= di.cus && p.grid <= 64 * CNT_GROUPS;
   return SV_OK;
 }
 
@@ -806,8 +804,7 @@ sv_status run_logits(const sv_model* m, const Shape& sh, const void* input, cons
       a.spart = at<SamplePart>(ws, L.spart);
       a.recs = rule->sample ? at<unsigned long long>(ws, L.recs) : nullptr;   // planned whenever this path can run
       a.rec_grid = GEMM_MAX_WG;
-      // SV_HEAD_SPIN_LIMIT lowers the bounded wait (tests force its timeout path with 0)
-      a.spin_limit = unsigned(env_int("SV_HEAD_SPIN_LIMIT", int(HEAD_SPIN_LIMIT)));
+      a.spin_limit = g_wait_limit.load(std::memory_order_relaxed);   // sv_set_option(SV_OPT_WAIT_LIMIT)
       rule->done = fused;
       rule->accepted = true;
     }
@@ -1405,6 +1402,18 @@ sv_status round_select_candidates(int32_t B, int32_t C, int32_t G1, const int32_
                      n_accepted, tokens, B, C, G1, best, n_out, tokens_out);
   SV_HIP(hipGetLastError());
   return SV_OK;
+}
+
+sv_status sv_set_option(int32_t option, int64_t value) {
+  g_err.clear();
+  switch (option) {
+    case SV_OPT_WAIT_LIMIT:
+      g_wait_limit.store(value < 0 ? HEAD_SPIN_LIMIT : unsigned(std::min<int64_t>(value, 0xfffffff0LL)),
+                         std::memory_order_relaxed);
+      return SV_OK;
+    default:
+      return fail(SV_ERR_ARG, "unknown option %d", int(option));
+  }
 }
 
 int32_t sv_version(void) { return VERSION; }

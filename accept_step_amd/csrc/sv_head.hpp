@@ -62,8 +62,9 @@ constexpr int CNT_GRP_ARRIVE = 1 * CNT_LINE, CNT_GRP_DONE = 9 * CNT_LINE;
 // The fused sampler hands data between workgroups as epoch-tagged 64-bit words (value
 // bits low, launch epoch high) and needs no counter: readers poll until every word they
 // need carries the current epoch.  The epoch lives in the counter block: each launch
-// uses the stored value plus one and its finishing workgroup stores it.  POISON marks a
-// workspace whose step timed out (see HEAD_SAMPLE below).
+// uses the stored value plus one and its finishing workgroup stores it once every
+// workgroup is known to have read it.  POISON marks a workspace on which some workgroup
+// had not run when the step gave up (see HEAD_SAMPLE below).
 constexpr int CNT_EPOCH = 17 * CNT_LINE, CNT_FAIL = 18 * CNT_LINE;
 constexpr unsigned EPOCH_POISON = 0xffffffffu;
 
@@ -871,11 +872,13 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   //      (same inputs, same arithmetic, same n), draws the Gumbel-max of row n over its
   //      slice and publishes its slice winner;
   //   4. workgroup 0 merges the winners, writes the outputs and stores the epoch.
-  // A wait that times out (the device could not run every workgroup at once) makes the
-  // step report every sequence invalid and poisons the workspace: a workgroup that
-  // started after the step gave up could otherwise leave records that a later launch
-  // takes for its own.  Later calls then report every sequence invalid until the
-  // workspace is zero-filled again.
+  // A wait that times out makes the step report every sequence invalid.  Workgroup 0
+  // still advances the stored epoch if every workgroup has published its statistics
+  // record (so every one of them read the epoch), and the next launch -- which starts
+  // after every workgroup of this one has ended -- ignores the records this one left.
+  // Only if some workgroup had not published (the device could not hold the whole grid)
+  // does it mark the workspace, so that such a late workgroup publishes nothing; calls
+  // on that workspace then report every sequence invalid until it is zero-filled.
   const unsigned ep = s_ep;
   const unsigned G = min(gridDim.x, unsigned(CNT_GROUPS));
   const int RG = a.rec_grid;
@@ -1059,9 +1062,12 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
           const float scp = t * LN2 - lnz + Gv;
           if (scp > sp) { sp = scp; ip = v; }
           if (resid) {
-            const float rr = fmaxf(exp2f(t) * inv_z - q_value(ac, qr[e]), 0.0f);
+            // where q is zero the residual is p itself: score it with p's expression, so
+            // a padded slot (q = 0 everywhere) draws exactly the bonus draw's token
+            const float qv = q_value(ac, qr[e]);
+            const float rr = fmaxf(exp2f(t) * inv_z - qv, 0.0f);
             if (rr > 0.0f) {
-              const float sc = __logf(rr) + Gv;
+              const float sc = qv == 0.0f ? scp : __logf(rr) + Gv;
               if (sc > sr) { sr = sc; ir = v; }
             }
           }
@@ -1133,7 +1139,16 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
     ac.n_accepted[b] = n;
     if (ac.len && n >= 0) ac.len[b] += n + 1;
   }
-  if (threadIdx.x == 0) atomic_store_agent(a.counter + CNT_EPOCH, done ? ep : EPOCH_POISON);
+  // every winner arrived: every workgroup has run; otherwise look for each one's
+  // statistics record (published right after its stream)
+  bool all_ran = done;
+  if (!done) {
+    bool mine = true;
+    for (int p = threadIdx.x; p < int(gridDim.x); p += blockDim.x)
+      mine = mine && tag_is(get_tagged(r_part + size_t(p) * M * 4), ep);
+    all_ran = __syncthreads_and(mine);
+  }
+  if (threadIdx.x == 0) atomic_store_agent(a.counter + CNT_EPOCH, all_ran ? ep : EPOCH_POISON);
 }
 
 }  // namespace sv

@@ -35,10 +35,13 @@
  *             scratch out of the first 4096 bytes (that state), so one workspace
  *             serves all of them.  The sampling step with a
  *             small batch runs as one kernel whose workgroups wait for each other
- *             (bounded): if the device cannot run them all at once for about a
- *             second (e.g. it is shared), the step reports every sequence invalid
- *             (see Data errors) and so does every later sampling call on that
- *             workspace until it is zero-filled again.
+ *             (bounded; one workgroup per compute unit): if a wait gives up (about a
+ *             second, e.g. on a device shared with other work; see
+ *             SV_OPT_WAIT_LIMIT), the step reports every sequence invalid (see Data
+ *             errors) and the next call on the workspace runs normally.  Only if
+ *             some workgroup of such a step had not even run does the step mark the
+ *             workspace, and later sampling calls on it report every sequence invalid
+ *             until it is zero-filled.
  *   Streams:  stream is a hipStream_t (NULL = the null stream).  All work is
  *             enqueued on it and the call returns before it completes;
  *             outputs are valid once the caller synchronises the stream.
@@ -336,6 +339,16 @@ sv_status round_update_gamma(int32_t B, const int32_t* n_accepted, int32_t* gamm
 sv_status round_select_candidates(int32_t B, int32_t C, int32_t G1, const int32_t* n_accepted,
                                   const int32_t* tokens, int32_t* best, int32_t* n_out, int32_t* tokens_out,
                                   void* stream);
+
+/* Process-wide options (every device, every later call).
+ *   SV_OPT_WAIT_LIMIT: polls that each bounded wait between the workgroups of the
+ *     fused sampling step makes before it gives up (default 1048576, about a second).
+ *     A step whose wait gives up reports every sequence invalid; the workspace stays
+ *     usable.  Small values force that path (tests of failure handling); value < 0
+ *     restores the default.
+ * Returns SV_ERR_ARG for an unknown option. */
+typedef enum sv_option { SV_OPT_WAIT_LIMIT = 0 } sv_option;
+sv_status sv_set_option(int32_t option, int64_t value);
 
 /* Library version (major * 10000 + minor * 100 + patch). */
 int32_t sv_version(void);

@@ -212,3 +212,12 @@ def test_round_policy_argument_errors(lib):
     assert lib.round_select_candidates(2, 3, 1, FAKE, FAKE, None, FAKE, FAKE, None) == 1
     assert lib.round_select_candidates(2, 0, 5, FAKE, FAKE, None, FAKE, FAKE, None) == 1
     assert lib.round_select_candidates(2, 3, 5, FAKE, None, None, FAKE, FAKE, None) == 1
+
+
+def test_options(lib):
+    """sv_set_option: the wait limit is accepted (and restored), an unknown option is an
+    argument error with a message; no device is touched."""
+    assert lib.sv_set_option(sv.SV_OPT_WAIT_LIMIT, 0) == 0
+    assert lib.sv_set_option(sv.SV_OPT_WAIT_LIMIT, -1) == 0
+    assert lib.sv_set_option(12345, 1) == 1
+    assert b"unknown option" in lib.sv_last_error()

@@ -19,7 +19,7 @@ import torch
 
 __all__ = ["SV_F32", "SV_BF16", "SV_IN_LOGITS", "SV_IN_HIDDEN", "SV_IN_TOKENS", "VerifyError",
            "Model", "KVCache", "Workspace", "lm_head_model", "logits_model", "decoder_model",
-           "verify_forward", "spec_verify_greedy", "spec_verify_sample", "library", "library_path",
+           "verify_forward", "spec_verify_greedy", "spec_verify_sample", "spec_verify_sample_noalloc", "library", "library_path",
            "timing_enable", "timing_read", "set_option", "SV_OPT_WAIT_LIMIT", "LAYER_KEYS", "MaskedHead", "masked_head", "draft_masked_logits"]
 
 SV_F32, SV_BF16 = 0, 1
@@ -92,6 +92,8 @@ def library():
     lib.spec_verify_greedy.argtypes = [M, i32, vp, i32, i32, vp, KV, vp, vp, vp, vp, sz, vp]
     lib.spec_verify_sample.argtypes = [M, i32, vp, i32, i32, vp, vp, i32, ctypes.c_float, ctypes.c_uint64, vp,
                                        KV, vp, vp, vp, vp, sz, vp]
+    lib.spec_verify_sample_noalloc.argtypes = [M, i32, vp, i32, i32, vp, vp, i32, ctypes.c_float, ctypes.c_uint64,
+                                               vp, KV, vp, vp, vp, vp]
     lib.spec_verify_sample_filtered.argtypes = [M, i32, vp, i32, i32, vp, vp, i32, ctypes.c_float, i32,
                                                 ctypes.c_float, ctypes.c_uint64, vp, KV, vp, vp, vp, vp, sz, vp]
     lib.draft_masked_logits.argtypes = [ctypes.POINTER(_SvMaskedHead), vp, i32, i32, vp, vp, vp, vp, sz, vp]
@@ -100,7 +102,8 @@ def library():
     lib.round_pad_drafts.argtypes = [i32, i32, i32, vp, vp, vp, i32, ctypes.c_float, vp, sz, vp]
     lib.round_update_gamma.argtypes = [i32, vp, vp, i32, i32, vp]
     lib.round_select_candidates.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp]
-    for f in (lib.verify_forward, lib.spec_verify_greedy, lib.spec_verify_sample, lib.sv_timing_enable,
+    for f in (lib.verify_forward, lib.spec_verify_greedy, lib.spec_verify_sample, lib.spec_verify_sample_noalloc,
+              lib.sv_timing_enable,
               lib.sv_timing_read, lib.draft_masked_logits, lib.spec_verify_sample_filtered, lib.mtp_draft,
               lib.round_pad_drafts, lib.round_update_gamma, lib.round_select_candidates):
         f.restype = i32
@@ -338,6 +341,32 @@ def spec_verify_sample(model, kind, inp, B, gamma, draft, q, temperature, seed, 
                    float(temperature), ctypes.c_uint64(int(seed)), _ptr(pos0),
                    ctypes.byref(kvs) if kvs is not None else None, _ptr(n), _ptr(tok), _ptr(logits_out)),
                   inp.device, ws, stream)
+    return n, tok
+
+
+def spec_verify_sample_noalloc(model, kind, inp, B, gamma, draft, q, temperature, seed, pos0, kv=None,
+                               logits_out=None, out=None, stream=None):
+    """spec_verify_sample without a workspace (C: spec_verify_sample_noalloc): the library's
+    fixed per-device scratch array serves instead; nothing is allocated by the library.
+    Returns (n_accepted, tokens_out); ``out`` may supply them."""
+    lib = library()
+    inp = _kind_input(kind, inp)
+    _dev_tensor(draft, "draft", torch.int32)
+    _dev_tensor(q, "q")
+    _dev_tensor(pos0, "pos0", torch.int64)
+    _dev_tensor(logits_out, "logits_out", torch.float32)
+    if q.dtype == torch.bfloat16:
+        qd = SV_BF16
+    elif q.dtype == torch.float32:
+        qd = SV_F32
+    else:
+        raise ValueError("q must be float32 or bfloat16")
+    n, tok = _outs(B, gamma, inp.device, out)
+    kvs = kv.struct() if kv is not None else None
+    _check(lib.spec_verify_sample_noalloc(ctypes.byref(model.struct), kind, _ptr(inp), B, gamma, _ptr(draft), _ptr(q),
+                                          qd, float(temperature), ctypes.c_uint64(int(seed)), _ptr(pos0),
+                                          ctypes.byref(kvs) if kvs is not None else None, _ptr(n), _ptr(tok),
+                                          _ptr(logits_out), _stream(stream)))
     return n, tok
 
 

@@ -32,6 +32,10 @@
 
 using namespace sv;
 
+// The scratch array of spec_verify_sample_noalloc (see below); file scope.
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(4) << 20;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 constexpr int32_t VERSION = 10000;   // 1.0.0
@@ -94,6 +98,15 @@ sv_status dev_info(DevInfo* out) {
 std::atomic<unsigned> g_wait_limit{HEAD_SPIN_LIMIT};
 
 // ---------------------------------------------------------------------------
+// The scratch of spec_verify_sample_noalloc: a fixed device array, one copy per device
+// the library runs on, kept until the process ends.  Host code never uses its name as an
+// address (that is a host-side stand-in): each device's address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and only that
+// address is passed to kernels.  Its first CNT_BYTES (the counter block) start at zero
+// (cleared by a fill kernel when the address is taken) and every call leaves them so.
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch;   // per device
+
 // timing with events on the caller's stream
 struct Timer {
   std::mutex mu;
@@ -793,7 +806,10 @@ sv_status run_logits(const sv_model* m, const Shape& sh, const void* input, cons
       bool fused = !rule->sample;
       if (rule->sample && (st = head_all_resident(hp, di, &fused))) return st;
       a.mode = !rule->sample ? HEAD_ACCEPT : (fused ? HEAD_SAMPLE : HEAD_ACCEPT);
-      if (rule->sample && !fused) out = logits;      // the separate sampler reads them
+      if (rule->sample && !fused) {
+        out = logits;                                // the separate sampler reads them
+        if (!out) return fail(SV_ERR_WORKSPACE, "the fused step does not apply on this device: no logits buffer");
+      }
       a.part = part;
       a.c_stat = c;
       a.xlogit = at<float>(ws, L.xlogit);
@@ -833,10 +849,31 @@ sv_status run_logits(const sv_model* m, const Shape& sh, const void* input, cons
   return SV_OK;
 }
 
+// Whether the bf16 LM-head step runs as the one fused launch that keeps the logits on
+// chip (the same decision run_logits takes on this device).
+sv_status fused_step(const sv_model* m, const Shape& sh, bool sample, bool* yes) {
+  *yes = false;
+  if (sh.M > HEAD_MAX_ROWS) return SV_OK;   // never fused, whatever the device
+  DevInfo di;
+  sv_status st = dev_info(&di);
+  if (st) return st;
+  const int K = sh.decoder ? m->d_model : sh.d;
+  const int Nv[1] = {sh.V};
+  const HeadPlan hp = plan_head_rule(sh.M, K, Nv, di);
+  if (!hp.ok) return SV_OK;
+  bool resident = true;
+  if (sample && (st = head_all_resident(hp, di, &resident))) return st;
+  *yes = resident;
+  return SV_OK;
+}
+
+// exact_query: with ws == NULL, report the bytes this call needs on the current device
+// (the plain query is device-independent and covers every path).
 sv_status verify_common(const sv_model* m, sv_input_kind kind, const void* input, int32_t B, int32_t gamma,
                         const int32_t* draft, const void* q, sv_dtype q_dtype, float temperature, uint64_t seed,
                         const int64_t* pos0, const sv_kv_cache* kv, int32_t* n_accepted, int32_t* tokens_out,
-                        float* logits_out, void* ws, size_t* ws_bytes, void* stream, bool sample) {
+                        float* logits_out, void* ws, size_t* ws_bytes, void* stream, bool sample,
+                        bool exact_query = false) {
   g_err.clear();
   Shape sh;
   sv_status st = check_common(m, kind, input, B, gamma, kv, &sh);
@@ -853,16 +890,32 @@ sv_status verify_common(const sv_model* m, sv_input_kind kind, const void* input
     if (!pos0) return fail(SV_ERR_ARG, "pos0 is NULL");
     if (q_dtype != SV_F32 && q_dtype != SV_BF16) return fail(SV_ERR_DTYPE, "q_dtype must be SV_F32 or SV_BF16");
   }
-  const bool need_buf = kind != SV_IN_LOGITS && logits_out == nullptr;
+  const bool bf16_head = kind != SV_IN_LOGITS && !(kind == SV_IN_HIDDEN && m->wdtype == SV_F32);
+  bool need_buf = kind != SV_IN_LOGITS && logits_out == nullptr;
   Layout L = plan(m, sh, kv, need_buf, sample);
+  // The fused step needs no logits buffer: where the caller's workspace is smaller than
+  // the device-independent size (or the exact size is asked for), see whether this device
+  // runs it (no device: keep the full size)
+  if (need_buf && bf16_head && ((ws && ws_bytes && *ws_bytes < L.total) || exact_query)) {
+    bool fused = false;
+    if (fused_step(m, sh, sample, &fused) != SV_OK) {
+      fused = false;
+      g_err.clear();
+    }
+    if (fused) {
+      need_buf = false;
+      L = plan(m, sh, kv, false, sample);
+    }
+  }
   bool query = false;
   if ((st = check_ws(ws, ws_bytes, L, &query))) return st;
   if (query) return SV_OK;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float c = sample ? LOG2E / temperature : 0.0f;
+  // (no buffer planned: the fused step keeps the logits on chip and never needs one)
   float* logits = kind == SV_IN_LOGITS ? const_cast<float*>(static_cast<const float*>(input))
-                                       : (logits_out ? logits_out : at<float>(ws, L.logits));
+                                       : (logits_out ? logits_out : need_buf ? at<float>(ws, L.logits) : nullptr);
   RowPart* part = at<RowPart>(ws, L.part);
   int* invalid = at<int>(ws, L.invalid);
   AcceptArgs aa;
@@ -875,7 +928,6 @@ sv_status verify_common(const sv_model* m, sv_input_kind kind, const void* input
   aa.n_accepted = n_accepted; aa.tokens_out = tokens_out;
   aa.state = at<SeqState>(ws, L.state);
   aa.seed = seed; aa.B = sh.B; aa.gamma = gamma; aa.V = sh.V; aa.c = c; aa.sample = sample ? 1 : 0;
-  const bool bf16_head = kind != SV_IN_LOGITS && !(kind == SV_IN_HIDDEN && m->wdtype == SV_F32);
   const bool fuse = bf16_head && sh.M <= FUSE_ACCEPT_MAX_ROWS;
   if (bf16_head) aa.xlogit = at<float>(ws, L.xlogit);
   int P = 0;
@@ -948,6 +1000,40 @@ sv_status spec_verify_sample(const sv_model* m, sv_input_kind kind, const void* 
                              float* logits_out, void* ws, size_t* ws_bytes, void* stream) {
   return verify_common(m, kind, input, B, gamma, draft, q, q_dtype, temperature, seed, pos0, kv, n_accepted,
                        tokens_out, logits_out, ws, ws_bytes, stream, true);
+}
+
+sv_status spec_verify_sample_noalloc(const sv_model* m, sv_input_kind kind, const void* input, int32_t B,
+                                     int32_t gamma, const int32_t* draft, const void* q, sv_dtype q_dtype,
+                                     float temperature, uint64_t seed, const int64_t* pos0, const sv_kv_cache* kv,
+                                     int32_t* n_accepted, int32_t* tokens_out, float* logits_out, void* stream) {
+  g_err.clear();
+  // the scratch this call needs (the size query of the workspace path: nothing launched)
+  size_t need = 0;
+  sv_status st = verify_common(m, kind, input, B, gamma, draft, q, q_dtype, temperature, seed, pos0, kv, n_accepted,
+                               tokens_out, logits_out, nullptr, &need, stream, true, true);
+  if (st) return st;
+  if (need > NOALLOC_SCRATCH_BYTES)
+    return fail(SV_ERR_UNSUPPORTED, "this request needs %zu bytes of scratch; the allocation-free entry point has %zu "
+                "(pass logits_out, or use spec_verify_sample with a workspace)", need, NOALLOC_SCRATCH_BYTES);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ptr = nullptr;
+  {
+    int dev = 0;
+    SV_HIP(hipGetDevice(&dev));
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (int(g_scratch.size()) <= dev) g_scratch.resize(dev + 1, nullptr);
+    if (!g_scratch[dev]) {
+      SV_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+      if (!ptr) return fail(SV_ERR_HIP, "hipGetSymbolAddress returned no address for the scratch array");
+      hipLaunchKernelGGL(k_zero_bytes, dim3(1), dim3(256), 0, s, static_cast<unsigned char*>(ptr), size_t(CNT_BYTES));
+      SV_HIP(hipGetLastError());
+      g_scratch[dev] = ptr;
+    }
+    ptr = g_scratch[dev];
+  }
+  size_t have = NOALLOC_SCRATCH_BYTES;
+  return verify_common(m, kind, input, B, gamma, draft, q, q_dtype, temperature, seed, pos0, kv, n_accepted,
+                       tokens_out, logits_out, ptr, &have, stream, true);
 }
 
 sv_status draft_masked_logits(const sv_masked_head* head, const void* hidden, int32_t M, int32_t top_k,

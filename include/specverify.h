@@ -182,6 +182,24 @@ sv_status spec_verify_sample(const sv_model* m, sv_input_kind kind, const void* 
                              const sv_kv_cache* kv, int32_t* n_accepted, int32_t* tokens_out,
                              float* logits_out, void* ws, size_t* ws_bytes, void* stream);
 
+/* spec_verify_sample without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops, harnesses that forbid
+ * allocation).  The same computation, outputs and bits as spec_verify_sample; its scratch
+ * is a fixed array of 4 MiB in the library's device memory, one per device, held until
+ * the process ends.  It makes no allocation and no memset: the array's counter block is
+ * cleared by a fill kernel on the first call on each device, and every call leaves it
+ * cleared.  All calls on one device share that array: calls that overlap in time on one
+ * device race (serialise them, e.g. on one stream).  A request whose scratch would
+ * exceed 4 MiB returns SV_ERR_UNSUPPORTED before anything is launched (the logits of the
+ * unfused path for large batches need more: pass logits_out, or use spec_verify_sample
+ * with a workspace).  Arguments as for spec_verify_sample. */
+sv_status spec_verify_sample_noalloc(const sv_model* m, sv_input_kind kind, const void* input,
+                                     int32_t B, int32_t gamma, const int32_t* draft,
+                                     const void* q, sv_dtype q_dtype, float temperature,
+                                     uint64_t seed, const int64_t* pos0,
+                                     const sv_kv_cache* kv, int32_t* n_accepted, int32_t* tokens_out,
+                                     float* logits_out, void* stream);
+
 /* Speculative sampling verify with the drafter's top-k / top-p filters applied alike to
  * the target ([Infra-ch8] "why the output does not change", [MTP-drafters] 5.2: the
  * sampling parameters must be handled by one rule in drafting and verifying;

@@ -221,3 +221,16 @@ def test_options(lib):
     assert lib.sv_set_option(sv.SV_OPT_WAIT_LIMIT, -1) == 0
     assert lib.sv_set_option(12345, 1) == 1
     assert b"unknown option" in lib.sv_last_error()
+
+
+def test_noalloc_refuses_oversized_request_without_device(lib):
+    """The allocation-free entry point checks its scratch size on the host, before any
+    device call: a request whose scratch exceeds the fixed array is SV_ERR_UNSUPPORTED."""
+    m = _model(vocab=65536, d=256)
+    st = lib.spec_verify_sample_noalloc(ctypes.byref(m), sv.SV_IN_HIDDEN, FAKE, 64, 8, FAKE, FAKE, sv.SV_BF16,
+                                        ctypes.c_float(1.0), ctypes.c_uint64(1), FAKE, None, FAKE, FAKE, None, None)
+    assert st == 6 and b"scratch" in lib.sv_last_error()
+    # argument errors come first, as on the workspace entry point
+    st = lib.spec_verify_sample_noalloc(ctypes.byref(m), sv.SV_IN_HIDDEN, FAKE, 1, 0, FAKE, FAKE, sv.SV_BF16,
+                                        ctypes.c_float(1.0), ctypes.c_uint64(1), FAKE, None, FAKE, FAKE, None, None)
+    assert st == 1

@@ -31,6 +31,7 @@ import numpy as np
 METRIC = "verified tokens/s + verify-step HBM GB/s (% of MI355X peak), γ=4, V=262144"
 HBM_PEAK_GBS = 8000.0
 N_SETS = 8
+POS_STRIDE = 11            # positions between consecutive timed steps (more than gamma + 1)
 
 
 def parse():
@@ -88,20 +89,25 @@ def main():
     def to_dev_bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    # ---- inputs (resident in HBM before timing)
+    # ---- inputs (resident in HBM before timing): the large-vocab workload at T = 1 (the
+    # headline) and T = 0, eight independent input sets each over one table
     B, gamma, T = 1, 4, 1.0
-    cases = []
-    w = None
-    for s in range(N_SETS):
-        cs = workloads.lm_head_case(262144, 1536, B, gamma, T, 1.0, 3, w=w, pos0=7 * s, variant=s)
+    V, d = 262144, 1536
+    cases, cases0, w = [], [], None
+    for s_ in range(N_SETS):
+        cs = workloads.lm_head_case(V, d, B, gamma, T, 1.0, 3, w=w, pos0=7 * s_, variant=s_)
         w = cs.w
         cases.append(cs)
+        cases0.append(workloads.lm_head_case(V, d, B, gamma, 0.0, 1.0, 3, w=w, pos0=7 * s_, variant=s_))
     W = to_dev_bf16(w)
     model = sv.lm_head_model(W)
-    sets = []
-    for cs in cases:
-        sets.append((to_dev_bf16(cs.h), torch.from_numpy(cs.draft.astype(np.int32)).to(dev), to_dev_bf16(cs.q),
-                     torch.from_numpy(cs.pos0).to(dev)))
+    sets = [(to_dev_bf16(cs.h), torch.from_numpy(cs.draft.astype(np.int32)).to(dev), to_dev_bf16(cs.q))
+            for cs in cases]
+    # step i verifies at positions pos0 + POS_STRIDE * i, so every step draws its own
+    # acceptance uniforms and noise (as consecutive rounds of one sequence would)
+    pos_all = torch.from_numpy(np.stack([cases[i % N_SETS].pos0 + POS_STRIDE * i
+                                         for i in range(max(args.steps, args.warmup))])).to(dev)
+    sets0 = [(to_dev_bf16(cs.h), torch.from_numpy(cs.draft.astype(np.int32)).to(dev)) for cs in cases0]
     K, Wm = args.steps, args.warmup
     n_out = torch.empty((K, B), dtype=torch.int32, device=dev)
     t_out = torch.empty((K, B, gamma + 1), dtype=torch.int32, device=dev)
@@ -109,8 +115,12 @@ def main():
     seed = cases[0].seed
 
     def step(i, out=None):
-        h, d, q, p0 = sets[i % N_SETS]
-        return sv.spec_verify_sample(model, sv.SV_IN_HIDDEN, h, B, gamma, d, q, T, seed, p0, out=out, ws=ws)
+        h, dr, q = sets[i % N_SETS]
+        return sv.spec_verify_sample(model, sv.SV_IN_HIDDEN, h, B, gamma, dr, q, T, seed, pos_all[i], out=out, ws=ws)
+
+    def step0(i, out=None):
+        h, dr = sets0[i % N_SETS]
+        return sv.spec_verify_greedy(model, sv.SV_IN_HIDDEN, h, B, gamma, dr, out=out, ws=ws)
 
     if args.calibration_copy_mib:
         src = torch.empty(args.calibration_copy_mib << 18, dtype=torch.float32, device=dev).fill_(1.0)
@@ -120,28 +130,30 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    for i in range(Wm):
-        step(i)
-    torch.cuda.synchronize()
-
     # ---- timed region.  One pair of HIP events on the stream the library launches on
     # (torch's current stream) brackets the K launches: at this batch a step is one
     # launch of the fused kernel, so the event time over K is that kernel's average
     # duration per launch, launch gaps included (an upper bound on its own duration).
     # Events around every launch would cost the GPU ~7 us per step on this system.
     stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(K):
-        step(i, out=(n_out[i], t_out[i]))
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    gemm_ms, gemm_n = ev0.elapsed_time(ev1), K
 
+    def timed(fn, steps, warm):
+        for i in range(warm):
+            fn(i)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for i in range(steps):
+            fn(i, out=(n_out[i], t_out[i]))
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, ev0.elapsed_time(ev1)
+
+    elapsed, gemm_ms = timed(step, K, Wm)
+    gemm_n = K
     n_host = n_out.to(torch.int64).cpu()
+    tok_host = t_out.cpu().numpy()
     require_valid(n_host, "large-vocab")
     committed = int((n_host + 1).sum().item())
     value = committed / elapsed
@@ -150,9 +162,40 @@ def main():
     # algorithmic bytes of one step: W once, the hidden states, and the q row of each
     # rejected sequence (the residual draw); the q gathers at the drafts are negligible
     rejected = int((n_host < gamma).sum().item())
-    algo_bytes = 262144 * 1536 * 2 + B * (gamma + 1) * 1536 * 2 + rejected * 262144 * 2 / K
+    algo_bytes = V * d * 2 + B * (gamma + 1) * d * 2 + rejected * V * 2 / K
     achieved = algo_bytes / gemm_avg_s / 1e9
     traffic = committed_traffic(args.traffic_summary, root)
+    # acceptance of the timed steps: per slot, the rate of acceptance given the slot was
+    # reached, and the mean committed tokens per step
+    nn = n_host.numpy().reshape(-1)
+    alpha = [float((nn > i).sum() / max((nn >= i).sum(), 1)) for i in range(gamma)]
+
+    # ---- the greedy rule (T = 0) on the same table
+    n_h1, tok_h1 = n_host.clone(), tok_host.copy()
+    el0, ms0 = timed(step0, K, Wm)
+    n0_host = n_out.to(torch.int64).cpu()
+    require_valid(n0_host, "large-vocab T=0")
+    us0 = ms0 / K * 1e3
+    algo0 = V * d * 2 + B * (gamma + 1) * d * 2
+
+    # ---- configuration 4's B = 1, gamma = 4 point (d = 4096, 2,147,483,648 bytes of W)
+    c4 = workloads.batch_sweep(B=1, gamma=4)
+    model4 = sv.lm_head_model(to_dev_bf16(c4.w))
+    set4 = (to_dev_bf16(c4.h), torch.from_numpy(c4.draft.astype(np.int32)).to(dev), to_dev_bf16(c4.q),
+            torch.from_numpy(c4.pos0).to(dev))
+    del c4
+
+    def step4(i, out=None):
+        h, dr, q, p0 = set4
+        return sv.spec_verify_sample(model4, sv.SV_IN_HIDDEN, h, 1, 4, dr, q, 1.0, seed + 1, p0, out=out, ws=ws)
+
+    K4 = max(1, K // 2)
+    el4, ms4 = timed(step4, K4, max(2, Wm // 2))
+    n4 = n_out[:K4].to(torch.int64).cpu()
+    require_valid(n4, "config-4 B=1")
+    us4 = ms4 / K4 * 1e3
+    algo4 = 262144 * 4096 * 2 + 5 * 4096 * 2 + int((n4 < 4).sum().item()) * 262144 * 2 / K4
+    del model4, set4
 
     out = {
         "metric": METRIC,
@@ -169,11 +212,21 @@ def main():
         "data": "synthetic",
         "config": {"workload": "large-vocab verify: bf16 LM head V=262144 d=1536, B=1, gamma=4, T=1.0 sampling "
                                "(min(1,p/q) accept, residual/bonus resample)",
-                   "B": B, "gamma": gamma, "V": 262144, "d": 1536, "temperature": T,
+                   "B": B, "gamma": gamma, "V": V, "d": d, "temperature": T,
                    "committed_tokens": committed, "candidate_positions_per_s": round(B * (gamma + 1) * K / elapsed, 1),
                    "verify_steps_per_s": round(K / elapsed, 1),
                    "step_hbm_gbs": round(algo_bytes / (elapsed / K) / 1e9, 1),
-                   "step_frac_of_peak": round(algo_bytes / (elapsed / K) / 1e9 / HBM_PEAK_GBS, 4)},
+                   "step_frac_of_peak": round(algo_bytes / (elapsed / K) / 1e9 / HBM_PEAK_GBS, 4),
+                   "acceptance_per_slot": [round(a_, 4) for a_ in alpha],
+                   "mean_committed_per_step": round(float((nn + 1).mean()), 4),
+                   "greedy_T0": {"us_per_step": round(us0, 2), "verified_tokens_per_s": round(
+                       int((n0_host + 1).sum().item()) / el0, 1),
+                       "step_hbm_gbs": round(algo0 / (us0 * 1e-6) / 1e9, 1),
+                       "step_frac_of_peak": round(algo0 / (us0 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+                   "config4_B1_gamma4_T1": {"workload": "bf16 LM head V=262144 d=4096, B=1, gamma=4, T=1.0",
+                                            "us_per_step": round(us4, 2),
+                                            "step_hbm_gbs": round(algo4 / (us4 * 1e-6) / 1e9, 1),
+                                            "step_frac_of_peak": round(algo4 / (us4 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}},
         "roofline": {"bound": "hbm", "kernel": "k_head (fused verify step: LM-head product, row statistics, "
                                                 "acceptance, residual/bonus draw, commit)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -183,7 +236,12 @@ def main():
                      "launches": gemm_n},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cases, args.cpu_seconds, elapsed / K)
+        out["cpu_baseline"] = cpu_baseline(cases, args.cpu_seconds, elapsed / K, n_h1.numpy(), tok_h1)
+        # the pages' alpha = sum_v min(p, q) per slot over the sampled steps, and the
+        # expected committed tokens 1 + sum_k prod_{i<k} alpha_i ([Infra-ch8] "how the
+        # benefit is computed"), beside the measured mean of the timed steps
+        out["config"]["alpha_sum_min_pq_per_slot"] = out["cpu_baseline"].pop("alpha_per_slot")
+        out["config"]["expected_committed_closed_form"] = out["cpu_baseline"].pop("expected_committed")
     print(json.dumps(out), flush=True)
 
 
@@ -598,37 +656,69 @@ def kernel_source_hash(root):
     return h.hexdigest()[:16]
 
 
-def cpu_baseline(cases, budget_s, gpu_step_s):
-    """The oracle as it stands, on a bounded sample of the same workload: whole
-    verify steps (float64 logits from the bf16 table, then the sampling rule),
-    as many as fit in ``budget_s`` seconds (at least one)."""
+def cpu_baseline(cases, budget_s, gpu_step_s, gpu_n, gpu_tok):
+    """The oracle as it stands, on a bounded sample of the same workload: whole verify
+    steps (float64 logits from the bf16 table, then the sampling rule) of the timed
+    steps' input sets.  The method of [Self-spec] 5.1: three warm-up steps, then the
+    median of at least five timed steps (more while the budget lasts).  Each oracle step
+    is also compared with the GPU's output for the same input set (``gpu_n``/``gpu_tok``
+    of the timed steps): the mismatches not flagged by the oracle must be zero."""
     from oracle import bf16 as obf16
     from oracle import rules
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
-        cores = os.cpu_count() or 1
-    t0 = time.perf_counter()
-    steps = committed = 0
-    while True:
-        cs = cases[steps % len(cases)]
+        blas = os.cpu_count() or 1
+    checked = {"compared": 0, "mismatched": 0, "flagged": 0, "unflagged_mismatches": 0}
+    alphas = []
+
+    def one(j):
+        cs = cases[j % len(cases)]
         h = obf16.bf16_to_f64(cs.h)
         V = cs.w.shape[0]
         logits = np.empty(h.shape[:-1] + (V,))
         for v0 in range(0, V, 32768):
             logits[..., v0:v0 + 32768] = rules.lm_head_logits(h, obf16.bf16_to_f64(cs.w[v0:v0 + 32768]))
         qf = (cs.q.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
-        n, _, _ = rules.verify_sample(logits, cs.draft, qf, cs.temperature, cs.seed, cs.pos0)
-        committed += int((n + 1).sum())
-        steps += 1
-        if time.perf_counter() - t0 >= budget_s:
+        n, tok, fl = rules.verify_sample(logits, cs.draft, qf, cs.temperature, cs.seed, cs.pos0 + POS_STRIDE * j)
+        p = rules.target_probs(rules.f32_logits(logits[:, :-1]), cs.temperature).astype(np.float64)
+        alphas.append(np.minimum(p, qf).sum(axis=-1).mean(axis=0))
+        if j < len(gpu_n):
+            same = (gpu_n[j] == n) & np.all(gpu_tok[j] == tok, axis=1)
+            checked["compared"] += len(n)
+            checked["mismatched"] += int((~same).sum())
+            checked["flagged"] += int(fl.sum())
+            checked["unflagged_mismatches"] += int((~same & ~fl).sum())
+        return int((n + 1).sum())
+
+    for j in range(3):
+        one(j)
+    times, committed, j = [], 0, 3
+    t_start = time.perf_counter()
+    while len(times) < 5 or time.perf_counter() - t_start < budget_s:
+        t0 = time.perf_counter()
+        committed += one(j)
+        times.append(time.perf_counter() - t0)
+        j += 1
+        if len(times) >= 200:
             break
-    el = time.perf_counter() - t0
-    return {"value": round(committed / el, 3), "unit": "verified tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{steps} whole verify steps of the same workload (float64 numpy oracle, bf16 table "
-                      f"converted per 32768-row chunk inside the timed region), {el:.1f} s",
-            "ms_per_step": round(el / steps * 1e3, 1), "gpu_speedup": round((el / steps) / gpu_step_s, 1)}
+    med = float(np.median(times))
+    per_step_tokens = committed / len(times)
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except Exception:
+        affinity = os.cpu_count() or 1
+    a_ = np.mean(alphas, axis=0)
+    expected = 1.0 + sum(float(np.prod(a_[:k])) for k in range(1, len(a_) + 1))
+    return {"value": round(per_step_tokens / med, 3), "unit": "verified tokens/s", "cores": int(blas),
+            "alpha_per_slot": [round(float(x), 4) for x in a_], "expected_committed": round(expected, 4),
+            "kind": "oracle", "os_cpu_count": os.cpu_count(), "sched_affinity": affinity,
+            "sample": f"{len(times)} whole verify steps of the same workload timed after 3 warm-ups (float64 numpy "
+                      f"oracle, bf16 table converted per 32768-row chunk inside the timed region); value = mean "
+                      f"committed tokens per step / median step time",
+            "ms_per_step_median": round(med * 1e3, 1), "gpu_speedup": round(med / gpu_step_s, 1),
+            "parity_spot_check": checked}
 
 
 if __name__ == "__main__":

@@ -89,11 +89,11 @@ def library():
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)
     M, KV = ctypes.POINTER(_SvModel), ctypes.POINTER(_SvKV)
     lib.verify_forward.argtypes = [M, i32, vp, i32, i32, KV, vp, vp, sz, vp]
-    lib.spec_verify_greedy.argtypes = [M, i32, vp, i32, i32, vp, KV, vp, vp, vp, vp, sz, vp]
+    lib.spec_verify_greedy.argtypes = [M, i32, vp, i32, i32, vp, KV, vp, vp, vp, vp, vp, sz, vp]
     lib.spec_verify_sample.argtypes = [M, i32, vp, i32, i32, vp, vp, i32, ctypes.c_float, ctypes.c_uint64, vp,
-                                       KV, vp, vp, vp, vp, sz, vp]
+                                       KV, vp, vp, vp, vp, vp, sz, vp]
     lib.spec_verify_sample_noalloc.argtypes = [M, i32, vp, i32, i32, vp, vp, i32, ctypes.c_float, ctypes.c_uint64,
-                                               vp, KV, vp, vp, vp, vp]
+                                               vp, KV, vp, vp, vp, vp, vp]
     lib.spec_verify_sample_filtered.argtypes = [M, i32, vp, i32, i32, vp, vp, i32, ctypes.c_float, i32,
                                                 ctypes.c_float, ctypes.c_uint64, vp, KV, vp, vp, vp, vp, sz, vp]
     lib.draft_masked_logits.argtypes = [ctypes.POINTER(_SvMaskedHead), vp, i32, i32, vp, vp, vp, vp, sz, vp]
@@ -303,23 +303,26 @@ def _outs(B, gamma, device, out):
 
 
 def spec_verify_greedy(model, kind, inp, B, gamma, draft=None, kv=None, logits_out=None, out=None, ws=None,
-                       stream=None):
-    """Greedy verify (C: spec_verify_greedy).  Returns (n_accepted [B], tokens_out [B, gamma+1])."""
+                       stream=None, diag=None):
+    """Greedy verify (C: spec_verify_greedy).  Returns (n_accepted [B], tokens_out [B, gamma+1]).
+    ``diag``: optional float32 [B, gamma+1] filled with the per-slot margins."""
     lib = library()
     inp = _kind_input(kind, inp)
     _dev_tensor(draft, "draft", torch.int32)
     _dev_tensor(logits_out, "logits_out", torch.float32)
+    _dev_tensor(diag, "diag", torch.float32)
     n, tok = _outs(B, gamma, inp.device, out)
     kvs = kv.struct() if kv is not None else None
     _call_with_ws(lib.spec_verify_greedy,
                   (ctypes.byref(model.struct), kind, _ptr(inp), B, gamma, _ptr(draft),
-                   ctypes.byref(kvs) if kvs is not None else None, _ptr(n), _ptr(tok), _ptr(logits_out)),
+                   ctypes.byref(kvs) if kvs is not None else None, _ptr(n), _ptr(tok), _ptr(logits_out),
+                   _ptr(diag)),
                   inp.device, ws, stream)
     return n, tok
 
 
 def spec_verify_sample(model, kind, inp, B, gamma, draft, q, temperature, seed, pos0, kv=None, logits_out=None,
-                       out=None, ws=None, stream=None):
+                       out=None, ws=None, stream=None, diag=None):
     """Speculative-sampling verify (C: spec_verify_sample).  ``q`` is float32 or
     bfloat16 [B, gamma, V]; ``pos0`` int64 [B].  Returns (n_accepted, tokens_out)."""
     lib = library()
@@ -334,18 +337,20 @@ def spec_verify_sample(model, kind, inp, B, gamma, draft, q, temperature, seed, 
         qd = SV_F32
     else:
         raise ValueError("q must be float32 or bfloat16")
+    _dev_tensor(diag, "diag", torch.float32)
     n, tok = _outs(B, gamma, inp.device, out)
     kvs = kv.struct() if kv is not None else None
     _call_with_ws(lib.spec_verify_sample,
                   (ctypes.byref(model.struct), kind, _ptr(inp), B, gamma, _ptr(draft), _ptr(q), qd,
                    float(temperature), ctypes.c_uint64(int(seed)), _ptr(pos0),
-                   ctypes.byref(kvs) if kvs is not None else None, _ptr(n), _ptr(tok), _ptr(logits_out)),
+                   ctypes.byref(kvs) if kvs is not None else None, _ptr(n), _ptr(tok), _ptr(logits_out),
+                   _ptr(diag)),
                   inp.device, ws, stream)
     return n, tok
 
 
 def spec_verify_sample_noalloc(model, kind, inp, B, gamma, draft, q, temperature, seed, pos0, kv=None,
-                               logits_out=None, out=None, stream=None):
+                               logits_out=None, out=None, stream=None, diag=None):
     """spec_verify_sample without a workspace (C: spec_verify_sample_noalloc): the library's
     fixed per-device scratch array serves instead; nothing is allocated by the library.
     Returns (n_accepted, tokens_out); ``out`` may supply them."""
@@ -366,7 +371,7 @@ def spec_verify_sample_noalloc(model, kind, inp, B, gamma, draft, q, temperature
     _check(lib.spec_verify_sample_noalloc(ctypes.byref(model.struct), kind, _ptr(inp), B, gamma, _ptr(draft), _ptr(q),
                                           qd, float(temperature), ctypes.c_uint64(int(seed)), _ptr(pos0),
                                           ctypes.byref(kvs) if kvs is not None else None, _ptr(n), _ptr(tok),
-                                          _ptr(logits_out), _stream(stream)))
+                                          _ptr(logits_out), _ptr(diag), _stream(stream)))
     return n, tok
 
 

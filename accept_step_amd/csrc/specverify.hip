@@ -29,6 +29,7 @@
 #include "sv_filter.hpp"
 #include "sv_drafter.hpp"
 #include "sv_rounds.hpp"
+#include "sv_diag.hpp"
 
 using namespace sv;
 
@@ -503,6 +504,7 @@ struct Layout {
   size_t rope = 0, x = 0, h = 0, q = 0, k = 0, v = 0, attp = 0, att = 0, gate = 0, up = 0;
   size_t attcnt = 0;    // [B, n_heads, query groups] split counters of the attention; zeroed by k_prep each call
   size_t ss = 0;        // [GEMM_MAX_WG, M] partial sums of squares of the residual stream's rows
+  size_t diag_rows = 0, diag_draws = 0;   // the margins' partials (sv_diag.hpp), when asked for
   size_t total = 0;
   int P = 0;          // row-statistics partials per row
   int nch = 0;        // sampling chunks per sequence
@@ -532,7 +534,8 @@ int att_splits(const sv_kv_cache* kv) {
   return std::max(1, std::min(S, ATT_SPLITS_MAX));
 }
 
-Layout plan(const sv_model* m, const Shape& sh, const sv_kv_cache* kv, bool need_logits_buf, bool sample) {
+Layout plan(const sv_model* m, const Shape& sh, const sv_kv_cache* kv, bool need_logits_buf, bool sample,
+            bool diag = false) {
   Layout L;
   Bump b;
   const int M = sh.M, V = sh.V;
@@ -573,6 +576,11 @@ Layout plan(const sv_model* m, const Shape& sh, const sv_kv_cache* kv, bool need
     L.att = b.take(size_t(M) * HD * 2);
     L.gate = b.take(size_t(M) * ff * 4);
     L.up = b.take(size_t(M) * std::max(ff, d) * 4);
+  }
+  if (diag) {
+    const int dch = (V + DIAG_CHUNK - 1) / DIAG_CHUNK;
+    L.diag_rows = b.take(size_t(M) * dch * sizeof(DiagRow));
+    L.diag_draws = b.take(size_t(sh.B) * dch * sizeof(DiagDraw));
   }
   L.total = b.off;
   return L;
@@ -872,7 +880,7 @@ sv_status fused_step(const sv_model* m, const Shape& sh, bool sample, bool* yes)
 sv_status verify_common(const sv_model* m, sv_input_kind kind, const void* input, int32_t B, int32_t gamma,
                         const int32_t* draft, const void* q, sv_dtype q_dtype, float temperature, uint64_t seed,
                         const int64_t* pos0, const sv_kv_cache* kv, int32_t* n_accepted, int32_t* tokens_out,
-                        float* logits_out, void* ws, size_t* ws_bytes, void* stream, bool sample,
+                        float* logits_out, float* diag, void* ws, size_t* ws_bytes, void* stream, bool sample,
                         bool exact_query = false) {
   g_err.clear();
   Shape sh;
@@ -892,11 +900,11 @@ sv_status verify_common(const sv_model* m, sv_input_kind kind, const void* input
   }
   const bool bf16_head = kind != SV_IN_LOGITS && !(kind == SV_IN_HIDDEN && m->wdtype == SV_F32);
   bool need_buf = kind != SV_IN_LOGITS && logits_out == nullptr;
-  Layout L = plan(m, sh, kv, need_buf, sample);
+  Layout L = plan(m, sh, kv, need_buf, sample, diag != nullptr);
   // The fused step needs no logits buffer: where the caller's workspace is smaller than
   // the device-independent size (or the exact size is asked for), see whether this device
   // runs it (no device: keep the full size)
-  if (need_buf && bf16_head && ((ws && ws_bytes && *ws_bytes < L.total) || exact_query)) {
+  if (need_buf && !diag && bf16_head && ((ws && ws_bytes && *ws_bytes < L.total) || exact_query)) {
     bool fused = false;
     if (fused_step(m, sh, sample, &fused) != SV_OK) {
       fused = false;
@@ -932,13 +940,29 @@ sv_status verify_common(const sv_model* m, sv_input_kind kind, const void* input
   if (bf16_head) aa.xlogit = at<float>(ws, L.xlogit);
   int P = 0;
   HeadRule rule;
-  rule.logits_out = logits_out;
+  rule.logits_out = diag && !logits_out ? logits : logits_out;   // the margins read the logits from memory
   rule.sample = sample;
   rule.acc = aa;
+  // the optional margins, after the step (sv_diag.hpp)
+  auto finish = [&]() -> sv_status {
+    if (!diag) return SV_OK;
+    DiagArgs da;
+    memset(&da, 0, sizeof da);
+    da.logits = logits; da.draft = aa.draft; da.draft_stride = aa.draft_stride; da.draft_offset = aa.draft_offset;
+    da.q = q; da.q_bf16 = aa.q_bf16; da.pos0 = pos0; da.n_accepted = n_accepted; da.diag = diag;
+    da.rows = at<DiagRow>(ws, L.diag_rows); da.draws = at<DiagDraw>(ws, L.diag_draws);
+    da.seed = seed; da.B = sh.B; da.gamma = gamma; da.V = sh.V; da.nch = (sh.V + DIAG_CHUNK - 1) / DIAG_CHUNK;
+    da.c = c;
+    hipLaunchKernelGGL(k_diag_rows, dim3(da.nch, sh.M), dim3(256), 0, s, da);
+    if (sample) hipLaunchKernelGGL(k_diag_draw, dim3(da.nch, sh.B), dim3(256), 0, s, da);
+    hipLaunchKernelGGL(k_diag_finish, dim3(sh.B), dim3(256), 0, s, da);
+    SV_HIP(hipGetLastError());
+    return SV_OK;
+  };
   if ((st = run_logits(m, sh, input, kv, L, ws, logits, part, c, &P, s, bf16_head ? &aa : nullptr, fuse,
                        bf16_head ? &rule : nullptr)))
     return st;
-  if (rule.done) return SV_OK;
+  if (rule.done) return finish();
   if (kind == SV_IN_LOGITS && logits_out)
     SV_HIP(hipMemcpyAsync(logits_out, input, size_t(sh.M) * sh.V * 4, hipMemcpyDeviceToDevice, s));
 
@@ -948,7 +972,7 @@ sv_status verify_common(const sv_model* m, sv_input_kind kind, const void* input
     hipLaunchKernelGGL(k_accept, dim3(sh.B), dim3(256), 0, s, aa);
     SV_HIP(hipGetLastError());
   }
-  if (!sample) return SV_OK;
+  if (!sample) return finish();
   SampleArgs sa;
   memset(&sa, 0, sizeof sa);
   sa.logits = logits; sa.q = q; sa.q_bf16 = aa.q_bf16; sa.pos0 = pos0; sa.state = aa.state;
@@ -960,7 +984,7 @@ sv_status verify_common(const sv_model* m, sv_input_kind kind, const void* input
   hipLaunchKernelGGL(k_sample, dim3(unsigned(L.nch) * unsigned(sh.B)), dim3(256), 0, s, sa);
   if (!fuse_finish) hipLaunchKernelGGL(k_sample_finish, dim3((sh.B + 3) / 4), dim3(256), 0, s, sa);
   SV_HIP(hipGetLastError());
-  return SV_OK;
+  return finish();
 }
 
 }  // namespace
@@ -989,28 +1013,29 @@ sv_status verify_forward(const sv_model* m, sv_input_kind kind, const void* inpu
 
 sv_status spec_verify_greedy(const sv_model* m, sv_input_kind kind, const void* input, int32_t B, int32_t gamma,
                              const int32_t* draft, const sv_kv_cache* kv, int32_t* n_accepted, int32_t* tokens_out,
-                             float* logits_out, void* ws, size_t* ws_bytes, void* stream) {
+                             float* logits_out, float* diag, void* ws, size_t* ws_bytes, void* stream) {
   return verify_common(m, kind, input, B, gamma, draft, nullptr, SV_F32, 0.0f, 0, nullptr, kv, n_accepted,
-                       tokens_out, logits_out, ws, ws_bytes, stream, false);
+                       tokens_out, logits_out, diag, ws, ws_bytes, stream, false);
 }
 
 sv_status spec_verify_sample(const sv_model* m, sv_input_kind kind, const void* input, int32_t B, int32_t gamma,
                              const int32_t* draft, const void* q, sv_dtype q_dtype, float temperature, uint64_t seed,
                              const int64_t* pos0, const sv_kv_cache* kv, int32_t* n_accepted, int32_t* tokens_out,
-                             float* logits_out, void* ws, size_t* ws_bytes, void* stream) {
+                             float* logits_out, float* diag, void* ws, size_t* ws_bytes, void* stream) {
   return verify_common(m, kind, input, B, gamma, draft, q, q_dtype, temperature, seed, pos0, kv, n_accepted,
-                       tokens_out, logits_out, ws, ws_bytes, stream, true);
+                       tokens_out, logits_out, diag, ws, ws_bytes, stream, true);
 }
 
 sv_status spec_verify_sample_noalloc(const sv_model* m, sv_input_kind kind, const void* input, int32_t B,
                                      int32_t gamma, const int32_t* draft, const void* q, sv_dtype q_dtype,
                                      float temperature, uint64_t seed, const int64_t* pos0, const sv_kv_cache* kv,
-                                     int32_t* n_accepted, int32_t* tokens_out, float* logits_out, void* stream) {
+                                     int32_t* n_accepted, int32_t* tokens_out, float* logits_out, float* diag,
+                                     void* stream) {
   g_err.clear();
   // the scratch this call needs (the size query of the workspace path: nothing launched)
   size_t need = 0;
   sv_status st = verify_common(m, kind, input, B, gamma, draft, q, q_dtype, temperature, seed, pos0, kv, n_accepted,
-                               tokens_out, logits_out, nullptr, &need, stream, true, true);
+                               tokens_out, logits_out, diag, nullptr, &need, stream, true, true);
   if (st) return st;
   if (need > NOALLOC_SCRATCH_BYTES)
     return fail(SV_ERR_UNSUPPORTED, "this request needs %zu bytes of scratch; the allocation-free entry point has %zu "
@@ -1033,7 +1058,7 @@ sv_status spec_verify_sample_noalloc(const sv_model* m, sv_input_kind kind, cons
   }
   size_t have = NOALLOC_SCRATCH_BYTES;
   return verify_common(m, kind, input, B, gamma, draft, q, q_dtype, temperature, seed, pos0, kv, n_accepted,
-                       tokens_out, logits_out, ptr, &have, stream, true);
+                       tokens_out, logits_out, diag, ptr, &have, stream, true);
 }
 
 sv_status draft_masked_logits(const sv_masked_head* head, const void* hidden, int32_t M, int32_t top_k,
@@ -1093,7 +1118,7 @@ sv_status spec_verify_sample_filtered(const sv_model* m, sv_input_kind kind, con
   if (!(top_p > 0.0f && top_p <= 1.0f)) return fail(SV_ERR_ARG, "top_p must be in (0, 1]");
   if (temperature == 0.0f)   // the greedy rule: the filters always keep the argmax
     return verify_common(m, kind, input, B, gamma, draft, nullptr, SV_F32, 0.0f, 0, nullptr, kv, n_accepted,
-                         tokens_out, logits_out, ws, ws_bytes, stream, false);
+                         tokens_out, logits_out, nullptr, ws, ws_bytes, stream, false);
   Shape sh;
   sv_status st = check_common(m, kind, input, B, gamma, kv, &sh);
   if (st) return st;

@@ -149,11 +149,18 @@ sv_status verify_forward(const sv_model* m, sv_input_kind kind, const void* inpu
  *   n_accepted: out int32 [B], accepted drafts 0..gamma (-1: see Data errors).
  *   tokens_out: out int32 [B, G1], emitted tokens: the n_b accepted drafts,
  *               then the correction or bonus token; -1 after those n_b + 1.
- *   logits_out: optional out float32 [B, G1, V] (NULL: kept in workspace). */
+ *   logits_out: optional out float32 [B, G1, V] (NULL: kept in workspace).
+ *   diag:       optional out float32 [B, G1] (NULL: not computed), how close each
+ *               decision came to going the other way ([Self-spec] 3.1: the rule
+ *               compares with the mode): diag[b][i] = the largest float32 logit of slot
+ *               i minus the second largest (0 when two tokens share the maximum) for the
+ *               decided slots i <= n_b; NaN past them and for invalid sequences.
+ *               Computed by extra passes over the logits after the step (the step then
+ *               keeps its logits in memory: in logits_out, else in the workspace). */
 sv_status spec_verify_greedy(const sv_model* m, sv_input_kind kind, const void* input,
                              int32_t B, int32_t gamma, const int32_t* draft,
                              const sv_kv_cache* kv, int32_t* n_accepted, int32_t* tokens_out,
-                             float* logits_out, void* ws, size_t* ws_bytes, void* stream);
+                             float* logits_out, float* diag, void* ws, size_t* ws_bytes, void* stream);
 
 /* Speculative sampling verify: p_i = softmax(logits_i / T).  Draft i is
  * accepted iff u_i * q_i(x) < p_i(x), i.e. with probability min(1, p/q); at
@@ -174,13 +181,19 @@ sv_status spec_verify_greedy(const sv_model* m, sv_input_kind kind, const void* 
  *                of block v >> 2, tag 1, U = ((w >> 41) + 0.5) * 2^-23,
  *                Gumbel G = -log(-log U), token = argmax_v log r_v + G_v.
  *                The result is a pure function of (inputs, seed, pos0).
+ *   diag:        optional out float32 [B, G1] (NULL: not computed; [Self-spec] 3.2):
+ *                diag[b][i] = |u_i - p_i(x) / q_i(x)| (infinity when q_i(x) = 0) for
+ *                the decided acceptance tests i <= min(n_b, gamma - 1), NaN for later
+ *                slots; diag[b][gamma] = the gap between the two best scores
+ *                log r_v + G_v of the final draw, in the class it took (the residual,
+ *                or p); NaN rows for invalid sequences.  T = 0: as for the greedy rule.
  *   Other arguments as for spec_verify_greedy. */
 sv_status spec_verify_sample(const sv_model* m, sv_input_kind kind, const void* input,
                              int32_t B, int32_t gamma, const int32_t* draft,
                              const void* q, sv_dtype q_dtype, float temperature,
                              uint64_t seed, const int64_t* pos0,
                              const sv_kv_cache* kv, int32_t* n_accepted, int32_t* tokens_out,
-                             float* logits_out, void* ws, size_t* ws_bytes, void* stream);
+                             float* logits_out, float* diag, void* ws, size_t* ws_bytes, void* stream);
 
 /* spec_verify_sample without a workspace, for callers that cannot allocate device
  * memory (code under HIP graph capture, serving loops, harnesses that forbid
@@ -192,13 +205,14 @@ sv_status spec_verify_sample(const sv_model* m, sv_input_kind kind, const void* 
  * device race (serialise them, e.g. on one stream).  A request whose scratch would
  * exceed 4 MiB returns SV_ERR_UNSUPPORTED before anything is launched (the logits of the
  * unfused path for large batches need more: pass logits_out, or use spec_verify_sample
- * with a workspace).  Arguments as for spec_verify_sample. */
+ * with a workspace; diag without logits_out needs a logits buffer too).  Arguments as for
+ * spec_verify_sample. */
 sv_status spec_verify_sample_noalloc(const sv_model* m, sv_input_kind kind, const void* input,
                                      int32_t B, int32_t gamma, const int32_t* draft,
                                      const void* q, sv_dtype q_dtype, float temperature,
                                      uint64_t seed, const int64_t* pos0,
                                      const sv_kv_cache* kv, int32_t* n_accepted, int32_t* tokens_out,
-                                     float* logits_out, void* stream);
+                                     float* logits_out, float* diag, void* stream);
 
 /* Speculative sampling verify with the drafter's top-k / top-p filters applied alike to
  * the target ([Infra-ch8] "why the output does not change", [MTP-drafters] 5.2: the

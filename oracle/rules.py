@@ -308,6 +308,63 @@ def verify_sample(logits64, draft, q, temperature, seed, pos0, seq0=0):
     return sample_rule(f32_logits(logits64), draft, q, temperature, seed, pos0, seq0)
 
 
+def verify_diag(logits64, draft, q, temperature, seed, pos0, n, seq0=0):
+    """How close each decision of a verify step came to going the other way: float64
+    [B, gamma+1], NaN where a slot was not decided ([Self-spec] 3.1: the greedy rule
+    compares the draft with the target's mode; 3.2: the sampling rule accepts with
+    probability min(1, p/q) and draws the correction from max(0, p - q)).
+
+    * T = 0: entry i <= n_b is the gap between the largest and second-largest float32
+      logit of slot i (0 when two tokens share the maximum).
+    * T > 0: entry i <= min(n_b, gamma - 1) is |u_i - p_i(x) / q_i(x)| (infinity when
+      q_i(x) = 0; out-of-range drafts have q = 0); entry gamma is the gap between the two
+      best scores log r_v + G_v of the final draw (:func:`resample`), infinity if only
+      one entry can win.
+    * Rows with n_b < 0 (invalid) are NaN.
+
+    These are the quantities the flags of :func:`greedy_rule`, :func:`accept_slots` and
+    :func:`resample` compare with FLAG_MARGIN.  ``n``: the step's accepted counts.
+
+    Pinned by: a hand-computed greedy example; a sequence is flagged exactly when one of
+    its defined entries is below FLAG_MARGIN (random greedy and sampling steps).
+    """
+    l32 = f32_logits(logits64)
+    B, G1, V = l32.shape
+    gamma = G1 - 1
+    n = np.asarray(n, dtype=np.int64)
+    out = np.full((B, G1), np.nan)
+    valid = n >= 0
+    if float(temperature) == 0.0:
+        _, gap = top2(l32)
+        reached = np.arange(G1)[None, :] <= n[:, None]
+        out = np.where(reached & valid[:, None], gap.astype(np.float64), np.nan)
+        return out
+    draft = np.asarray(draft, dtype=np.int64)
+    q = np.asarray(q, dtype=np.float64)
+    pos0 = np.broadcast_to(np.asarray(pos0, dtype=np.int64), (B,))
+    seq = seq0 + np.arange(B, dtype=np.int64)
+    p32 = target_probs(l32, temperature)
+    bi = np.arange(B)
+    for i in range(gamma):
+        u = philox.accept_uniform(seed, seq, pos0 + i + 1)
+        x = draft[:, i]
+        inr = (x >= 0) & (x < V)
+        xc = np.where(inr, x, 0)
+        px = np.where(inr, p32[bi, i, xc].astype(np.float64), 0.0)
+        qx = np.where(inr, q[bi, i, xc], 0.0)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            margin = np.where(qx > 0, np.abs(u - px / np.where(qx > 0, qx, 1.0)), np.inf)
+        out[:, i] = np.where((i <= n) & valid, margin, np.nan)
+    nn = np.where(valid, n, gamma)
+    r = resample_rows(p32, q, nn)
+    sc = gumbel_scores(r, seed, seq, pos0 + nn + 1).astype(np.float64)
+    t2 = np.sort(sc, axis=-1)
+    with np.errstate(invalid="ignore"):
+        gap = np.where(np.isfinite(t2[:, -2]), t2[:, -1] - t2[:, -2], np.inf) if V >= 2 else np.full(B, np.inf)
+    out[:, gamma] = np.where(valid, gap, np.nan)
+    return out
+
+
 def filtered_probs(l32, temperature, top_k, top_p):
     """Target probabilities after the top-k and top-p filters, float32, zero outside the
     kept tokens, together with the kept masks and boundary flags.

@@ -50,10 +50,10 @@ def _model(vocab=1000, d=64, n_layers=0, wdtype=sv.SV_BF16):
 FAKE = ctypes.c_void_p(0x20000)     # 256-byte aligned stand-in pointer, never dereferenced
 
 
-def greedy(lib, m, kind=sv.SV_IN_HIDDEN, inp=FAKE, B=1, gamma=4, draft=FAKE, ws=None, nbytes=0):
+def greedy(lib, m, kind=sv.SV_IN_HIDDEN, inp=FAKE, B=1, gamma=4, draft=FAKE, ws=None, nbytes=0, diag=None):
     n = ctypes.c_size_t(nbytes)
     st = lib.spec_verify_greedy(ctypes.byref(m) if m is not None else None, kind, inp, B, gamma, draft, None,
-                                FAKE, FAKE, None, ws, ctypes.byref(n), None)
+                                FAKE, FAKE, None, diag, ws, ctypes.byref(n), None)
     return st, n.value
 
 
@@ -80,7 +80,7 @@ def test_sampling_argument_errors(lib):
     def sample(T=1.0, q=FAKE, qd=sv.SV_BF16, pos0=FAKE):
         n = ctypes.c_size_t(0)
         return lib.spec_verify_sample(ctypes.byref(m), sv.SV_IN_HIDDEN, FAKE, 2, 4, FAKE, q, qd, T, 7, pos0, None,
-                                      FAKE, FAKE, None, None, ctypes.byref(n), None)
+                                      FAKE, FAKE, None, None, None, ctypes.byref(n), None)
 
     assert sample() == 0
     assert sample(T=-1.0) == 1
@@ -228,9 +228,20 @@ def test_noalloc_refuses_oversized_request_without_device(lib):
     device call: a request whose scratch exceeds the fixed array is SV_ERR_UNSUPPORTED."""
     m = _model(vocab=65536, d=256)
     st = lib.spec_verify_sample_noalloc(ctypes.byref(m), sv.SV_IN_HIDDEN, FAKE, 64, 8, FAKE, FAKE, sv.SV_BF16,
-                                        ctypes.c_float(1.0), ctypes.c_uint64(1), FAKE, None, FAKE, FAKE, None, None)
+                                        ctypes.c_float(1.0), ctypes.c_uint64(1), FAKE, None, FAKE, FAKE, None, None,
+                                        None)
     assert st == 6 and b"scratch" in lib.sv_last_error()
     # argument errors come first, as on the workspace entry point
     st = lib.spec_verify_sample_noalloc(ctypes.byref(m), sv.SV_IN_HIDDEN, FAKE, 1, 0, FAKE, FAKE, sv.SV_BF16,
-                                        ctypes.c_float(1.0), ctypes.c_uint64(1), FAKE, None, FAKE, FAKE, None, None)
+                                        ctypes.c_float(1.0), ctypes.c_uint64(1), FAKE, None, FAKE, FAKE, None, None,
+                                        None)
     assert st == 1
+
+
+def test_diag_is_optional_and_sized(lib):
+    """diag = NULL computes nothing and needs no extra scratch; a non-NULL diag plans its
+    partials (and the logits buffer) in the workspace query."""
+    m = _model(vocab=262144, d=1536)
+    st, need = greedy(lib, m)
+    st2, need_diag = greedy(lib, m, diag=FAKE)
+    assert st == 0 and st2 == 0 and need_diag > need

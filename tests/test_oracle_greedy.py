@@ -4,6 +4,7 @@ import json
 import os
 
 import numpy as np
+import pytest
 
 from oracle import rules
 
@@ -125,3 +126,37 @@ def test_sampling_at_zero_temperature_is_greedy():
     n0, tok0, _ = b
     ok = ~fl
     assert np.array_equal(n[ok], n0[ok]) and np.array_equal(tok[ok], tok0[ok])
+
+
+def test_diag_hand_example():
+    """Greedy margins by hand: slot 0 logits (0, 1, 3) -> gap 2; slot 1 (2, 2, 1) -> a tie,
+    gap 0; slot 2 (5, 1, 0) -> gap 4.  Drafts (2, 1): slot 0 accepts, slot 1 rejects
+    (its argmax is 0, the lower index of the tie), so slot 2 is not decided.  Drafts
+    (2, 0): every slot is decided."""
+    logits = np.array([[[0.0, 1.0, 3.0], [2.0, 2.0, 1.0], [5.0, 1.0, 0.0]]])
+    n, tok, fl = rules.verify_greedy(logits, np.array([[2, 1]]))
+    assert n.tolist() == [1] and tok.tolist() == [[2, 0, -1]]        # draft 1 != argmax 0 at slot 1
+    d = rules.verify_diag(logits, np.array([[2, 1]]), None, 0.0, 0, np.zeros(1), n)
+    assert d[0, :2].tolist() == [2.0, 0.0] and np.isnan(d[0, 2])
+    assert fl.tolist() == [True]                                      # the tie is a flagged decision
+    d = rules.verify_diag(logits, np.array([[2, 0]]), None, 0.0, 0, np.zeros(1), np.array([2]))
+    assert d[0].tolist() == [2.0, 0.0, 4.0]
+    assert np.isnan(rules.verify_diag(logits, np.array([[2, 0]]), None, 0.0, 0, np.zeros(1), np.array([-1]))).all()
+
+
+@pytest.mark.parametrize("T", [0.0, 1.0])
+def test_diag_agrees_with_flags(T):
+    """A sequence is flagged exactly when one of its defined margins is below the flag
+    margin (random steps with small gaps, so both outcomes occur)."""
+    rng = np.random.default_rng(5)
+    B, gamma, V = 400, 3, 6
+    logits = np.round(rng.standard_normal((B, gamma + 1, V)) * 3, 2)     # ties and near ties
+    q = rng.dirichlet(np.ones(V), size=(B, gamma))
+    draft = np.array([[rng.choice(V, p=q[b, i]) for i in range(gamma)] for b in range(B)])
+    if T == 0.0:
+        draft = np.where(rng.random((B, gamma)) < 0.7, np.argmax(logits[:, :gamma], -1), draft)
+    n, tok, fl = rules.verify_sample(logits, draft, q, T, 11, np.arange(B) * 7)
+    d = rules.verify_diag(logits, draft, q, T, 11, np.arange(B) * 7, n)
+    below = np.any(np.nan_to_num(d, nan=np.inf) < rules.FLAG_MARGIN, axis=1)
+    assert np.array_equal(below, fl)
+    assert fl.any() and (~fl).any()

@@ -15,11 +15,22 @@ LIB = os.path.join(HERE, "libspecverify.so")
 SRC = os.path.join(HERE, "csrc", "specverify.hip")
 
 
-def hipcc_command(out=LIB, arch="gfx950"):
+def hipcc_command(out=LIB, arch="gfx950", host_sanitizers=False):
+    """The hipcc command line of the library.  ``host_sanitizers``: a checking build of
+    the host code only (AddressSanitizer and UndefinedBehaviorSanitizer, each flag
+    passed to the host compilation alone; device code unoptimised, to build quickly),
+    for CPU tests of the argument and workspace logic.  Never for GPU runs."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    return [hipcc, f"--offload-arch={arch}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    opt = ["-O1", "-Xarch_device", "-O0"] if host_sanitizers else ["-O3"]
+    san = []
+    if host_sanitizers:
+        for f in ("-g", "-fsanitize=address", "-fsanitize=undefined", "-fno-omit-frame-pointer",
+                  "-fno-sanitize-recover=undefined"):
+            san += ["-Xarch_host", f]
+        san.append("-shared-libasan")
+    return [hipcc, f"--offload-arch={arch}"] + opt + ["-std=c++17", "-fPIC", "-shared",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Wno-unused-result",
+            "-Wno-unused-result"] + san + [
             "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
             "-o", out, SRC]
 

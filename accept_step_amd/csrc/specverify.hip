@@ -1080,7 +1080,7 @@ sv_status draft_masked_logits(const sv_masked_head* head, const void* hidden, in
   b.take(CNT_BYTES);                 // the counter block other calls keep state in: never scratch
   const size_t cl_off = cluster_logits ? 0 : b.take(size_t(M) * C * 4);
   Layout L;
-  L.total = cluster_logits ? 0 : b.off;
+  L.total = b.off;   // never 0: a NULL ws is always the size query, never a call that runs
   bool query = false;
   sv_status st = check_ws(ws, ws_bytes, L, &query);
   if (st || query) return st;

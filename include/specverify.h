@@ -78,14 +78,25 @@ typedef enum sv_status {
   SV_ERR_UNSUPPORTED = 6   /* valid request this library does not implement */
 } sv_status;
 
-typedef enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+/* The two range markers of each enumeration a caller passes in (sv_dtype,
+ * sv_input_kind) make every int32 value a valid value of the type, so that a value the
+ * library does not know is an error it reports (SV_ERR_DTYPE / SV_ERR_ARG), not undefined
+ * behaviour in the C++ implementation; they also fix the type's size at 32 bits.  They
+ * are not values to pass. */
+typedef enum sv_dtype {
+  SV_F32 = 0, SV_BF16 = 1,
+  SV_DTYPE_RANGE_MIN_ = -2147483647 - 1, SV_DTYPE_RANGE_MAX_ = 2147483647
+} sv_dtype;
 
 /* What ``input`` holds:
  *   SV_IN_LOGITS  float32 [B, G1, V] target logits (the forward is skipped);
  *   SV_IN_HIDDEN  wdtype  [B, G1, d] final hidden states (LM head only);
  *   SV_IN_TOKENS  int32   [B, G1] token ids, slot 0 = last accepted token,
  *                 slots 1..gamma = the drafts (full decoder forward). */
-typedef enum sv_input_kind { SV_IN_LOGITS = 0, SV_IN_HIDDEN = 1, SV_IN_TOKENS = 2 } sv_input_kind;
+typedef enum sv_input_kind {
+  SV_IN_LOGITS = 0, SV_IN_HIDDEN = 1, SV_IN_TOKENS = 2,
+  SV_INPUT_RANGE_MIN_ = -2147483647 - 1, SV_INPUT_RANGE_MAX_ = 2147483647
+} sv_input_kind;
 
 /* Target model; all pointers are device pointers except ``layers``.
  * n_layers == 0: LM head only (SV_IN_LOGITS / SV_IN_HIDDEN).

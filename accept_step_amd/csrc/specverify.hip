@@ -30,6 +30,7 @@
 #include "sv_drafter.hpp"
 #include "sv_rounds.hpp"
 #include "sv_diag.hpp"
+#include "sv_wide.hpp"
 
 using namespace sv;
 
@@ -440,6 +441,55 @@ sv_status launch_head(const HeadPlan& p, HeadArgs a, hipStream_t s) {
   return SV_OK;
 }
 
+// Plan of the wide-batch product (sv_wide.hpp), for batches above 16 rows (up to 16
+// rows the streaming product keeps all of X in LDS and needs no barrier per chunk:
+// 446 against 505 us at 12 rows of the 4096-wide head).  The 16-row blocks of X are
+// split into as few M-tiles of at most WIDE_MB_MAX blocks as possible, the tile size
+// rounded up to an instantiated one (rows past M are zeros in LDS, their products
+// discarded).  Every tile size keeps four W blocks of 16 rows per wavefront (chunks
+// of 128 k): one or two blocks per wavefront with longer chunks (runs of 1 KB / 512 B
+// of each W row per chunk instead of 256 B) measured slower, 615 against 511 us at 12
+// rows, 687 against 646 at 80.
+constexpr int WIDE_MAX_ROWS = 16 * WIDE_MB_MAX * 8;
+struct WidePlan {
+  bool ok = false;
+  int MB = 0, BLK = 0, m_tiles = 0, n_tiles = 0, grid = 0;
+  bool nt = true;
+  size_t lds = 0;
+};
+
+WidePlan plan_wide(int M, int K, int N) {
+  WidePlan p;
+  if (M <= 16 || M > WIDE_MAX_ROWS || N < 1) return p;
+  const int mblocks = (M + 15) / 16;
+  const int tiles = (mblocks + WIDE_MB_MAX - 1) / WIDE_MB_MAX;
+  const int per = (mblocks + tiles - 1) / tiles;
+  p.MB = per <= 4 ? 4 : per <= 8 ? 8 : WIDE_MB_MAX;
+  p.BLK = 4;
+  const int kch = wide_kch(p.BLK);
+  if (K < 2 * kch || K % (2 * kch)) return p;
+  p.m_tiles = (mblocks + p.MB - 1) / p.MB;
+  p.nt = p.m_tiles == 1;                      // sibling M-tiles read W again from L2
+  p.n_tiles = (N + 64 * p.BLK - 1) / (64 * p.BLK);
+  p.grid = (p.n_tiles + 7) / 8 * 8 * p.m_tiles;
+  p.lds = size_t(2) * 16 * p.MB * (kch + 8) * 2;
+  p.ok = true;
+  return p;
+}
+
+sv_status launch_wide(const WidePlan& p, WideArgs a, hipStream_t s) {
+  a.m_tiles = p.m_tiles; a.n_tiles = p.n_tiles;
+  const void* fn = p.MB == 4 ? reinterpret_cast<const void*>(&k_wide<4, 4, true>)
+                 : p.MB == 8 ? reinterpret_cast<const void*>(&k_wide<8, 4, true>)
+                 : p.nt ? reinterpret_cast<const void*>(&k_wide<WIDE_MB_MAX, 4, true>)
+                        : reinterpret_cast<const void*>(&k_wide<WIDE_MB_MAX, 4, false>);
+  sv_status st = head_set_lds(fn, p.lds);
+  if (st) return st;
+  void* args[] = {&a};
+  SV_HIP(hipLaunchKernel(fn, dim3(p.grid), dim3(256), args, p.lds, s));
+  return SV_OK;
+}
+
 // Decoder fusions of a k-split product: X normalised from float32 rows while it is
 // staged (norm_w set), and the products added into out with per-workgroup sums of
 // squares of the updated rows (residual).
@@ -548,6 +598,8 @@ Layout plan(const sv_model* m, const Shape& sh, const sv_kv_cache* kv, bool need
   } else {
     L.head = plan_gemm(M, (V + 15) / 16, sh.decoder ? m->d_model : sh.d);
     L.P = L.head.grid_x_max;
+    const WidePlan wp = plan_wide(M, sh.decoder ? m->d_model : sh.d, V);
+    if (wp.ok) L.P = std::max(L.P, wp.n_tiles);
   }
   // per-workgroup partials of either product kernel, then the k-split kernel's group partials
   L.part = b.take(size_t(std::max(L.P, GEMM_MAX_WG) + CNT_GROUPS) * M * sizeof(RowPart));
@@ -836,6 +888,31 @@ sv_status run_logits(const sv_model* m, const Shape& sh, const void* input, cons
     a.write_out = out != nullptr;
     *P = hp.grid;
     return launch_head(hp, a, s);
+  }
+  // wider batches: the tiled product that reads W once per M-tile (sv_wide.hpp); the
+  // acceptance runs as its own launch
+  const WidePlan wp = plan_wide(M, K, V);
+  if (wp.ok) {
+    WideArgs w;
+    memset(&w, 0, sizeof w);
+    w.W = static_cast<const bf16_t*>(m->lm_head); w.X = hb; w.out = logits; w.part = part;
+    w.M = M; w.N = V; w.K = K; w.c_stat = c;
+    if (acc) {
+      w.xlogit = at<float>(ws, L.xlogit);
+      w.draft = acc->draft; w.draft_stride = acc->draft_stride; w.draft_offset = acc->draft_offset;
+      w.gamma = acc->gamma;
+    }
+    if ((st = launch_wide(wp, w, s))) return st;
+    *P = wp.n_tiles;
+    if (acc && fuse) {                     // the caller expects the rule to have run
+      AcceptArgs aa = *acc;
+      aa.P = wp.n_tiles;
+      aa.xlogit = w.xlogit;
+      hipLaunchKernelGGL(k_accept, dim3(aa.B), dim3(256), 0, s, aa);
+      SV_HIP(hipGetLastError());
+      if (rule) rule->accepted = true;
+    }
+    return SV_OK;
   }
   GemmArgs a = gemm_args(hb, M, K);
   gemm_add_seg(a, m->lm_head, logits, V);

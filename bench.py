@@ -45,13 +45,14 @@ def parse():
                     help="before timing, copy a buffer of this many MiB five times (a plain copy kernel of known "
                          "size, used to scale the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--workload", choices=("large-vocab", "full-model", "masked-head", "filtered", "drafter",
-                                           "rounds"),
+                                           "rounds", "sweep"),
                     default="large-vocab",
                     help="large-vocab (default, the headline metric), full-model (the 32-layer decoder verify), "
                          "masked-head (the drafter's centroid-masked LM head), filtered (the large-vocab step "
                          "with top_k 64 / top_p 0.95 applied alike to the target), drafter (the MTP drafter's "
-                         "gamma = 4 draft steps) or rounds (draft, per-sequence padding, verify and the heuristic "
-                         "schedule, on the device)")
+                         "gamma = 4 draft steps), rounds (draft, per-sequence padding, verify and the heuristic "
+                         "schedule, on the device) or sweep (the batch x gamma sweep over the d = 4096 head: "
+                         "B in {1, 4, 16, 64} x gamma in {2, 4, 8}, T = 1 sampling)")
     ap.add_argument("--rows", type=int, default=1, help="masked-head: hidden states per call")
     ap.add_argument("--graph", action="store_true",
                     help="drafter, full-model: capture one call into a HIP graph (torch.cuda.graph on the launch "
@@ -81,6 +82,8 @@ def main():
         return drafter(args, torch, sv, workloads)
     if args.workload == "rounds":
         return rounds_bench(args, torch, sv, workloads)
+    if args.workload == "sweep":
+        return sweep(args, torch, sv)
     root = os.path.dirname(os.path.abspath(__file__))
     sys.path.insert(0, root)
     dev = torch.device("cuda:0")
@@ -242,6 +245,82 @@ def main():
         # benefit is computed"), beside the measured mean of the timed steps
         out["config"]["alpha_sum_min_pq_per_slot"] = out["cpu_baseline"].pop("alpha_per_slot")
         out["config"]["expected_committed_closed_form"] = out["cpu_baseline"].pop("expected_committed")
+    print(json.dumps(out), flush=True)
+
+
+def sweep(args, torch, sv):
+    """The batch x gamma sweep: bf16 LM head W[262144, 4096] (2,147,483,648 bytes),
+    B in {1, 4, 16, 64} x gamma in {2, 4, 8} (M = B (gamma + 1) from 3 to 576 rows),
+    T = 1 sampling.  W, the hidden states N(0, 1) and the draft distributions are drawn
+    on the GPU from a seeded generator: q = softmax(l + N(0, 1)) of the true logits l
+    (bf16 product in torch), drafts drawn from q.  Per point: microseconds per verify
+    step (HIP events around the timed launches on the launch stream), the step's
+    algorithmic bytes (W once, the hidden states, the q rows of rejected sequences) per
+    second against the 8 TB/s HBM peak, and MFMA utilisation 2 M V d / t against the
+    2.5 PFLOP/s dense bf16 peak.  The points below M ~ 300 are bound by HBM, the largest
+    by the matrix cores."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    V, d, T = 262144, 4096, 1.0
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4004)
+    W = (torch.randn((V, d), generator=gen, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+    model = sv.lm_head_model(W)
+    ws = sv.Workspace()
+    stream = torch.cuda.current_stream()
+    K = max(2, min(args.steps, 50))
+    points = []
+    for B in (1, 4, 16, 64):
+        for gamma in (2, 4, 8):
+            M = B * (gamma + 1)
+            h = torch.randn((B, gamma + 1, d), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+            lt = (h[:, :gamma].reshape(-1, d) @ W.t()).float()
+            lt += torch.randn(lt.shape, generator=gen, device=dev, dtype=torch.float32)
+            q32 = torch.softmax(lt / T, dim=-1)
+            draft = torch.multinomial(q32, 1, generator=gen).view(B, gamma).to(torch.int32)
+            q = q32.to(torch.bfloat16).view(B, gamma, V)
+            del lt, q32
+            pos = torch.arange(0, 11 * (K + 4), 11, device=dev, dtype=torch.int64)[:, None].expand(-1, B).contiguous()
+            n_out = torch.empty((K, B), dtype=torch.int32, device=dev)
+            t_out = torch.empty((K, B, gamma + 1), dtype=torch.int32, device=dev)
+
+            def step(i, out=None):
+                return sv.spec_verify_sample(model, sv.SV_IN_HIDDEN, h, B, gamma, draft, q, T, 77, pos[i], out=out,
+                                             ws=ws)
+            for i in range(3):
+                step(i)
+            torch.cuda.synchronize()
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for i in range(K):
+                step(i, out=(n_out[i], t_out[i]))
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            us = ev0.elapsed_time(ev1) / K * 1e3
+            n_host = n_out.to(torch.int64).cpu()
+            require_valid(n_host, f"sweep B={B} gamma={gamma}")
+            rejected = int((n_host < gamma).sum().item()) / K
+            algo = V * d * 2 + M * d * 2 + rejected * V * 2
+            gbs = algo / (us * 1e-6) / 1e9
+            tflops = 2.0 * M * V * d / (us * 1e-6) / 1e12
+            points.append({"B": B, "gamma": gamma, "M": M, "us_per_step": round(us, 2),
+                           "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                           "mfma_tflops": round(tflops, 1), "mfma_frac": round(tflops / 2500.0, 4),
+                           "mean_accepted": round(float(n_host.float().mean()), 3)})
+            print(f"# sweep B={B} gamma={gamma} M={M}: {us:.1f} us, {gbs:.0f} GB/s, {tflops:.0f} TFLOP/s",
+                  file=sys.stderr, flush=True)
+            del h, q, draft, pos, n_out, t_out
+    worst = min(points, key=lambda p_: max(p_["hbm_frac"], p_["mfma_frac"]))
+    out = {
+        "metric": "verify-step time over the batch x gamma sweep (HBM GB/s below the crossover, MFMA use above)",
+        "value": round(sum(p_["us_per_step"] for p_ in points), 1),
+        "unit": "us (sum of the 12 points' step times)",
+        "n_gpus": 1, "steps": K, "warmup": 3, "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "batch x gamma sweep: bf16 LM head V=262144 d=4096, T=1 sampling",
+                   "points": points,
+                   "furthest_from_its_roof": {k_: worst[k_] for k_ in ("B", "gamma", "M")}},
+    }
     print(json.dumps(out), flush=True)
 
 

@@ -45,10 +45,14 @@ constexpr size_t ALIGN = 256;
 constexpr int GEMM_WAVES = 4;
 constexpr int GEMM_MAX_WG = 2048;    // upper bound of workgroups along the vocabulary
 constexpr size_t GEMM_LDS_BUDGET = 64 * 1024;
-constexpr int SAMPLE_CHUNK = 1024;
+constexpr int SAMPLE_CHUNK = 1024;          // the sampler's smallest vocabulary chunk
+constexpr int SAMPLE_MAX_WG = 2048;         // ... doubled until the grid is at most this many workgroups
 constexpr int ATT_SPLITS_MAX = ATT_SPLITS_CAP;
 constexpr int FUSE_ACCEPT_MAX_ROWS = 20;   // B * (gamma + 1) merged by the product's last workgroup
-constexpr int FUSE_FINISH_MAX_B = 64;      // sequences finished by the sampler's last workgroup
+// sequences finished by the sampler's last workgroup; more are merged by a launch of
+// their own, one wavefront per sequence (at B = 64 the last workgroup's 16 sequences per
+// wavefront and 16384 workgroups counting on one word took the sampler to 250 us)
+constexpr int FUSE_FINISH_MAX_B = 8;
 constexpr size_t STATIC_LDS_RESERVE = 2048;
 
 thread_local std::string g_err;
@@ -548,6 +552,14 @@ sv_status run_product(const bf16_t* X, int M, int K, int nseg, const void* const
 
 // ---------------------------------------------------------------------------
 // workspace layout
+// The sampler's vocabulary chunk: SAMPLE_CHUNK, doubled while B chunks per sequence would
+// need more than SAMPLE_MAX_WG workgroups (any partition draws the same token).
+int sample_chunk(int V, int B) {
+  int c = SAMPLE_CHUNK;
+  while (c < V && int64_t((V + c - 1) / c) * B > SAMPLE_MAX_WG) c *= 2;
+  return c;
+}
+
 struct Layout {
   size_t counters = 0;   // CNT_BYTES of one-shot counters; zero before first use, left zero
   size_t logits = 0, part = 0, state = 0, spart = 0, invalid = 0, xlogit = 0, recs = 0;
@@ -558,6 +570,7 @@ struct Layout {
   size_t total = 0;
   int P = 0;          // row-statistics partials per row
   int nch = 0;        // sampling chunks per sequence
+  int chunk = 0;      // ... of this many vocabulary entries
   int S = 0;          // attention key splits
   GemmPlan head;
 };
@@ -605,7 +618,8 @@ Layout plan(const sv_model* m, const Shape& sh, const sv_kv_cache* kv, bool need
   L.part = b.take(size_t(std::max(L.P, GEMM_MAX_WG) + CNT_GROUPS) * M * sizeof(RowPart));
   L.state = b.take(size_t(sh.B) * sizeof(SeqState));
   L.xlogit = b.take(size_t(M) * 4);
-  L.nch = (V + SAMPLE_CHUNK - 1) / SAMPLE_CHUNK;
+  L.chunk = sample_chunk(V, sh.B);
+  L.nch = (V + L.chunk - 1) / L.chunk;
   if (sample) L.spart = b.take(size_t(sh.B) * std::max(L.nch, GEMM_MAX_WG) * sizeof(SamplePart));   // either sampler
   L.invalid = b.take(size_t(sh.B) * 4);
   // the fused sampler's epoch-tagged hand-off records (k-split kernel with a bf16 head and
@@ -1054,7 +1068,7 @@ sv_status verify_common(const sv_model* m, sv_input_kind kind, const void* input
   memset(&sa, 0, sizeof sa);
   sa.logits = logits; sa.q = q; sa.q_bf16 = aa.q_bf16; sa.pos0 = pos0; sa.state = aa.state;
   sa.spart = at<SamplePart>(ws, L.spart); sa.seed = seed; sa.B = sh.B; sa.gamma = gamma; sa.V = sh.V;
-  sa.chunk = SAMPLE_CHUNK; sa.nch = L.nch; sa.c = c;
+  sa.chunk = L.chunk; sa.nch = L.nch; sa.c = c;
   sa.n_accepted = n_accepted; sa.tokens_out = tokens_out; sa.len = aa.len;
   const bool fuse_finish = sh.B <= FUSE_FINISH_MAX_B;
   if (fuse_finish) sa.counter = at<unsigned>(ws, L.counters) + 1;

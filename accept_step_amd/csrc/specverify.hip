@@ -707,15 +707,16 @@ sv_status run_decoder(const sv_model* m, const Shape& sh, const int* tokens, con
   SV_HIP(hipGetLastError());
 
   const float scale = 1.0f / sqrtf(float(hd));
-  // RoPE and the cache append of the new positions, then attention (the last
-  // workgroup of each head merges the key splits).
+  // Attention over the cache and the new positions, which the same launch rotates and
+  // appends (RoPE on the queries as they are staged and on the new keys as the workgroup
+  // holding their cache rows writes them; the last workgroup of each head merges the
+  // key splits).
   auto attention = [&](int l) -> sv_status {
-    hipLaunchKernelGGL(k_rope_append, dim3(M, H), dim3(hd / 2), 0, s, q, k, v, rope, kc, vc, kv->len, invalid, da, l);
     const int NQ = att_query_groups(sh.G1), QS = att_query_slots(sh.G1);
     const dim3 ag(L.S, H, sh.B * NQ);
     const float qscale = scale * 1.4426950408889634f;   // scores in base-2 units
 #define SV_ATTN(HDv, QGv) hipLaunchKernelGGL((k_attn<HDv, QGv>), ag, dim3(256), 0, s, q, kc, vc, kv->len, invalid, attp, \
-                                             att, attcnt, da, l, L.S, NQ, qscale)
+                                             att, attcnt, da, l, L.S, NQ, qscale, rope, k, v)
 #define SV_ATTN_Q(HDv) do { if (QS == 2) SV_ATTN(HDv, 2); else if (QS == 4) SV_ATTN(HDv, 4); \
                             else if (QS == 5) SV_ATTN(HDv, 5); else SV_ATTN(HDv, 8); } while (0)
     if (hd == 128) SV_ATTN_Q(128); else SV_ATTN_Q(64);
@@ -761,6 +762,9 @@ sv_status run_decoder(const sv_model* m, const Shape& sh, const int* tokens, con
         fn.norm_w = static_cast<const bf16_t*>(w[5]);
         if ((st = run_product_fused(nullptr, M, d, 2, w2, o2, n2, fn, nullptr, di, s))) return st;
       }
+      // silu(gate) * up as its own small launch: folded into the down projection's
+      // staging, every one of its workgroups recomputed all M * d_ff activations
+      // (products 25.8 -> 30.8 us on average)
       hipLaunchKernelGGL(k_silu_mul, dim3((nf + 255) / 256), dim3(256), 0, s, gate, up, h, nf);
       {
         const void* w1[1] = {w[8]};

@@ -135,29 +135,6 @@ __device__ __forceinline__ size_t cache_index(const DecArgs& a, int layer, int b
   return ((((size_t(layer) * a.B + b) * a.H + h) * size_t(a.max_len) + pos) * a.hd) + j;
 }
 
-// Rotate q and k of the new positions (rotate-half pairs j, j + hd/2), then append
-// bf16 K and V into the cache at len[b] + i.  grid (M, H), hd/2 threads.
-__global__ void k_rope_append(float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-                              const float2* __restrict__ rope_cs, bf16_t* __restrict__ kc, bf16_t* __restrict__ vc,
-                              const int* __restrict__ len, const int* __restrict__ invalid, DecArgs a, int layer) {
-  const int m = blockIdx.x, h = blockIdx.y, j = threadIdx.x;
-  const int half = a.hd / 2;
-  if (j >= half) return;
-  const int b = m / a.G1, i = m - b * a.G1;
-  const float2 cs = rope_cs[m * half + j];
-  const size_t base = size_t(m) * a.H * a.hd + size_t(h) * a.hd;
-  const float q1 = q[base + j], q2 = q[base + j + half];
-  q[base + j] = q1 * cs.x - q2 * cs.y;
-  q[base + j + half] = q2 * cs.x + q1 * cs.y;
-  if (invalid[b]) return;
-  const float k1 = k[base + j], k2 = k[base + j + half];
-  const int pos = len[b] + i;
-  kc[cache_index(a, layer, b, h, pos, j)] = f32_to_bf16(k1 * cs.x - k2 * cs.y);
-  kc[cache_index(a, layer, b, h, pos, j + half)] = f32_to_bf16(k2 * cs.x + k1 * cs.y);
-  vc[cache_index(a, layer, b, h, pos, j)] = f32_to_bf16(v[base + j]);
-  vc[cache_index(a, layer, b, h, pos, j + half)] = f32_to_bf16(v[base + j + half]);
-}
-
 constexpr int ATT_KEYS = 256;   // keys per workgroup and pass (64 per wavefront)
 constexpr int ATT_SPLITS_CAP = 16;   // key splits per head at most
 constexpr int ATT_QMAX = 8;     // query slots per workgroup; more new positions use several query groups
@@ -189,14 +166,17 @@ __device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) 
 // merged in LDS and the workgroup's partial (max, sum, unnormalised output) per query
 // is stored for the other workgroups of the head; the last of the S workgroups to
 // finish combines them and writes the bf16 attention output.  cnt[(b*H + h)*NQ + g]
-// counts the finished workgroups and is reset by the last one.
+// counts the finished workgroups and is reset by the last one.  kc and vc are not
+// __restrict__: a launch that appends writes cache rows its own workgroup then loads.
 template <int HD, int QG>
-__global__ __launch_bounds__(256) void k_attn(const float* __restrict__ q, const bf16_t* __restrict__ kc,
-                                              const bf16_t* __restrict__ vc, const int* __restrict__ len,
+__global__ __launch_bounds__(256) void k_attn(const float* __restrict__ q, const bf16_t* kc,
+                                              const bf16_t* vc, const int* __restrict__ len,
                                               const int* __restrict__ invalid, float* __restrict__ part,
                                               bf16_t* __restrict__ out, unsigned* __restrict__ cnt, DecArgs a,
                                               int layer, int S, int NQ, float qscale,
-                                              const float2* __restrict__ rope = nullptr) {
+                                              const float2* __restrict__ rope = nullptr,
+                                              const float* __restrict__ knew = nullptr,
+                                              const float* __restrict__ vnew = nullptr) {
   static_assert(HD == 64 || HD == 128, "head_dim 64 or 128");
   static_assert(QG >= 1 && QG <= ATT_QMAX, "query slots per workgroup");
   constexpr int KC = HD / 32;          // 32-dimension chunks of a score product
@@ -264,6 +244,31 @@ __global__ __launch_bounds__(256) void k_attn(const float* __restrict__ q, const
         x1[e] = x1[e] * c1.x + sg * (p1[e] * c1.y);
       }
     }
+  }
+  // With knew / vnew given (float32 [B * G1, H * HD], the projections of the new
+  // positions) the launch also appends them: the workgroup whose key blocks hold new
+  // position L + i rotates that key (RoPE from the same table as the queries), writes
+  // bf16 K and V at L + i of the cache, and only then loads its keys (the barrier
+  // makes its own stores visible to its loads).  Other workgroups never read them.
+  bool appends = false;
+  if (knew && rope && !invalid[b])
+    for (int i = 0; i < G1; ++i) appends |= ((L + i) / ATT_KEYS) % S == s && L + i < a.max_len;
+  if (appends) {
+    constexpr int HALF = HD / 2;
+    for (int t = threadIdx.x; t < G1 * HALF; t += blockDim.x) {
+      const int i = t / HALF, jd = t - i * HALF, pos = L + i;
+      if (((pos / ATT_KEYS) % S) != s || pos >= a.max_len) continue;
+      const size_t row = (size_t(b) * G1 + i) * a.H * HD + size_t(h) * HD;
+      const float2 cs = rope[(size_t(b) * G1 + i) * HALF + jd];
+      const float k1 = knew[row + jd], k2 = knew[row + jd + HALF];
+      bf16_t* kd = const_cast<bf16_t*>(kbase) + size_t(pos) * HD;
+      bf16_t* vd = const_cast<bf16_t*>(vbase) + size_t(pos) * HD;
+      kd[jd] = f32_to_bf16(k1 * cs.x - k2 * cs.y);
+      kd[jd + HALF] = f32_to_bf16(k2 * cs.x + k1 * cs.y);
+      vd[jd] = f32_to_bf16(vnew[row + jd]);
+      vd[jd + HALF] = f32_to_bf16(vnew[row + jd + HALF]);
+    }
+    __syncthreads();
   }
   int k0 = s * ATT_KEYS + wave * 64;
   load_block(k0);

@@ -1,24 +1,33 @@
 """Benchmark of the verify step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --workload full-model|sweep|masked-head|filtered|drafter|rounds
 
 One step is one verify pass of the large-vocabulary workload: bf16 LM head
 W[262144, 1536] (about 805 MB), final hidden states [B=1, gamma+1=5, 1536],
 gamma = 4 drafts with a bf16 draft distribution q, temperature 1: logits of
 all five slots, vocab-wide softmax statistics, the min(1, p/q) acceptance
 test, the residual/bonus resample and the commit of n_accepted / tokens.
-Inputs are seeded synthetic arrays resident in HBM before timing starts; the
-step rotates over eight input sets so acceptance varies.
+Inputs are seeded synthetic arrays resident in HBM before timing starts; step i
+verifies one of eight input sets at its own positions (pos0 + 11 i), so
+acceptance and the random draws vary from step to step.
 
 Prints one JSON line: the metric is committed (verified) tokens per second,
 sum over steps of (n_accepted + 1) divided by the timed wall time between two
-device synchronisations.  ``roofline`` reports the LM-head product (the
-dominant kernel): algorithmic bytes per launch (W once plus the hidden
-states) over its average duration measured with HIP events on the stream the
-library launches it on (one event pair around the timed loop; a step is one launch
-of that kernel here, so this is its duration per launch including launch gaps),
-against the 8 TB/s HBM peak.  ``cpu_baseline`` times
-the CPU oracle (float64 numpy) on a bounded sample of the same workload.
+device synchronisations.  ``roofline`` reports the fused verify kernel (the
+whole step is one launch): algorithmic bytes per launch (W once, the hidden
+states, the q row of a rejected step) over its average duration measured with
+HIP events on the stream the library launches it on (one event pair around the
+timed loop, so launch gaps are included), against the 8 TB/s HBM peak.
+``config`` also carries:
+- the acceptance per slot and the mean committed tokens of the timed steps;
+- the greedy rule (T = 0) on the same table;
+- the d = 4096 head's B = 1, gamma = 4 point.
+``cpu_baseline`` times the CPU oracle (float64 numpy) on a bounded sample of
+the same workload: three warm-up steps, then the median of the timed ones.  It
+reports the core counts, a spot check of the oracle against the GPU's decisions,
+and the pages' closed form for the expected committed tokens from the
+measured alpha = sum_v min(p, q) per slot.
 """
 import argparse
 import json

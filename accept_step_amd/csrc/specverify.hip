@@ -458,7 +458,7 @@ constexpr int WIDE_MAX_ROWS = 16 * WIDE_MB_MAX * 8;
 struct WidePlan {
   bool ok = false;
   int MB = 0, BLK = 0, m_tiles = 0, n_tiles = 0, grid = 0;
-  bool nt = true;
+  bool nt = true, wl = false;
   size_t lds = 0;
 };
 
@@ -476,15 +476,16 @@ WidePlan plan_wide(int M, int K, int N) {
   p.nt = p.m_tiles == 1;                      // sibling M-tiles read W again from L2
   p.n_tiles = (N + 64 * p.BLK - 1) / (64 * p.BLK);
   p.grid = (p.n_tiles + 7) / 8 * 8 * p.m_tiles;
-  p.lds = size_t(2) * 16 * p.MB * (kch + 8) * 2;
+  p.wl = p.MB <= 8;                          // W through LDS in 256-byte runs (sv_wide.hpp)
+  p.lds = size_t(2) * 16 * p.MB * (kch + 8) * 2 + (p.wl ? size_t(4) * 64 * WIDE_WLD * 2 : 0);
   p.ok = true;
   return p;
 }
 
 sv_status launch_wide(const WidePlan& p, WideArgs a, hipStream_t s) {
   a.m_tiles = p.m_tiles; a.n_tiles = p.n_tiles;
-  const void* fn = p.MB == 4 ? reinterpret_cast<const void*>(&k_wide<4, 4, true>)
-                 : p.MB == 8 ? reinterpret_cast<const void*>(&k_wide<8, 4, true>)
+  const void* fn = p.MB == 4 ? reinterpret_cast<const void*>(&k_wide<4, 4, true, true>)
+                 : p.MB == 8 ? reinterpret_cast<const void*>(&k_wide<8, 4, true, true>)
                  : p.nt ? reinterpret_cast<const void*>(&k_wide<WIDE_MB_MAX, 4, true>)
                         : reinterpret_cast<const void*>(&k_wide<WIDE_MB_MAX, 4, false>);
   sv_status st = head_set_lds(fn, p.lds);

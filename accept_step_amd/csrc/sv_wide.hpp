@@ -8,16 +8,23 @@
 // above it by the matrix cores.  So W must be read from HBM once whatever M is, and
 // the MFMA work must keep its operands in registers and LDS, not in HBM.
 //
-// Tiling.  A workgroup (four wavefronts) computes a tile of 16 * MB rows of X (MB <=
-// WIDE_MB_MAX: up to 192 rows) by WIDE_BN = 256 rows of W over all of K.  Wavefront w
-// owns W rows [64 w, 64 w + 64) of the tile: four MFMA blocks of 16 rows that it
-// streams from HBM straight into registers, k-chunk by k-chunk (WIDE_KCH = 128), the
-// next chunk's loads in flight while the current one is multiplied.  The X chunk
-// [16 MB x 128] is shared by the four wavefronts through LDS (double-buffered: the
-// next chunk is loaded into registers during the multiplication and stored to the
-// other buffer after it, one barrier per chunk).  Per MFMA step (32 k) a wavefront
-// reads MB X fragments from LDS and multiplies each with its four W fragments, so the
-// LDS traffic per MFMA is a quarter fragment.
+// Tiling.  A workgroup (four wavefronts) computes a tile of 16 * MB rows of X (MB = 4,
+// 8 or 12: up to 192 rows) by 256 rows of W over all of K.  Wavefront w owns W rows
+// [64 w, 64 w + 64) of the tile (four MFMA blocks of 16 rows) and streams them chunk by
+// chunk (128 k), the next chunk's loads in flight while the current one is multiplied.
+// The X chunk [16 MB x 128] is shared by the four wavefronts through LDS (double-
+// buffered: the next chunk is loaded into registers during the multiplication and
+// stored to the other buffer after it, one barrier per chunk).  Per MFMA step (32 k) a
+// wavefront reads MB X fragments from LDS and multiplies each with its four W
+// fragments, so the X traffic per MFMA is a quarter fragment.
+//
+// W loads.  The 192-row tile loads its W fragments straight into registers in the
+// operand layout: one load instruction covers 64 bytes of each of 16 rows.  The 64- and
+// 128-row tiles (bound by HBM) load W in runs of 256 contiguous bytes of 4 rows per
+// instruction and pass it through a wavefront-private LDS area (WL below): 477 against
+// 527 us at 20 rows of the 4096-wide head, 487 against 548 at 48.  The 192-row tile
+// has no LDS left for it.  (The template keeps BLK, the W blocks per wavefront, as a
+// parameter: one or two blocks with longer chunks measured slower.)
 //
 // MFMA v_mfma_f32_16x16x32_bf16: operand A = 16 W rows x 32 k, operand B = 32 k x 16
 // X rows; lane (r, g) = (lane % 16, lane / 16) holds row r and k-group g.  The k-slots
@@ -128,10 +135,62 @@ __device__ __forceinline__ void wide_chunk(const u32x4 (&w)[BLK][16 / BLK], cons
   }
 }
 
+// ---- W through LDS (WL): the 64-row, four-block shape with W loaded in long runs.
+// A load instruction of the register path covers 64 bytes of each of 16 rows (the MFMA
+// operand layout); here instruction u of a chunk covers 256 contiguous bytes of each of
+// 4 rows (lane l: row 4 u + l / 16, piece l % 16), the wavefront writes the chunk to its
+// own LDS area [64 rows][WIDE_WLD] and reads the A fragments back in the operand layout.
+constexpr int WIDE_WLD = 128 + 8;       // row stride of a wavefront's W chunk in LDS (elements)
+
+template <bool NT>
+__device__ __forceinline__ void wide_load_wl(const bf16_t* W, const int (&wro)[16], int k0, u32x4 (&w)[16]) {
+#pragma unroll
+  for (int u = 0; u < 16; ++u) w[u] = NT ? load_stream16(W + size_t(wro[u]) + k0) : load16(W + size_t(wro[u]) + k0);
+}
+
+__device__ __forceinline__ void wide_store_wl(const u32x4 (&w)[16], bf16_t* wl) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int u = 0; u < 16; ++u)
+    *reinterpret_cast<u32x4*>(wl + (4 * u + (lane >> 4)) * WIDE_WLD + 8 * (lane & 15)) = w[u];
+}
+
+// One chunk from LDS: step j's four A fragments (blocks 0-3; ab = wl + r * WIDE_WLD + 8 g)
+// are read during step j - 1; X fragments two groups ahead as in wide_chunk.
+template <int MB>
+__device__ __forceinline__ void wide_chunk_wl(const bf16_t* ab, const bf16_t* xb, f32x4 (&acc)[4][MB]) {
+  constexpr int NQ = 4 * MB;
+  u32x4 ac[4], an[4];
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) ac[blk] = *reinterpret_cast<const u32x4*>(ab + 16 * blk * WIDE_WLD);
+  u32x4 x0 = wide_xfrag<MB, 4>(xb, 0), x1 = wide_xfrag<MB, 4>(xb, 1 < NQ ? 1 : 0);
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int j = q / MB, mb = q % MB;
+    u32x4 x2 = x1;
+    if (q + 2 < NQ) x2 = wide_xfrag<MB, 4>(xb, q + 2);
+    if (mb == 0 && j + 1 < 4) {
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk)
+        an[blk] = *reinterpret_cast<const u32x4*>(ab + 16 * blk * WIDE_WLD + 32 * (j + 1));
+    }
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) acc[blk][mb] = mfma16x16x32(ac[blk], x0, acc[blk][mb]);
+    x0 = x1;
+    x1 = x2;
+    if (mb == MB - 1 && j + 1 < 4) {
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) ac[blk] = an[blk];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // grid: ceil(n_tiles / 8) * 8 * m_tiles workgroups of 256 threads; M-tiles of 16 * MB
 // rows, W tiles of 64 * BLK rows; dynamic LDS 2 * 16 * MB * (KCH + 8) * 2 bytes.
-template <int MB, int BLK, bool NT>
+template <int MB, int BLK, bool NT, bool WL = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_wide(WideArgs a) {
+  static_assert(!WL || BLK == 4, "W through LDS: the four-block shape");
   using XC = WideX<MB, BLK>;
   constexpr int STEPS = 16 / BLK;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -161,6 +220,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const bf16_t* xb0 = sx0 + r * XC::LD + 8 * g;
   const bf16_t* xb1 = sx1 + r * XC::LD + 8 * g;
   const int nch = K / XC::KCH;
+  // WL: the wavefront's LDS area after the two X buffers, and the element offsets of its
+  // 16 load rows (4 u + lane / 16, clamped) and piece (lane % 16)
+  bf16_t* wl = sx1 + 16 * MB * XC::LD + wave * 64 * WIDE_WLD;
+  const bf16_t* ab = wl + r * WIDE_WLD + 8 * g;
+  int wro[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) wro[u] = min(vw + 4 * u + (lane >> 4), N - 1) * K + 8 * (lane & 15);
 
   f32x4 acc[BLK][MB];
 #pragma unroll
@@ -168,6 +234,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[blk][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   u32x4 wa[BLK][STEPS], wb[BLK][STEPS], xr[XC::NX];
+  u32x4 (&wla)[16] = reinterpret_cast<u32x4 (&)[16]>(wa);    // WL: the same registers, load-run order
+  u32x4 (&wlb)[16] = reinterpret_cast<u32x4 (&)[16]>(wb);
 
   // chunk 0; then two chunks per iteration (K is a multiple of two chunks), the next
   // one's loads (the last iteration's clamped to the last chunk, so every load is
@@ -179,20 +247,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // body: two exits would give the accumulators two sets of registers and copies
   // between them.
   wide_load_x<MB, BLK>(a.X, xo, 0, xr);
-  wide_load_w<BLK, NT>(wp, 0, wa);
+  if constexpr (WL) wide_load_wl<NT>(a.W, wro, 0, wla);
+  else wide_load_w<BLK, NT>(wp, 0, wa);
   wide_store_x<MB, BLK>(rows, xr, sx0);
   __syncthreads();
   for (int c = 0; c < nch; c += 2) {
     const int k1 = (c + 1) * XC::KCH;
     wide_load_x<MB, BLK>(a.X, xo, k1, xr);
-    wide_load_w<BLK, NT>(wp, k1, wb);
-    wide_chunk<MB, BLK>(wa, xb0, acc);
+    if constexpr (WL) {
+      wide_load_wl<NT>(a.W, wro, k1, wlb);
+      wide_store_wl(wla, wl);                  // this wavefront's area: no barrier needed
+      wide_chunk_wl<MB>(ab, xb0, reinterpret_cast<f32x4 (&)[4][MB]>(acc));
+    } else {
+      wide_load_w<BLK, NT>(wp, k1, wb);
+      wide_chunk<MB, BLK>(wa, xb0, acc);
+    }
     wide_store_x<MB, BLK>(rows, xr, sx1);
     __syncthreads();
     const int k2 = min(c + 2, nch - 1) * XC::KCH;
     wide_load_x<MB, BLK>(a.X, xo, k2, xr);
-    wide_load_w<BLK, NT>(wp, k2, wa);
-    wide_chunk<MB, BLK>(wb, xb1, acc);
+    if constexpr (WL) {
+      wide_load_wl<NT>(a.W, wro, k2, wla);
+      wide_store_wl(wlb, wl);
+      wide_chunk_wl<MB>(ab, xb1, reinterpret_cast<f32x4 (&)[4][MB]>(acc));
+    } else {
+      wide_load_w<BLK, NT>(wp, k2, wa);
+      wide_chunk<MB, BLK>(wb, xb1, acc);
+    }
     wide_store_x<MB, BLK>(rows, xr, sx0);
     __syncthreads();
   }

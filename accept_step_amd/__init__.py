@@ -20,7 +20,7 @@ import torch
 __all__ = ["SV_F32", "SV_BF16", "SV_IN_LOGITS", "SV_IN_HIDDEN", "SV_IN_TOKENS", "VerifyError",
            "Model", "KVCache", "Workspace", "lm_head_model", "logits_model", "decoder_model",
            "verify_forward", "spec_verify_greedy", "spec_verify_sample", "spec_verify_sample_noalloc", "library", "library_path",
-           "timing_enable", "timing_read", "set_option", "SV_OPT_WAIT_LIMIT", "LAYER_KEYS", "MaskedHead", "masked_head", "draft_masked_logits"]
+           "timing_enable", "timing_read", "set_option", "SV_OPT_WAIT_LIMIT", "tune_verify", "LAYER_KEYS", "MaskedHead", "masked_head", "draft_masked_logits"]
 
 SV_F32, SV_BF16 = 0, 1
 SV_IN_LOGITS, SV_IN_HIDDEN, SV_IN_TOKENS = 0, 1, 2
@@ -109,6 +109,10 @@ def library():
         f.restype = i32
     lib.sv_set_option.argtypes = [i32, ctypes.c_int64]
     lib.sv_set_option.restype = i32
+    lib.sv_tune_verify.argtypes = [M, i32, i32, vp]
+    lib.sv_tune_verify.restype = i32
+    lib.sv_tuned_item.argtypes = [M, i32, i32]
+    lib.sv_tuned_item.restype = i32
     lib.sv_version.restype = i32
     lib.sv_status_string.restype = ctypes.c_char_p
     lib.sv_status_string.argtypes = [i32]
@@ -229,6 +233,15 @@ SV_OPT_WAIT_LIMIT = 0
 def set_option(option, value):
     """Process-wide library option (C: sv_set_option); value < 0 restores the default."""
     _check(library().sv_set_option(int(option), int(value)))
+
+
+def tune_verify(model, B, gamma, stream=None):
+    """Choose the fused step's load grouping for this device and shape (C:
+    sv_tune_verify): a setup call (allocates, synchronises); results are the same bits
+    whatever it picks.  Returns the item size now in use (0: nothing to tune)."""
+    lib = library()
+    _check(lib.sv_tune_verify(ctypes.byref(model.struct), int(B), int(gamma), _stream(stream)))
+    return int(lib.sv_tuned_item(ctypes.byref(model.struct), int(B), int(gamma)))
 
 
 class Workspace:

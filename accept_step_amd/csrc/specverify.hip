@@ -15,6 +15,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <string>
@@ -78,6 +79,7 @@ size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 // ---------------------------------------------------------------------------
 // device properties (per device, lazily)
 struct DevInfo {
+  int dev = 0;
   int cus = 0;
   size_t lds_max = 64 * 1024;   // dynamic LDS per workgroup the streaming product may use
 };
@@ -97,7 +99,31 @@ sv_status dev_info(DevInfo* out) {
     g_dev[dev].lds_max = lds >= 64 * 1024 ? size_t(lds) : size_t(64 * 1024);
   }
   *out = g_dev[dev];
+  out->dev = dev;
   return SV_OK;
+}
+
+// Item sizes chosen by sv_tune_verify for the fused step, per (device, M, K, V).  The
+// item size changes how the stream's loads are grouped, not the summation order: the
+// logits and every decision are the same bits whichever is used.
+struct TunedItem {
+  int dev, M, K, N, grp;
+};
+std::mutex g_tune_mu;
+std::vector<TunedItem> g_tuned;
+
+int tuned_item(int dev, int M, int K, int N) {
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  for (const TunedItem& t : g_tuned)
+    if (t.dev == dev && t.M == M && t.K == K && t.N == N) return t.grp;
+  return 0;
+}
+
+void set_tuned_item(int dev, int M, int K, int N, int grp) {
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  for (TunedItem& t : g_tuned)
+    if (t.dev == dev && t.M == M && t.K == K && t.N == N) { t.grp = grp; return; }
+  g_tuned.push_back({dev, M, K, N, grp});
 }
 
 // Process-wide options (sv_set_option).
@@ -316,7 +342,8 @@ int head_nb_max(int S) { return S == 4 ? 5 : 3; }
 // 130.6 us against 137.1 us with items of 4).  only_s != 0 admits that split factor
 // alone.  The plan depends on the shapes and the device only, so the summation order
 // (and so every logit bit) is the same from call to call.
-HeadPlan plan_head(int M, int K, const int* N, int nseg, const DevInfo& di, bool rule = false, int only_s = 0) {
+HeadPlan plan_head(int M, int K, const int* N, int nseg, const DevInfo& di, bool rule = false, int only_s = 0,
+                   int want_grp = 0) {
   HeadPlan p;
   if (M < 1 || M > HEAD_MAX_ROWS || K % 8) return p;
   for (int i = 0; i < nseg; ++i)    // weights are addressed with 32-bit byte offsets
@@ -328,10 +355,10 @@ HeadPlan plan_head(int M, int K, const int* N, int nseg, const DevInfo& di, bool
     const int TR = 16 / S, NB = (M + TR - 1) / TR;
     if (NB > head_nb_max(S) || K % (32 * S)) continue;
     const int steps = K / (32 * S);
-    int GRP = 0;
-    for (int i = 0; i < 3; ++i) {
+    int GRP = want_grp && steps % want_grp == 0 ? want_grp : 0;
+    for (int i = 0; i < 3 && !GRP; ++i) {
       const int gc = order[i];
-      if (steps % gc == 0) { GRP = gc; break; }
+      if (steps % gc == 0) GRP = gc;
     }
     if (!GRP) GRP = 4;   // the last item of a tile runs past K over zeros in X
     const int gpt = (steps + GRP - 1) / GRP, Kp = gpt * GRP * 32 * S;
@@ -355,7 +382,7 @@ HeadPlan plan_head(int M, int K, const int* N, int nseg, const DevInfo& di, bool
 HeadPlan plan_head_rule(int M, int K, const int* N, const DevInfo& di) {
   HeadPlan hp = plan_head(M, K, N, 1, di);
   if (!hp.ok) return hp;
-  const HeadPlan r = plan_head(M, K, N, 1, di, true, hp.S);
+  const HeadPlan r = plan_head(M, K, N, 1, di, true, hp.S, tuned_item(di.dev, M, K, N[0]));
   return r.ok ? r : hp;
 }
 
@@ -1155,6 +1182,91 @@ sv_status spec_verify_sample_noalloc(const sv_model* m, sv_input_kind kind, cons
   size_t have = NOALLOC_SCRATCH_BYTES;
   return verify_common(m, kind, input, B, gamma, draft, q, q_dtype, temperature, seed, pos0, kv, n_accepted,
                        tokens_out, logits_out, diag, ptr, &have, stream, true);
+}
+
+sv_status sv_tune_verify(const sv_model* m, int32_t B, int32_t gamma, void* stream) {
+  g_err.clear();
+  if (!m) return fail(SV_ERR_ARG, "model is NULL");
+  if (m->n_layers != 0 || m->wdtype != SV_BF16) return SV_OK;     // only the bf16 LM-head step is tuned
+  Shape sh;
+  alignas(16) const bf16_t dummy[8] = {};   // a size query reads no argument's memory
+  sv_status st = check_common(m, SV_IN_HIDDEN, dummy, B, gamma, nullptr, &sh);
+  if (st) return st;
+  DevInfo di;
+  if ((st = dev_info(&di))) return st;
+  const int M = sh.M, K = sh.d, Nv[1] = {sh.V};
+  const HeadPlan hp = plan_head(M, K, Nv, 1, di);
+  if (!hp.ok) return SV_OK;                                        // no fused step for this shape
+  const int steps = K / (32 * hp.S);
+  std::vector<int> cand;
+  for (int gc : {6, 4, 8})
+    if (steps % gc == 0) cand.push_back(gc);
+  if (cand.size() < 2) return SV_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // the workspace the greedy step needs (size query), then zero inputs: the stream's
+  // timing does not depend on the values
+  size_t need = 0;
+  int32_t hn = 0, ht = 0;
+  if ((st = spec_verify_greedy(m, SV_IN_HIDDEN, dummy, B, gamma, &hn, nullptr, &hn, &ht, nullptr, nullptr, nullptr,
+                               &need, stream)))
+    return st;
+  void *x = nullptr, *dr = nullptr, *n = nullptr, *tok = nullptr, *ws = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  auto cleanup = [&]() {
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    for (void* p : {x, dr, n, tok, ws})
+      if (p) (void)hipFree(p);
+  };
+  const int before = tuned_item(di.dev, M, K, sh.V);
+  std::vector<std::vector<float>> times(cand.size());
+  hipError_t he = hipSuccess;
+  do {
+    if ((he = hipMalloc(&x, size_t(M) * K * 2)) || (he = hipMalloc(&dr, size_t(B) * gamma * 4)) ||
+        (he = hipMalloc(&n, size_t(B) * 4)) || (he = hipMalloc(&tok, size_t(M) * 4)) || (he = hipMalloc(&ws, need)) ||
+        (he = hipMemsetAsync(x, 0, size_t(M) * K * 2, s)) || (he = hipMemsetAsync(dr, 0, size_t(B) * gamma * 4, s)) ||
+        (he = hipMemsetAsync(ws, 0, need, s)) || (he = hipEventCreate(&e0)) || (he = hipEventCreate(&e1)))
+      break;
+    for (int round = 0; round < 3 && he == hipSuccess && !st; ++round)
+      for (size_t ci = 0; ci < cand.size() && he == hipSuccess && !st; ++ci) {
+        set_tuned_item(di.dev, M, K, sh.V, cand[ci]);
+        for (int i = 0; i < 10 && he == hipSuccess && !st; ++i) {
+          if (i == 2) he = hipEventRecord(e0, s);
+          size_t have = need;
+          st = spec_verify_greedy(m, SV_IN_HIDDEN, x, B, gamma, static_cast<const int32_t*>(dr), nullptr,
+                                  static_cast<int32_t*>(n), static_cast<int32_t*>(tok), nullptr, nullptr, ws, &have,
+                                  stream);
+        }
+        float ms = 0.0f;
+        if (he == hipSuccess && !st && (he = hipEventRecord(e1, s)) == hipSuccess &&
+            (he = hipEventSynchronize(e1)) == hipSuccess && (he = hipEventElapsedTime(&ms, e0, e1)) == hipSuccess)
+          times[ci].push_back(ms);
+      }
+  } while (false);
+  if (he != hipSuccess || st) {
+    set_tuned_item(di.dev, M, K, sh.V, before);
+    cleanup();
+    if (st) return st;
+    return fail(SV_ERR_HIP, "tuning: %s", hipGetErrorString(he));
+  }
+  size_t best = 0;
+  float best_t = 0.0f;
+  for (size_t ci = 0; ci < cand.size(); ++ci) {
+    std::vector<float> t = times[ci];
+    std::sort(t.begin(), t.end());
+    const float med = t[t.size() / 2];
+    if (ci == 0 || med < best_t) { best = ci; best_t = med; }
+  }
+  set_tuned_item(di.dev, M, K, sh.V, cand[best]);
+  cleanup();
+  return SV_OK;
+}
+
+int32_t sv_tuned_item(const sv_model* m, int32_t B, int32_t gamma) {
+  if (!m || m->n_layers != 0 || m->wdtype != SV_BF16 || B < 1 || gamma < 1) return 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  return tuned_item(dev, B * (gamma + 1), m->d_model, m->vocab);
 }
 
 sv_status draft_masked_logits(const sv_masked_head* head, const void* hidden, int32_t M, int32_t top_k,

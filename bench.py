@@ -125,6 +125,8 @@ def main():
     t_out = torch.empty((K, B, gamma + 1), dtype=torch.int32, device=dev)
     ws = sv.Workspace()
     seed = cases[0].seed
+    # the fused step's load grouping for this device (a setup call; same bits either way)
+    tuned = sv.tune_verify(model, B, gamma)
 
     def step(i, out=None):
         h, dr, q = sets[i % N_SETS]
@@ -193,6 +195,7 @@ def main():
     # ---- configuration 4's B = 1, gamma = 4 point (d = 4096, 2,147,483,648 bytes of W)
     c4 = workloads.batch_sweep(B=1, gamma=4)
     model4 = sv.lm_head_model(to_dev_bf16(c4.w))
+    tuned4 = sv.tune_verify(model4, 1, 4)
     set4 = (to_dev_bf16(c4.h), torch.from_numpy(c4.draft.astype(np.int32)).to(dev), to_dev_bf16(c4.q),
             torch.from_numpy(c4.pos0).to(dev))
     del c4
@@ -229,6 +232,7 @@ def main():
                    "verify_steps_per_s": round(K / elapsed, 1),
                    "step_hbm_gbs": round(algo_bytes / (elapsed / K) / 1e9, 1),
                    "step_frac_of_peak": round(algo_bytes / (elapsed / K) / 1e9 / HBM_PEAK_GBS, 4),
+                   "fused_step_item_size": tuned,
                    "acceptance_per_slot": [round(a_, 4) for a_ in alpha],
                    "mean_committed_per_step": round(float((nn + 1).mean()), 4),
                    "greedy_T0": {"us_per_step": round(us0, 2), "verified_tokens_per_s": round(
@@ -236,6 +240,7 @@ def main():
                        "step_hbm_gbs": round(algo0 / (us0 * 1e-6) / 1e9, 1),
                        "step_frac_of_peak": round(algo0 / (us0 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
                    "config4_B1_gamma4_T1": {"workload": "bf16 LM head V=262144 d=4096, B=1, gamma=4, T=1.0",
+                                            "fused_step_item_size": tuned4,
                                             "us_per_step": round(us4, 2),
                                             "step_hbm_gbs": round(algo4 / (us4 * 1e-6) / 1e9, 1),
                                             "step_frac_of_peak": round(algo4 / (us4 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}},

@@ -393,6 +393,27 @@ sv_status round_select_candidates(int32_t B, int32_t C, int32_t G1, const int32_
 typedef enum sv_option { SV_OPT_WAIT_LIMIT = 0 } sv_option;
 sv_status sv_set_option(int32_t option, int64_t value);
 
+/* Per-device choice of the fused step's load grouping, for callers that run the same
+ * bf16 LM-head shape many times.  The fused verify kernel issues its weight loads in
+ * items of 4, 6 or 8 16-byte loads per lane; which item size streams fastest depends on
+ * the device (on some MI355X boards items of 6 leave the odd XCDs about 4 us behind,
+ * on others items of 4 are 1-2 us slower).  sv_tune_verify times the fused greedy step
+ * of this model at B x (gamma + 1) rows with each item size that divides the work
+ * (three alternating rounds of eight launches on zero inputs; the timing does not depend
+ * on the values) and keeps the faster one for this device and shape, for every later
+ * call with that shape (greedy, sampling, noalloc).  The item size changes only the
+ * grouping of the loads, not the summation order: logits and decisions are the same
+ * bits with any item size.
+ *   A setup call: it allocates and frees device memory (inputs, outputs, a workspace),
+ *   synchronises the stream and must not be captured into a graph.  Models other than
+ *   a bf16 LM head, or shapes without a fused step, are left as they are (SV_OK).
+ *   Errors: SV_ERR_ARG / SV_ERR_SHAPE as for spec_verify_greedy; SV_ERR_HIP if an
+ *   allocation or launch fails (the previous choice is kept).  Thread-safe.
+ * sv_tuned_item returns the item size in use for that model and shape on the current
+ * device (0: not tuned; the default order applies). */
+sv_status sv_tune_verify(const sv_model* m, int32_t B, int32_t gamma, void* stream);
+int32_t sv_tuned_item(const sv_model* m, int32_t B, int32_t gamma);
+
 /* Library version (major * 10000 + minor * 100 + patch). */
 int32_t sv_version(void);
 

@@ -246,3 +246,17 @@ def test_diag_is_optional_and_sized(lib):
     st, need = greedy(lib, m)
     st2, need_diag = greedy(lib, m, diag=FAKE)
     assert st == 0 and st2 == 0 and need_diag > need
+
+
+def test_tuning_entry_points_without_device(lib):
+    """sv_tune_verify checks its arguments before touching a device; models it does not
+    tune are left alone; sv_tuned_item reports nothing tuned."""
+    h = sv._SvModel()
+    h.n_layers, h.vocab, h.d_model, h.wdtype, h.lm_head = 0, 262144, 1536, sv.SV_BF16, FAKE
+    assert lib.sv_tune_verify(None, 1, 4, None) == 1
+    h32 = sv._SvModel()
+    h32.n_layers, h32.vocab, h32.d_model, h32.wdtype, h32.lm_head = 0, 1024, 64, sv.SV_F32, FAKE
+    assert lib.sv_tune_verify(ctypes.byref(h32), 1, 4, None) == 0          # float32 heads: nothing to tune
+    assert lib.sv_tune_verify(ctypes.byref(h), 0, 4, None) == 1            # B out of range
+    assert lib.sv_tune_verify(ctypes.byref(h), 1, 0, None) == 1            # gamma out of range
+    assert lib.sv_tuned_item(ctypes.byref(h), 1, 4) == 0

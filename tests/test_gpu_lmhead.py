@@ -309,3 +309,29 @@ def test_fused_sampler_wait_timeout():
             n, tok = sv.spec_verify_sample(*args, ws=ws)
             torch.cuda.synchronize()
             compare_decisions(n.cpu().numpy(), tok.cpu().numpy(), n0, t0, fl, f"after timeout {rnd}")
+
+
+def test_tuning_keeps_every_bit():
+    """sv_tune_verify picks the fused step's item size for this device; logits, accepted
+    counts and tokens are the same bits before and after (the item size groups the
+    loads, it does not reorder the sums)."""
+    cs = workloads.large_vocab(B=1, temperature=1.0)
+    model = sv.lm_head_model(dev_bf16(cs.w))
+    h, d, q, p0 = dev_bf16(cs.h), dev(cs.draft.astype(np.int32)), dev_bf16(cs.q), dev(cs.pos0)
+
+    def run():
+        lg = torch.empty((1, 5, 262144), dtype=torch.float32, device="cuda")
+        n, tok = sv.spec_verify_sample(model, sv.SV_IN_HIDDEN, h, 1, 4, d, q, 1.0, cs.seed, p0, logits_out=lg)
+        ng, tg = sv.spec_verify_greedy(model, sv.SV_IN_HIDDEN, h, 1, 4, d)
+        torch.cuda.synchronize()
+        return [t.cpu().numpy() for t in (n, tok, lg, ng, tg)]
+
+    before = run()
+    item = sv.tune_verify(model, 1, 4)
+    log(f"[tune] V=262144 d=1536 M=5: item size {item}")
+    assert item in (4, 6, 8)
+    after = run()
+    for a, b in zip(before, after):
+        assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                              b.view(np.uint32) if b.dtype == np.float32 else b)
+    assert sv.tune_verify(model, 1, 4) in (4, 6, 8)

@@ -330,6 +330,7 @@ constexpr size_t HEAD_STATIC_LDS = 8 * 1024;   // the kernel's static LDS (reduc
 struct HeadPlan {
   bool ok = false;
   int S = 0, NB = 0, GRP = 0, grid = 0, gpt = 0, nloc = 0;
+  bool pair = false;   // gate and up tiles paired in each wavefront, SwiGLU in the epilogue
   size_t lds = 0;
 };
 
@@ -343,9 +344,10 @@ int head_nb_max(int S) { return S == 4 ? 5 : 3; }
 // alone.  The plan depends on the shapes and the device only, so the summation order
 // (and so every logit bit) is the same from call to call.
 HeadPlan plan_head(int M, int K, const int* N, int nseg, const DevInfo& di, bool rule = false, int only_s = 0,
-                   int want_grp = 0) {
+                   int want_grp = 0, bool pair = false) {
   HeadPlan p;
   if (M < 1 || M > HEAD_MAX_ROWS || K % 8) return p;
+  if (pair && (nseg != 2 || N[0] != N[1])) return p;
   for (int i = 0; i < nseg; ++i)    // weights are addressed with 32-bit byte offsets
     if (int64_t(N[i]) * K * 2 > int64_t(0xffffffffLL) - 4096) return p;
   const int order_product[3] = {4, 8, 6}, order_rule[3] = {6, 4, 8};
@@ -366,10 +368,13 @@ HeadPlan plan_head(int M, int K, const int* N, int nseg, const DevInfo& di, bool
     for (int i = 0; i < nseg; ++i) ntiles += (N[i] + TR - 1) / TR;
     int grid = std::min(di.cus, GEMM_MAX_WG);
     grid = std::max(1, std::min(grid, (ntiles + HEAD_WAVES - 1) / HEAD_WAVES));
-    const int tpw = (ntiles + grid * HEAD_WAVES - 1) / (grid * HEAD_WAVES) * HEAD_WAVES;
+    const int span = grid * HEAD_WAVES;
+    // paired: a wavefront takes the gate and the up tile of each of its rows
+    const int tpw = pair ? 2 * ((ntiles / 2 + span - 1) / span) * HEAD_WAVES
+                         : (ntiles + span - 1) / span * HEAD_WAVES;
     const size_t lds = head_lds(M, Kp, S, tpw * TR);
     if (lds + HEAD_STATIC_LDS > di.lds_max) continue;
-    p.ok = true; p.S = S; p.NB = NB; p.GRP = GRP; p.grid = grid; p.gpt = gpt; p.nloc = tpw * TR;
+    p.ok = true; p.S = S; p.NB = NB; p.GRP = GRP; p.grid = grid; p.gpt = gpt; p.nloc = tpw * TR; p.pair = pair;
     p.lds = lds;
     return p;
   }
@@ -461,10 +466,22 @@ sv_status head_all_resident(const HeadPlan& p, const DevInfo& di, bool* yes) {
   return SV_OK;
 }
 
-sv_status launch_head(const HeadPlan& p, HeadArgs a, hipStream_t s) {
+// The decoder products' instantiation (honours HeadArgs::pair): split 4, items of 4.
+bool head_pairable(const HeadPlan& p) { return p.S == 4 && p.GRP == 4; }
+const void* head_fn_pairable(int NB) {
+  switch (NB) {
+    case 1: return reinterpret_cast<const void*>(&k_head<4, 1, 4, true>);
+    case 2: return reinterpret_cast<const void*>(&k_head<4, 2, 4, true>);
+    case 3: return reinterpret_cast<const void*>(&k_head<4, 3, 4, true>);
+    case 4: return reinterpret_cast<const void*>(&k_head<4, 4, 4, true>);
+    default: return reinterpret_cast<const void*>(&k_head<4, 5, 4, true>);
+  }
+}
+
+sv_status launch_head(const HeadPlan& p, HeadArgs a, hipStream_t s, bool pairable = false) {
   a.gpt = p.gpt;
   a.nloc = p.nloc;
-  const void* fn = head_fn(p);
+  const void* fn = pairable ? head_fn_pairable(p.NB) : head_fn(p);
   sv_status st = head_set_lds(fn, p.lds);
   if (st) return st;
   void* args[] = {&a};
@@ -533,31 +550,61 @@ struct ProductFuse {
   float eps = 0.0f;
   bool residual = false;
   float* ss_out = nullptr;
+  bf16_t* silu_out = nullptr;   // gate and up (two segments of equal N): bf16 SiLU(gate) * up here instead
+  bool pairable = false;        // launch on the instantiation that pairs (set for every product of a
+                                // decoder whose gate/up pairs: one kernel's code for all of them)
 };
 
 // Whether the decoder's fused sequence applies: every product of a layer runs on the
 // k-split kernel.
 bool fused_products_ok(int M, int d, int HD, int ff, const DevInfo& di) {
   const int n3[3] = {HD, HD, HD}, n1[1] = {d}, n2[2] = {ff, ff};
-  return plan_head(M, d, n3, 3, di).ok && plan_head(M, HD, n1, 1, di).ok && plan_head(M, d, n2, 2, di).ok &&
-         plan_head(M, ff, n1, 1, di).ok && M <= ACC_MAX_ROWS;
+  return plan_head(M, d, n3, 3, di).ok && plan_head(M, HD, n1, 1, di).ok &&
+         plan_head(M, d, n2, 2, di).ok && plan_head(M, ff, n1, 1, di).ok && M <= ACC_MAX_ROWS;
+}
+
+// Whether a decoder's gate/up product [2 x ff, K] pairs its tiles (SwiGLU in the
+// epilogue): the paired plan exists on the pairing instantiation and gives no wavefront
+// more tiles than the plain plan (a wavefront of a paired plan takes whole pairs; where
+// the plain plan gives each wavefront one tile, pairing doubles the chain of a launch
+// that is latency-bound: the drafter's 2048-wide FFN measured 758 -> 780 us per round).
+bool swiglu_paired(int M, int K, int ff, const DevInfo& di) {
+  const int n2[2] = {ff, ff};
+  const HeadPlan pp = plan_head(M, K, n2, 2, di, false, 0, 0, true), p = plan_head(M, K, n2, 2, di);
+  return pp.ok && p.ok && head_pairable(pp) && pp.nloc <= p.nloc;
 }
 
 // A k-split product with decoder fusions; *grid_out receives the launch's grid (the
 // number of sums-of-squares partials it leaves).
 sv_status run_product_fused(const bf16_t* X, int M, int K, int nseg, const void* const* W, float* const* out,
                             const int* N, const ProductFuse& f, int* grid_out, const DevInfo& di, hipStream_t s) {
-  const HeadPlan hp = plan_head(M, K, N, nseg, di);
+  HeadPlan hp;
+  if (f.silu_out && f.pairable) {
+    hp = plan_head(M, K, N, nseg, di, false, 0, 0, true);
+    if (!head_pairable(hp)) hp = HeadPlan();
+  }
+  const bool pair = hp.ok;
+  if (!pair) hp = plan_head(M, K, N, nseg, di);
   if (!hp.ok) return fail(SV_ERR_UNSUPPORTED, "fused decoder product does not fit the k-split kernel");
   HeadArgs a = head_args(X, M, K);
   for (int i = 0; i < nseg; ++i) head_add_seg(a, W[i], out[i], N[i], 16 / hp.S);
-  a.write_out = 1;
+  a.write_out = pair ? 2 : 1;
+  a.hout = pair ? f.silu_out : nullptr;
   a.mode = HEAD_PRODUCT;
   a.Xf = f.Xf; a.norm_w = f.norm_w; a.ss_in = f.ss_in; a.ss_parts = f.ss_parts; a.eps = f.eps;
   a.residual = f.residual ? 1 : 0;
   a.ss_out = f.ss_out;
   if (grid_out) *grid_out = hp.grid;
-  return launch_head(hp, a, s);
+  // every fused product on one instantiation where it can: products of one kernel in a
+  // row keep its code in the instruction caches (with the paired gate/up on a kernel of
+  // its own, the other products of a layer took 0.5-1.6 us longer each)
+  sv_status st = launch_head(hp, a, s, f.pairable && head_pairable(hp));
+  if (st || pair || !f.silu_out) return st;
+  // no paired plan (split 2, other items, LDS): the products, then SiLU(gate) * up
+  const int n = M * N[0];
+  hipLaunchKernelGGL(k_silu_mul, dim3((n + 255) / 256), dim3(256), 0, s, out[0], out[1], f.silu_out, n);
+  SV_HIP(hipGetLastError());
+  return SV_OK;
 }
 
 // A product out_s[M, N_s] = X[M, K] W_s^T for up to three weights sharing X: the
@@ -762,12 +809,13 @@ sv_status run_decoder(const sv_model* m, const Shape& sh, const int* tokens, con
     // rows left (k_embed: one per row; the output projections: one per workgroup, as
     // they add their products into x).
     int parts = 1;
+    const bool pairs = swiglu_paired(M, d, ff, di);
     for (int l = 0; l < m->n_layers; ++l) {
       const void* const* w = m->layers + size_t(l) * 9;
       ProductFuse fn;
-      fn.Xf = x; fn.ss_in = ss; fn.ss_parts = parts; fn.eps = m->rms_eps;
+      fn.Xf = x; fn.ss_in = ss; fn.ss_parts = parts; fn.eps = m->rms_eps; fn.pairable = pairs;
       ProductFuse fr;
-      fr.residual = true; fr.ss_out = ss;
+      fr.residual = true; fr.ss_out = ss; fr.pairable = pairs;
       {
         const void* ws3[3] = {w[1], w[2], w[3]};
         float* o3[3] = {q, k, v};
@@ -788,12 +836,10 @@ sv_status run_decoder(const sv_model* m, const Shape& sh, const int* tokens, con
         const int n2[2] = {ff, ff};
         fn.ss_parts = parts;
         fn.norm_w = static_cast<const bf16_t*>(w[5]);
-        if ((st = run_product_fused(nullptr, M, d, 2, w2, o2, n2, fn, nullptr, di, s))) return st;
+        ProductFuse fg = fn;
+        fg.silu_out = h;   // SwiGLU in the epilogue: each wavefront holds matching gate and up tiles
+        if ((st = run_product_fused(nullptr, M, d, 2, w2, o2, n2, fg, nullptr, di, s))) return st;
       }
-      // silu(gate) * up as its own small launch: folded into the down projection's
-      // staging, every one of its workgroups recomputed all M * d_ff activations
-      // (products 25.8 -> 30.8 us on average)
-      hipLaunchKernelGGL(k_silu_mul, dim3((nf + 255) / 256), dim3(256), 0, s, gate, up, h, nf);
       {
         const void* w1[1] = {w[8]};
         float* o1[1] = {x};
@@ -1536,8 +1582,10 @@ sv_status mtp_draft(const sv_drafter* dr, const sv_shared_kv* kv, int32_t B, int
     if (k == 0)
       hipLaunchKernelGGL(k_mtp_join, dim3(B), dim3(256), 0, s, tok, static_cast<const bf16_t*>(dr->embed), hcur, z, D,
                          x, H);
+    const bool pairs = swiglu_paired(B, H, ff, di);
     ProductFuse fr;
     fr.residual = true;
+    fr.pairable = pairs;
     fr.ss_out = ss;
     int parts = 1;
     {
@@ -1549,7 +1597,7 @@ sv_status mtp_draft(const sv_drafter* dr, const sv_shared_kv* kv, int32_t B, int
     for (int l = 0; l < nl; ++l) {
       const void* const* w = dr->layers + size_t(l) * 7;
       ProductFuse fn;
-      fn.Xf = x; fn.ss_in = ss; fn.ss_parts = parts; fn.eps = dr->rms_eps;
+      fn.Xf = x; fn.ss_in = ss; fn.ss_parts = parts; fn.eps = dr->rms_eps; fn.pairable = pairs;
       fn.norm_w = static_cast<const bf16_t*>(w[0]);
       {
         const void* w1[1] = {w[1]};
@@ -1578,9 +1626,10 @@ sv_status mtp_draft(const sv_drafter* dr, const sv_shared_kv* kv, int32_t B, int
         const void* w2[2] = {w[4], w[5]};
         float* o2[2] = {gate, up};
         const int n2[2] = {ff, ff};
-        if ((st = run_product_fused(nullptr, B, H, 2, w2, o2, n2, fn, nullptr, di, s))) return st;
+        ProductFuse fg = fn;
+        fg.silu_out = f;   // SwiGLU in the epilogue
+        if ((st = run_product_fused(nullptr, B, H, 2, w2, o2, n2, fg, nullptr, di, s))) return st;
       }
-      hipLaunchKernelGGL(k_silu_mul, dim3((B * ff + 255) / 256), dim3(256), 0, s, gate, up, f, B * ff);
       {
         const void* w1[1] = {w[6]};
         float* o1[1] = {x};
@@ -1590,7 +1639,7 @@ sv_status mtp_draft(const sv_drafter* dr, const sv_shared_kv* kv, int32_t B, int
     }
     {
       ProductFuse fn;
-      fn.Xf = x; fn.ss_in = ss; fn.ss_parts = parts; fn.eps = dr->rms_eps;
+      fn.Xf = x; fn.ss_in = ss; fn.ss_parts = parts; fn.eps = dr->rms_eps; fn.pairable = pairs;
       fn.norm_w = static_cast<const bf16_t*>(dr->final_norm);
       const void* w1[1] = {dr->post_proj};
       float* o1[1] = {gp};

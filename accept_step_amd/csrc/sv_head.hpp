@@ -100,7 +100,14 @@ struct HeadArgs {
   float eps;
   int residual;               // the products are added into out (out[m, n] += ...)
   float* ss_out;              // residual: [gridDim.x, M] sums of squares of the updated rows per workgroup
+  // write_out == 2: SwiGLU pairing (two segments of equal N, gate then up): the wavefront
+  // that streams gate tile t streams up tile t right after it, and the epilogue writes
+  // hout[m, n] = bf16(SiLU(gate) * up) instead of the two products
+  bf16_t* hout;               // [M, N_0]
 };
+// Launches cost more once the explicit arguments pass 368 bytes (+0.2-0.3 us each
+// measured at 376: the MTP draft round 758 -> 775 us, the full-model step +0.03 ms).
+static_assert(sizeof(HeadArgs) <= 368, "k_head's arguments past the cheap launch size");
 
 // Bytes of dynamic LDS: the M rows of X plus one zero row that the lanes of padding
 // rows (past M in the last column block) read, each row padded by 16*S bytes so the
@@ -121,6 +128,35 @@ __device__ __forceinline__ TileRef head_tile(const HeadArgs& a, int tile, int TR
   t.N = pick(seg, a.N[0], a.N[1], a.N[2]);
   t.v0 = (tile - pick(seg, 0, a.tile_end[0], a.tile_end[1])) * TR;
   return t;
+}
+
+// Paired tiles.  Wavefront ``first`` (= workgroup * HEAD_WAVES + wave) takes the gate
+// and the up tile of rows u * span + slot, u = 0, 1, ..., with slot = wave * grid +
+// workgroup: numbered wavefront-major, the last partial round spreads over all
+// workgroups before any takes two (workgroup-major, the first workgroups would each take
+// four while the rest idle).  Its rounds 2u and 2u + 1 are that gate and up tile.
+__device__ __forceinline__ int head_pair_slot(int first, int grid) {
+  return (first % HEAD_WAVES) * grid + first / HEAD_WAVES;
+}
+// Tile ``tile`` = round * span + first (span = grid * HEAD_WAVES) of a paired product.
+__device__ __forceinline__ TileRef head_tile_pair(const HeadArgs& a, int tile, int TR) {
+  const int span = int(gridDim.x) * HEAD_WAVES, i = tile / span, f = tile - i * span;
+  TileRef t;
+  t.W = (i & 1) ? a.W[1] : a.W[0];
+  t.out = (i & 1) ? a.out[1] : a.out[0];
+  t.N = a.N[0];
+  t.v0 = ((i >> 1) * span + head_pair_slot(f, gridDim.x)) * TR;
+  return t;
+}
+
+// Tiles of the wavefront whose first tile is ``first``: paired, two for each gate tile
+// slot, slot + span, ... below the segment's tile count.
+__device__ __forceinline__ int head_tiles_of(const HeadArgs& a, int first, int span, int ntiles, bool pair) {
+  if (pair) {
+    const int P = a.tile_end[0], slot = head_pair_slot(first, span / HEAD_WAVES);
+    return slot < P ? 2 * ((P - 1 - slot) / span + 1) : 0;
+  }
+  return first < ntiles ? (ntiles - 1 - first) / span + 1 : 0;
 }
 
 // Global tile of local tile ``lt`` of workgroup ``wg``: wavefront lt % 4, its (lt / 4)-th tile.
@@ -151,13 +187,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const bf16_t* W, int
 
 // Work item k of a wavefront whose tiles are first, first + tstride, ...: the segment's
 // descriptor and the item's offset.  The lane adds (r / S) * K * 2 + its piece offset.
-template <int S>
-__device__ __forceinline__ HeadItem head_item(const HeadArgs& a, int k, int first, int tstride, int item_k) {
+// Work item k of the wavefront whose tiles are round * tstride + slot (round = i >> psh
+// for its i-th tile): plain (psh = 0, slot = first), tile i is round i over all segments;
+// paired (psh = 1, slot = head_pair_slot), tiles 2u and 2u + 1 are the gate and the up
+// tile of round u.  Selects only: a branch inside the stream loop makes the compiler keep
+// fewer loads in flight across it (every product measured 15-25 % slower).
+template <int S, bool PAIRABLE>
+__device__ __forceinline__ HeadItem head_item(const HeadArgs& a, int k, int slot, int psh, int tstride, int item_k) {
   const int i = k / a.gpt, gg = k - i * a.gpt;
-  const TileRef tr = head_tile(a, first + i * tstride, 16 / S);
+  if constexpr (!PAIRABLE) {
+    const TileRef tr = head_tile(a, slot + i * tstride, 16 / S);
+    HeadItem it;
+    it.rs = head_rsrc(tr.W, tr.N, a.K);
+    it.soff = __builtin_amdgcn_readfirstlane((unsigned(tr.v0) * unsigned(a.K) + unsigned(gg * item_k)) * 2u);
+    return it;
+  }
+  const int tile = (i >> psh) * tstride + slot;
+  const int segn = (a.nseg > 1 && tile >= a.tile_end[0]) ? ((a.nseg > 2 && tile >= a.tile_end[1]) ? 2 : 1) : 0;
+  const int seg = psh ? (i & 1) : segn;
+  const int t0 = tile - (psh ? 0 : pick(segn, 0, a.tile_end[0], a.tile_end[1]));
   HeadItem it;
-  it.rs = head_rsrc(tr.W, tr.N, a.K);
-  it.soff = __builtin_amdgcn_readfirstlane((unsigned(tr.v0) * unsigned(a.K) + unsigned(gg * item_k)) * 2u);
+  it.rs = head_rsrc(pick(seg, a.W[0], a.W[1], a.W[2]), pick(seg, a.N[0], a.N[1], a.N[2]), a.K);
+  it.soff = __builtin_amdgcn_readfirstlane((unsigned(t0 * (16 / S)) * unsigned(a.K) + unsigned(gg * item_k)) * 2u);
   return it;
 }
 
@@ -179,16 +230,16 @@ __device__ __forceinline__ void head_load(const HeadItem& it, unsigned voff, u32
 // the wavefront has fewer; those registers are never used), so no branch hides them from
 // the compiler's count of outstanding loads.
 struct HeadFirst {
-  int items, first, tstride, item_k, ntiles;
+  int items, slot, psh, tstride, item_k, ntiles;
   unsigned voff;
 };
 
-template <int S, int NB, int GRP>
+template <int S, int NB, int GRP, bool PAIRABLE>
 __device__ __forceinline__ void head_first_loads(const HeadArgs& a, const HeadFirst& hf, u32x4 (&bufA)[GRP],
                                                  u32x4 (&bufB)[GRP]) {
-  const int f = min(hf.first, hf.ntiles - 1), k1 = hf.items > 1 ? 1 : 0;
-  head_load<S, NB, GRP>(head_item<S>(a, 0, f, hf.tstride, hf.item_k), hf.voff, bufA);
-  head_load<S, NB, GRP>(head_item<S>(a, k1, f, hf.tstride, hf.item_k), hf.voff, bufB);
+  const int f = min(hf.slot, (hf.psh ? a.tile_end[0] : hf.ntiles) - 1), k1 = hf.items > 1 ? 1 : 0;
+  head_load<S, NB, GRP>(head_item<S, PAIRABLE>(a, 0, f, hf.psh, hf.tstride, hf.item_k), hf.voff, bufA);
+  head_load<S, NB, GRP>(head_item<S, PAIRABLE>(a, k1, f, hf.psh, hf.tstride, hf.item_k), hf.voff, bufB);
 }
 
 template <int S, int NB, int GRP>
@@ -467,7 +518,7 @@ __device__ __forceinline__ void head_norm_convert(const HeadArgs& a, int t0, int
 // before the stream's first work items (HeadFirst): vector loads complete in issue
 // order, so staging loads requested after the weights would wait for them, HBM reads
 // queued behind the whole chip's stream.
-template <int S, int NB, int GRP>
+template <int S, int NB, int GRP, bool PAIRABLE>
 __device__ __forceinline__ void head_stage_norm(const HeadArgs& a, bf16_t* sX, int ld, int Kp, const HeadFirst& hf,
                                                 u32x4 (&bufA)[GRP], u32x4 (&bufB)[GRP]) {
   __shared__ float s_scale[HEAD_MAX_ROWS];
@@ -490,7 +541,7 @@ __device__ __forceinline__ void head_stage_norm(const HeadArgs& a, bf16_t* sX, i
 #pragma unroll
     for (int m = 0; m < MR; ++m) part[m] = a.ss_in[size_t(pc) * M + min(m, M - 1)];
   }
-  head_first_loads<S, NB, GRP>(a, hf, bufA, bufB);
+  head_first_loads<S, NB, GRP, PAIRABLE>(a, hf, bufA, bufB);
   for (int p0 = int(blockDim.x); p0 < a.ss_parts; p0 += int(blockDim.x)) {
     const int p = p0 + int(threadIdx.x);
 #pragma unroll
@@ -625,7 +676,9 @@ __device__ __forceinline__ unsigned long long wave_allmax_u64(unsigned long long
   return max_u64(max_u64(readlane_u64(k, 0), readlane_u64(k, 16)), max_u64(readlane_u64(k, 32), readlane_u64(k, 48)));
 }
 
-template <int S, int NB, int GRP>
+// PAIRABLE: the instantiation that honours write_out == 2 (the decoder's products use it for
+// all their launches, paired or not, so that they share one kernel's code).
+template <int S, int NB, int GRP, bool PAIRABLE = false>
 __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_head(HeadArgs a) {
   constexpr int TR = 16 / S, CPB = 16 / S;
   constexpr int NW = HEAD_WAVES;
@@ -661,7 +714,10 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   // Vector loads complete in issue order, so loads requested after the weights would wait
   // for them; this way the stream starts two items deep while X is converted and stored.
   const int first = blockIdx.x * HEAD_WAVES + wave, tstride = gridDim.x * HEAD_WAVES;
-  const int n_my = first < ntiles ? (ntiles - 1 - first) / tstride + 1 : 0;
+  const bool pair = PAIRABLE && a.write_out == 2;
+  const int n_my = head_tiles_of(a, first, tstride, ntiles, pair);
+  const int psh = pair ? 1 : 0;
+  const int slot = psh ? head_pair_slot(first, gridDim.x) : first;
   const int items = n_my * a.gpt;
   const int item_k = 32 * S * GRP;                // elements of a row per work item
   const int lane_ofs = 8 * (S * g + r % S);       // element offset of the lane's piece in step 0
@@ -678,7 +734,7 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
     my_bad = ac.invalid ? ac.invalid[threadIdx.x] : 0;
   }
   if (sample && threadIdx.x == 0) my_ep = load_coherent(a.counter + CNT_EPOCH);
-  const HeadFirst hf{items, first, tstride, item_k, ntiles,
+  const HeadFirst hf{items, slot, psh, tstride, item_k, ntiles,
                      (unsigned(r / S) * unsigned(a.K) + unsigned(lane_ofs)) * 2u};   // the lane's W bytes
   const unsigned voff = hf.voff;
   u32x4 bufA[GRP], bufB[GRP];
@@ -686,14 +742,14 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   // stage all of X (zeros from K to Kp) and the zero row, HEAD_STAGE pieces per thread
   // in flight at a time (one load and store at a time would chain the L2 round trips)
   if (a.Xf) {
-    head_stage_norm<S, NB, GRP>(a, sX, ld, Kp, hf, bufA, bufB);
+    head_stage_norm<S, NB, GRP, PAIRABLE>(a, sX, ld, Kp, hf, bufA, bufB);
   } else {
     const int pieces = Kp / 8, kpieces = a.K / 8, total = (M + 1) * pieces;
     // the first round's loads, then the stream's first work items, then its stores; the
     // later rounds (long or many rows) after
     u32x4 v[HEAD_STAGE];
     head_plain_issue(a, threadIdx.x, pieces, kpieces, total, v);
-    head_first_loads<S, NB, GRP>(a, hf, bufA, bufB);
+    head_first_loads<S, NB, GRP, PAIRABLE>(a, hf, bufA, bufB);
     head_plain_store(a, threadIdx.x, pieces, kpieces, total, v, sX, ld);
     for (int base = HEAD_STAGE * int(blockDim.x); base < total; base += HEAD_STAGE * int(blockDim.x)) {
       head_plain_issue(a, base + int(threadIdx.x), pieces, kpieces, total, v);
@@ -753,13 +809,13 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
     // items k (bufA) and k + 1 (bufB) are in flight at the top of each iteration
     for (; k + 3 < items; k += 2) {
       SV_HEAD_ITEM(k, bufA)
-      head_load<S, NB, GRP>(head_item<S>(a, k + 2, first, tstride, item_k), voff, bufA);
+      head_load<S, NB, GRP>(head_item<S, PAIRABLE>(a, k + 2, slot, psh, tstride, item_k), voff, bufA);
       SV_HEAD_ITEM(k + 1, bufB)
-      head_load<S, NB, GRP>(head_item<S>(a, k + 3, first, tstride, item_k), voff, bufB);
+      head_load<S, NB, GRP>(head_item<S, PAIRABLE>(a, k + 3, slot, psh, tstride, item_k), voff, bufB);
     }
     if (k + 2 < items) {
       SV_HEAD_ITEM(k, bufA)
-      head_load<S, NB, GRP>(head_item<S>(a, k + 2, first, tstride, item_k), voff, bufA);
+      head_load<S, NB, GRP>(head_item<S, PAIRABLE>(a, k + 2, slot, psh, tstride, item_k), voff, bufA);
       SV_HEAD_ITEM(k + 1, bufB)
       SV_HEAD_ITEM(k + 2, bufA)
     } else if (k + 1 < items) {
@@ -798,7 +854,23 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   // ---- write the products (residual: add them into out, and leave each tile's sum of
   // squares of the updated entries in its first LDS slot, summed per row below in
   // tile order)
-  if (a.write_out) {
+  if (pair) {
+    // gate tile of round 2u (local tile lt) and up tile of round 2u + 1 (lt + HEAD_WAVES):
+    // the same rows, the same formula as the separate SwiGLU kernel
+    for (int idx = threadIdx.x; idx < M * tpw; idx += blockDim.x) {
+      const int m = idx / tpw, lt = idx - m * tpw;
+      const int i = lt / HEAD_WAVES, f = blockIdx.x * HEAD_WAVES + lt % HEAD_WAVES;
+      if ((i & 1) || 2 * (i >> 1) >= head_tiles_of(a, f, gridDim.x * HEAD_WAVES, ntiles, true)) continue;
+      const TileRef tr = head_tile_pair(a, head_global_tile(blockIdx.x, lt, gridDim.x), TR);
+      const float* gs = sL + m * nloc + lt * TR;
+      const float* us = gs + HEAD_WAVES * TR;
+      bf16_t* dst = a.hout + size_t(m) * tr.N + tr.v0;
+      for (int w = 0; w < TR && tr.v0 + w < tr.N; ++w) {
+        const float gv = gs[w];
+        dst[w] = f32_to_bf16(gv / (1.0f + expf(-gv)) * us[w]);
+      }
+    }
+  } else if (a.write_out) {
     const bool res = a.residual != 0;
     for (int idx = threadIdx.x; idx < M * tpw; idx += blockDim.x) {
       const int m = idx / tpw, lt = idx - m * tpw;

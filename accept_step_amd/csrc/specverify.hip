@@ -788,7 +788,7 @@ sv_status run_decoder(const sv_model* m, const Shape& sh, const int* tokens, con
   // key splits).
   auto attention = [&](int l) -> sv_status {
     const int NQ = att_query_groups(sh.G1), QS = att_query_slots(sh.G1);
-    const dim3 ag(L.S, H, sh.B * NQ);
+    const dim3 ag(H, sh.B * NQ, L.S);
     const float qscale = scale * 1.4426950408889634f;   // scores in base-2 units
 #define SV_ATTN(HDv, QGv) hipLaunchKernelGGL((k_attn<HDv, QGv>), ag, dim3(256), 0, s, q, kc, vc, kv->len, invalid, attp, \
                                              att, attcnt, da, l, L.S, NQ, qscale, rope, k, v)
@@ -1609,10 +1609,10 @@ sv_status mtp_draft(const sv_drafter* dr, const sv_shared_kv* kv, int32_t B, int
       const bf16_t* vc = static_cast<const bf16_t*>(kv->v[l]);
       const float2* rk = rope + size_t(k) * B * (hd / 2);   // RoPE applied while the queries are staged
       if (hd == 128)
-        hipLaunchKernelGGL((k_attn<128, 2>), dim3(S, nh, B), dim3(256), 0, s, qb, kc, vc, lenq, invalid, attp, att,
+        hipLaunchKernelGGL((k_attn<128, 2>), dim3(nh, B, S), dim3(256), 0, s, qb, kc, vc, lenq, invalid, attp, att,
                            cnt, da, 0, S, 1, qscale, rk);
       else
-        hipLaunchKernelGGL((k_attn<64, 2>), dim3(S, nh, B), dim3(256), 0, s, qb, kc, vc, lenq, invalid, attp, att,
+        hipLaunchKernelGGL((k_attn<64, 2>), dim3(nh, B, S), dim3(256), 0, s, qb, kc, vc, lenq, invalid, attp, att,
                            cnt, da, 0, S, 1, qscale, rk);
       {
         const void* w1[1] = {w[2]};
@@ -1675,10 +1675,10 @@ sv_status mtp_draft(const sv_drafter* dr, const sv_shared_kv* kv, int32_t B, int
       const bf16_t* kc = static_cast<const bf16_t*>(kv->k[l]);
       const bf16_t* vc = static_cast<const bf16_t*>(kv->v[l]);
       if (hd == 128)
-        hipLaunchKernelGGL((k_attn<128, 2>), dim3(S, nh, B), dim3(256), 0, s, qb, kc, vc, lenq, invalid, attp, att,
+        hipLaunchKernelGGL((k_attn<128, 2>), dim3(nh, B, S), dim3(256), 0, s, qb, kc, vc, lenq, invalid, attp, att,
                            cnt, da, 0, S, 1, qscale);
       else
-        hipLaunchKernelGGL((k_attn<64, 2>), dim3(S, nh, B), dim3(256), 0, s, qb, kc, vc, lenq, invalid, attp, att,
+        hipLaunchKernelGGL((k_attn<64, 2>), dim3(nh, B, S), dim3(256), 0, s, qb, kc, vc, lenq, invalid, attp, att,
                            cnt, da, 0, S, 1, qscale);
       {
         const void* w1[1] = {w[2]};

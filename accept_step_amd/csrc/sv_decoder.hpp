@@ -147,7 +147,11 @@ __device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) 
 }
 
 // Split-K decode attention of the new positions, with the merge of the splits.
-// grid (S, H, B * NQ): workgroup (s, h, b, g) handles query slots [g*QG, g*QG + QG)
+// grid (H, B * NQ, S), the split outermost so that the workgroups dispatched first
+// hold the most keys (split s takes blocks s, s + S, ...; a grid larger than the chip
+// then doubles up the light ones on a CU, not two full ones), and a head's splits sit
+// on one XCD (workgroup id % 8 = head % 8 when H is a multiple of 8).
+// Workgroup (s, h, b, g) handles query slots [g*QG, g*QG + QG)
 // (those below G1) of head h and the keys [256 s, 256 s + 256), then every 256 S
 // further, of the len[b] + G1 keys; wavefront w takes 64 keys from 64 w of each such
 // block.  Scores in base-2 units (the queries carry scale * log2 e):
@@ -183,8 +187,8 @@ __global__ __launch_bounds__(256) void k_attn(const float* __restrict__ q, const
   constexpr int LPK = HD / 8;          // lanes per value row in the coalesced value loads
   constexpr int KPI = 64 / LPK;        // value rows per load
   constexpr int NV = HD / 8;           // value loads per 64 keys
-  const int s = blockIdx.x, h = blockIdx.y;
-  const int b = blockIdx.z / NQ, qg = blockIdx.z - b * NQ;
+  const int s = blockIdx.z, h = blockIdx.x;
+  const int b = blockIdx.y / NQ, qg = blockIdx.y - b * NQ;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int G1 = a.G1;
   const int q0 = qg * QG;

@@ -151,11 +151,14 @@ def check_case(c, T, label, tol=2e-2):
 
 
 @pytest.mark.parametrize("T", [0.0, 1.0])
-@pytest.mark.parametrize("hd,B,ff", [(128, 1, 512), (64, 2, 512), (128, 2, 640), (64, 1, 704), (64, 5, 512)])
+@pytest.mark.parametrize("hd,B,ff", [(128, 1, 512), (64, 2, 512), (128, 2, 640), (64, 1, 704), (64, 5, 512),
+                                     (128, 1, 6400), (64, 2, 6400)])
 def test_small_decoder(T, hd, B, ff):
     """d_ff 640 and 704: the down projection's K is not a whole number of work items.
     B = 5 (25 rows): the products exceed the k-split kernel's rows, so the layers run
-    unfused (separate RMSNorm passes, fallback products)."""
+    unfused (separate RMSNorm passes, fallback products).  d_ff 6400 (1600 tile pairs
+    over 1024 wavefronts): the gate/up product pairs its tiles and writes the SwiGLU
+    itself, with a partial last round; at 512-704 it keeps the separate SwiGLU launch."""
     c = workloads.small_decoder_case(n_layers=2, d_model=256, n_heads=256 // hd, head_dim=hd, d_ff=ff, vocab=1000,
                                      cache_len=100, B=B, gamma=4, std=0.05)
     check_case(c, T, f"small hd={hd} B={B} ff={ff}")

@@ -33,7 +33,10 @@ section.  Page titles used in citations:
                   for LLM inference acceleration".
 
 Pin status of each function is recorded in its docstring ("pinned by ...").
-Parity unpinned: the end-to-end logit *values* of the random-init full-model
-configuration (no published values exist); the per-operation formulas it is
-built from are pinned individually.
+The reference decoder is pinned end to end as well: without its bf16 rounding
+points its logits equal those of the Llama implementation in the ``transformers``
+library (float64, CPU) on small random models (tests/test_oracle_decoder_hf.py);
+the rounding points themselves are the GPU's storage points, pinned by the
+per-operation tests.  No published values exist for the random-init full-model
+configuration itself.
 """

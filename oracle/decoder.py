@@ -31,8 +31,9 @@ Pinned by (tests/test_oracle_decoder.py): per-operation closed forms
 scores, attention over one key / identical keys, SiLU values); verifying
 G positions in one pass equals G single-position passes; changing a later
 token leaves earlier slots unchanged; greedy speculative decoding reproduces
-plain greedy autoregressive decoding token for token.  The end-to-end logit
-values of a random model are "parity unpinned" beyond these properties.
+plain greedy autoregressive decoding token for token; and, with ``exact``, the
+end-to-end logits of random small models equal those of the Llama implementation
+in the ``transformers`` library run in float64 (tests/test_oracle_decoder_hf.py).
 """
 from dataclasses import dataclass, field
 from typing import List
@@ -111,13 +112,18 @@ def _w(a):
     return bf16_to_f64(a)
 
 
-def forward(wts: DecoderWeights, tokens, kv: KVCache):
+def forward(wts: DecoderWeights, tokens, kv: KVCache, exact: bool = False):
     """Verify forward over ``tokens`` [B, G] (G = gamma + 1 new positions).
 
     Writes K/V of the G positions into ``kv`` at ``length[b] + i`` and returns
     float64 logits [B, G, vocab].  ``kv.length`` is left unchanged; commit with
     :func:`commit`.
+
+    ``exact``: the same model without the five bf16 rounding points (the new
+    positions' K/V enter the attention in float64; the cache still stores them as
+    bf16), for comparison with other float64 implementations of the architecture.
     """
+    rnd = (lambda a: a) if exact else round_bf16
     tokens = np.asarray(tokens, dtype=np.int64)
     B, G = tokens.shape
     H, hd, d = wts.n_heads, wts.head_dim, wts.d_model
@@ -127,7 +133,7 @@ def forward(wts: DecoderWeights, tokens, kv: KVCache):
     pos = base[:, None] + np.arange(G)[None, :]                       # [B, G]
     x = _w(wts.embed[tokens])                                          # [B, G, d]
     for li, L in enumerate(wts.layers):
-        h = round_bf16(rmsnorm(x, _w(L["attn_norm"]), wts.rms_eps))
+        h = rnd(rmsnorm(x, _w(L["attn_norm"]), wts.rms_eps))
         q = (h @ _w(L["wq"]).T).reshape(B, G, H, hd)
         k = (h @ _w(L["wk"]).T).reshape(B, G, H, hd)
         v = (h @ _w(L["wv"]).T).reshape(B, G, H, hd)
@@ -143,16 +149,19 @@ def forward(wts: DecoderWeights, tokens, kv: KVCache):
             nk = int(base[b]) + G
             kk = bf16_to_f64(kv.k[li, b, :, :nk, :])                  # [H, nk, hd]
             vv = bf16_to_f64(kv.v[li, b, :, :nk, :])
+            if exact:
+                kk[:, int(base[b]):nk] = k[b].transpose(1, 0, 2)
+                vv[:, int(base[b]):nk] = v[b].transpose(1, 0, 2)
             for i in range(G):
                 lim = int(base[b]) + i + 1                             # causal
                 for hh in range(H):
                     o[b, i, hh] = attention(q[b, i, hh][None, :], kk[hh, :lim], vv[hh, :lim])[0]
-        a = round_bf16(o.reshape(B, G, H * hd))
+        a = rnd(o.reshape(B, G, H * hd))
         x = x + a @ _w(L["wo"]).T
-        h2 = round_bf16(rmsnorm(x, _w(L["ffn_norm"]), wts.rms_eps))
-        f = round_bf16(silu(h2 @ _w(L["w_gate"]).T) * (h2 @ _w(L["w_up"]).T))
+        h2 = rnd(rmsnorm(x, _w(L["ffn_norm"]), wts.rms_eps))
+        f = rnd(silu(h2 @ _w(L["w_gate"]).T) * (h2 @ _w(L["w_up"]).T))
         x = x + f @ _w(L["w_down"]).T
-    hf = round_bf16(rmsnorm(x, _w(wts.final_norm), wts.rms_eps))
+    hf = rnd(rmsnorm(x, _w(wts.final_norm), wts.rms_eps))
     return hf @ _w(wts.lm_head).T
 
 

@@ -1346,17 +1346,18 @@ sv_status draft_masked_logits(const sv_masked_head* head, const void* hidden, in
   const void* W1[1] = {head->centroids};
   float* O1[1] = {cl};
   if ((st = run_product(static_cast<const bf16_t*>(hidden), M, d, 1, W1, O1, N1, di, s))) return st;
-  if (top_k <= MASK_FAST_K) {
-    hipLaunchKernelGGL(k_select_topk, dim3(M), dim3(256), 0, s, cl, C, top_k, clusters);
+  const int cs = V / C;
+  const dim3 gg(top_k, (cs + MASK_ROWS_PER_WG - 1) / MASK_ROWS_PER_WG, M);
+  if (top_k <= MASK_FAST_K) {   // the gather's workgroups select the clusters themselves
+    hipLaunchKernelGGL(k_gather_logits<true>, gg, dim3(256), size_t(d) * 4, s, static_cast<const bf16_t*>(head->embed),
+                       static_cast<const bf16_t*>(hidden), clusters, d, cs, top_k, logits, cl, C);
   } else {
     int P = 1;
     while (P < C) P <<= 1;
     hipLaunchKernelGGL(k_select_clusters, dim3(M), dim3(256), 0, s, cl, C, P, top_k, clusters);
+    hipLaunchKernelGGL(k_gather_logits<false>, gg, dim3(256), size_t(d) * 4, s, static_cast<const bf16_t*>(head->embed),
+                       static_cast<const bf16_t*>(hidden), clusters, d, cs, top_k, logits, nullptr, 0);
   }
-  const int cs = V / C;
-  hipLaunchKernelGGL(k_gather_logits, dim3(top_k, (cs + MASK_ROWS_PER_WG - 1) / MASK_ROWS_PER_WG, M), dim3(256),
-                     size_t(d) * 4, s, static_cast<const bf16_t*>(head->embed), static_cast<const bf16_t*>(hidden),
-                     clusters, d, cs, top_k, logits);
   SV_HIP(hipGetLastError());
   return SV_OK;
 }
@@ -1536,9 +1537,9 @@ sv_status mtp_draft(const sv_drafter* dr, const sv_shared_kv* kv, int32_t B, int
       const int n1[1] = {C};
       sv_status r = run_product(g, B, D, 1, w1, o1, n1, di, s);
       if (r) return r;
-      hipLaunchKernelGGL(k_select_topk, dim3(B), dim3(256), 0, s, cl, C, tk, sel);
-      hipLaunchKernelGGL(k_gather_logits, dim3(tk, (cs + MASK_ROWS_PER_WG - 1) / MASK_ROWS_PER_WG, B), dim3(256),
-                         size_t(D) * 4, s, static_cast<const bf16_t*>(dr->embed), g, sel, D, cs, tk, logits);
+      // the gather's workgroups select the kept clusters themselves (tk <= MASK_FAST_K)
+      hipLaunchKernelGGL(k_gather_logits<true>, dim3(tk, (cs + MASK_ROWS_PER_WG - 1) / MASK_ROWS_PER_WG, B), dim3(256),
+                         size_t(D) * 4, s, static_cast<const bf16_t*>(dr->embed), g, sel, D, cs, tk, logits, cl, C);
     } else {
       const void* w1[1] = {dr->embed};
       float* o1[1] = {logits};

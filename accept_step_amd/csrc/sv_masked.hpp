@@ -4,9 +4,10 @@
 // clusters of tokens through a table of one representative embedding per cluster; the
 // top_k clusters are kept and exact logits are computed only for their member tokens.
 // With ordered embeddings cluster c is the contiguous token block [c * cs, (c+1) * cs).
-// Three launches: the cluster scores on the k-split product kernel (sv_head.hpp), the
-// selection below (one workgroup per row), and the gathered product of the kept
-// clusters' rows below.
+// Two launches: the cluster scores on the k-split product kernel (sv_head.hpp), then
+// the gathered product of the kept clusters' rows below, whose workgroups each select
+// their row's kept clusters first (a separate selection launch, one workgroup per row,
+// above MASK_FAST_K kept clusters).
 #pragma once
 
 #include "sv_device.hpp"
@@ -186,46 +187,56 @@ __device__ unsigned long long block_top_keys(SelScratch& S, const unsigned long 
   return r;
 }
 
-// Kept clusters of row blockIdx.x for top_k <= MASK_FAST_K (256 threads): the keys of the
-// C cluster scores through block_top_keys; wavefront 0 writes the ids.
-__global__ __launch_bounds__(256) void k_select_topk(const float* __restrict__ cl, int C, int top_k,
-                                                     int32_t* __restrict__ clusters) {
-  constexpr int PER = MASK_MAX_CLUSTERS / 256;
-  __shared__ SelScratch sel;
-  const int m = blockIdx.x, t = threadIdx.x;
-  float v[PER];
-#pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int c = t + 256 * u;
-    v[u] = c < C ? cl[size_t(m) * C + c] : 0.0f;
-  }
-  sel_prepare(sel);
-  unsigned long long key[PER];
-#pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int c = t + 256 * u;
-    key[u] = c < C ? cluster_key(v[u], c) : 0ull;
-  }
-  const unsigned long long kv = block_top_keys(sel, key, top_k);
-  if (t < top_k) clusters[size_t(m) * top_k + t] = int32_t(0xffffffffu - unsigned(kv));
-}
-
 // Token logits of the kept clusters: workgroup (j, chunk, m) computes rows
 // chunk * 16 .. chunk * 16 + 15 of cluster clusters[m, j] (row r = token c * cs + r):
 // out[m, j * cs + r] = W[c * cs + r] . h[m].  Each group of 16 lanes takes one row, 16
 // bytes per lane per step (256 contiguous bytes of the row), accumulates in float32
 // and sums its 16 lanes with DPP; a wavefront takes four rows.  h is staged in LDS as
 // float32.  Rows past cs read the last row and are not stored.
+// SELECT (top_k <= MASK_FAST_K): every workgroup selects row m's top_k clusters itself
+// from the C cluster scores cl[m, 0..C) (block_top_keys: the same inputs and code in
+// every workgroup, so the same ranking) and takes the j-th; workgroup (0, 0, m) also
+// stores the ranking in clusters[m, 0..top_k).  This replaces a selection launch of
+// its own: the saved launch outweighs the selection repeated per workgroup.
+template <bool SELECT = false>
 __global__ __launch_bounds__(256) void k_gather_logits(const bf16_t* __restrict__ W, const bf16_t* __restrict__ h,
-                                                       const int32_t* __restrict__ clusters, int d, int cs, int top_k,
-                                                       float* __restrict__ out) {
+                                                       int32_t* __restrict__ clusters, int d, int cs, int top_k,
+                                                       float* __restrict__ out, const float* __restrict__ cl = nullptr,
+                                                       int C = 0) {
   extern __shared__ float sh[];
   const int j = blockIdx.x, chunk = blockIdx.y, m = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
-  const int c = __builtin_amdgcn_readfirstlane(clusters[size_t(m) * top_k + j]);
   for (int i = threadIdx.x; i < d; i += blockDim.x) sh[i] = bf16_to_f32(h[size_t(m) * d + i]);
-  __syncthreads();
+  int c;
+  if constexpr (SELECT) {
+    constexpr int PER = MASK_MAX_CLUSTERS / 256;
+    __shared__ SelScratch sel;
+    __shared__ int s_c;
+    const int t = threadIdx.x;
+    float v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int cc = t + 256 * u;
+      v[u] = cc < C ? cl[size_t(m) * C + cc] : 0.0f;
+    }
+    sel_prepare(sel);
+    unsigned long long key[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int cc = t + 256 * u;
+      key[u] = cc < C ? cluster_key(v[u], cc) : 0ull;
+    }
+    const unsigned long long kv = block_top_keys(sel, key, top_k);   // thread t < 64: the t-th largest
+    const int id = int(0xffffffffu - unsigned(kv));
+    if (t == j) s_c = id;
+    if (j == 0 && chunk == 0 && t < top_k) clusters[size_t(m) * top_k + t] = id;
+    __syncthreads();
+    c = __builtin_amdgcn_readfirstlane(s_c);
+  } else {
+    c = __builtin_amdgcn_readfirstlane(clusters[size_t(m) * top_k + j]);
+    __syncthreads();
+  }
   const int steps = (d + 127) / 128;
   {
     const int r = chunk * MASK_ROWS_PER_WG + wave * 4 + g;

@@ -371,6 +371,7 @@ __device__ __forceinline__ bool last_workgroup_2l(unsigned* cnt, int grp_word, i
 }
 
 // Raw bits of q[qrow + vb + e], e < 4 (bf16 zero-extended or float32), clamped to V - 1.
+// (One 8- or 16-byte load where aligned measured no faster: 129.1-130.0 us per step.)
 __device__ __forceinline__ void load_q4(const AcceptArgs& ac, size_t qrow, int vb, unsigned (&o)[4]) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -383,7 +384,6 @@ __device__ __forceinline__ float q_value(const AcceptArgs& ac, unsigned raw) {
   return ac.q_bf16 ? __uint_as_float(raw << 16) : __uint_as_float(raw);
 }
 
-constexpr int HEAD_QPF = 8;   // (row, group) entries of q a thread prefetches for the draw
 constexpr int HEAD_STAGE = 16;   // X pieces per thread in flight while staging
 constexpr int HEAD_STAGE_F = 12; // the same when X is normalised from float32 rows (K = 4096: one round)
 // Vocab index of the first entry of the thread's k-th group of four (or >= V).
@@ -392,31 +392,6 @@ __device__ __forceinline__ int head_group_v(int k, int nloc, int TR) {
   if (j0 >= nloc) return 0x7fffffff;
   const int lt = j0 / TR;
   return head_global_tile(blockIdx.x, lt, gridDim.x) * TR + (j0 - lt * TR);
-}
-
-// The thread's q entries for the residual draw: entry e < npf = (drafted row e / kg,
-// the thread's group e % kg of four).  The loads issue as one batch: every index is
-// clamped into the q array (groups past the slice or past V read a valid word that the
-// draw never uses) and each entry has registers of its own, so none waits for another.
-template <bool BF16>
-__device__ __forceinline__ void head_prefetch_q(const AcceptArgs& ac, unsigned (&qpf)[HEAD_QPF][4], int npf, int kg,
-                                                int nloc, int TR) {
-#pragma unroll
-  for (int e = 0; e < HEAD_QPF; ++e) {
-    qpf[e][0] = qpf[e][1] = qpf[e][2] = qpf[e][3] = 0u;
-    if (e >= npf) continue;
-    const int rowslot = e / kg, k = e - rowslot * kg;
-    const int j0 = 4 * (int(threadIdx.x) + k * int(blockDim.x));
-    const int lt = min(j0, nloc - 4) / TR;
-    const int vb = min(head_global_tile(blockIdx.x, lt, gridDim.x) * TR + (min(j0, nloc - 4) - lt * TR), ac.V - 1);
-    const size_t row = size_t(rowslot) * ac.V;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const size_t idx = row + min(vb + i, ac.V - 1);
-      qpf[e][i] = BF16 ? unsigned(reinterpret_cast<const unsigned short*>(ac.q)[idx])
-                       : __float_as_uint(reinterpret_cast<const float*>(ac.q)[idx]);
-    }
-  }
 }
 
 // Gumbel noise G = -log(-log U) of the four vocab entries vb .. vb+3 at absolute
@@ -776,17 +751,9 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   }
 
   const int kg = (nloc / 4 + int(blockDim.x) - 1) / int(blockDim.x);   // groups of four per thread
-  // sampling: q over this slice for every drafted slot, for the residual draw after the
-  // decision (about gamma rows x 2 bytes x V per step).  Fetched here so the loads have
-  // long completed when the draw needs them: issued after the stream, they would sit in
-  // front of the polls of the hand-off records (a poll waits for every older load).
-  const int npf = sample ? ac.B * ac.gamma * kg : 0;
-  const bool prefetched = npf <= HEAD_QPF;
-  unsigned qpf[HEAD_QPF][4];
-  if (sample && prefetched) {
-    if (ac.q_bf16) head_prefetch_q<true>(ac, qpf, npf, kg, nloc, TR);
-    else head_prefetch_q<false>(ac, qpf, npf, kg, nloc, TR);
-  }
+  // q of the residual draw is read in the draw, for row n only.  Prefetched here for every
+  // drafted row (2 MB a step, issued ahead of the stream), it delayed the stream's first
+  // loads: 131.8-132.0 against 128.7-129.9 us per step.
 
   HeadStats<NB> st;
 #pragma unroll
@@ -1113,16 +1080,7 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
         const int vb = head_group_v(k, nloc, TR);
         if (vb >= ac.V) continue;
         unsigned qr[4] = {0u, 0u, 0u, 0u};
-        if (resid) {
-          if (prefetched) {
-            const int want = (b * ac.gamma + n) * kg + k;
-#pragma unroll
-            for (int e = 0; e < HEAD_QPF; ++e)
-              if (e == want) { qr[0] = qpf[e][0]; qr[1] = qpf[e][1]; qr[2] = qpf[e][2]; qr[3] = qpf[e][3]; }
-          } else {
-            load_q4(ac, (size_t(b) * ac.gamma + n) * ac.V, vb, qr);
-          }
-        }
+        if (resid) load_q4(ac, (size_t(b) * ac.gamma + n) * ac.V, vb, qr);
         float gn[4];
         gumbel4(ac.seed, b, pos, vb, gn);
 #pragma unroll

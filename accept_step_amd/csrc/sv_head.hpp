@@ -683,11 +683,11 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   __shared__ long long s_pos0[HEAD_MAX_ROWS];
   __shared__ unsigned s_ep;                       // HEAD_SAMPLE: this launch's epoch
 
-  // What the prologue waits for is requested before the wavefront's first two work
-  // items: the rule's per-row inputs and the launch epoch here, the first round of X
-  // (and the norm's partial sums) by the staging code, which then requests the two items.
-  // Vector loads complete in issue order, so loads requested after the weights would wait
-  // for them; this way the stream starts two items deep while X is converted and stored.
+  // What the staging waits for is requested before the wavefront's first two work items:
+  // the first round of X (and the norm's partial sums), then the two items, then the
+  // rule's per-row inputs and the launch epoch.  Vector loads complete in issue order, so
+  // loads requested after the weights would wait for them; this way the stream starts two
+  // items deep while X is converted and stored.
   const int first = blockIdx.x * HEAD_WAVES + wave, tstride = gridDim.x * HEAD_WAVES;
   const bool pair = PAIRABLE && a.write_out == 2;
   const int n_my = head_tiles_of(a, first, tstride, ntiles, pair);
@@ -699,16 +699,22 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   int my_draft = -1, my_bad = 0;
   long long my_pos0 = 0, my_pos0_row = 0;        // pos0 of sequence threadIdx.x, of row threadIdx.x's sequence
   unsigned my_ep = 0u;
-  if (rule && threadIdx.x < M) {
-    const int b = threadIdx.x / G1, i = threadIdx.x - b * G1;
-    if (i < ac.gamma) my_draft = ac.draft[size_t(b) * ac.draft_stride + ac.draft_offset + i];
-    if (sample) my_pos0_row = ac.pos0[b];
-  }
-  if (sample && threadIdx.x < ac.B) {
-    my_pos0 = ac.pos0[threadIdx.x];
-    my_bad = ac.invalid ? ac.invalid[threadIdx.x] : 0;
-  }
-  if (sample && threadIdx.x == 0) my_ep = load_coherent(a.counter + CNT_EPOCH);
+  // The rule's inputs, requested after the first round of X and the stream's first two
+  // work items: loads complete in issue order, so the staging waits only for X (the
+  // epoch is a load that bypasses the caches; requested before X, the staging waited for
+  // it) and the stream's later waits find them arrived.
+  auto rule_inputs = [&]() {
+    if (rule && threadIdx.x < M) {
+      const int b = threadIdx.x / G1, i = threadIdx.x - b * G1;
+      if (i < ac.gamma) my_draft = ac.draft[size_t(b) * ac.draft_stride + ac.draft_offset + i];
+      if (sample) my_pos0_row = ac.pos0[b];
+    }
+    if (sample && threadIdx.x < ac.B) {
+      my_pos0 = ac.pos0[threadIdx.x];
+      my_bad = ac.invalid ? ac.invalid[threadIdx.x] : 0;
+    }
+    if (sample && threadIdx.x == 0) my_ep = load_coherent(a.counter + CNT_EPOCH);
+  };
   const HeadFirst hf{items, slot, psh, tstride, item_k, ntiles,
                      (unsigned(r / S) * unsigned(a.K) + unsigned(lane_ofs)) * 2u};   // the lane's W bytes
   const unsigned voff = hf.voff;
@@ -717,14 +723,16 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   // stage all of X (zeros from K to Kp) and the zero row, HEAD_STAGE pieces per thread
   // in flight at a time (one load and store at a time would chain the L2 round trips)
   if (a.Xf) {
+    rule_inputs();
     head_stage_norm<S, NB, GRP, PAIRABLE>(a, sX, ld, Kp, hf, bufA, bufB);
   } else {
     const int pieces = Kp / 8, kpieces = a.K / 8, total = (M + 1) * pieces;
-    // the first round's loads, then the stream's first work items, then its stores; the
-    // later rounds (long or many rows) after
+    // the first round's loads, then the stream's first work items and the rule's inputs,
+    // then its stores; the later rounds (long or many rows) after
     u32x4 v[HEAD_STAGE];
     head_plain_issue(a, threadIdx.x, pieces, kpieces, total, v);
     head_first_loads<S, NB, GRP, PAIRABLE>(a, hf, bufA, bufB);
+    rule_inputs();
     head_plain_store(a, threadIdx.x, pieces, kpieces, total, v, sX, ld);
     for (int base = HEAD_STAGE * int(blockDim.x); base < total; base += HEAD_STAGE * int(blockDim.x)) {
       head_plain_issue(a, base + int(threadIdx.x), pieces, kpieces, total, v);

@@ -91,6 +91,11 @@ def test_small_and_ragged(V, d, B, gamma, T, top_k, top_p):
     check_token_structure(n.cpu().numpy(), tok.cpu().numpy(), gamma)
     m, f = compare_decisions(n.cpu().numpy(), tok.cpu().numpy(), n0, t0, fl, f"V={V} k={top_k} p={top_p}")
     log(f"[filtered] n={n.cpu().numpy().tolist()} mismatched {m} flagged {f}")
+    # the same logits given as logits input (the chunked selection over the logits
+    # instead of the product's per-workgroup candidates) decide identically
+    n2, tok2 = run(sv.logits_model(V), c, B, gamma, kind=sv.SV_IN_LOGITS, inp=logits)
+    torch.cuda.synchronize()
+    assert torch.equal(n, n2) and torch.equal(tok, tok2)
     # every emitted token lies in the kept set of its slot
     p32, kept, _ = rules.filtered_probs(rules.f32_logits(c["ref"]), T, top_k, top_p)
     nh, th = n.cpu().numpy(), tok.cpu().numpy()
@@ -172,3 +177,44 @@ def test_ties_at_the_top_k_cut(V, top_k):
         assert tok[b, :n[b]].tolist() == draft[b, :n[b]].tolist()
         assert kept[b, n[b], tok[b, n[b]]]
     log(f"[filtered ties] V={V} top_k={top_k} accepted drafts {int(n.sum())} of {B * gamma}")
+
+
+@pytest.mark.parametrize("V,top_k,seed", [(10000, 64, 0), (10000, 7, 1), (4096, 64, 2), (3001, 33, 3)])
+def test_ties_at_the_top_k_cut_hidden_input(V, top_k, seed):
+    """The same exact-tie check through the LM-head product, whose workgroups keep their
+    own top_k per row: one-hot hidden states pick an integer-valued column of W, so the
+    logits are those integers exactly and many tie at the cut, within and across the
+    workgroups' shares of the vocabulary.  n must equal the oracle's exactly."""
+    B, gamma, T, d = 4, 4, 4.0, 32
+    G1 = gamma + 1
+    rng = np.random.default_rng(1000 + seed)
+    cols = np.floor(rng.standard_normal((V, d)) * 3.0).astype(np.float32)     # bf16-exact integers
+    h = np.zeros((B, G1, d), dtype=np.float32)
+    for b in range(B):
+        for i in range(G1):
+            h[b, i, (b * G1 + i + seed) % d] = 1.0
+    l32 = np.einsum("bgd,vd->bgv", h, cols).astype(np.float32)                 # exact: one nonzero term
+    draft = np.empty((B, gamma), dtype=np.int32)
+    for b in range(B):
+        for i in range(gamma):
+            row = l32[b, i].astype(np.float64)
+            order = np.lexsort((np.arange(V), -row))
+            cut = row[order[top_k - 1]]
+            tied = np.nonzero(row == cut)[0]
+            draft[b, i] = tied[rng.integers(len(tied))]
+    q = np.full((B, gamma, V), 1e-7, dtype=np.float32)
+    pos0 = rng.integers(0, 1000, B).astype(np.int64)
+    model = sv.lm_head_model(dev_bf16(workloads.to_bf16_bits(cols)))
+    logits = torch.empty((B, G1, V), dtype=torch.float32, device="cuda")
+    n, tok = sv.spec_verify_sample_filtered(model, sv.SV_IN_HIDDEN, dev_bf16(workloads.to_bf16_bits(h)), B, gamma,
+                                            dev(draft), dev(q), T, top_k, 1.0, 99, dev(pos0), logits_out=logits)
+    torch.cuda.synchronize()
+    assert np.array_equal(logits.cpu().numpy(), l32)
+    n, tok = n.cpu().numpy(), tok.cpu().numpy()
+    n0, t0, _ = rules.sample_rule_filtered(l32, draft, q.astype(np.float64), T, top_k, 1.0, 99, pos0)
+    assert n.tolist() == n0.tolist()
+    _, kept, _ = rules.filtered_probs(l32, T, top_k, 1.0)
+    for b in range(B):
+        assert tok[b, :n[b]].tolist() == draft[b, :n[b]].tolist()
+        assert kept[b, n[b], tok[b, n[b]]]
+    log(f"[filtered ties, hidden input] V={V} top_k={top_k} accepted drafts {int(n.sum())} of {B * gamma}")

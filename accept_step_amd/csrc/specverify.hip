@@ -325,7 +325,10 @@ void gemm_add_seg(GemmArgs& a, const void* W, float* out, int N) {
 
 // ---------------------------------------------------------------------------
 // k-split product (sv_head.hpp) planning
-constexpr size_t HEAD_STATIC_LDS = 8 * 1024;   // the kernel's static LDS (reductions, acceptance)
+// The k-split kernel's static LDS (reductions, the rule's per-row inputs; 3.7 KB in
+// this build), checked against each instantiation before its first launch: at 8 KB the
+// plan for 12 rows of a 4096-wide head (156.5 KB of X and products) did not fit 160 KB.
+constexpr size_t HEAD_STATIC_LDS = 4 * 1024;
 
 struct HeadPlan {
   bool ok = false;
@@ -432,17 +435,28 @@ void head_add_seg(HeadArgs& a, const void* W, float* out, int N, int TR) {
   a.tile_end[i] = (i ? a.tile_end[i - 1] : 0) + (N + TR - 1) / TR;
 }
 
-// Raise the kernel's dynamic LDS limit to what a launch needs (monotone per kernel).
+// Raise the kernel's dynamic LDS limit to what a launch needs (monotone per kernel); on
+// a kernel's first use, check that its static LDS is within what the plans reserve.
 sv_status head_set_lds(const void* fn, size_t lds) {
   static std::mutex mu;
   static std::vector<std::pair<const void*, size_t>> lds_set;
   std::lock_guard<std::mutex> lk(mu);
-  size_t cur = 64 * 1024;
-  for (auto& e : lds_set) if (e.first == fn) cur = e.second;
+  size_t cur = 0;
+  bool known = false;
+  for (auto& e : lds_set)
+    if (e.first == fn) { cur = e.second; known = true; }
+  if (!known) {
+    hipFuncAttributes fa;
+    SV_HIP(hipFuncGetAttributes(&fa, fn));
+    if (fa.sharedSizeBytes > HEAD_STATIC_LDS)
+      return fail(SV_ERR_UNSUPPORTED, "a streaming kernel uses %zu bytes of static LDS, more than the %zu its plans reserve",
+                  size_t(fa.sharedSizeBytes), HEAD_STATIC_LDS);
+    lds_set.push_back({fn, size_t(64 * 1024)});
+    cur = 64 * 1024;
+  }
   if (lds <= cur) return SV_OK;
   SV_HIP(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)));
-  for (auto& e : lds_set) if (e.first == fn) { e.second = lds; return SV_OK; }
-  lds_set.push_back({fn, lds});
+  for (auto& e : lds_set) if (e.first == fn) e.second = lds;
   return SV_OK;
 }
 

@@ -921,6 +921,15 @@ struct HeadRule {
 
 // Logits of all slots plus (if part != NULL) the row-statistics partials.
 // Returns the number of partials per row in *P.
+// The acceptance as a launch of its own (after the wide product, or before the
+// two-launch sampler): a wavefront per row of a sequence.
+sv_status launch_accept(const AcceptArgs& a, hipStream_t s) {
+  const int waves = std::min(a.gamma + 1, 16);   // gamma <= 15
+  hipLaunchKernelGGL(k_accept, dim3(a.B), dim3(64 * std::max(waves, 4)), 0, s, a);
+  SV_HIP(hipGetLastError());
+  return SV_OK;
+}
+
 // With ``acc`` non-null, the bf16 LM-head product records each slot's draft-token
 // logit; with ``fuse`` as well, its last workgroup runs the acceptance for all
 // sequences.  With ``rule`` non-null the k-split kernel runs the rule when it fits
@@ -1014,8 +1023,7 @@ sv_status run_logits(const sv_model* m, const Shape& sh, const void* input, cons
       AcceptArgs aa = *acc;
       aa.P = wp.n_tiles;
       aa.xlogit = w.xlogit;
-      hipLaunchKernelGGL(k_accept, dim3(aa.B), dim3(256), 0, s, aa);
-      SV_HIP(hipGetLastError());
+      if ((st = launch_accept(aa, s))) return st;
       if (rule) rule->accepted = true;
     }
     return SV_OK;
@@ -1152,8 +1160,7 @@ sv_status verify_common(const sv_model* m, sv_input_kind kind, const void* input
   TimeScope ts(s, 2);
   if (!fuse && !rule.accepted) {
     aa.P = P;
-    hipLaunchKernelGGL(k_accept, dim3(sh.B), dim3(256), 0, s, aa);
-    SV_HIP(hipGetLastError());
+    if ((st = launch_accept(aa, s))) return st;
   }
   if (!sample) return finish();
   SampleArgs sa;

@@ -191,8 +191,10 @@ __device__ __forceinline__ void accept_block(const AcceptArgs& a, int b0, int nb
   }
 }
 
-// One workgroup per sequence.
-__global__ __launch_bounds__(256) void k_accept(AcceptArgs a) { accept_block(a, blockIdx.x, 1); }
+// The acceptance as a launch of its own: one workgroup per sequence with a wavefront
+// per row of it (at least four), so that every row's partials are merged at once (the
+// same merge order, so the same bits, as four wavefronts taking the rows in turn).
+__global__ __launch_bounds__(1024) void k_accept(AcceptArgs a) { accept_block(a, blockIdx.x, 1); }
 
 // Ticket of the calling workgroup on a one-shot counter.  Every thread first waits
 // for its own stores to complete (the data handed over was written with

@@ -22,7 +22,9 @@ timed loop, so launch gaps are included), against the 8 TB/s HBM peak.
 ``config`` also carries:
 - the acceptance per slot and the mean committed tokens of the timed steps;
 - the greedy rule (T = 0) on the same table;
-- the d = 4096 head's B = 1, gamma = 4 point.
+- the d = 4096 head's B = 1, gamma = 4 point;
+- the settle phase: before tuning and timing, the sampling step runs untimed for
+  --settle-seconds (5 s by default), since the device's clocks ramp with load.
 ``cpu_baseline`` times the CPU oracle (float64 numpy) on a bounded sample of
 the same workload: three warm-up steps, then the median of the timed ones.  It
 reports the core counts, a spot check of the oracle against the GPU's decisions,
@@ -49,6 +51,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-seconds", type=float, default=5.0,
+                    help="large-vocab: run the sampling step untimed for this long before the tuning, the "
+                         "warm-up and the timed region (the device's clocks ramp with load)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB five times (a plain copy kernel of known "
@@ -125,6 +130,22 @@ def main():
     t_out = torch.empty((K, B, gamma + 1), dtype=torch.int32, device=dev)
     ws = sv.Workspace()
     seed = cases[0].seed
+
+    # ---- settle.  The device's clocks follow its load: after minutes of light work (a
+    # test run) the first seconds of this step ran about 3.5 % slower (133.3, 131.7, then
+    # 128.6 us per launch at two-second intervals, steady after), while a device that
+    # had been idle ran at full speed at once.  The same sampling step therefore runs
+    # untimed for --settle-seconds before the tuning, the warm-up and the timed region.
+    settle_steps = 0
+    t_settle = time.perf_counter() + max(args.settle_seconds, 0.0)
+    while time.perf_counter() < t_settle:
+        for _ in range(50):
+            h, dr, q = sets[settle_steps % N_SETS]
+            sv.spec_verify_sample(model, sv.SV_IN_HIDDEN, h, B, gamma, dr, q, T, seed,
+                                  pos_all[settle_steps % len(pos_all)], ws=ws)
+            settle_steps += 1
+        torch.cuda.synchronize()
+
     # the fused step's load grouping for this device (a setup call; same bits either way)
     tuned = sv.tune_verify(model, B, gamma)
 
@@ -233,6 +254,7 @@ def main():
                    "step_hbm_gbs": round(algo_bytes / (elapsed / K) / 1e9, 1),
                    "step_frac_of_peak": round(algo_bytes / (elapsed / K) / 1e9 / HBM_PEAK_GBS, 4),
                    "fused_step_item_size": tuned,
+                   "settle": {"seconds": args.settle_seconds, "untimed_steps": settle_steps},
                    "acceptance_per_slot": [round(a_, 4) for a_ in alpha],
                    "mean_committed_per_step": round(float((nn + 1).mean()), 4),
                    "greedy_T0": {"us_per_step": round(us0, 2), "verified_tokens_per_s": round(

@@ -52,8 +52,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--settle-seconds", type=float, default=5.0,
-                    help="large-vocab: run the sampling step untimed for this long before the tuning, the "
-                         "warm-up and the timed region (the device's clocks ramp with load)")
+                    help="run the workload's step untimed for this long before the tuning, the warm-up and "
+                         "the timed region (the device's clocks ramp with load; sweep: before its first point)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB five times (a plain copy kernel of known "
@@ -323,6 +323,8 @@ def sweep(args, torch, sv):
             def step(i, out=None):
                 return sv.spec_verify_sample(model, sv.SV_IN_HIDDEN, h, B, gamma, draft, q, T, 77, pos[i], out=out,
                                              ws=ws)
+            if not points:          # the first point brings the clocks up; the rest follow under load
+                settled = settle(torch, lambda i: step(i % K), args.settle_seconds)
             for i in range(3):
                 step(i)
             torch.cuda.synchronize()
@@ -357,6 +359,7 @@ def sweep(args, torch, sv):
                    "points": points,
                    "furthest_from_its_roof": {k_: worst[k_] for k_ in ("B", "gamma", "M")}},
     }
+    out["config"]["settle"] = {"seconds": args.settle_seconds, "untimed_calls": settled}
     print(json.dumps(out), flush=True)
 
 
@@ -404,6 +407,7 @@ def full_model(args, torch, sv):
         return sv.spec_verify_sample(model, sv.SV_IN_TOKENS, tokens, B, gamma, None, q, T, 0x5EED0005, pos0, kv=kv,
                                      out=out, ws=ws)
 
+    settled = settle(torch, lambda i: step(None), args.settle_seconds)
     for _ in range(Wm):
         step(None)
     torch.cuda.synchronize()
@@ -451,6 +455,7 @@ def full_model(args, torch, sv):
                    "bytes_params": params_bytes, "gbs_params": round(params_bytes / (ms * 1e-3) / 1e9, 1),
                    "decoder_ms": round(dec_ms / max(dec_n, 1), 4), "lm_head_step_ms": round(head_ms / max(head_n, 1), 4)},
     }
+    out["config"]["settle"] = {"seconds": args.settle_seconds, "untimed_calls": settled}
     print(json.dumps(out), flush=True)
 
 
@@ -474,6 +479,8 @@ def masked_head(args, torch, sv, workloads):
     logits = torch.empty((M, top_k * cs), dtype=torch.float32, device=dev)
     ws = sv.Workspace()
     K, Wm = args.steps, args.warmup
+    settled = settle(torch, lambda i: sv.draft_masked_logits(head, hs[i % 8], top_k, clusters=sel, logits=logits,
+                                                             ws=ws), args.settle_seconds)
     for i in range(Wm):
         sv.draft_masked_logits(head, hs[i % 8], top_k, clusters=sel, logits=logits, ws=ws)
     torch.cuda.synchronize()
@@ -500,6 +507,7 @@ def masked_head(args, torch, sv, workloads):
                    "frac_of_peak": round(algo / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                    "full_head_bytes": V * d * 2, "full_head_us_at_peak": round(V * d * 2 / (HBM_PEAK_GBS * 1e3), 2)},
     }
+    out["config"]["settle"] = {"seconds": args.settle_seconds, "untimed_calls": settled}
     print(json.dumps(out), flush=True)
 
 
@@ -537,6 +545,7 @@ def filtered(args, torch, sv, workloads):
         return sv.spec_verify_sample_filtered(model, sv.SV_IN_HIDDEN, h, B, gamma, dr, q, T, top_k, top_p,
                                               cases[0].seed, p0, out=out, ws=ws)
 
+    settled = settle(torch, lambda i: step(i % K), args.settle_seconds)
     for i in range(Wm):
         step(i)
     torch.cuda.synchronize()
@@ -565,6 +574,7 @@ def filtered(args, torch, sv, workloads):
                    "step_hbm_gbs": round(algo / (us * 1e-6) / 1e9, 1),
                    "step_frac_of_peak": round(algo / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
     }
+    out["config"]["settle"] = {"seconds": args.settle_seconds, "untimed_calls": settled}
     print(json.dumps(out), flush=True)
 
 
@@ -598,6 +608,8 @@ def drafter(args, torch, sv, workloads):
     q = torch.empty((B, gamma, c.vocab), dtype=torch.bfloat16, device=dev)
     ws = sv.Workspace()
     K, Wm = args.steps, args.warmup
+    settled = settle(torch, lambda i: sv.mtp_draft(dr, kv, tok, hid, gamma, T, 1234 + i, draft=draft, q=q, ws=ws),
+                     args.settle_seconds)
     for i in range(Wm):
         sv.mtp_draft(dr, kv, tok, hid, gamma, T, 1234 + i, draft=draft, q=q, ws=ws)
     torch.cuda.synchronize()
@@ -638,6 +650,7 @@ def drafter(args, torch, sv, workloads):
                    "step_gbs": round(algo / (us / gamma * 1e-6) / 1e9, 1),
                    "step_frac_of_peak": round(algo / (us / gamma * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
     }
+    out["config"]["settle"] = {"seconds": args.settle_seconds, "untimed_calls": settled}
     print(json.dumps(out), flush=True)
 
 
@@ -686,6 +699,7 @@ def rounds_bench(args, torch, sv, workloads):
                               ws=wsv)
         sv.round_update_gamma(n_out, gamma_b, 1, G)
 
+    settled = settle(torch, lambda i: one(i, n_all[0]), args.settle_seconds)
     for i in range(Wm):
         one(i, n_all[0])
     torch.cuda.synchronize()
@@ -714,7 +728,21 @@ def rounds_bench(args, torch, sv, workloads):
                    "committed_tokens": committed, "mean_gamma": round(float(g_all.float().mean().item()), 3),
                    "note": "synthetic target hidden states: acceptance is not meaningful"},
     }
+    out["config"]["settle"] = {"seconds": args.settle_seconds, "untimed_calls": settled}
     print(json.dumps(out), flush=True)
+
+
+def settle(torch, fn, seconds):
+    """Call fn(i) untimed until ``seconds`` have passed, synchronising every eight calls
+    (the device's clocks ramp with load; see main).  Returns the number of calls."""
+    n = 0
+    t_end = time.perf_counter() + max(seconds, 0.0)
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            fn(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
 
 
 def capture_graph(torch, fn):

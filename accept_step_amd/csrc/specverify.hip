@@ -325,9 +325,10 @@ void gemm_add_seg(GemmArgs& a, const void* W, float* out, int N) {
 
 // ---------------------------------------------------------------------------
 // k-split product (sv_head.hpp) planning
-// The k-split kernel's static LDS (reductions, the rule's per-row inputs; 3.7 KB in
-// this build), checked against each instantiation before its first launch: at 8 KB the
-// plan for 12 rows of a 4096-wide head (156.5 KB of X and products) did not fit 160 KB.
+// The k-split kernel's static LDS (reductions, the rule's per-row inputs: 3,760 bytes
+// per instantiation as compiled for gfx950), checked against each instantiation before
+// its first launch.  Reserving 8 KB, the plan for 12 rows of a 4096-wide head (156.5 KB
+// of X and products) did not fit the 160 KB.
 constexpr size_t HEAD_STATIC_LDS = 4 * 1024;
 
 struct HeadPlan {

@@ -343,9 +343,12 @@ int head_nb_max(int S) { return S == 4 ? 5 : 3; }
 
 // Plan of the k-split kernel, one workgroup per CU.  Loads per lane per work item are
 // tried in the order 4, 8, 6 for products (decoder linears, verify_forward) and 6, 4, 8
-// for the LM-head launch that applies the rule (rule = true; 805 MB head, K = 1536:
-// 130.6 us against 137.1 us with items of 4).  only_s != 0 admits that split factor
-// alone.  The plan depends on the shapes and the device only, so the summation order
+// for the LM-head launch that applies the rule (rule = true).  For the latter the better
+// item depends on the device's clocks: on the 805 MB head (K = 1536) items of 6 took
+// 130.6 us against 137.1 with items of 4 on a device just out of idle, and items of 4
+// 124.8 against 128.7 under sustained load; sv_tune_verify measures it per device (a
+// tuned item size, want_grp, wins over this order).  only_s != 0 admits that split
+// factor alone.  The plan depends on the shapes and the device only, so the summation order
 // (and so every logit bit) is the same from call to call.
 HeadPlan plan_head(int M, int K, const int* N, int nseg, const DevInfo& di, bool rule = false, int only_s = 0,
                    int want_grp = 0, bool pair = false) {

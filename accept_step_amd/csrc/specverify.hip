@@ -453,8 +453,8 @@ sv_status head_set_lds(const void* fn, size_t lds) {
     hipFuncAttributes fa;
     SV_HIP(hipFuncGetAttributes(&fa, fn));
     if (fa.sharedSizeBytes > HEAD_STATIC_LDS)
-      return fail(SV_ERR_UNSUPPORTED, "a streaming kernel uses %zu bytes of static LDS, more than the %zu its plans reserve",
-                  size_t(fa.sharedSizeBytes), HEAD_STATIC_LDS);
+      return fail(SV_ERR_UNSUPPORTED, "a streaming kernel uses %zu bytes of static LDS, more than the %zu its "
+                  "plans reserve", size_t(fa.sharedSizeBytes), HEAD_STATIC_LDS);
     lds_set.push_back({fn, size_t(64 * 1024)});
     cur = 64 * 1024;
   }
@@ -923,8 +923,6 @@ struct HeadRule {
   bool accepted = false;  // the acceptance ran (the sampler still has to)
 };
 
-// Logits of all slots plus (if part != NULL) the row-statistics partials.
-// Returns the number of partials per row in *P.
 // The acceptance as a launch of its own (after the wide product, or before the
 // two-launch sampler): a wavefront per row of a sequence.
 sv_status launch_accept(const AcceptArgs& a, hipStream_t s) {
@@ -934,6 +932,8 @@ sv_status launch_accept(const AcceptArgs& a, hipStream_t s) {
   return SV_OK;
 }
 
+// Logits of all slots plus (if part != NULL) the row-statistics partials.
+// Returns the number of partials per row in *P.
 // With ``acc`` non-null, the bf16 LM-head product records each slot's draft-token
 // logit; with ``fuse`` as well, its last workgroup runs the acceptance for all
 // sequences.  With ``rule`` non-null the k-split kernel runs the rule when it fits

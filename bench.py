@@ -205,8 +205,11 @@ def main():
     nn = n_host.numpy().reshape(-1)
     alpha = [float((nn > i).sum() / max((nn >= i).sum(), 1)) for i in range(gamma)]
 
-    # ---- the greedy rule (T = 0) on the same table
+    # ---- the greedy rule (T = 0) on the same table.  The host work above leaves the
+    # device idle for a moment, and without a settle phase the first ~60 greedy launches
+    # ran at 130-153 us before coming down to 117-120
     n_h1, tok_h1 = n_host.clone(), tok_host.copy()
+    settle0 = settle(torch, step0, args.settle_seconds)
     el0, ms0 = timed(step0, K, Wm)
     n0_host = n_out.to(torch.int64).cpu()
     require_valid(n0_host, "large-vocab T=0")
@@ -260,7 +263,8 @@ def main():
                    "settle": {"seconds": args.settle_seconds, "untimed_steps": settle_steps},
                    "acceptance_per_slot": [round(a_, 4) for a_ in alpha],
                    "mean_committed_per_step": round(float((nn + 1).mean()), 4),
-                   "greedy_T0": {"us_per_step": round(us0, 2), "verified_tokens_per_s": round(
+                   "greedy_T0": {"settle_untimed_calls": settle0, "us_per_step": round(us0, 2),
+                                 "verified_tokens_per_s": round(
                        int((n0_host + 1).sum().item()) / el0, 1),
                        "step_hbm_gbs": round(algo0 / (us0 * 1e-6) / 1e9, 1),
                        "step_frac_of_peak": round(algo0 / (us0 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},

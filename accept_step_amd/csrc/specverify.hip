@@ -342,13 +342,13 @@ struct HeadPlan {
 int head_nb_max(int S) { return S == 4 ? 5 : 3; }
 
 // Plan of the k-split kernel, one workgroup per CU.  Loads per lane per work item are
-// tried in the order 4, 8, 6 for products (decoder linears, verify_forward) and 6, 4, 8
+// tried in the order 4, 8, 6 for products (decoder linears, verify_forward) and 4, 6, 8
 // for the LM-head launch that applies the rule (rule = true).  For the latter the better
-// item depends on the device's clocks: on the 805 MB head (K = 1536) items of 6 took
-// 130.6 us against 137.1 with items of 4 on a device just out of idle, and items of 4
-// 124.8 against 128.7 under sustained load; sv_tune_verify measures it per device (a
-// tuned item size, want_grp, wins over this order).  only_s != 0 admits that split
-// factor alone.  The plan depends on the shapes and the device only, so the summation order
+// item depends on the device's clocks: on the 805 MB head (K = 1536) items of 4 took
+// 124.5 us against 128.6 with items of 6 under sustained load (greedy 119.5 against
+// 123.5), and 137.1 against 130.6 on a device just out of idle; sv_tune_verify measures
+// it per device (a tuned item size, want_grp, wins over this order).  only_s != 0 admits
+// that split factor alone.  The plan depends on the shapes and the device only, so the summation order
 // (and so every logit bit) is the same from call to call.
 HeadPlan plan_head(int M, int K, const int* N, int nseg, const DevInfo& di, bool rule = false, int only_s = 0,
                    int want_grp = 0, bool pair = false) {
@@ -357,7 +357,7 @@ HeadPlan plan_head(int M, int K, const int* N, int nseg, const DevInfo& di, bool
   if (pair && (nseg != 2 || N[0] != N[1])) return p;
   for (int i = 0; i < nseg; ++i)    // weights are addressed with 32-bit byte offsets
     if (int64_t(N[i]) * K * 2 > int64_t(0xffffffffLL) - 4096) return p;
-  const int order_product[3] = {4, 8, 6}, order_rule[3] = {6, 4, 8};
+  const int order_product[3] = {4, 8, 6}, order_rule[3] = {4, 6, 8};
   const int* order = rule ? order_rule : order_product;
   for (int S : {4, 2}) {
     if (only_s && S != only_s) continue;

@@ -1374,8 +1374,14 @@ sv_status draft_masked_logits(const sv_masked_head* head, const void* hidden, in
   const int cs = V / C;
   const dim3 gg(top_k, (cs + MASK_ROWS_PER_WG - 1) / MASK_ROWS_PER_WG, M);
   if (top_k <= MASK_FAST_K) {   // the gather's workgroups select the clusters themselves
-    hipLaunchKernelGGL(k_gather_logits<true>, gg, dim3(256), size_t(d) * 4, s, static_cast<const bf16_t*>(head->embed),
-                       static_cast<const bf16_t*>(hidden), clusters, d, cs, top_k, logits, cl, C);
+    if (C <= 2048)
+      hipLaunchKernelGGL((k_gather_logits<true, 8>), gg, dim3(256), size_t(d) * 4, s,
+                         static_cast<const bf16_t*>(head->embed), static_cast<const bf16_t*>(hidden), clusters, d, cs,
+                         top_k, logits, cl, C);
+    else
+      hipLaunchKernelGGL((k_gather_logits<true, 16>), gg, dim3(256), size_t(d) * 4, s,
+                         static_cast<const bf16_t*>(head->embed), static_cast<const bf16_t*>(hidden), clusters, d, cs,
+                         top_k, logits, cl, C);
   } else {
     int P = 1;
     while (P < C) P <<= 1;
@@ -1563,8 +1569,13 @@ sv_status mtp_draft(const sv_drafter* dr, const sv_shared_kv* kv, int32_t B, int
       sv_status r = run_product(g, B, D, 1, w1, o1, n1, di, s);
       if (r) return r;
       // the gather's workgroups select the kept clusters themselves (tk <= MASK_FAST_K)
-      hipLaunchKernelGGL(k_gather_logits<true>, dim3(tk, (cs + MASK_ROWS_PER_WG - 1) / MASK_ROWS_PER_WG, B), dim3(256),
-                         size_t(D) * 4, s, static_cast<const bf16_t*>(dr->embed), g, sel, D, cs, tk, logits, cl, C);
+      const dim3 gg(tk, (cs + MASK_ROWS_PER_WG - 1) / MASK_ROWS_PER_WG, B);
+      if (C <= 2048)
+        hipLaunchKernelGGL((k_gather_logits<true, 8>), gg, dim3(256), size_t(D) * 4, s,
+                           static_cast<const bf16_t*>(dr->embed), g, sel, D, cs, tk, logits, cl, C);
+      else
+        hipLaunchKernelGGL((k_gather_logits<true, 16>), gg, dim3(256), size_t(D) * 4, s,
+                           static_cast<const bf16_t*>(dr->embed), g, sel, D, cs, tk, logits, cl, C);
     } else {
       const void* w1[1] = {dr->embed};
       float* o1[1] = {logits};

@@ -76,10 +76,11 @@ __device__ __forceinline__ void sel_prepare(SelScratch& S) {
   if (t == 0) S.nc = 0u;
 }
 
-// The k (<= MASK_FAST_K) largest of up to MASK_MAX_CLUSTERS distinct 64-bit keys held by
-// a workgroup of 256 threads (16 per thread, in any order; 0 = no entry, smaller than
-// every real key), returned in descending order in wavefront 0's lanes (lane j: the
-// j-th largest, 0 past the number of real keys).  Every thread must call it.
+// The k (<= MASK_FAST_K) largest of up to 256 * PER (at most MASK_MAX_CLUSTERS) distinct
+// 64-bit keys held by a workgroup of 256 threads (PER per thread, in any order; 0 = no
+// entry, smaller than every real key), returned in descending order in wavefront 0's
+// lanes (lane j: the j-th largest, 0 past the number of real keys).  Every thread must
+// call it.
 //   (1) Radix refinement from the top: an LDS histogram of 12 key bits (bits 52..63
 //       first: for a float score the sign, exponent and three mantissa bits) over the
 //       keys that share the prefix fixed so far; a block scan from the top bin finds the
@@ -91,9 +92,9 @@ __device__ __forceinline__ void sel_prepare(SelScratch& S) {
 //       keys) is gathered in LDS (one LDS atomic per wavefront) and ranks itself by
 //       counting the larger ones in 32-key blocks; the key of rank r < k is stored at
 //       position r, which leaves them sorted.
-__device__ unsigned long long block_top_keys(SelScratch& S, const unsigned long long (&key)[MASK_MAX_CLUSTERS / 256],
-                                             int k) {
-  constexpr int PER = MASK_MAX_CLUSTERS / 256;
+template <int PER>
+__device__ unsigned long long block_top_keys(SelScratch& S, const unsigned long long (&key)[PER], int k) {
+  static_assert(PER * 256 <= MASK_MAX_CLUSTERS, "more keys than the selection's candidate bound assumes");
   constexpr int NBINS = 4096, BPT = NBINS / 256;   // bins per thread in the scan
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   uint4* h4 = reinterpret_cast<uint4*>(S.hist + NBINS - BPT * (t + 1));   // bins NBINS-16(t+1) .. NBINS-16t-1
@@ -197,8 +198,10 @@ __device__ unsigned long long block_top_keys(SelScratch& S, const unsigned long 
 // from the C cluster scores cl[m, 0..C) (block_top_keys: the same inputs and code in
 // every workgroup, so the same ranking) and takes the j-th; workgroup (0, 0, m) also
 // stores the ranking in clusters[m, 0..top_k).  This replaces a selection launch of
-// its own: the saved launch outweighs the selection repeated per workgroup.
-template <bool SELECT = false>
+// its own: the saved launch outweighs the selection repeated per workgroup.  SP: cluster
+// scores per thread in the selection (C <= 256 * SP; 8 for the pages' 2048 clusters,
+// half the work per pass of 16).
+template <bool SELECT = false, int SP = MASK_MAX_CLUSTERS / 256>
 __global__ __launch_bounds__(256) void k_gather_logits(const bf16_t* __restrict__ W, const bf16_t* __restrict__ h,
                                                        int32_t* __restrict__ clusters, int d, int cs, int top_k,
                                                        float* __restrict__ out, const float* __restrict__ cl = nullptr,
@@ -210,7 +213,7 @@ __global__ __launch_bounds__(256) void k_gather_logits(const bf16_t* __restrict_
   for (int i = threadIdx.x; i < d; i += blockDim.x) sh[i] = bf16_to_f32(h[size_t(m) * d + i]);
   int c;
   if constexpr (SELECT) {
-    constexpr int PER = MASK_MAX_CLUSTERS / 256;
+    constexpr int PER = SP;
     __shared__ SelScratch sel;
     __shared__ int s_c;
     const int t = threadIdx.x;
